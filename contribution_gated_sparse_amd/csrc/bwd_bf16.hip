@@ -1,0 +1,555 @@
+// MALA backward for bf16 inputs on gfx950 (Algorithm 2; Sec. 2.2 "Offline
+// Sparse Probability"; App. A.1 "Fused backward execution").
+//
+// Three kernels:
+//   1. bwd_prep:  D_q = rowsum(O o dO) in fp32, and clears the decision bits
+//                 and the kept-tile counters.
+//   2. bwd_dkdv:  key-major. A workgroup owns 128 keys of one KV head (4 waves
+//                 x 32 keys) and walks every query head of the group and every
+//                 64-row query tile from the diagonal down the sequence. Each
+//                 wave recomputes S = Q K^T for its 32 keys, applies the offline
+//                 gate (Eq. 4) per 32 x 32 tile against the saved z_q, and for
+//                 kept tiles forms P = exp(S - z), dP = dO V^T, dS = P o (dP - D)
+//                 and accumulates dV += P^T dO and dK += dS^T Q on chip. The
+//                 decisions are written as one bit per tile.
+//   3. bwd_dq:    query-major. A workgroup owns 256 query rows (8 waves x 32);
+//                 each wave reads the decision bits of its rows and, for kept
+//                 tiles only, recomputes S, P, dP, dS and accumulates
+//                 dQ += dS K on chip. No atomics on dQ.
+// Both kernels see the same decisions, so dQ, dK and dV use one support.
+//
+// dS enters the dK and dQ products as a bf16 MFMA operand. By default it is
+// split into hi = bf16(dS) and lo = bf16(dS - hi) and both halves are
+// multiplied (two MFMAs), which carries dS to ~16 significant bits: dK and
+// dQ are sums of many terms that largely cancel (sum_k dS_qk = 0 for the
+// full support), and a single bf16 rounding of dS leaves errors of ~2^-9 of
+// the terms rather than of the result. MALA_FLAG_FAST_GRAD skips the lo half.
+#include "mala_device.h"
+#include "mala_internal.h"
+
+namespace mala {
+namespace {
+
+constexpr int kBQ = 32;     // query rows per backward decision tile
+constexpr int kBK = 32;     // keys per backward decision tile
+
+// Same permutation as the forward's V^T layout: position of row x (0..63) in
+// a transposed tile so that 8 consecutive bf16 match the order of one 16-wide
+// k-step of an S accumulator (row 8(r/4) + 4(l/32) + r%4).
+__device__ __forceinline__ int perm16(int x) {
+  const int u = (x >> 2) & 3;
+  const int pu = (u == 1) ? 2 : (u == 2 ? 1 : u);
+  return (x & ~15) + 4 * pu + (x & 3);
+}
+
+// ---------------------------------------------------------------- prep
+__global__ __launch_bounds__(256) void bwd_prep_kernel(int rows, int d, const bf16* __restrict__ O,
+                                                       const bf16* __restrict__ dO,
+                                                       float* __restrict__ Dq, uint32_t* bits,
+                                                       size_t nbits_words, int32_t* kept,
+                                                       size_t nkept, int8_t* mask, size_t nmask) {
+  const size_t gtid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t nthr = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = gtid; i < nbits_words; i += nthr) bits[i] = 0u;
+  if (kept != nullptr)
+    for (size_t i = gtid; i < nkept; i += nthr) kept[i] = 0;
+  if (mask != nullptr)
+    for (size_t i = gtid; i < nmask; i += nthr) mask[i] = -1;   // not a legal tile
+  // one wave per row: 64 lanes x (d/64) elements
+  const int lane = threadIdx.x & 63;
+  const size_t wave = gtid >> 6, nwave = nthr >> 6;
+  for (size_t r = wave; r < (size_t)rows; r += nwave) {
+    float acc = 0.f;
+    for (int e = lane; e < d; e += 64)
+      acc += (float)O[r * d + e] * (float)dO[r * d + e];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0) Dq[r] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <int D>
+struct alignas(16) DkdvSmem {
+  bf16 q[2][64][D + 8];       // Q_i rows (A operand of S = Q K^T)
+  bf16 dout[2][64][D + 8];    // dO_i rows (A operand of dP = dO V^T)
+  bf16 qt[2][D][64 + 8];      // Q_i^T, rows permuted (A operand of dK^T = Q^T dS)
+  bf16 dot[2][D][64 + 8];     // dO_i^T, permuted (A operand of dV^T = dO^T P)
+  alignas(16) float z2[2][64];   // z_q * log2 e
+  float u2[2][64];            // z_q * log2 e + log2(tau / L_q): skip iff s2 < u2 everywhere
+  float dd[2][64];            // D_q
+};
+
+template <int D, bool kSplit>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+    Shape s, const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dq,
+    bf16* __restrict__ dK, bf16* __restrict__ dV, uint32_t* __restrict__ bits,
+    int8_t* __restrict__ mask, int32_t* __restrict__ kept, int n_kb) {
+  __shared__ DkdvSmem<D> sm;
+  constexpr int KT = D / 16;      // k-steps over d
+  constexpr int DB = D / 32;      // 32-row blocks of dK^T / dV^T
+  constexpr int CPR = D / 8;      // 16-byte chunks per row
+  constexpr int QPT = 64 * CPR / 256 ;   // rows per thread when staging a 64-row tile
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int bk_count = s.batch * s.hkv;
+  const int J = (int)(blockIdx.x / bk_count);          // key block (0 = longest)
+  const int bkv = (int)(blockIdx.x % bk_count);
+  const int b = bkv / s.hkv, hk = bkv % s.hkv;
+  const int kw0 = J * 128 + w * kBK;                   // this wave's first key
+  const size_t krow0 = ((size_t)b * s.hkv + hk) * (size_t)s.nk;
+  const int tr32 = (s.nq + kBQ - 1) / kBQ;
+  const int tc32 = (s.nk + kBK - 1) / kBK;
+  const int words = (tc32 + 31) / 32;
+  const int tr64 = (s.nq + 63) / 64;
+  const int key = kw0 + l32;
+
+  // K and V of this wave as B operands: lane (key l32, half hf) holds row[16t + 8hf .. +7].
+  const auto krs = make_rsrc(K + krow0 * D, (uint32_t)((size_t)s.nk * D * 2));
+  const auto vrs = make_rsrc(V + krow0 * D, (uint32_t)((size_t)s.nk * D * 2));
+  bf16x8 kr[KT], vr[KT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    kr[t] = buf_load16(krs, (uint32_t)(key * D + 16 * t + 8 * hf) * 2);
+    vr[t] = buf_load16(vrs, (uint32_t)(key * D + 16 * t + 8 * hf) * 2);
+  }
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { dk[db][r] = 0.f; dv[db][r] = 0.f; }
+
+  // first query tile (64 rows) with a legal entry for the block's first key
+  int i_start = 0;
+  if (s.causal) {
+    const int need = J * 128 - s.offset;              // smallest legal row of key J*128
+    i_start = need <= 0 ? 0 : need / 64;
+  }
+  const int n_i = tr64 - i_start;
+  const int total = s.group * n_i;                    // (head, query tile) iterations
+
+  // staging: thread owns QPT consecutive rows x one 16-byte column chunk
+  const int sc = tid % CPR, srow = (tid / CPR) * QPT;
+  bf16x8 qreg[QPT], oreg[QPT];
+  float zreg = 0.f, dreg = 0.f;
+  auto load_tile = [&](int it) {
+    const int h = hk * s.group + it / n_i;
+    const int i = i_start + it % n_i;
+    const size_t qrow0 = ((size_t)b * s.hq + h) * (size_t)s.nq;
+    const auto qrs = make_rsrc(Q + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
+    const auto ors = make_rsrc(dO + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
+#pragma unroll
+    for (int p = 0; p < QPT; ++p) {
+      const uint32_t off = (uint32_t)((i * 64 + srow + p) * D + 8 * sc) * 2;
+      qreg[p] = buf_load16(qrs, off);
+      oreg[p] = buf_load16(ors, off);
+    }
+    if (tid < 64) {
+      const int q = i * 64 + tid;
+      zreg = q < s.nq ? LSE[qrow0 + q] : 0.f;
+      dreg = q < s.nq ? Dq[qrow0 + q] : 0.f;
+    }
+  };
+  auto store_tile = [&](int buf, int it) {
+    const int i = i_start + it % n_i;
+#pragma unroll
+    for (int p = 0; p < QPT; ++p) {
+      store16(&sm.q[buf][srow + p][8 * sc], qreg[p]);
+      store16(&sm.dout[buf][srow + p][8 * sc], oreg[p]);
+    }
+    const int pos = perm16(srow);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (QPT == 4) {
+        bf16x4 a = {qreg[0][e], qreg[1][e], qreg[2][e], qreg[3][e]};
+        bf16x4 c = {oreg[0][e], oreg[1][e], oreg[2][e], oreg[3][e]};
+        *reinterpret_cast<bf16x4*>(&sm.qt[buf][8 * sc + e][pos]) = a;
+        *reinterpret_cast<bf16x4*>(&sm.dot[buf][8 * sc + e][pos]) = c;
+      } else {
+        bf16x2 a = {qreg[0][e], qreg[1][e]};
+        bf16x2 c = {oreg[0][e], oreg[1][e]};
+        *reinterpret_cast<bf16x2*>(&sm.qt[buf][8 * sc + e][pos]) = a;
+        *reinterpret_cast<bf16x2*>(&sm.dot[buf][8 * sc + e][pos]) = c;
+      }
+    }
+    if (tid < 64) {
+      const int q = i * 64 + tid;
+      const float L = s.causal ? (float)(q + s.offset + 1) : (float)s.nk;
+      const float z2 = zreg * 1.4426950408889634f;
+      sm.z2[buf][tid] = z2;
+      sm.u2[buf][tid] = z2 + (s.log2_tau - fast_log2(L));
+      sm.dd[buf][tid] = dreg;
+    }
+  };
+
+  if (total > 0) {
+    load_tile(0);
+    store_tile(0, 0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < total; ++it) {
+    const int buf = it & 1;
+    const int h = hk * s.group + it / n_i;
+    const int i = i_start + it % n_i;
+    if (it + 1 < total) load_tile(it + 1);
+    const int qt0 = i * 64;                 // first row of the tile
+    const size_t bh = (size_t)b * s.hq + h;
+
+    // which of the two 32-row halves have a legal entry for this wave's keys
+    bool legal[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int r0 = qt0 + 32 * qb;
+      legal[qb] = r0 < s.nq && kw0 < s.nk && (!s.causal || kw0 <= min(r0 + 31, s.nq - 1) + s.offset);
+    }
+    if (legal[0] || legal[1]) {
+      // ---- recompute S = Q K^T: lane (key l32, half hf), regs = queries
+      f32x16 sacc[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[qb][r] = 0.f;
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          if (legal[qb])
+            sacc[qb] = mfma32(load16(&sm.q[buf][32 * qb + l32][16 * t + 8 * hf]), kr[t], sacc[qb]);
+      const bool boundary = (qt0 + 64 > s.nq) || (kw0 + kBK > s.nk) ||
+                            (s.causal && kw0 + kBK - 1 > qt0 + s.offset);
+      // ---- offline gate, Eq. 4: skip iff S - z < log(tau / L) on every legal entry
+      bool keep[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float x = kNegInf;
+        if (legal[qb]) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.u2[buf][32 * qb + 8 * g + 4 * hf]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const int r = 4 * g + c;
+              const int q = qt0 + 32 * qb + 8 * g + 4 * hf + c;
+              bool ok = true;
+              if (boundary) ok = q < s.nq && key < s.nk && (!s.causal || key <= q + s.offset);
+              if (!ok) sacc[qb][r] = kNegInf;
+              const float y = ok ? fmaf(sacc[qb][r], s.scale_log2, -u[c]) : kNegInf;
+              x = fmaxf(x, y);
+            }
+          }
+        }
+        keep[qb] = wave_any(x >= 0.f);
+      }
+      // decisions: one bit per (query head, 32-row tile, 32-key tile)
+      if (lane == 0) {
+        const int j32 = kw0 / kBK;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          if (!legal[qb]) continue;
+          const int i32 = (qt0 >> 5) + qb;
+          if (keep[qb])
+            atomicOr(&bits[(bh * tr32 + i32) * words + (j32 >> 5)], 1u << (j32 & 31));
+          if (mask != nullptr) mask[(bh * tr32 + i32) * tc32 + j32] = keep[qb] ? 1 : 0;
+          if (kept != nullptr && keep[qb]) atomicAdd(&kept[bh * tr32 + i32], 1);
+        }
+      }
+      if (keep[0] || keep[1]) {
+        // ---- P = exp(S - z), dP = dO V^T, dS = P o (dP - D)
+        f32x16 dp[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dp[qb][r] = 0.f;
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            if (keep[qb])
+              dp[qb] = mfma32(load16(&sm.dout[buf][32 * qb + l32][16 * t + 8 * hf]), vr[t], dp[qb]);
+        bf16x8 pb[4], dsb[4], dsl[4];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          if (!keep[qb]) continue;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 z = *reinterpret_cast<const f32x4*>(&sm.z2[buf][32 * qb + 8 * g + 4 * hf]);
+            const f32x4 dd = *reinterpret_cast<const f32x4*>(&sm.dd[buf][32 * qb + 8 * g + 4 * hf]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const int r = 4 * g + c;
+              const float p = fast_exp2(fmaf(sacc[qb][r], s.scale_log2, -z[c]));
+              const float ds = p * (dp[qb][r] - dd[c]);
+              pb[2 * qb + (r >> 3)][r & 7] = (bf16)p;
+              const bf16 hi = (bf16)ds;
+              dsb[2 * qb + (r >> 3)][r & 7] = hi;
+              if constexpr (kSplit) dsl[2 * qb + (r >> 3)][r & 7] = (bf16)(ds - (float)hi);
+            }
+          }
+        }
+        // ---- dV^T += dO^T P and dK^T += Q^T dS (k-steps of 16 query rows)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (!keep[t >> 1]) continue;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            dv[db] = mfma32(load16(&sm.dot[buf][32 * db + l32][16 * t + 8 * hf]), pb[t], dv[db]);
+            const bf16x8 qa = load16(&sm.qt[buf][32 * db + l32][16 * t + 8 * hf]);
+            dk[db] = mfma32(qa, dsb[t], dk[db]);
+            if constexpr (kSplit) dk[db] = mfma32(qa, dsl[t], dk[db]);
+          }
+        }
+      }
+    }
+    if (it + 1 < total) store_tile(buf ^ 1, it + 1);
+    __syncthreads();
+  }
+
+  // ---- store dK = scale * sum dS^T Q and dV (summed over the group's heads)
+  if (key >= s.nk) return;
+  bf16* dkr = dK + (krow0 + key) * D;
+  bf16* dvr = dV + (krow0 + key) * D;
+  const float sc_nat = s.scale_log2 * 0.69314718055994531f;   // softmax scale
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 a = {(bf16)(dk[db][4 * g] * sc_nat), (bf16)(dk[db][4 * g + 1] * sc_nat),
+                  (bf16)(dk[db][4 * g + 2] * sc_nat), (bf16)(dk[db][4 * g + 3] * sc_nat)};
+      bf16x4 c = {(bf16)dv[db][4 * g], (bf16)dv[db][4 * g + 1], (bf16)dv[db][4 * g + 2],
+                  (bf16)dv[db][4 * g + 3]};
+      *reinterpret_cast<bf16x4*>(dkr + 32 * db + 8 * g + 4 * hf) = a;
+      *reinterpret_cast<bf16x4*>(dvr + 32 * db + 8 * g + 4 * hf) = c;
+    }
+  (void)n_kb;
+}
+
+// ---------------------------------------------------------------- dQ
+template <int D>
+struct DqSmem {
+  bf16 k[2][64][D + 8];       // K_j rows (A operand of S^T = K Q^T)
+  bf16 v[2][64][D + 8];       // V_j rows (A operand of dP^T = V dO^T)
+  bf16 kt[2][D][64 + 8];      // K_j^T, keys permuted (A operand of dQ^T = K^T dS^T)
+  uint32_t need[2];           // does any wave of the block keep a half of tile j
+};
+
+template <int D, bool kSplit>
+__global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
+    Shape s, const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dq,
+    bf16* __restrict__ dQ, const uint32_t* __restrict__ bits, int n_qb) {
+  __shared__ DqSmem<D> sm;
+  constexpr int KT = D / 16, DB = D / 32, CPR = D / 8;
+  constexpr int RPP = 512 / CPR;            // rows per load pass
+  constexpr int KPASS = 64 / RPP;
+  constexpr int KPT = 64 / RPP;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int bh_count = s.batch * s.hq;
+  const int I = n_qb - 1 - (int)(blockIdx.x / bh_count);
+  const int bh = (int)(blockIdx.x % bh_count);
+  const int b = bh / s.hq, h = bh % s.hq, hk = h / s.group;
+  const size_t qrow0 = (size_t)bh * (size_t)s.nq;
+  const size_t krow0 = ((size_t)b * s.hkv + hk) * (size_t)s.nk;
+  const int tr32 = (s.nq + kBQ - 1) / kBQ;
+  const int tc32 = (s.nk + kBK - 1) / kBK;
+  const int words = (tc32 + 31) / 32;
+  const int q0 = I * 256 + w * 32;
+  const bool active = q0 < s.nq;
+  const int q = q0 + l32;
+
+  const auto qrs = make_rsrc(Q + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
+  const auto ors = make_rsrc(dO + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
+  const auto krs = make_rsrc(K + krow0 * D, (uint32_t)((size_t)s.nk * D * 2));
+  const auto vrs = make_rsrc(V + krow0 * D, (uint32_t)((size_t)s.nk * D * 2));
+
+  bf16x8 qr[KT], orr[KT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    qr[t] = buf_load16(qrs, (uint32_t)(q * D + 16 * t + 8 * hf) * 2);
+    orr[t] = buf_load16(ors, (uint32_t)(q * D + 16 * t + 8 * hf) * 2);
+  }
+  const float z2 = q < s.nq ? LSE[qrow0 + q] * 1.4426950408889634f : 0.f;
+  const float dd = q < s.nq ? Dq[qrow0 + q] : 0.f;
+  f32x16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
+
+  // key tiles (64 keys) that may be legal for the block's last row
+  const int last_row = min(I * 256 + 255, s.nq - 1);
+  const int lastkey = s.causal ? min(last_row + s.offset, s.nk - 1) : s.nk - 1;
+  const int ntiles = lastkey < 0 ? 0 : lastkey / 64 + 1;
+  const uint32_t* mybits = bits + ((size_t)bh * tr32 + (active ? q0 / kBQ : 0)) * words;
+
+  bf16x8 kreg[KPASS], vreg[KPASS];
+  const int kc = tid % CPR, kr = tid / CPR;
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int p = 0; p < KPASS; ++p) {
+      // rows kr*KPT + p: consecutive per thread so K^T writes are packed
+      const uint32_t off = (uint32_t)((j * 64 + kr * KPT + p) * D + 8 * kc) * 2;
+      kreg[p] = buf_load16(krs, off);
+      vreg[p] = buf_load16(vrs, off);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < KPASS; ++p) {
+      store16(&sm.k[buf][kr * KPT + p][8 * kc], kreg[p]);
+      store16(&sm.v[buf][kr * KPT + p][8 * kc], vreg[p]);
+    }
+    const int pos = perm16(kr * KPT);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (KPT == 2) {
+        bf16x2 x = {kreg[0][e], kreg[1][e]};
+        *reinterpret_cast<bf16x2*>(&sm.kt[buf][8 * kc + e][pos]) = x;
+      } else {
+        sm.kt[buf][8 * kc + e][pos] = kreg[0][e];
+      }
+    }
+  };
+  // Is either 32-key half of tile j kept by some wave of the block?
+  auto block_needs = [&](int j) -> uint32_t {
+    uint32_t any = 0;
+    for (int ww = 0; ww < 8; ++ww) {
+      const int qq = I * 256 + ww * 32;
+      if (qq >= s.nq) break;
+      const uint32_t wd = bits[((size_t)bh * tr32 + qq / kBQ) * words + ((2 * j) >> 5)];
+      any |= (wd >> ((2 * j) & 31)) & 3u;
+    }
+    return any;
+  };
+
+  // walk only the tiles some wave needs; stage each one in LDS. The staging
+  // buffer alternates per staged tile (not per tile index: skipped tiles are
+  // jumped over, so index parity would reuse the buffer being read).
+  int j = ntiles - 1;
+  while (j >= 0 && block_needs(j) == 0) --j;
+  int buf = 0;
+  if (j >= 0) {
+    load_tile(j);
+    store_tile(buf);
+  }
+  __syncthreads();
+  while (j >= 0) {
+    int jn = j - 1;
+    while (jn >= 0 && block_needs(jn) == 0) --jn;
+    if (jn >= 0) load_tile(jn);
+
+    if (active) {
+      const uint32_t wd = mybits[(2 * j) >> 5] >> ((2 * j) & 31);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if (!((wd >> half) & 1u)) continue;       // skipped (or not legal) tile
+        const int key0 = j * 64 + 32 * half;
+        // ---- S^T = K Q^T: lane (query l32, half hf), regs = keys
+        f32x16 sacc, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; dp[r] = 0.f; }
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+          sacc = mfma32(load16(&sm.k[buf][32 * half + l32][16 * t + 8 * hf]), qr[t], sacc);
+          dp = mfma32(load16(&sm.v[buf][32 * half + l32][16 * t + 8 * hf]), orr[t], dp);
+        }
+        const bool boundary = (key0 + 32 > s.nk) || (q0 + 32 > s.nq) ||
+                              (s.causal && key0 + 31 > q0 + s.offset);
+        bf16x8 dsb[2], dsl[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = key0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          bool ok = true;
+          if (boundary) ok = kk < s.nk && q < s.nq && (!s.causal || kk <= q + s.offset);
+          const float p = ok ? fast_exp2(fmaf(sacc[r], s.scale_log2, -z2)) : 0.f;
+          const float ds = p * (dp[r] - dd);
+          const bf16 hi = (bf16)ds;
+          dsb[r >> 3][r & 7] = hi;
+          if constexpr (kSplit) dsl[r >> 3][r & 7] = (bf16)(ds - (float)hi);
+        }
+        // ---- dQ^T += K^T dS^T
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+          {
+            const bf16x8 ka = load16(&sm.kt[buf][32 * db + l32][32 * half + 16 * t + 8 * hf]);
+            dq[db] = mfma32(ka, dsb[t], dq[db]);
+            if constexpr (kSplit) dq[db] = mfma32(ka, dsl[t], dq[db]);
+          }
+      }
+    }
+    if (jn >= 0) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    j = jn;
+  }
+
+  if (!active || q >= s.nq) return;
+  const float sc_nat = s.scale_log2 * 0.69314718055994531f;
+  bf16* row = dQ + (qrow0 + q) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 y = {(bf16)(dq[db][4 * g] * sc_nat), (bf16)(dq[db][4 * g + 1] * sc_nat),
+                  (bf16)(dq[db][4 * g + 2] * sc_nat), (bf16)(dq[db][4 * g + 3] * sc_nat)};
+      *reinterpret_cast<bf16x4*>(row + 32 * db + 8 * g + 4 * hf) = y;
+    }
+}
+
+}  // namespace
+
+size_t bwd_ws_d_floats(const Shape& s) { return (size_t)s.batch * s.hq * s.nq; }
+
+size_t bwd_bits_words(const Shape& s) {
+  const size_t tr32 = (s.nq + kBQ - 1) / kBQ, tc32 = (s.nk + kBK - 1) / kBK;
+  return (size_t)s.batch * s.hq * tr32 * ((tc32 + 31) / 32);
+}
+
+hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* d_o, void* dq, void* dk,
+                           void* dv, float* ws_d, uint32_t* ws_bits, int8_t* mask, int32_t* kept,
+                           hipStream_t st) {
+  const int rows = s.batch * s.hq * s.nq;
+  const size_t nwords = bwd_bits_words(s);
+  const size_t nkept = (size_t)s.batch * s.hq * ((s.nq + kBQ - 1) / kBQ);
+  {
+    const size_t nmask =
+        mask ? (size_t)s.batch * s.hq * ((s.nq + kBQ - 1) / kBQ) * ((s.nk + kBK - 1) / kBK) : 0;
+    size_t work = (size_t)rows;
+    if (nwords / 64 > work) work = nwords / 64;
+    if (nmask / 64 > work) work = nmask / 64;
+    size_t blocks = (work + 3) / 4 + 1;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, st, rows, s.d,
+                       (const bf16*)o, (const bf16*)d_o, ws_d, ws_bits, nwords, kept, nkept,
+                       mask, nmask);
+  }
+  const int n_kb = (s.nk + 127) / 128;
+  const dim3 g1((unsigned)(n_kb * s.batch * s.hkv));
+  const int n_qb = (s.nq + 255) / 256;
+  const dim3 g2((unsigned)(n_qb * s.batch * s.hq));
+  auto launch = [&](auto dkdv, auto dqk) {
+    if (g1.x)
+      hipLaunchKernelGGL(dkdv, g1, dim3(256), 0, st, s, (const bf16*)q, (const bf16*)k,
+                         (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dk, (bf16*)dv,
+                         ws_bits, mask, kept, n_kb);
+    if (g2.x)
+      hipLaunchKernelGGL(dqk, g2, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
+                         (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dq, ws_bits, n_qb);
+  };
+  const bool split = !(s.flags & MALA_FLAG_FAST_GRAD);
+  if (s.d == 128) {
+    if (split) launch(bwd_dkdv_kernel<128, true>, bwd_dq_kernel<128, true>);
+    else launch(bwd_dkdv_kernel<128, false>, bwd_dq_kernel<128, false>);
+  } else {
+    if (split) launch(bwd_dkdv_kernel<64, true>, bwd_dq_kernel<64, true>);
+    else launch(bwd_dkdv_kernel<64, false>, bwd_dq_kernel<64, false>);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mala

@@ -1,0 +1,259 @@
+// MALA forward for bf16 inputs on gfx950: the online gate (Eq. 3) inside a
+// tiled flash-style loop (Algorithm 1; App. A.1 "Fused forward execution").
+//
+// Work decomposition
+//   - one workgroup = 8 waves = 256 query rows of one (batch, query head);
+//     wave w owns query rows [q0, q0 + 32), which is one decision block
+//     (B_q = 32), so the keep/skip vote of a tile is a wave ballot;
+//   - key tiles of B_k = 64 keys are visited from the diagonal down to tile 0;
+//     K_j (row-major) and V_j (transposed) are staged in double-buffered LDS
+//     and shared by the 8 waves; the next tile is prefetched into registers
+//     with buffer loads (zero past the end of the sequence) while the current
+//     one is consumed, so one barrier per tile suffices;
+//   - scores are formed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA,
+//     so each lane owns one query column: the row max and row sum are in-lane
+//     reductions plus one permlane32 swap;
+//   - a wave that skips a tile leaves m, l and O untouched and issues no
+//     exponentials and no P V MFMAs (Algorithm 1, "skip block");
+//   - scores are kept in base 2 (scale * log2 e folded into one FMA); the gate
+//     is Eq. 3 multiplied by log2 e;
+//   - the running max is moved lazily: only when a row max exceeds it by more
+//     than kLazy (base 2), so the 64 O accumulators are rarely rescaled. The
+//     pair (m, l) still represents log Z = m + log l exactly (Eq. 1).
+#include "mala_device.h"
+#include "mala_internal.h"
+
+namespace mala {
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kRowsPerWave = 32;
+constexpr int kRowsPerBlock = kWaves * kRowsPerWave;   // 256
+constexpr int kBK = 64;
+constexpr float kLazy = 8.0f;
+
+template <int D>
+struct FwdSmem {
+  bf16 k[2][kBK][D + 8];      // +8 bf16: 16-byte row skew, conflict-free 16 B reads
+  bf16 vt[2][D][kBK + 8];     // V transposed; keys permuted inside each group of 16
+};
+
+// Position of key x (0..63) inside a V^T row. Quads 1 and 2 of every group of
+// 16 keys are swapped so that the 8 consecutive bf16 a lane reads as the MFMA
+// A operand are the 8 keys it holds for one 16-key step of P^T, whose order is
+// fixed by the accumulator layout of S^T (row 8(r/4) + 4(l/32) + r%4).
+__device__ __forceinline__ int vt_pos(int x) {
+  const int u = (x >> 2) & 3;
+  const int pu = (u == 1) ? 2 : (u == 2 ? 1 : u);
+  return (x & ~15) + 4 * pu + (x & 3);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
+    Shape s, const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    bf16* __restrict__ O, float* __restrict__ LSE, int8_t* __restrict__ mask,
+    int32_t* __restrict__ kept, int n_qb) {
+  __shared__ FwdSmem<D> sm;
+  constexpr int KT = D / 16;              // 16-wide k-steps of the QK contraction
+  constexpr int DB = D / 32;              // 32-row blocks of O^T
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int RPP = kThreads / CPR;     // K rows per load pass
+  constexpr int KPASS = kBK / RPP;
+  constexpr int KPT = kBK / RPP;          // consecutive V keys per thread
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+
+  const int bh_count = s.batch * s.hq;
+  const int I = n_qb - 1 - (int)(blockIdx.x / bh_count);     // longest blocks first
+  const int bh = (int)(blockIdx.x % bh_count);
+  const int b = bh / s.hq, h = bh % s.hq;
+  const int hk = h / s.group;
+  const size_t qrow0 = ((size_t)b * s.hq + h) * (size_t)s.nq;
+  const size_t krow0 = ((size_t)b * s.hkv + hk) * (size_t)s.nk;
+  const int tr = (s.nq + kRowsPerWave - 1) / kRowsPerWave;
+  const int tc = (s.nk + kBK - 1) / kBK;
+
+  const int q0 = I * kRowsPerBlock + w * kRowsPerWave;
+  const bool active = q0 < s.nq;
+  auto top_tile = [&](int last_row) {
+    const int lastkey = s.causal ? min(last_row + s.offset, s.nk - 1) : s.nk - 1;
+    return lastkey / kBK;
+  };
+  const int top_b = top_tile(min(I * kRowsPerBlock + kRowsPerBlock - 1, s.nq - 1));
+  const int top_w = active ? top_tile(min(q0 + kRowsPerWave - 1, s.nq - 1)) : -1;
+
+  const auto qrs = make_rsrc(Q + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
+  const auto krs = make_rsrc(K + krow0 * D, (uint32_t)((size_t)s.nk * D * 2));
+  const auto vrs = make_rsrc(V + krow0 * D, (uint32_t)((size_t)s.nk * D * 2));
+
+  // Q^T as the B operand: lane (query l32, half hf) holds Q[q][16t + 8hf .. +7].
+  const int q = q0 + l32;
+  const bool rvalid = q < s.nq;
+  bf16x8 qr[KT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) qr[t] = buf_load16(qrs, (uint32_t)(q * D + 16 * t + 8 * hf) * 2);
+  const float c2 = s.log2_tau - fast_log2(s.causal ? (float)(q + s.offset + 1) : (float)s.nk);
+  float m2 = kNegInf, lsum = 0.f;
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+
+  bf16x8 kreg[KPASS], vreg[KPT];
+  const int kc = tid % CPR, kr = tid / CPR;
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int p = 0; p < KPASS; ++p)
+      kreg[p] = buf_load16(krs, (uint32_t)((j * kBK + p * RPP + kr) * D + 8 * kc) * 2);
+#pragma unroll
+    for (int p = 0; p < KPT; ++p)
+      vreg[p] = buf_load16(vrs, (uint32_t)((j * kBK + kr * KPT + p) * D + 8 * kc) * 2);
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < KPASS; ++p) store16(&sm.k[buf][p * RPP + kr][8 * kc], kreg[p]);
+    const int pos = vt_pos(kr * KPT);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (KPT == 4) {
+        bf16x4 x = {vreg[0][e], vreg[1][e], vreg[2][e], vreg[3][e]};
+        *reinterpret_cast<bf16x4*>(&sm.vt[buf][8 * kc + e][pos]) = x;
+      } else if constexpr (KPT == 2) {
+        bf16x2 x = {vreg[0][e], vreg[1][e]};
+        *reinterpret_cast<bf16x2*>(&sm.vt[buf][8 * kc + e][pos]) = x;
+      } else {
+        sm.vt[buf][8 * kc + e][pos] = vreg[0][e];
+      }
+    }
+  };
+
+  int nkept = 0;
+  if (top_b >= 0) {
+    load_tile(top_b);
+    store_tile(top_b & 1);
+  }
+  __syncthreads();
+
+  for (int j = top_b; j >= 0; --j) {
+    const int buf = j & 1;
+    if (j > 0) load_tile(j - 1);
+
+    if (active && j <= top_w) {
+      // ---- score discovery: S^T[key][query], 64 keys x 32 queries
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          sacc[kb] = mfma32(load16(&sm.k[buf][32 * kb + l32][16 * t + 8 * hf]), qr[t], sacc[kb]);
+      // ---- causal mask at the diagonal and the ragged key tail
+      const int key0 = j * kBK;
+      if ((key0 + kBK > s.nk) || (s.causal && key0 + kBK - 1 > q0 + s.offset)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const bool ok = key < s.nk && (!s.causal || key <= q + s.offset);
+            if (!ok) sacc[kb][r] = kNegInf;
+          }
+      }
+      // ---- gate, Eq. 3: skip iff rowmax(S) - m - log l < log(tau / L) for
+      // every valid row with a legal key; l = 0 (nothing retained) keeps.
+      float x = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x = fmaxf(x, sacc[kb][r]);
+      const float tm = max_halves(x) * s.scale_log2;
+      const bool constrained = rvalid && tm > kNegInf;
+      const bool row_keeps =
+          constrained && (lsum == 0.f || tm - (m2 + fast_log2(lsum)) >= c2);
+      const bool keep = wave_any(row_keeps);
+      if (keep) {
+        // ---- online softmax update and P V (Algorithm 1, kept branch)
+        const bool need = tm > m2 + kLazy;
+        if (wave_any(need)) {
+          const float alpha = need ? fast_exp2(m2 - tm) : 1.f;
+          if (need) m2 = tm;
+          lsum *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
+        const float mu = (m2 == kNegInf) ? 0.f : m2;
+        bf16x8 pb[4];
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = fast_exp2(fmaf(sacc[kb][r], s.scale_log2, -mu));
+            rs += p;
+            pb[2 * kb + (r >> 3)][r & 7] = (bf16)p;
+          }
+        lsum += sum_halves(rs);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            oacc[db] = mfma32(load16(&sm.vt[buf][32 * db + l32][16 * t + 8 * hf]), pb[t], oacc[db]);
+        ++nkept;
+      }
+      if (mask != nullptr && lane == 0)
+        mask[((size_t)bh * tr + (q0 / kRowsPerWave)) * tc + j] = keep ? 1 : 0;
+    }
+
+    if (j > 0) store_tile((j - 1) & 1);
+    __syncthreads();
+  }
+
+  if (!active) return;
+  const int i = q0 / kRowsPerWave;
+  if (mask != nullptr)
+    for (int jj = top_w + 1 + lane; jj < tc; jj += 64) mask[((size_t)bh * tr + i) * tc + jj] = -1;
+  if (kept != nullptr && lane == 0) kept[(size_t)bh * tr + i] = nkept;
+
+  // ---- epilogue: O <- O / l and z = m + log l (Algorithm 1, final update)
+  if (!rvalid) return;
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  bf16* orow = O + (qrow0 + q) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 y = {(bf16)(oacc[db][4 * g + 0] * inv), (bf16)(oacc[db][4 * g + 1] * inv),
+                  (bf16)(oacc[db][4 * g + 2] * inv), (bf16)(oacc[db][4 * g + 3] * inv)};
+      *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * g + 4 * hf) = y;
+    }
+  if (hf == 0) LSE[qrow0 + q] = lsum > 0.f ? (m2 + fast_log2(lsum)) * kLn2 : kNegInf;
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const Shape& s, const void* q, const void* k, const void* v, void* o,
+                           float* lse, int8_t* mask, int32_t* kept, hipStream_t st) {
+  const int n_qb = (s.nq + kRowsPerBlock - 1) / kRowsPerBlock;
+  const dim3 grid((unsigned)(n_qb * s.batch * s.hq));
+  if (grid.x == 0) return hipSuccess;
+  if (s.d == 128)
+    hipLaunchKernelGGL(fwd_bf16_kernel<128>, grid, dim3(kThreads), 0, st, s, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (bf16*)o, lse, mask, kept, n_qb);
+  else
+    hipLaunchKernelGGL(fwd_bf16_kernel<64>, grid, dim3(kThreads), 0, st, s, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (bf16*)o, lse, mask, kept, n_qb);
+  return hipGetLastError();
+}
+
+}  // namespace mala

@@ -1,0 +1,76 @@
+// Internal declarations shared by the host layer and the kernel sources of libmala.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mala.h"
+
+namespace mala {
+
+// Decision partition (exposed through mala_get_tiling).
+constexpr int kFwdBq = 32;      // query rows per forward decision block (one wave)
+constexpr int kFwdBk = 64;      // keys per forward tile
+constexpr int kBwdBq = 32;      // query rows per backward tile
+constexpr int kBwdBk = 32;      // keys per backward tile (refines the forward tile)
+constexpr int kDecBk = 64;      // keys per decode tile
+constexpr int kDecChunk = 256;  // keys per decode split
+
+// Everything a kernel needs about one prefill/training problem.
+struct Shape {
+  int batch, hq, hkv, nq, nk, d, group;
+  int dtype;         // mala_dtype
+  int flags;         // MALA_FLAG_*
+  int causal;
+  int offset;        // n_k - n_q (bottom-right causal alignment)
+  float scale_log2;  // softmax_scale * log2(e): scores in base 2
+  float log2_tau;    // log2(tau), -inf when tau == 0
+  double scale;      // softmax scale (fp64 copies for the fp32-input kernels)
+  double log_tau;    // ln(tau), -inf when tau == 0
+  bool dtype_is_bf16() const { return dtype == MALA_BF16; }
+};
+
+struct DecodeShape {
+  int batch, hq, hkv, d, group, cap, max_nk, n_chunks;
+  float scale_log2;
+  float log2_tau;
+  double scale;
+  double log_tau;
+};
+
+// Launchers (return hipGetLastError() of the launch).
+hipError_t launch_fwd_bf16(const Shape& s, const void* q, const void* k, const void* v, void* o,
+                           float* lse, int8_t* mask, int32_t* kept, hipStream_t st);
+hipError_t launch_fwd_f32(const Shape& s, const float* q, const float* k, const float* v, float* o,
+                          float* lse, int8_t* mask, int32_t* kept, hipStream_t st);
+
+hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* d_o, void* dq, void* dk,
+                           void* dv, float* ws_d, uint32_t* ws_bits, int8_t* mask, int32_t* kept,
+                           hipStream_t st);
+hipError_t launch_bwd_f32(const Shape& s, const float* q, const float* k, const float* v,
+                          const float* o, const float* lse, const float* d_o, float* dq, float* dk,
+                          float* dv, float* ws_d, uint32_t* ws_bits, int8_t* mask, int32_t* kept,
+                          hipStream_t st);
+
+hipError_t launch_decode_bf16(const DecodeShape& s, const void* q, const void* kc, const void* vc,
+                              const int32_t* seqlens, void* o, float* lse, float* ws,
+                              int8_t* mask, int32_t* kept, hipStream_t st);
+hipError_t launch_decode_f32(const DecodeShape& s, const float* q, const float* kc,
+                             const float* vc, const int32_t* seqlens, float* o, float* lse,
+                             float* ws, int8_t* mask, int32_t* kept, hipStream_t st);
+
+// Small helpers (fill kernels instead of memsets, so the calls stay capturable).
+hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t st);
+hipError_t launch_fill_i8(int8_t* p, int8_t value, size_t n, hipStream_t st);
+hipError_t launch_decode_combine_bf16(const DecodeShape& s, const float* ws, void* o, float* lse,
+                                      hipStream_t st);
+hipError_t launch_decode_combine_f32(const DecodeShape& s, const float* ws, float* o, float* lse,
+                                     hipStream_t st);
+
+// Workspace layouts.
+size_t bwd_ws_d_floats(const Shape& s);    // D = rowsum(O o dO), fp32 [B, Hq, Nq]
+size_t bwd_bits_words(const Shape& s);     // backward decisions, one bit per tile
+size_t decode_ws_floats(const DecodeShape& s);
+
+}  // namespace mala

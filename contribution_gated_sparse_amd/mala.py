@@ -1,0 +1,249 @@
+"""Thin Python binding of libmala (ctypes). Argument marshalling only: every
+step of the operator runs in the library's HIP kernels on the caller's current
+stream. PyTorch is used for device memory and streams.
+
+Functions carry the names of the C entry points: ``mala_fwd``, ``mala_bwd``,
+``mala_decode``, ``mala_get_tiling``; the C ABI is documented in
+``include/mala.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmala.so")
+
+MALA_OK, MALA_ERR_INVALID_ARG, MALA_ERR_UNSUPPORTED, MALA_ERR_WORKSPACE, MALA_ERR_HIP = range(5)
+MALA_F32, MALA_BF16 = 0, 1
+OP_FWD, OP_BWD, OP_DECODE = 0, 1, 2
+
+
+class MalaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libmala status {status}: {message}")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("n_q", ctypes.c_int32),
+                ("n_k", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
+                ("tau", ctypes.c_float), ("softmax_scale", ctypes.c_float),
+                ("flags", ctypes.c_int32)]
+
+
+MALA_FLAG_FAST_GRAD = 1
+
+
+class DecodeProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("cache_capacity", ctypes.c_int32), ("max_n_k", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("tau", ctypes.c_float),
+                ("softmax_scale", ctypes.c_float)]
+
+
+EXPORTS = ("mala_get_tiling", "mala_fwd", "mala_bwd_workspace_size", "mala_bwd",
+           "mala_decode_workspace_size", "mala_decode", "mala_last_error", "mala_version")
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libmala.so (built in place by ``contribution_gated_sparse_amd.build``).
+    Raises if it is missing: there is no fallback path."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libmala.so not found at {p}; build it with "
+                           "`python -m contribution_gated_sparse_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float
+    P = ctypes.POINTER(Problem)
+    DP = ctypes.POINTER(DecodeProblem)
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    lib.mala_get_tiling.argtypes = [i32, i32, i32, pi32, pi32, pi32]
+    lib.mala_get_tiling.restype = i32
+    lib.mala_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.mala_fwd.restype = i32
+    lib.mala_bwd_workspace_size.argtypes = [P]
+    lib.mala_bwd_workspace_size.restype = sz
+    lib.mala_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    lib.mala_bwd.restype = i32
+    lib.mala_decode_workspace_size.argtypes = [DP]
+    lib.mala_decode_workspace_size.restype = sz
+    lib.mala_decode.argtypes = [DP, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    lib.mala_decode.restype = i32
+    lib.mala_last_error.argtypes = []
+    lib.mala_last_error.restype = ctypes.c_char_p
+    lib.mala_version.argtypes = []
+    lib.mala_version.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != MALA_OK:
+        msg = load_library().mala_last_error().decode()
+        raise MalaError(status, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MALA_BF16
+    if t.dtype == torch.float32:
+        return MALA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def mala_get_tiling(op: int, dtype: int = MALA_BF16, head_dim: int = 128):
+    bq, bk, ch = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(load_library().mala_get_tiling(op, dtype, head_dim, ctypes.byref(bq),
+                                          ctypes.byref(bk), ctypes.byref(ch)))
+    return bq.value, bk.value, ch.value
+
+
+def make_problem(q: torch.Tensor, k: torch.Tensor, tau: float, causal: bool = True,
+                 softmax_scale: Optional[float] = None, flags: int = 0) -> Problem:
+    b, hq, nq, d = q.shape
+    hkv, nk = k.shape[1], k.shape[2]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    return Problem(b, hq, hkv, nq, nk, d, _dtype_code(q), 1 if causal else 0, float(tau),
+                   float(scale), int(flags))
+
+
+def mala_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float, causal: bool = True,
+             softmax_scale: Optional[float] = None, want_mask: bool = False,
+             want_kept: bool = True, out: Optional[dict] = None) -> dict:
+    """Forward. q [B,Hq,Nq,d], k/v [B,Hkv,Nk,d] -> dict(o, lse, mask, kept)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n)
+    p = make_problem(q, k, tau, causal, softmax_scale)
+    bq, bk, _ = mala_get_tiling(OP_FWD)
+    tr, tc = -(-p.n_q // bq), -(-p.n_k // bk)
+    if out is None:
+        out = {}
+    o = out.get("o")
+    if o is None:
+        o = torch.empty_like(q)
+    lse = out.get("lse")
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    mask = out.get("mask") if want_mask else None
+    if want_mask and mask is None:
+        mask = torch.empty((p.batch, p.n_q_heads, tr, tc), dtype=torch.int8, device=q.device)
+    kept = out.get("kept") if want_kept else None
+    if want_kept and kept is None:
+        kept = torch.empty((p.batch, p.n_q_heads, tr), dtype=torch.int32, device=q.device)
+    _check(load_library().mala_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                   _ptr(mask), _ptr(kept), _stream()))
+    return dict(o=o, lse=lse, mask=mask, kept=kept)
+
+
+def mala_bwd(q, k, v, o, lse, d_o, tau: float, causal: bool = True,
+             softmax_scale: Optional[float] = None, want_mask: bool = False,
+             want_kept: bool = True, out: Optional[dict] = None, fast_grad: bool = False) -> dict:
+    """Backward -> dict(dq, dk, dv, mask, kept)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (d_o, "d_o")):
+        _dev(t, n)
+    p = make_problem(q, k, tau, causal, softmax_scale,
+                     MALA_FLAG_FAST_GRAD if fast_grad else 0)
+    lib = load_library()
+    bq, bk, _ = mala_get_tiling(OP_BWD)
+    tr, tc = -(-p.n_q // bq), -(-p.n_k // bk)
+    out = {} if out is None else out
+    dq = out.get("dq")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = out.get("dk")
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = out.get("dv")
+    dv = torch.empty_like(v) if dv is None else dv
+    nws = lib.mala_bwd_workspace_size(ctypes.byref(p))
+    ws = out.get("ws")
+    if ws is None or ws.numel() < nws:
+        ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=q.device)
+    mask = out.get("mask") if want_mask else None
+    if want_mask and mask is None:
+        mask = torch.empty((p.batch, p.n_q_heads, tr, tc), dtype=torch.int8, device=q.device)
+    kept = out.get("kept") if want_kept else None
+    if want_kept and kept is None:
+        kept = torch.empty((p.batch, p.n_q_heads, tr), dtype=torch.int32, device=q.device)
+    _check(lib.mala_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o),
+                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _ptr(mask), _ptr(kept),
+                        _stream()))
+    return dict(dq=dq, dk=dk, dv=dv, mask=mask, kept=kept, ws=ws)
+
+
+def make_decode_problem(q, k_cache, tau: float, max_n_k: int,
+                        softmax_scale: Optional[float] = None) -> DecodeProblem:
+    b, hq, d = q.shape
+    hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
+    return DecodeProblem(b, hq, hkv, d, cap, int(max_n_k), _dtype_code(q), float(tau), float(scale))
+
+
+def mala_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                seqlens_k: torch.Tensor, tau: float, max_n_k: Optional[int] = None,
+                softmax_scale: Optional[float] = None, want_mask: bool = False,
+                want_kept: bool = True, out: Optional[dict] = None) -> dict:
+    """One split-KV decode step. q [B,Hq,d]; caches [B,Hkv,cap,d]; seqlens_k
+    int32 [B] on the device (N_k including the current token)."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seqlens_k, "seqlens_k")):
+        _dev(t, n)
+    if seqlens_k.dtype != torch.int32:
+        raise TypeError("seqlens_k must be int32")
+    if max_n_k is None:
+        max_n_k = k_cache.shape[2]
+    p = make_decode_problem(q, k_cache, tau, max_n_k, softmax_scale)
+    lib = load_library()
+    _, bk, chunk = mala_get_tiling(OP_DECODE)
+    nch = -(-int(max_n_k) // chunk)
+    out = {} if out is None else out
+    o = out.get("o")
+    o = torch.empty_like(q) if o is None else o
+    lse = out.get("lse")
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if lse is None else lse
+    nws = lib.mala_decode_workspace_size(ctypes.byref(p))
+    ws = out.get("ws")
+    if ws is None or ws.numel() < nws:
+        ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=q.device)
+    mask = out.get("mask") if want_mask else None
+    if want_mask and mask is None:
+        mask = torch.empty((p.batch, p.n_q_heads, nch, chunk // bk), dtype=torch.int8,
+                           device=q.device)
+    kept = out.get("kept") if want_kept else None
+    if want_kept and kept is None:
+        kept = torch.empty((p.batch, p.n_q_heads + p.n_kv_heads), dtype=torch.int32,
+                           device=q.device)
+    _check(lib.mala_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                           _ptr(seqlens_k), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _ptr(mask),
+                           _ptr(kept), _stream()))
+    return dict(o=o, lse=lse, mask=mask, kept=kept, ws=ws)
+
+
+def version() -> str:
+    return load_library().mala_version().decode()

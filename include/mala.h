@@ -1,0 +1,185 @@
+/*
+ * mala.h - C ABI of libmala, MassAlloc Attention (MALA) for AMD MI355X (gfx950).
+ *
+ * The operator is the one defined in "MassAlloc Attention: Let Attention
+ * Allocate Its Own Compute" (arXiv 2609.32712):
+ *   - forward: every legal causal Q K^T tile is scored; the post-score work
+ *     (softmax update, V load, P V) runs only for tiles whose largest
+ *     contribution ratio against the running normalizer clears tau / L_q
+ *     (Sec. 2.2, Eq. 1-3, Algorithm 1);
+ *   - backward: S is recomputed and each tile is tested against the saved
+ *     log-normalizer (Sec. 2.2, Eq. 4, Algorithm 2);
+ *   - split-KV decode: each split tests its tiles against its own partial
+ *     normalizer with L counting the full context; partials are merged by
+ *     the normalizer-aware reduction (Sec. 2.4, App. A.1).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major, head-major: Q, O, dO, dQ are
+ *     [batch, n_q_heads, n_q, head_dim]; K, V, dK, dV are
+ *     [batch, n_kv_heads, n_k, head_dim]; LSE is [batch, n_q_heads, n_q].
+ *     Query head h reads KV head h / (n_q_heads / n_kv_heads) (grouped-query
+ *     attention). Base pointers must be 16-byte aligned.
+ *   - Element type: MALA_BF16 (bfloat16 Q/K/V/O/dO/dQ/dK/dV) or MALA_F32.
+ *     LSE, workspaces and all internal accumulation are fp32.
+ *   - Scores are s = softmax_scale * <q, k>; logarithms are natural (Sec. 2.1).
+ *   - Causal legality is bottom-right aligned: key k is visible to query row q
+ *     iff k <= q + (n_k - n_q); L_q = q + (n_k - n_q) + 1 (L_q = n_k when not
+ *     causal). tau must be finite and >= 0; tau = 0 skips nothing, which is
+ *     dense softmax attention (Sec. 2.3).
+ *   - All pointers except `p` and the tiling outputs are device pointers.
+ *     The caller owns every buffer; the library allocates nothing, keeps no
+ *     state between calls and never synchronizes: work is enqueued on
+ *     `stream` (a hipStream_t; NULL = the default stream) and the call returns.
+ *   - Errors: a non-MALA_OK status means nothing was enqueued and no output
+ *     was written; mala_last_error() describes it (thread-local). A fault
+ *     inside a kernel surfaces at the caller's next synchronization.
+ *   - Optional diagnostics (pass NULL to disable) report the decisions, which
+ *     the operator itself never materializes (Sec. 2.4): an int8 tile mask
+ *     (1 kept, 0 skipped, -1 not a legal tile) and int32 kept-tile counters.
+ */
+#ifndef MALA_H_
+#define MALA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MALA_OK = 0,
+  MALA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size, bad tau  */
+  MALA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. head_dim)   */
+  MALA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required  */
+  MALA_ERR_HIP = 4            /* a HIP launch reported an error              */
+} mala_status;
+
+typedef enum { MALA_F32 = 0, MALA_BF16 = 1 } mala_dtype;
+
+typedef enum { MALA_OP_FWD = 0, MALA_OP_BWD = 1, MALA_OP_DECODE = 2 } mala_op;
+
+/* Problem flags. */
+enum {
+  /* bf16 backward: multiply dS into dK and dQ as one bf16 operand instead of
+   * a hi + lo pair of bf16 operands. Faster (two fewer matrix products per
+   * kept tile) and less accurate: gradient errors grow to ~2^-9 of the
+   * summed terms, which exceeds 1% of the result where they cancel. */
+  MALA_FLAG_FAST_GRAD = 1
+};
+
+/* One prefill/training attention problem. */
+typedef struct {
+  int32_t batch;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;      /* divides n_q_heads                              */
+  int32_t n_q;             /* query rows per head (>= 0)                     */
+  int32_t n_k;             /* key rows per head (>= 0; >= n_q when causal)   */
+  int32_t head_dim;        /* 64 or 128                                      */
+  int32_t dtype;           /* mala_dtype                                     */
+  int32_t causal;          /* nonzero: causal mask (bottom-right aligned)    */
+  float tau;               /* tolerance, finite, >= 0                        */
+  float softmax_scale;     /* finite, > 0; usually 1/sqrt(head_dim)          */
+  int32_t flags;           /* MALA_FLAG_* (0 = defaults)                     */
+} mala_problem;
+
+/* One split-KV decode step: a single query token per sequence. */
+typedef struct {
+  int32_t batch;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;        /* 128 for MALA_BF16; 64 or 128 for MALA_F32      */
+  int32_t cache_capacity;  /* rows per (sequence, KV head) in the caches     */
+  int32_t max_n_k;         /* upper bound of seqlens_k; sizes the launch     */
+  int32_t dtype;           /* mala_dtype                                     */
+  float tau;
+  float softmax_scale;
+} mala_decode_problem;
+
+/*
+ * Decision partition used by an operation (the pages leave B_q and B_k open,
+ * Sec. 2.1; the realized support depends on it).
+ *   op = MALA_OP_FWD:    *bq x *bk query x key tiles, both tiled from 0.
+ *   op = MALA_OP_BWD:    *bq x *bk tiles; they refine the forward tiles, so a
+ *                        forward-skipped tile is backward-skipped (Sec. 2.2).
+ *   op = MALA_OP_DECODE: *bq = 1 (one decision per query head), *bk keys per
+ *                        tile, *chunk keys per split; splits are aligned to
+ *                        position 0 and tiles to the split start; the newest
+ *                        tile of a split is tested first.
+ * *chunk is 0 for FWD/BWD. Returns MALA_ERR_INVALID_ARG for an unknown op or
+ * a null output pointer.
+ */
+mala_status mala_get_tiling(int32_t op, int32_t dtype, int32_t head_dim,
+                            int32_t* bq, int32_t* bk, int32_t* chunk);
+
+/*
+ * Forward (Algorithm 1; Sec. 2.2 "Online Sparse Softmax").
+ *   q [B,Hq,Nq,d], k, v [B,Hkv,Nk,d]  inputs
+ *   o [B,Hq,Nq,d]                     output: softmax over the retained keys
+ *   lse [B,Hq,Nq] fp32                output: z_q = log Z_{R,q} (natural log),
+ *                                     the state the backward needs
+ *   tile_mask  int8 [B,Hq,Tr,Tc] or NULL, Tr = ceil(Nq/bq), Tc = ceil(Nk/bk)
+ *   kept_tiles int32 [B,Hq,Tr] or NULL: kept tiles per query block; the
+ *              post-score key slots of each row are bk * kept_tiles (Eq. 11).
+ */
+mala_status mala_fwd(const mala_problem* p, const void* q, const void* k, const void* v,
+                     void* o, float* lse, int8_t* tile_mask, int32_t* kept_tiles,
+                     void* stream);
+
+/* Bytes of device workspace mala_bwd needs for problem p (the per-row
+ * D = rowsum(O o dO) in fp32 and one decision bit per backward tile); 0 if p
+ * is invalid. */
+size_t mala_bwd_workspace_size(const mala_problem* p);
+
+/*
+ * Backward (Algorithm 2; Sec. 2.2 "Offline Sparse Probability").
+ *   q, k, v, o, lse  as produced/consumed by mala_fwd (o and lse from the
+ *                    forward call on the same q, k, v, tau)
+ *   d_o [B,Hq,Nq,d]  upstream gradient
+ *   dq [B,Hq,Nq,d], dk, dv [B,Hkv,Nk,d]  outputs (dk, dv summed over the
+ *                    query heads sharing a KV head)
+ *   workspace, ws_bytes  >= mala_bwd_workspace_size(p), 256-byte aligned
+ *   tile_mask  int8 [B,Hq,Tr,Tcb] or NULL with the backward tiling
+ *   kept_tiles int32 [B,Hq,Tr] or NULL: kept backward tiles per query block
+ */
+mala_status mala_bwd(const mala_problem* p, const void* q, const void* k, const void* v,
+                     const void* o, const float* lse, const void* d_o,
+                     void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                     int8_t* tile_mask, int32_t* kept_tiles, void* stream);
+
+/* Bytes of device workspace mala_decode needs (per-split partial states). */
+size_t mala_decode_workspace_size(const mala_decode_problem* p);
+
+/*
+ * Split-KV decode (Sec. 2.4; App. A.1 "Fused decoding execution").
+ *   q [B,Hq,d]                     the query token of each sequence, at
+ *                                  position seqlens_k[b] - 1
+ *   k_cache, v_cache [B,Hkv,cache_capacity,d]  persistent caches (read only;
+ *                                  the current token's K/V already written)
+ *   seqlens_k int32 [B] (device)   N_k per sequence, 1 <= N_k <= max_n_k
+ *                                  <= cache_capacity (checked on the device:
+ *                                  out-of-range lengths are clamped)
+ *   o [B,Hq,d], lse [B,Hq] fp32    outputs
+ *   workspace, ws_bytes            >= mala_decode_workspace_size(p)
+ *   tile_mask  int8 [B,Hq,n_chunks,chunk/bk] or NULL (n_chunks =
+ *              ceil(max_n_k/chunk)); entries past a sequence's end are -1
+ *   kept_tiles int32 [B,Hq+Hkv] or NULL: [b][h] kept tiles of query head h,
+ *              [b][Hq+g] tiles of KV head g whose V was read (kept by at least
+ *              one query head of the group)
+ */
+mala_status mala_decode(const mala_decode_problem* p, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* seqlens_k, void* o, float* lse,
+                        void* workspace, size_t ws_bytes, int8_t* tile_mask,
+                        int32_t* kept_tiles, void* stream);
+
+/* Description of the last error on the calling thread ("" if none). */
+const char* mala_last_error(void);
+
+/* Library version string. */
+const char* mala_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MALA_H_ */

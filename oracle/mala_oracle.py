@@ -232,8 +232,26 @@ def mala_fwd(q, k, v, tau: float, scale: float, causal: bool = True,
 # Sparse Probability", Eq. 4, Algorithm 2, App. A.1 "Fused backward")
 # --------------------------------------------------------------------------
 
+def round_storage(x, dtype: Optional[str]) -> np.ndarray:
+    """Value of x once stored in a tensor of ``dtype`` ("f32", "bf16", or
+    None for no rounding): round to nearest even at each narrowing."""
+    x = _f64(x)
+    if dtype is None:
+        return x
+    f = x.astype(np.float32)
+    if dtype == "f32":
+        return f.astype(np.float64)
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def mala_bwd(q, k, v, o, lse, do, tau: float, scale: float, causal: bool = True,
-             bq: int = 64, bk: int = 64, qblocks: Optional[Iterable] = None):
+             bq: int = 64, bk: int = 64, qblocks: Optional[Iterable] = None,
+             replay: Optional[np.ndarray] = None, band: float = 0.0,
+             o_storage: Optional[str] = None):
     """MALA backward on the saved z = lse.
 
     Returns dict with dq [B,Hq,Nq,d], dk, dv [B,Hkv,Nk,d] (summed over the
@@ -241,6 +259,12 @@ def mala_bwd(q, k, v, o, lse, do, tau: float, scale: float, causal: bool = True,
     margin > 0, margin = -max over legal entries of s - z_q - log(tau/L_q)).
     ``qblocks`` restricts the query blocks processed (an iterable of i); then
     dq is exact on those rows, dk/dv hold only their contributions.
+    ``replay`` (a mask of the same shape) is adopted where |margin| < band:
+    such a decision sits on the threshold within rounding (App. B, last
+    paragraph), and the gradients then follow the replayed support.
+    ``o_storage``: Algorithm 2 forms rowsum(O o dO) from the output the forward
+    stored; when that output is kept in a narrower dtype ("bf16", "f32"),
+    D is computed from o rounded to it.
     """
     q, k, v, o, lse, do = map(_f64, (q, k, v, o, lse, do))
     b_, hq, nq, _ = q.shape
@@ -254,7 +278,7 @@ def mala_bwd(q, k, v, o, lse, do, tau: float, scale: float, causal: bool = True,
     margin = np.full((b_, hq, tr, tc), np.nan)
     counts = visible_counts(nq, nk, causal)
     cthr = row_threshold(tau, counts)
-    dvec = np.sum(o * do, axis=-1)          # rowsum(O o dO), Algorithm 2
+    dvec = np.sum(round_storage(o, o_storage) * do, axis=-1)   # rowsum(O o dO), Algorithm 2
     ilist = list(range(tr)) if qblocks is None else list(qblocks)
     for b in range(b_):
         for h in range(hq):
@@ -275,7 +299,10 @@ def mala_bwd(q, k, v, o, lse, do, tau: float, scale: float, causal: bool = True,
                     if not np.isfinite(tmax[j]) and tmax[j] < 0:
                         continue                              # no legal entry
                     margin[b, h, i, j] = -tmax[j]
-                    if tmax[j] < 0.0:                         # all entries below: skip
+                    skip = tmax[j] < 0.0                      # all entries below: skip
+                    if replay is not None and abs(tmax[j]) < band:
+                        skip = replay[b, h, i, j] == SKIPPED
+                    if skip:
                         mask[b, h, i, j] = SKIPPED
                     else:
                         mask[b, h, i, j] = KEPT

@@ -1,0 +1,150 @@
+"""C ABI of libmala, on the CPU: the library loads, exports every function
+include/mala.h declares, reports its tiling, sizes workspaces, and rejects bad
+arguments with a status code and a message before touching any device (no
+call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from contribution_gated_sparse_amd import mala as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(M.LIB_PATH):
+        from contribution_gated_sparse_amd import build
+        build.build()
+    return M.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "mala.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mala_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+    assert set(names) == set(M.EXPORTS)
+
+
+def test_tiling(lib):
+    assert M.mala_get_tiling(M.OP_FWD) == (32, 64, 0)
+    assert M.mala_get_tiling(M.OP_BWD) == (32, 32, 0)
+    assert M.mala_get_tiling(M.OP_DECODE) == (1, 64, 256)
+    fb = M.mala_get_tiling(M.OP_FWD)
+    bb = M.mala_get_tiling(M.OP_BWD)
+    assert fb[0] % bb[0] == 0 and fb[1] % bb[1] == 0     # backward refines forward
+    with pytest.raises(M.MalaError):
+        M.mala_get_tiling(7)
+
+
+def prob(**kw):
+    base = dict(batch=1, n_q_heads=4, n_kv_heads=2, n_q=100, n_k=100, head_dim=128,
+                dtype=M.MALA_BF16, causal=1, tau=1e-4, softmax_scale=0.088, flags=0)
+    base.update(kw)
+    return M.Problem(*[base[f] for f, _ in M.Problem._fields_])
+
+
+BAD = [
+    (dict(n_kv_heads=3), M.MALA_ERR_INVALID_ARG, "multiple"),
+    (dict(head_dim=96), M.MALA_ERR_UNSUPPORTED, "head_dim"),
+    (dict(tau=-1.0), M.MALA_ERR_INVALID_ARG, "tau"),
+    (dict(tau=float("nan")), M.MALA_ERR_INVALID_ARG, "tau"),
+    (dict(tau=float("inf")), M.MALA_ERR_INVALID_ARG, "tau"),
+    (dict(softmax_scale=0.0), M.MALA_ERR_INVALID_ARG, "softmax_scale"),
+    (dict(n_q=101), M.MALA_ERR_INVALID_ARG, "causal"),
+    (dict(n_k=0, n_q=0, causal=0), None, None),
+    (dict(n_k=0, causal=0), M.MALA_ERR_INVALID_ARG, "n_k"),
+    (dict(batch=0), M.MALA_ERR_INVALID_ARG, "batch"),
+    (dict(dtype=5), M.MALA_ERR_INVALID_ARG, "dtype"),
+    (dict(flags=8), M.MALA_ERR_INVALID_ARG, "flags"),
+    (dict(n_k=20_000_000, n_q=1), M.MALA_ERR_UNSUPPORTED, "2 GiB"),
+]
+
+
+@pytest.mark.parametrize("kw,status,word", BAD)
+def test_forward_rejects_bad_problems(lib, kw, status, word):
+    p = prob(**kw)
+    buf = (ctypes.c_char * 64)()
+    addr = ctypes.addressof(buf)
+    addr += (-addr) % 16
+    ptr = ctypes.c_void_p(addr)
+    if status is None:      # n_q = 0: nothing to do, returns OK without a launch
+        assert lib.mala_fwd(ctypes.byref(p), None, None, None, None, None, None, None, None) == 0
+        return
+    st = lib.mala_fwd(ctypes.byref(p), ptr, ptr, ptr, ptr, ptr, None, None, None)
+    assert st == status
+    assert word in lib.mala_last_error().decode()
+
+
+def test_null_and_misaligned_pointers(lib):
+    p = prob()
+    buf = (ctypes.c_char * 64)()
+    addr = ctypes.addressof(buf)
+    addr += (-addr) % 16
+    good, bad = ctypes.c_void_p(addr), ctypes.c_void_p(addr + 2)
+    assert lib.mala_fwd(ctypes.byref(p), None, good, good, good, good, None, None,
+                        None) == M.MALA_ERR_INVALID_ARG
+    assert "q is NULL" in lib.mala_last_error().decode()
+    assert lib.mala_fwd(ctypes.byref(p), good, bad, good, good, good, None, None,
+                        None) == M.MALA_ERR_INVALID_ARG
+    assert "aligned" in lib.mala_last_error().decode()
+    assert lib.mala_fwd(None, good, good, good, good, good, None, None, None) == \
+        M.MALA_ERR_INVALID_ARG
+
+
+def test_backward_workspace(lib):
+    p = prob()
+    need = lib.mala_bwd_workspace_size(ctypes.byref(p))
+    # D (B*Hq*Nq fp32) + decision bits, each rounded up to 256 bytes
+    tr, tc = -(-100 // 32), -(-100 // 32)
+    expect = -(-(4 * 100 * 4) // 256) * 256 + -(-(4 * tr * -(-tc // 32) * 4) // 256) * 256
+    assert need == expect
+    assert lib.mala_bwd_workspace_size(ctypes.byref(prob(head_dim=80))) == 0
+    buf = (ctypes.c_char * 1024)()
+    addr = ctypes.addressof(buf)
+    addr += (-addr) % 256
+    g = ctypes.c_void_p(addr)
+    st = lib.mala_bwd(ctypes.byref(p), g, g, g, g, g, g, g, g, g, g, need - 1, None, None, None)
+    assert st == M.MALA_ERR_WORKSPACE
+    st = lib.mala_bwd(ctypes.byref(p), g, g, g, g, g, g, g, g, g, ctypes.c_void_p(addr + 16),
+                      need, None, None, None)
+    assert st == M.MALA_ERR_INVALID_ARG and "256-byte" in lib.mala_last_error().decode()
+
+
+def dprob(**kw):
+    base = dict(batch=2, n_q_heads=8, n_kv_heads=1, head_dim=128, cache_capacity=1000,
+                max_n_k=900, dtype=M.MALA_BF16, tau=1e-4, softmax_scale=0.088)
+    base.update(kw)
+    return M.DecodeProblem(*[base[f] for f, _ in M.DecodeProblem._fields_])
+
+
+def test_decode_validation_and_workspace(lib):
+    p = dprob()
+    n = lib.mala_decode_workspace_size(ctypes.byref(p))
+    assert n == -(-(2 * 8 * 4 * 130 * 4) // 256) * 256      # 4 splits of 256 keys
+    for kw, word in [(dict(n_q_heads=34, n_kv_heads=2), "16"), (dict(max_n_k=2000), "max_n_k"),
+                     (dict(head_dim=64), "head_dim"), (dict(tau=-2.0), "tau"),
+                     (dict(n_q_heads=7, n_kv_heads=2), "multiple")]:
+        q = dprob(**kw)
+        assert lib.mala_decode_workspace_size(ctypes.byref(q)) == 0
+        buf = (ctypes.c_char * 64)()
+        addr = ctypes.addressof(buf)
+        addr += (-addr) % 256
+        g = ctypes.c_void_p(addr)
+        st = lib.mala_decode(ctypes.byref(q), g, g, g, g, g, g, g, 1 << 20, None, None, None)
+        assert st != 0 and word in lib.mala_last_error().decode()
+    # fp32 decode supports head_dim 64
+    assert lib.mala_decode_workspace_size(ctypes.byref(dprob(head_dim=64, dtype=M.MALA_F32))) > 0
+
+
+def test_version(lib):
+    assert "gfx950" in M.version()

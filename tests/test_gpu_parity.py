@@ -1,0 +1,231 @@
+"""GPU parity: libmala (through its C ABI) against the CPU fp64 oracle on the
+same seeded inputs. Decisions must match outside the near-tie band (forward
+near ties are replayed so that later decisions stay comparable), kept-tile
+counters exactly, and values within the stated tolerances."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import mala_oracle as O
+from parity_util import (BAND, check_forward, check_nesting, compare_values, dtype_name, np64,
+                         tiling)
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():   # collected on CPU only to be deselected
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+DEV = "cuda"
+
+
+def lib():
+    import contribution_gated_sparse_amd as m
+    return m
+
+
+def to_dev(x):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+
+
+def check_backward(x, tau, g_fwd, r_fwd, causal=True, qblocks=None, key_rows=None):
+    m = lib()
+    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    kind = dtype_name(q)
+    _, (bq, bk, _), _ = tiling()
+    g = m.mala_bwd(q, k, v, g_fwd["o"], g_fwd["lse"], do, tau, causal=causal,
+                   softmax_scale=x["scale"], want_mask=True)
+    torch.cuda.synchronize()
+    gmask = g["mask"].cpu().numpy()
+    r = O.mala_bwd(np64(q), np64(k), np64(v), r_fwd["o"], r_fwd["lse"], np64(do), tau,
+                   x["scale"], causal, bq, bk, qblocks=qblocks, replay=gmask, band=BAND[kind],
+                   o_storage=kind)
+    checked = r["mask"] != O.NOT_VISITED
+    clear = checked & ~(np.abs(r["margin"]) < BAND[kind])
+    assert np.array_equal(gmask[clear], r["mask"][clear]), (
+        f"backward decisions differ: {int((gmask[clear] != r['mask'][clear]).sum())}")
+    if qblocks is None:
+        assert np.array_equal(gmask != O.NOT_VISITED, checked)
+        kept_o = (gmask == O.KEPT).sum(-1)
+        assert np.array_equal(kept_o, g["kept"].cpu().numpy())
+    nq = q.shape[2]
+    if qblocks is None:
+        rows = np.ones(q.shape[:3], bool)
+    else:
+        rows = np.zeros(q.shape[:3], bool)
+        for i in qblocks:
+            rows[:, :, i * bq:min(nq, (i + 1) * bq)] = True
+    st = {}
+    st["dq"] = compare_values("dQ", np64(g["dq"]), r["dq"], kind, rows)
+    if key_rows is not None or qblocks is None:
+        kr = slice(None) if key_rows is None else key_rows
+        st["dk"] = compare_values("dK", np64(g["dk"])[:, :, kr], r["dk"][:, :, kr], kind)
+        st["dv"] = compare_values("dV", np64(g["dv"])[:, :, kr], r["dv"][:, :, kr], kind)
+    st["ties"] = int((checked & ~clear).sum())
+    return g, r, st
+
+
+# ------------------------------------------------------------- tiny fp32 config
+
+@pytest.mark.parametrize("tau", [1e-4, 0.0, 1.0, 2.0, 10.0, 1e3])
+def test_config1_fp32_fwd_bwd(tau):
+    x = to_dev(W.make_prefill(W.CONFIGS[1]))
+    g, r, st = check_forward(x, tau, max_ties=2)
+    gb, rb, stb = check_backward(x, tau, g, r)
+    check_nesting(g["mask"].cpu().numpy(), gb["mask"].cpu().numpy())
+
+
+# ------------------------------------------------------------- bf16 shapes
+
+SHAPES = [
+    # (batch, hq, hkv, nq, nk, d)
+    (1, 2, 2, 1, 1, 128),
+    (1, 2, 1, 63, 63, 128),
+    (1, 4, 1, 65, 65, 128),
+    (2, 4, 2, 200, 200, 128),
+    (1, 8, 2, 777, 777, 128),
+    (1, 2, 2, 300, 300, 64),
+    (1, 4, 4, 100, 356, 128),     # chunked prefill: bottom-right causal alignment
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("tau", [0.0, 1e-4, 1.0, 100.0])
+def test_bf16_shapes_fwd_bwd(shape, tau):
+    b, hq, hkv, nq, nk, d = shape
+    cfg = W.CONFIGS[2]
+    x = W.make_prefill(cfg, n=nk, hq=hq, hkv=hkv, d=d, batch=b, planted=4, seed=7 + nq)
+    if nq < nk:   # queries are the last nq rows
+        x["q"] = x["q"][:, :, nk - nq:].contiguous()
+        x["do"] = x["do"][:, :, nk - nq:].contiguous()
+    x = to_dev(x)
+    g, r, st = check_forward(x, tau, max_ties=4)
+    gb, rb, stb = check_backward(x, tau, g, r)
+    check_nesting(g["mask"].cpu().numpy(), gb["mask"].cpu().numpy())
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_noncausal(dtype):
+    cfg = W.CONFIGS[2] if dtype == torch.bfloat16 else W.CONFIGS[1]
+    d = 128 if dtype == torch.bfloat16 else 64
+    x = W.make_prefill(cfg, n=160, hq=2, hkv=1, d=d, planted=3)
+    x = to_dev(x)
+    for tau in (0.0, 0.5, 50.0):
+        g, r, _ = check_forward(x, tau, causal=False, max_ties=4)
+        check_backward(x, tau, g, r, causal=False)
+
+
+def test_fp32_d128_and_gqa():
+    x = W.make_prefill(W.CONFIGS[1], n=150, hq=4, hkv=2, d=128, planted=4)
+    x["scale"] = 1 / math.sqrt(128)
+    x = to_dev(x)
+    for tau in (0.0, 1e-4, 3.0):
+        g, r, _ = check_forward(x, tau, max_ties=2)
+        check_backward(x, tau, g, r)
+
+
+# ------------------------------------------------------------- skipping inputs
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("tau", [1e-4, 1e-2, 1.0])
+def test_structured_skipping_fwd_bwd(dtype, tau):
+    """Structured logits (sinks, local band, retrieval keys) make the gate
+    skip most far tiles; decisions, counters and values still match."""
+    d = 128 if dtype == "bf16" else 64
+    x = to_dev(W.make_structured(1000, hq=4, hkv=2, d=d, dtype=dtype,
+                                 freqs=48 if d == 128 else 24))
+    g, r, st = check_forward(x, tau, max_ties=4)
+    assert st["kept_frac"] < 0.8
+    gb, rb, stb = check_backward(x, tau, g, r)
+    bm = gb["mask"].cpu().numpy()
+    assert (bm == O.SKIPPED).sum() > 0
+    check_nesting(g["mask"].cpu().numpy(), bm)
+
+
+# ------------------------------------------------------------- decode
+
+def check_decode(x, lens, tau, steps_q, max_ties=4):
+    m = lib()
+    kc, vc = x["k_cache"], x["v_cache"]
+    kind = dtype_name(kc)
+    _, _, (_, dbk, chunk) = tiling()
+    q = steps_q
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    g = m.mala_decode(q, kc, vc, seq, tau, max_n_k=max(lens), softmax_scale=x["scale"],
+                      want_mask=True)
+    torch.cuda.synchronize()
+    gmask = g["mask"].cpu().numpy()
+    r = O.mala_decode(np64(q), np64(kc), np64(vc), lens, tau, x["scale"], chunk, dbk,
+                      replay=gmask, band=BAND[kind])
+    assert np.array_equal(gmask, r["mask"]), "decode decisions differ outside the near-tie band"
+    assert r["near_ties"] <= max_ties
+    kept = g["kept"].cpu().numpy()
+    hq = q.shape[1]
+    assert np.array_equal(kept[:, :hq], (r["mask"] == O.KEPT).sum((-1, -2)))
+    assert np.array_equal(kept[:, hq:], r["v_tiles"].sum((-1, -2)))
+    compare_values("decode O", np64(g["o"]), r["o"], kind)
+    dl = float(np.abs(np64(g["lse"]) - r["lse"]).max())
+    assert dl <= (1e-5 if kind == "f32" else 2e-3)
+    return g, r
+
+
+@pytest.mark.parametrize("tau", [0.0, 1e-4, 1.0, 50.0])
+def test_decode_bf16_small(tau):
+    x = W.make_decode(W.CONFIGS[5], cache=1100, steps=3, batch=3, planted=16)
+    x = to_dev(x)
+    lens = [1103, 1101, 257]
+    q = x["q_steps"][2]
+    check_decode(x, lens, tau, q.contiguous())
+
+
+@pytest.mark.parametrize("tau", [0.0, 1e-4, 1.0, 50.0])
+def test_decode_f32_small(tau):
+    x = W.make_decode(W.CONFIGS[5], cache=600, steps=2, batch=2, hq=4, hkv=2, planted=8)
+    x = {k: (v.float() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    x = to_dev(x)
+    check_decode(x, [602, 65], tau, x["q_steps"][1].contiguous())
+
+
+def test_decode_group16_and_single_key():
+    x = W.make_decode(W.CONFIGS[5], cache=300, steps=1, batch=2, hq=16, hkv=1, planted=4)
+    x = to_dev(x)
+    check_decode(x, [1, 301], 1e-4, x["q_steps"][0].contiguous())
+
+
+# ------------------------------------------------------------- empty / errors on device
+
+def test_empty_query_rows():
+    m = lib()
+    q = torch.zeros((1, 2, 0, 128), dtype=torch.bfloat16, device=DEV)
+    k = torch.randn((1, 2, 5, 128), device=DEV).to(torch.bfloat16)
+    out = m.mala_fwd(q, k, k, 1e-4)
+    assert out["o"].shape == (1, 2, 0, 128)
+    b = m.mala_bwd(q, k, k, out["o"], out["lse"], q, 1e-4)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(b["dk"]) == 0 and torch.count_nonzero(b["dv"]) == 0
+
+
+def test_fast_grad_flag_same_support():
+    """MALA_FLAG_FAST_GRAD changes only the precision of dS in dK and dQ: the
+    decisions are identical and the gradients stay within tolerance on the
+    Gaussian workload."""
+    m = lib()
+    x = to_dev(W.make_prefill(W.CONFIGS[3], n=600, hq=4, hkv=1, planted=8))
+    f = m.mala_fwd(x["q"], x["k"], x["v"], 1e-4, softmax_scale=x["scale"])
+    a = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], 1e-4,
+                   softmax_scale=x["scale"], want_mask=True)
+    b = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], 1e-4,
+                   softmax_scale=x["scale"], want_mask=True, fast_grad=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a["mask"], b["mask"])
+    assert torch.equal(a["dv"], b["dv"])
+    r = O.mala_fwd(np64(x["q"]), np64(x["k"]), np64(x["v"]), 1e-4, x["scale"], True,
+                   *tiling()[0][:2], replay=m.mala_fwd(x["q"], x["k"], x["v"], 1e-4,
+                   softmax_scale=x["scale"], want_mask=True)["mask"].cpu().numpy(), band=1e-3)
+    rb = O.mala_bwd(np64(x["q"]), np64(x["k"]), np64(x["v"]), r["o"], r["lse"], np64(x["do"]),
+                    1e-4, x["scale"], True, *tiling()[1][:2], o_storage="bf16")
+    for name in ("dq", "dk"):
+        compare_values(name + " fast", np64(b[name]), rb[name], "bf16")
+        compare_values(name + " split", np64(a[name]), rb[name], "bf16")

@@ -462,3 +462,15 @@ def test_pins_catch_forced_backward_diagonal(monkeypatch):
     monkeypatch.setattr(O, "mala_bwd", mutant)
     with pytest.raises(AssertionError):
         test_constant_scores_closed_form(2.0, 4)
+
+
+def test_round_storage_matches_torch_casts():
+    """The oracle's model of a stored bf16/fp32 tensor is torch's round-to-
+    nearest-even cast."""
+    rng = np.random.default_rng(80)
+    x = rng.standard_normal(100000) * np.exp(rng.uniform(-20, 20, 100000))
+    t = torch.from_numpy(x)
+    np.testing.assert_array_equal(O.round_storage(x, "bf16"),
+                                  t.float().to(torch.bfloat16).double().numpy())
+    np.testing.assert_array_equal(O.round_storage(x, "f32"), t.float().double().numpy())
+    np.testing.assert_array_equal(O.round_storage(x, None), x)

@@ -204,3 +204,76 @@ def make_decode(cfg: DecodeConfig, *, seed: Optional[int] = None, device="cpu",
     q = torch.stack(qs).permute(2, 0, 1, 3).contiguous()   # [steps, B, Hq, d]
     return dict(k_cache=k, v_cache=v, q_steps=q, cache=cache, steps=steps,
                 scale=1.0 / math.sqrt(cfg.d), dtype=cfg.dtype, chunk=cfg.chunk)
+
+
+def make_structured(n: int, hq: int = 2, hkv: int = 1, d: int = 128, *, seed: int = 20269001,
+                    device="cpu", dtype: str = "bf16", freqs: int = 48, peak: float = 25.0,
+                    window: int = 128, n_sink: int = 4, sink_logit: float = 18.0,
+                    retrieval: int = 16, retrieval_logit: float = 22.0,
+                    noise: float = 0.3, batch: int = 1, with_do: bool = True) -> dict:
+    """Structured-logit inputs whose attention mass concentrates the way the
+    paper describes real attention (sink tokens, a local band and sparse
+    retrieval keys), so that the tolerance actually skips tiles.
+
+    Logit of query t and key s (scale 1/sqrt(d) included):
+      peak/F * sum_f cos(w_f (t - s))    local band: F = ``freqs`` rotary pairs,
+                                         periods log-uniform in [4, 64] x window
+      + sink_logit                       for s < n_sink
+      + retrieval_logit                  for ``retrieval`` planted (s, t) pairs
+                                         per query head
+      + noise                            N(0, noise^2) in the remaining dims
+    """
+    assert 2 * freqs + 8 <= d
+    g = _gen(device, seed, TAG_Q)
+    scale = 1.0 / math.sqrt(d)
+    pos = torch.arange(n, device=device, dtype=torch.float64)
+    periods = window * torch.exp(torch.linspace(math.log(4.0), math.log(64.0), freqs,
+                                                dtype=torch.float64, device=device))
+    w = 2 * math.pi / periods
+    ang = pos[:, None] * w[None, :]                     # [n, F]
+    rot = torch.stack([torch.cos(ang), torch.sin(ang)], -1).reshape(n, 2 * freqs)
+    # every logit term is split evenly between Q and K (each carries the
+    # square root), so neither side holds outsized components
+    amp = math.sqrt(peak / freqs / scale)
+    q = torch.zeros((batch, hq, n, d), dtype=torch.float64, device=device)
+    k = torch.zeros((batch, hkv, n, d), dtype=torch.float64, device=device)
+    q[..., : 2 * freqs] = amp * rot
+    k[..., : 2 * freqs] = amp * rot
+    # sinks: one shared direction
+    sdim = 2 * freqs
+    q[..., sdim] = math.sqrt(sink_logit / scale)
+    k[:, :, :n_sink, sdim] = math.sqrt(sink_logit / scale)
+    # noise in the remaining dims
+    rest = d - (sdim + 1)
+    qn = torch.randn((batch, hq, n, rest), generator=g, device=device, dtype=torch.float32)
+    kn = torch.randn((batch, hkv, n, rest), generator=_gen(device, seed, TAG_K), device=device,
+                     dtype=torch.float32)
+    nscale = math.sqrt(noise / math.sqrt(rest) / scale)
+    q[..., sdim + 1:] = qn.double() * nscale
+    k[..., sdim + 1:] = kn.double() * nscale
+    # retrieval keys: key s gets a random unit direction u in the noise dims,
+    # its target query t > s gets the same direction, each scaled so that the
+    # pair adds retrieval_logit
+    group = hq // hkv
+    gp = _gen("cpu", seed, TAG_PLANT)
+    ramp = math.sqrt(retrieval_logit / scale)
+    for b in range(batch):
+        for h in range(hq):
+            if n < 2 or retrieval == 0:
+                continue
+            u = torch.rand((retrieval, 2), generator=gp, dtype=torch.float64)
+            ss = (u[:, 0] * (n - 1)).floor().long().clamp(max=n - 2)
+            tt = ss + 1 + (u[:, 1] * (n - 1 - ss).double()).floor().long()
+            tt = torch.minimum(tt, torch.full_like(tt, n - 1))
+            dirs = torch.randn((retrieval, rest), generator=gp, dtype=torch.float64)
+            dirs = dirs / dirs.norm(dim=-1, keepdim=True)
+            for r in range(retrieval):
+                k[b, h // group, ss[r], sdim + 1:] += dirs[r].to(device) * ramp
+                q[b, h, tt[r], sdim + 1:] += dirs[r].to(device) * ramp
+    v = torch.randn((batch, hkv, n, d), generator=_gen(device, seed, TAG_V), device=device,
+                    dtype=torch.float32)
+    do = (torch.randn((batch, hq, n, d), generator=_gen(device, seed, TAG_DO), device=device,
+                      dtype=torch.float32) if with_do else None)
+    out = dict(q=_cast(q.float(), dtype), k=_cast(k.float(), dtype), v=_cast(v, dtype),
+               do=_cast(do, dtype) if do is not None else None, scale=scale, dtype=dtype)
+    return out
