@@ -1,0 +1,395 @@
+#!/usr/bin/env python3
+"""Benchmark of the MALA operator on one MI355X.
+
+One step = one pass of the whole hot path over synthetic inputs resident in
+HBM: MALA forward + backward on the 32K causal GQA problem (B=1, 32 query /
+8 KV heads, d=128, bf16, tau=1e-4) followed by one split-KV decode step on the
+128K decode batch (8 sequences, 8 query / 1 KV head, 256-key splits), whose
+new K/V rows are appended to the caches inside the step.
+
+Prints one JSON line. ``value`` is the step's dense-equivalent throughput:
+the FLOPs dense causal attention would spend on the same work (forward 4d and
+backward 10d per legal query/key pair, decode 4d per key), divided by the
+measured step time. Per-stage times come from HIP events on the stream the
+library launches on. The CPU fp64 oracle is timed on a bounded sample of the
+same 32K problem as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--tau", type=float, default=1e-4)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time budget of the CPU oracle baseline sample (0 = skip)")
+    ap.add_argument("--no-128k", action="store_true", help="skip the 128K prefill extra")
+    ap.add_argument("--fast-grad", action="store_true", help="single-bf16 dS in the backward")
+    ap.add_argument("--only", default="", help="profiling: 'fwd', 'bwd' or 'decode' alone")
+    ap.add_argument("--profile", action="store_true",
+                    help="for rocprofv3: one warm-up step, one step, then a 1 GiB device copy "
+                         "that calibrates the byte counters; prints no JSON")
+    return ap.parse_args()
+
+
+def causal_pairs(n: int) -> int:
+    return n * (n + 1) // 2
+
+
+def fwd_tiles(nq, nk, bq, bk):
+    """Score tiles visited by the causal forward (per head)."""
+    off = nk - nq
+    tot = 0
+    for i in range(-(-nq // bq)):
+        last = min(i * bq + bq - 1, nq - 1)
+        tot += min(last + off, nk - 1) // bk + 1
+    return tot
+
+
+def bwd_tiles(nq, nk, bq, bk):
+    """Legal backward tiles (per head)."""
+    off = nk - nq
+    tot = 0
+    for i in range(-(-nq // bq)):
+        last = min(i * bq + bq - 1, nq - 1)
+        tot += min(last + off, nk - 1) // bk + 1
+    return tot
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the MALA operator "
+              "runs on a single MI355X here (heads are independent, so a multi-GPU run would "
+              "shard heads across GPUs with no exchange inside the operator).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import contribution_gated_sparse_amd as m
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = m.load_library()
+    (fbq, fbk, _), (bbq, bbk, _) = m.mala_get_tiling(0), m.mala_get_tiling(1)
+    _, dbk, dchunk = m.mala_get_tiling(2)
+    tau = args.tau
+
+    # ------------------------------------------------------------ inputs
+    cfg = W.CONFIGS[3]
+    x = W.make_prefill(cfg, device=dev)
+    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    B, HQ, N, D = q.shape
+    HKV = k.shape[1]
+    scale = x["scale"]
+    fo = dict(o=torch.empty_like(q), lse=torch.empty(q.shape[:3], device=dev),
+              kept=torch.empty((B, HQ, -(-N // fbq)), dtype=torch.int32, device=dev))
+    bo = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+              kept=torch.empty((B, HQ, -(-N // bbq)), dtype=torch.int32, device=dev))
+    dcfg = W.CONFIGS[5]
+    y = W.make_decode(dcfg, device=dev)
+    kc, vc, qs = y["k_cache"], y["v_cache"], y["q_steps"]
+    DB, DHQ, DHKV = kc.shape[0], qs.shape[2], kc.shape[1]
+    cache0, nsteps = y["cache"], y["steps"]
+    cap = kc.shape[2]
+    # the rows each step appends, staged outside the caches
+    k_new = kc[:, :, cache0:cache0 + nsteps].clone()
+    v_new = vc[:, :, cache0:cache0 + nsteps].clone()
+    seqlens = [torch.full((DB,), cache0 + t + 1, dtype=torch.int32, device=dev)
+               for t in range(nsteps)]
+    do_ = dict(o=torch.empty_like(qs[0]), lse=torch.empty(qs.shape[1:3], device=dev),
+               kept=torch.empty((DB, DHQ + DHKV), dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+
+    def prefill(tau_, events=True):
+        if events:
+            ev[0].record()
+        m.mala_fwd(q, k, v, tau_, softmax_scale=scale, out=fo)
+        if events:
+            ev[1].record()
+        m.mala_bwd(q, k, v, fo["o"], fo["lse"], do, tau_, softmax_scale=scale, out=bo,
+                   fast_grad=args.fast_grad, events=ev[2:5] if events else None,
+                   stages=(m.mala.BWD_PREP, m.mala.BWD_DKDV, m.mala.BWD_DQ) if events else None)
+
+    def decode(t, events=True):
+        n = cache0 + t + 1
+        kc[:, :, n - 1].copy_(k_new[:, :, t])          # append the current token (caller-owned)
+        vc[:, :, n - 1].copy_(v_new[:, :, t])
+        if events:
+            ev[5].record()
+        m.mala_decode(qs[t], kc, vc, seqlens[t], tau, max_n_k=n, softmax_scale=y["scale"],
+                      out=do_, events=ev[6:8] if events else None)
+
+    names = ["fwd", "bwd_prep", "bwd_dkdv", "bwd_dq", "append", "dec_split", "dec_combine"]
+
+    def phase_ms():
+        return [ev[i].elapsed_time(ev[i + 1]) for i in range(7)]
+
+    if args.profile:
+        prefill(tau, events=False)
+        decode(0, events=False)
+        torch.cuda.synchronize()
+        prefill(tau, events=False)
+        decode(1, events=False)
+        torch.cuda.synchronize()
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)                         # 1 GiB read + 1 GiB written
+        torch.cuda.synchronize()
+        print("profile run done: 2 steps + 1 GiB copy", flush=True)
+        return
+
+    only = args.only
+    # ------------------------------------------------------------ warmup + timed steps
+    for i in range(args.warmup):
+        if only in ("", "fwd", "bwd"):
+            prefill(tau)
+        if only in ("", "decode"):
+            decode(i % nsteps)
+    torch.cuda.synchronize()
+    acc = np.zeros(7)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if only in ("", "fwd", "bwd"):
+            prefill(tau)
+        if only in ("", "decode"):
+            decode(i % nsteps)
+        if only == "":
+            torch.cuda.synchronize()
+            acc += phase_ms()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / max(1, args.steps)
+    if only:
+        print(json.dumps({"only": only, "ms_per_step": wall}))
+        return
+    ph = acc / args.steps
+    fwd_ms, bwd_ms = ph[0], ph[1] + ph[2] + ph[3]
+    dec_us = (ph[5] + ph[6]) * 1e3
+    step_ms = float(ph.sum())
+
+    # counters of the last step
+    fk = fo["kept"].cpu().numpy()
+    bk_ = bo["kept"].cpu().numpy()
+    vis_f = fwd_tiles(N, N, fbq, fbk) * B * HQ
+    vis_b = bwd_tiles(N, N, bbq, bbk) * B * HQ
+    kept_f, kept_b = int(fk.sum()), int(bk_.sum())
+
+    # ------------------------------------------------------------ tau = 0, same kernels
+    for _ in range(args.warmup):
+        prefill(0.0)
+    torch.cuda.synchronize()
+    acc0 = np.zeros(7)
+    for _ in range(args.steps):
+        prefill(0.0)
+        torch.cuda.synchronize()
+        acc0 += phase_ms()
+    ph0 = acc0 / args.steps
+    fwd0_ms, bwd0_ms = ph0[0], ph0[1] + ph0[2] + ph0[3]
+
+    # ------------------------------------------------------------ decode: all steps
+    for t in range(nsteps):
+        decode(t)
+    torch.cuda.synchronize()
+    dacc = 0.0
+    dsplit = 0.0
+    for t in range(nsteps):
+        decode(t)
+        torch.cuda.synchronize()
+        p = phase_ms()
+        dacc += p[5] + p[6]
+        dsplit += p[5]
+    dec_all_us = dacc / nsteps * 1e3
+    dsplit_us = dsplit / nsteps * 1e3
+    dkept = do_["kept"].cpu().numpy()
+    n_last = cache0 + nsteps
+    dec_vtiles = int(dkept[:, DHQ:].sum())
+    dec_tiles_total = DB * DHKV * sum(min(4, -(-(min(n_last, c * dchunk + dchunk) - c * dchunk)
+                                                // dbk)) for c in range(-(-n_last // dchunk)))
+
+    # ------------------------------------------------------------ work accounting
+    pairs = B * HQ * causal_pairs(N)
+    dense_fwd = 4 * D * pairs
+    dense_bwd = 10 * D * pairs
+    dec_keys = DB * DHQ * (cache0 + 1)          # approx. per step (N_k of step 0)
+    dense_dec = 4 * D * DB * DHQ * (cache0 + nsteps // 2)
+    step_flops = dense_fwd + dense_bwd + dense_dec
+    value = step_flops / (step_ms * 1e-3) / 1e12
+    E_f = vis_f * fbq * fbk
+    S_f = kept_f * fbq * fbk
+    E_b = vis_b * bbq * bbk
+    S_b = kept_b * bbq * bbk
+    alg = {
+        "fwd": 2 * D * E_f + 2 * D * S_f,                         # QK on visited, PV on kept
+        "bwd_dkdv": 2 * D * E_b + 6 * D * S_b,                    # S on legal; dP, dV, dK on kept
+        "bwd_dq": 2 * D * S_b,                                    # dQ on kept
+    }
+    tms = {"fwd": ph[0], "bwd_dkdv": ph[2], "bwd_dq": ph[3]}
+    dec_bytes = (DB * DHKV * n_last * D * 2                      # every K row
+                 + dec_vtiles * dbk * D * 2                      # V of kept tiles
+                 + 2 * DB * DHQ * D * 2)                         # q in, o out
+    dominant = max(tms, key=lambda n: tms[n])
+    roof = {"kernel": dominant, "bound": "mfma",
+            "achieved": alg[dominant] / (tms[dominant] * 1e-3) / 1e12,
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["algorithmic_per_launch"] = alg[dominant]
+
+    out = {
+        "metric": "MALA fwd+bwd ms & effective TFLOP/s vs tau=0 dense at 32K/128K; decode us/step",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "wall_ms_per_step": round(wall, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill_32k_bf16_gqa32x8 fwd+bwd (B=1, Hq=32, Hkv=8, L=32768, "
+                               "d=128, tau=%g) + decode_128k_bf16_b8_gqa8x1 one step" % tau,
+                   "tau": tau, "grad_mode": "fast" if args.fast_grad else "split"},
+        "roofline": roof,
+        "prefill_32k": {
+            "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
+            "bwd_stage_ms": {"prep": round(ph[1], 3), "dkdv": round(ph[2], 3),
+                             "dq": round(ph[3], 3)},
+            "fwd_eff_tflops": round(dense_fwd / (fwd_ms * 1e-3) / 1e12, 1),
+            "bwd_eff_tflops": round(dense_bwd / (bwd_ms * 1e-3) / 1e12, 1),
+            "fwd_kept_frac": kept_f / vis_f, "bwd_kept_frac": kept_b / vis_b,
+            "slots_f": S_f / (B * HQ * N), "slots_b": S_b / (B * HQ * N),
+            "tau0_fwd_ms": round(fwd0_ms, 3), "tau0_bwd_ms": round(bwd0_ms, 3),
+            "speedup_vs_tau0": round((fwd0_ms + bwd0_ms) / (fwd_ms + bwd_ms), 4),
+            "alg_tflops": {n: round(alg[n] / (tms[n] * 1e-3) / 1e12, 1) for n in alg},
+        },
+        "decode_128k": {
+            "us_per_step": round(dec_all_us, 2), "split_us": round(dsplit_us, 2),
+            "append_us": round(ph[4] * 1e3, 2),
+            "v_tiles_kept_frac": dec_vtiles / dec_tiles_total,
+            "hbm_gbs": round(dec_bytes / (dsplit_us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(dec_bytes / (dsplit_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "bytes_per_step": dec_bytes,
+        },
+    }
+
+    # ------------------------------------------------------------ 128K prefill extra
+    if not args.no_128k:
+        del x, q, k, v, do, fo, bo
+        torch.cuda.empty_cache()
+        x4 = W.make_prefill(W.CONFIGS[4], device=dev)
+        q4, k4, v4, do4 = x4["q"], x4["k"], x4["v"], x4["do"]
+        n4 = q4.shape[2]
+        f4 = dict(o=torch.empty_like(q4), lse=torch.empty(q4.shape[:3], device=dev))
+        b4 = dict(dq=torch.empty_like(q4), dk=torch.empty_like(k4), dv=torch.empty_like(v4))
+        res = {}
+        for tau_ in (tau, 0.0):
+            for _ in range(max(1, args.warmup // 2)):
+                m.mala_fwd(q4, k4, v4, tau_, softmax_scale=x4["scale"], out=f4)
+                m.mala_bwd(q4, k4, v4, f4["o"], f4["lse"], do4, tau_, softmax_scale=x4["scale"],
+                           out=b4, fast_grad=args.fast_grad)
+            torch.cuda.synchronize()
+            tf = tb = 0.0
+            reps = max(1, args.steps // 2)
+            for _ in range(reps):
+                ev[0].record()
+                m.mala_fwd(q4, k4, v4, tau_, softmax_scale=x4["scale"], out=f4)
+                ev[1].record()
+                m.mala_bwd(q4, k4, v4, f4["o"], f4["lse"], do4, tau_, softmax_scale=x4["scale"],
+                           out=b4, fast_grad=args.fast_grad)
+                ev[2].record()
+                torch.cuda.synchronize()
+                tf += ev[0].elapsed_time(ev[1])
+                tb += ev[1].elapsed_time(ev[2])
+            res[tau_] = (tf / reps, tb / reps)
+        p4 = q4.shape[0] * q4.shape[1] * causal_pairs(n4)
+        out["prefill_128k"] = {
+            "fwd_ms": round(res[tau][0], 3), "bwd_ms": round(res[tau][1], 3),
+            "fwd_eff_tflops": round(4 * 128 * p4 / (res[tau][0] * 1e-3) / 1e12, 1),
+            "bwd_eff_tflops": round(10 * 128 * p4 / (res[tau][1] * 1e-3) / 1e12, 1),
+            "tau0_fwd_ms": round(res[0.0][0], 3), "tau0_bwd_ms": round(res[0.0][1], 3),
+            "speedup_vs_tau0": round(sum(res[0.0]) / sum(res[tau]), 4),
+        }
+        del x4, q4, k4, v4, do4, f4, b4
+        torch.cuda.empty_cache()
+        x = W.make_prefill(cfg, device=dev)   # for the CPU sample below
+        q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(q, k, v, do, scale, tau, (fbq, fbk), (bbq, bbk),
+                                           args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(q, k, v, do, scale, tau, ftile, btile, budget):
+    """Times the fp64 oracle on a bounded, seeded sample of 32-row query
+    blocks of the 32K problem (forward + backward of those rows), and reports
+    the dense-equivalent TFLOP/s of the sample."""
+    import numpy as np
+
+    from oracle import mala_oracle as O
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    B, HQ, N, D = q.shape
+    g = HQ // k.shape[1]
+    rng = np.random.default_rng(7)
+    bq = ftile[0]
+    nblk = -(-N // bq)
+    done_rows, flops, elapsed, nb = 0, 0.0, 0.0, 0
+    kv_cache = {}
+    while elapsed < budget and nb < 256:
+        h = int(rng.integers(HQ))
+        i = int(rng.integers(nblk))
+        kh = h // g
+        if kh not in kv_cache:
+            kv_cache[kh] = (k[0, kh].float().cpu().numpy().astype(np.float64)[None, None],
+                            v[0, kh].float().cpu().numpy().astype(np.float64)[None, None])
+        kn, vn = kv_cache[kh]
+        r0, r1 = i * bq, min(N, i * bq + bq)
+        qn = q[0, h].float().cpu().numpy().astype(np.float64)[None, None]
+        dn = do[0, h].float().cpu().numpy().astype(np.float64)[None, None]
+        t0 = time.perf_counter()
+        f = O.mala_fwd(qn, kn, vn, tau, scale, True, ftile[0], ftile[1], blocks=[(0, 0, i)])
+        o = np.nan_to_num(f["o"])
+        lse = np.nan_to_num(f["lse"])
+        O.mala_bwd(qn, kn, vn, o, lse, dn, tau, scale, True, btile[0], btile[1],
+                   qblocks=range(i * (bq // btile[0]), min(-(-N // btile[0]),
+                                                          (i + 1) * (bq // btile[0]))))
+        elapsed += time.perf_counter() - t0
+        nb += 1
+        rows = np.arange(r0, r1)
+        flops += 14 * D * float((rows + 1).sum())
+        done_rows += r1 - r0
+    return {"value": round(flops / elapsed / 1e12, 6) if elapsed else None, "unit": "TFLOP/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{nb} random 32-row query blocks (random heads) of the 32K problem, "
+                      f"forward + backward of their rows against all causal keys, numpy fp64; "
+                      f"{elapsed:.1f} s; dense-equivalent FLOPs / time",
+            "cpu": platform.processor() or platform.machine()}
+
+
+if __name__ == "__main__":
+    main()

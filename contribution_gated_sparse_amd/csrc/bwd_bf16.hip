@@ -69,15 +69,22 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int rows, int d, const bf
 }
 
 // ---------------------------------------------------------------- dK, dV
+// LDS: the block's K and V rows (B operands of S = Q K^T and dP = dO V^T,
+// staged once), and one 64-row query tile: Q and dO rows (A operands of S and
+// dP) plus their transposes (A operands of dK^T = Q^T dS and dV^T = dO^T P).
+// Single-buffered: the next tile is prefetched into registers during the
+// current one and stored between two barriers.
 template <int D>
 struct alignas(16) DkdvSmem {
-  bf16 q[2][64][D + 8];       // Q_i rows (A operand of S = Q K^T)
-  bf16 dout[2][64][D + 8];    // dO_i rows (A operand of dP = dO V^T)
-  bf16 qt[2][D][64 + 8];      // Q_i^T, rows permuted (A operand of dK^T = Q^T dS)
-  bf16 dot[2][D][64 + 8];     // dO_i^T, permuted (A operand of dV^T = dO^T P)
-  alignas(16) float z2[2][64];   // z_q * log2 e
-  float u2[2][64];            // z_q * log2 e + log2(tau / L_q): skip iff s2 < u2 everywhere
-  float dd[2][64];            // D_q
+  bf16 k[128][D + 8];
+  bf16 v[128][D + 8];
+  bf16 q[64][D + 8];
+  bf16 dout[64][D + 8];
+  bf16 qt[D][64 + 8];         // rows permuted within groups of 16
+  bf16 dot[D][64 + 8];
+  alignas(16) float z2[64];   // z_q * log2 e
+  float u2[64];               // z_q * log2 e + log2(tau / L_q): skip iff s2 < u2 everywhere
+  float dd[64];               // D_q
 };
 
 template <int D, bool kSplit>
@@ -90,7 +97,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   constexpr int KT = D / 16;      // k-steps over d
   constexpr int DB = D / 32;      // 32-row blocks of dK^T / dV^T
   constexpr int CPR = D / 8;      // 16-byte chunks per row
-  constexpr int QPT = 64 * CPR / 256 ;   // rows per thread when staging a 64-row tile
+  constexpr int QPT = 64 * CPR / 256;   // consecutive rows per thread when staging a tile
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hf = lane >> 5;
   const int bk_count = s.batch * s.hkv;
@@ -105,14 +112,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int tr64 = (s.nq + 63) / 64;
   const int key = kw0 + l32;
 
-  // K and V of this wave as B operands: lane (key l32, half hf) holds row[16t + 8hf .. +7].
-  const auto krs = make_rsrc(K + krow0 * D, (uint32_t)((size_t)s.nk * D * 2));
-  const auto vrs = make_rsrc(V + krow0 * D, (uint32_t)((size_t)s.nk * D * 2));
-  bf16x8 kr[KT], vr[KT];
-#pragma unroll
-  for (int t = 0; t < KT; ++t) {
-    kr[t] = buf_load16(krs, (uint32_t)(key * D + 16 * t + 8 * hf) * 2);
-    vr[t] = buf_load16(vrs, (uint32_t)(key * D + 16 * t + 8 * hf) * 2);
+  // stage the block's K and V rows (zero past N_k)
+  {
+    const auto krs = make_rsrc(K + krow0 * D, (uint32_t)((size_t)s.nk * D * 2));
+    const auto vrs = make_rsrc(V + krow0 * D, (uint32_t)((size_t)s.nk * D * 2));
+    for (int idx = tid; idx < 128 * CPR; idx += 256) {
+      const int r = idx / CPR, c = idx % CPR;
+      const uint32_t off = (uint32_t)((J * 128 + r) * D + 8 * c) * 2;
+      store16(&sm.k[r][8 * c], buf_load16(krs, off));
+      store16(&sm.v[r][8 * c], buf_load16(vrs, off));
+    }
   }
   f32x16 dk[DB], dv[DB];
 #pragma unroll
@@ -151,12 +160,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       dreg = q < s.nq ? Dq[qrow0 + q] : 0.f;
     }
   };
-  auto store_tile = [&](int buf, int it) {
+  auto store_tile = [&](int it) {
     const int i = i_start + it % n_i;
 #pragma unroll
     for (int p = 0; p < QPT; ++p) {
-      store16(&sm.q[buf][srow + p][8 * sc], qreg[p]);
-      store16(&sm.dout[buf][srow + p][8 * sc], oreg[p]);
+      store16(&sm.q[srow + p][8 * sc], qreg[p]);
+      store16(&sm.dout[srow + p][8 * sc], oreg[p]);
     }
     const int pos = perm16(srow);
 #pragma unroll
@@ -164,146 +173,120 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       if constexpr (QPT == 4) {
         bf16x4 a = {qreg[0][e], qreg[1][e], qreg[2][e], qreg[3][e]};
         bf16x4 c = {oreg[0][e], oreg[1][e], oreg[2][e], oreg[3][e]};
-        *reinterpret_cast<bf16x4*>(&sm.qt[buf][8 * sc + e][pos]) = a;
-        *reinterpret_cast<bf16x4*>(&sm.dot[buf][8 * sc + e][pos]) = c;
+        *reinterpret_cast<bf16x4*>(&sm.qt[8 * sc + e][pos]) = a;
+        *reinterpret_cast<bf16x4*>(&sm.dot[8 * sc + e][pos]) = c;
       } else {
         bf16x2 a = {qreg[0][e], qreg[1][e]};
         bf16x2 c = {oreg[0][e], oreg[1][e]};
-        *reinterpret_cast<bf16x2*>(&sm.qt[buf][8 * sc + e][pos]) = a;
-        *reinterpret_cast<bf16x2*>(&sm.dot[buf][8 * sc + e][pos]) = c;
+        *reinterpret_cast<bf16x2*>(&sm.qt[8 * sc + e][pos]) = a;
+        *reinterpret_cast<bf16x2*>(&sm.dot[8 * sc + e][pos]) = c;
       }
     }
     if (tid < 64) {
       const int q = i * 64 + tid;
       const float L = s.causal ? (float)(q + s.offset + 1) : (float)s.nk;
       const float z2 = zreg * 1.4426950408889634f;
-      sm.z2[buf][tid] = z2;
-      sm.u2[buf][tid] = z2 + (s.log2_tau - fast_log2(L));
-      sm.dd[buf][tid] = dreg;
+      sm.z2[tid] = z2;
+      sm.u2[tid] = z2 + (s.log2_tau - fast_log2(L));
+      sm.dd[tid] = dreg;
     }
   };
 
   if (total > 0) {
     load_tile(0);
-    store_tile(0, 0);
+    store_tile(0);
   }
   __syncthreads();
 
   for (int it = 0; it < total; ++it) {
-    const int buf = it & 1;
     const int h = hk * s.group + it / n_i;
     const int i = i_start + it % n_i;
     if (it + 1 < total) load_tile(it + 1);
     const int qt0 = i * 64;                 // first row of the tile
     const size_t bh = (size_t)b * s.hq + h;
 
-    // which of the two 32-row halves have a legal entry for this wave's keys
-    bool legal[2];
-#pragma unroll
+#pragma unroll 1
     for (int qb = 0; qb < 2; ++qb) {
+      // does this 32-row half have a legal entry for this wave's keys
       const int r0 = qt0 + 32 * qb;
-      legal[qb] = r0 < s.nq && kw0 < s.nk && (!s.causal || kw0 <= min(r0 + 31, s.nq - 1) + s.offset);
-    }
-    if (legal[0] || legal[1]) {
+      const bool legal =
+          r0 < s.nq && kw0 < s.nk && (!s.causal || kw0 <= min(r0 + 31, s.nq - 1) + s.offset);
+      if (!legal) continue;
       // ---- recompute S = Q K^T: lane (key l32, half hf), regs = queries
-      f32x16 sacc[2];
+      f32x16 sacc;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[qb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
 #pragma unroll
       for (int t = 0; t < KT; ++t)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          if (legal[qb])
-            sacc[qb] = mfma32(load16(&sm.q[buf][32 * qb + l32][16 * t + 8 * hf]), kr[t], sacc[qb]);
-      const bool boundary = (qt0 + 64 > s.nq) || (kw0 + kBK > s.nk) ||
-                            (s.causal && kw0 + kBK - 1 > qt0 + s.offset);
+        sacc = mfma32(load16(&sm.q[32 * qb + l32][16 * t + 8 * hf]),
+                      load16(&sm.k[32 * w + l32][16 * t + 8 * hf]), sacc);
+      const bool boundary = (r0 + 32 > s.nq) || (kw0 + kBK > s.nk) ||
+                            (s.causal && kw0 + kBK - 1 > r0 + s.offset);
       // ---- offline gate, Eq. 4: skip iff S - z < log(tau / L) on every legal entry
-      bool keep[2];
+      float x = kNegInf;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float x = kNegInf;
-        if (legal[qb]) {
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.u2[32 * qb + 8 * g + 4 * hf]);
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.u2[buf][32 * qb + 8 * g + 4 * hf]);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const int r = 4 * g + c;
-              const int q = qt0 + 32 * qb + 8 * g + 4 * hf + c;
-              bool ok = true;
-              if (boundary) ok = q < s.nq && key < s.nk && (!s.causal || key <= q + s.offset);
-              if (!ok) sacc[qb][r] = kNegInf;
-              const float y = ok ? fmaf(sacc[qb][r], s.scale_log2, -u[c]) : kNegInf;
-              x = fmaxf(x, y);
-            }
-          }
+        for (int c = 0; c < 4; ++c) {
+          const int r = 4 * g + c;
+          const int q = r0 + 8 * g + 4 * hf + c;
+          const bool ok = !boundary || ((q < s.nq) & (key < s.nk) &
+                                        ((key <= q + s.offset) | !s.causal));
+          sacc[r] = ok ? sacc[r] : kNegInf;
+          x = fmaxf(x, ok ? fmaf(sacc[r], s.scale_log2, -u[c]) : kNegInf);
         }
-        keep[qb] = wave_any(x >= 0.f);
       }
+      const bool keep = wave_any(x >= 0.f);
       // decisions: one bit per (query head, 32-row tile, 32-key tile)
       if (lane == 0) {
         const int j32 = kw0 / kBK;
+        const int i32 = r0 / kBQ;
+        if (keep) atomicOr(&bits[(bh * tr32 + i32) * words + (j32 >> 5)], 1u << (j32 & 31));
+        if (mask != nullptr) mask[(bh * tr32 + i32) * tc32 + j32] = keep ? 1 : 0;
+        if (kept != nullptr && keep) atomicAdd(&kept[bh * tr32 + i32], 1);
+      }
+      if (!keep) continue;
+      // ---- P = exp(S - z), dP = dO V^T, dS = P o (dP - D)
+      f32x16 dp;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          if (!legal[qb]) continue;
-          const int i32 = (qt0 >> 5) + qb;
-          if (keep[qb])
-            atomicOr(&bits[(bh * tr32 + i32) * words + (j32 >> 5)], 1u << (j32 & 31));
-          if (mask != nullptr) mask[(bh * tr32 + i32) * tc32 + j32] = keep[qb] ? 1 : 0;
-          if (kept != nullptr && keep[qb]) atomicAdd(&kept[bh * tr32 + i32], 1);
+      for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+        dp = mfma32(load16(&sm.dout[32 * qb + l32][16 * t + 8 * hf]),
+                    load16(&sm.v[32 * w + l32][16 * t + 8 * hf]), dp);
+      bf16x8 pb[2], dsb[2], dsl[2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 z = *reinterpret_cast<const f32x4*>(&sm.z2[32 * qb + 8 * g + 4 * hf]);
+        const f32x4 ddv = *reinterpret_cast<const f32x4*>(&sm.dd[32 * qb + 8 * g + 4 * hf]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int r = 4 * g + c;
+          const float p = fast_exp2(fmaf(sacc[r], s.scale_log2, -z[c]));
+          const float ds = p * (dp[r] - ddv[c]);
+          pb[r >> 3][r & 7] = (bf16)p;
+          const bf16 hi = (bf16)ds;
+          dsb[r >> 3][r & 7] = hi;
+          if constexpr (kSplit) dsl[r >> 3][r & 7] = (bf16)(ds - (float)hi);
         }
       }
-      if (keep[0] || keep[1]) {
-        // ---- P = exp(S - z), dP = dO V^T, dS = P o (dP - D)
-        f32x16 dp[2];
+      // ---- dV^T += dO^T P and dK^T += Q^T dS over the half's two 16-row k-steps
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+      for (int t = 0; t < 2; ++t) {
+        const int col = 32 * qb + 16 * t + 8 * hf;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) dp[qb][r] = 0.f;
-#pragma unroll
-        for (int t = 0; t < KT; ++t)
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            if (keep[qb])
-              dp[qb] = mfma32(load16(&sm.dout[buf][32 * qb + l32][16 * t + 8 * hf]), vr[t], dp[qb]);
-        bf16x8 pb[4], dsb[4], dsl[4];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          if (!keep[qb]) continue;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 z = *reinterpret_cast<const f32x4*>(&sm.z2[buf][32 * qb + 8 * g + 4 * hf]);
-            const f32x4 dd = *reinterpret_cast<const f32x4*>(&sm.dd[buf][32 * qb + 8 * g + 4 * hf]);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const int r = 4 * g + c;
-              const float p = fast_exp2(fmaf(sacc[qb][r], s.scale_log2, -z[c]));
-              const float ds = p * (dp[qb][r] - dd[c]);
-              pb[2 * qb + (r >> 3)][r & 7] = (bf16)p;
-              const bf16 hi = (bf16)ds;
-              dsb[2 * qb + (r >> 3)][r & 7] = hi;
-              if constexpr (kSplit) dsl[2 * qb + (r >> 3)][r & 7] = (bf16)(ds - (float)hi);
-            }
-          }
-        }
-        // ---- dV^T += dO^T P and dK^T += Q^T dS (k-steps of 16 query rows)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if (!keep[t >> 1]) continue;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            dv[db] = mfma32(load16(&sm.dot[buf][32 * db + l32][16 * t + 8 * hf]), pb[t], dv[db]);
-            const bf16x8 qa = load16(&sm.qt[buf][32 * db + l32][16 * t + 8 * hf]);
-            dk[db] = mfma32(qa, dsb[t], dk[db]);
-            if constexpr (kSplit) dk[db] = mfma32(qa, dsl[t], dk[db]);
-          }
+        for (int db = 0; db < DB; ++db) {
+          dv[db] = mfma32(load16(&sm.dot[32 * db + l32][col]), pb[t], dv[db]);
+          const bf16x8 qa = load16(&sm.qt[32 * db + l32][col]);
+          dk[db] = mfma32(qa, dsb[t], dk[db]);
+          if constexpr (kSplit) dk[db] = mfma32(qa, dsl[t], dk[db]);
         }
       }
     }
-    if (it + 1 < total) store_tile(buf ^ 1, it + 1);
-    __syncthreads();
+    __syncthreads();                       // every wave is done with tile it
+    if (it + 1 < total) store_tile(it + 1);
+    __syncthreads();                       // tile it + 1 is visible
   }
 
   // ---- store dK = scale * sum dS^T Q and dV (summed over the group's heads)
@@ -461,8 +444,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kk = key0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          bool ok = true;
-          if (boundary) ok = kk < s.nk && q < s.nq && (!s.causal || kk <= q + s.offset);
+          const bool ok = !boundary || ((kk < s.nk) & (q < s.nq) &
+                                        ((kk <= q + s.offset) | !s.causal));
           const float p = ok ? fast_exp2(fmaf(sacc[r], s.scale_log2, -z2)) : 0.f;
           const float ds = p * (dp[r] - dd);
           const bf16 hi = (bf16)ds;
@@ -512,11 +495,11 @@ size_t bwd_bits_words(const Shape& s) {
 hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* d_o, void* dq, void* dk,
                            void* dv, float* ws_d, uint32_t* ws_bits, int8_t* mask, int32_t* kept,
-                           hipStream_t st) {
+                           hipStream_t st, int stages) {
   const int rows = s.batch * s.hq * s.nq;
   const size_t nwords = bwd_bits_words(s);
   const size_t nkept = (size_t)s.batch * s.hq * ((s.nq + kBQ - 1) / kBQ);
-  {
+  if (stages & kStagePrep) {
     const size_t nmask =
         mask ? (size_t)s.batch * s.hq * ((s.nq + kBQ - 1) / kBQ) * ((s.nk + kBK - 1) / kBK) : 0;
     size_t work = (size_t)rows;
@@ -533,11 +516,11 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
   const int n_qb = (s.nq + 255) / 256;
   const dim3 g2((unsigned)(n_qb * s.batch * s.hq));
   auto launch = [&](auto dkdv, auto dqk) {
-    if (g1.x)
+    if (g1.x && (stages & kStageMain))
       hipLaunchKernelGGL(dkdv, g1, dim3(256), 0, st, s, (const bf16*)q, (const bf16*)k,
                          (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dk, (bf16*)dv,
                          ws_bits, mask, kept, n_kb);
-    if (g2.x)
+    if (g2.x && (stages & kStageDq))
       hipLaunchKernelGGL(dqk, g2, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
                          (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dq, ws_bits, n_qb);
   };

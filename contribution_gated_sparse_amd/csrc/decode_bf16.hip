@@ -295,16 +295,20 @@ hipError_t launch_decode_combine_f32(const DecodeShape& s, const float* ws, floa
 
 hipError_t launch_decode_bf16(const DecodeShape& s, const void* q, const void* kc, const void* vc,
                               const int32_t* seqlens, void* o, float* lse, float* ws,
-                              int8_t* mask, int32_t* kept, hipStream_t st) {
-  if (kept != nullptr) {
-    hipError_t e = launch_fill_i32(kept, 0, (size_t)s.batch * (s.hq + s.hkv), st);
+                              int8_t* mask, int32_t* kept, hipStream_t st, int stages) {
+  if (stages & kStageMain) {
+    if (kept != nullptr) {
+      hipError_t e = launch_fill_i32(kept, 0, (size_t)s.batch * (s.hq + s.hkv), st);
+      if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(decode_split_kernel, dim3(s.n_chunks, s.batch * s.hkv), dim3(256), 0, st,
+                       s, (const bf16*)q, (const bf16*)kc, (const bf16*)vc, seqlens, ws, mask,
+                       kept);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(decode_split_kernel, dim3(s.n_chunks, s.batch * s.hkv), dim3(256), 0, st, s,
-                     (const bf16*)q, (const bf16*)kc, (const bf16*)vc, seqlens, ws, mask, kept);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_decode_combine_bf16(s, ws, o, lse, st);
+  if (stages & kStageCombine) return launch_decode_combine_bf16(s, ws, o, lse, st);
+  return hipSuccess;
 }
 
 }  // namespace mala

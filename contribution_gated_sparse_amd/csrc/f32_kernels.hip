@@ -476,7 +476,7 @@ hipError_t launch_fwd_f32(const Shape& s, const float* q, const float* k, const 
 hipError_t launch_bwd_f32(const Shape& s, const float* q, const float* k, const float* v,
                           const float* o, const float* lse, const float* d_o, float* dq, float* dk,
                           float* dv, float* ws_d, uint32_t* ws_bits, int8_t* mask, int32_t* kept,
-                          hipStream_t st) {
+                          hipStream_t st, int stages) {
   const int rows = s.batch * s.hq * s.nq;
   const size_t nwords = bwd_bits_words(s);
   const size_t tr = (s.nq + 31) / 32, tc = (s.nk + 31) / 32;
@@ -485,10 +485,13 @@ hipError_t launch_bwd_f32(const Shape& s, const float* q, const float* k, const 
   size_t work = (size_t)rows;
   if (nwords > work) work = nwords;
   if (nmask > work) work = nmask;
-  hipLaunchKernelGGL(bwd_prep_f32_kernel, dim3(grid_for(work)), dim3(256), 0, st, rows, s.d, o,
-                     d_o, ws_d, ws_bits, nwords, kept, nkept, mask, nmask);
-  const dim3 g1((unsigned)(((s.nk + 63) / 64) * s.batch * s.hkv));
-  const dim3 g2((unsigned)(((s.nq + 63) / 64) * s.batch * s.hq));
+  if (stages & kStagePrep)
+    hipLaunchKernelGGL(bwd_prep_f32_kernel, dim3(grid_for(work)), dim3(256), 0, st, rows, s.d, o,
+                       d_o, ws_d, ws_bits, nwords, kept, nkept, mask, nmask);
+  dim3 g1((unsigned)(((s.nk + 63) / 64) * s.batch * s.hkv));
+  dim3 g2((unsigned)(((s.nq + 63) / 64) * s.batch * s.hq));
+  if (!(stages & kStageMain)) g1.x = 0;
+  if (!(stages & kStageDq)) g2.x = 0;
   if (s.d == 128) {
     if (g1.x)
       hipLaunchKernelGGL(bwd_dkdv_f32_kernel<128>, g1, dim3(64), 0, st, s, q, k, v, d_o, lse,
@@ -509,7 +512,8 @@ hipError_t launch_bwd_f32(const Shape& s, const float* q, const float* k, const 
 
 hipError_t launch_decode_f32(const DecodeShape& s, const float* q, const float* kc,
                              const float* vc, const int32_t* seqlens, float* o, float* lse,
-                             float* ws, int8_t* mask, int32_t* kept, hipStream_t st) {
+                             float* ws, int8_t* mask, int32_t* kept, hipStream_t st, int stages) {
+  if (stages & kStageMain) {
   if (kept != nullptr) {
     hipError_t e = launch_fill_i32(kept, 0, (size_t)s.batch * (s.hq + s.hkv), st);
     if (e != hipSuccess) return e;
@@ -523,7 +527,9 @@ hipError_t launch_decode_f32(const DecodeShape& s, const float* q, const float* 
                        ws, mask, kept);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_decode_combine_f32(s, ws, o, lse, st);
+  }
+  if (stages & kStageCombine) return launch_decode_combine_f32(s, ws, o, lse, st);
+  return hipSuccess;
 }
 
 }  // namespace mala

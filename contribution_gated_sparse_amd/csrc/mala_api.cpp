@@ -146,6 +146,73 @@ mala_status check_decode(const mala_decode_problem* p, mala::DecodeShape* s) {
   return MALA_OK;
 }
 
+mala_status bwd_impl(int stages, const mala_problem* p, const void* q, const void* k,
+                     const void* v, const void* o, const float* lse, const void* d_o, void* dq,
+                     void* dk, void* dv, void* workspace, size_t ws_bytes, int8_t* tile_mask,
+                     int32_t* kept_tiles, void* stream) {
+  mala::Shape s;
+  MALA_TRY(check_problem(p, &s));
+  const bool rows = s.nq > 0;
+  MALA_TRY(check_ptr(q, "q", rows));
+  MALA_TRY(check_ptr(k, "k", true));
+  MALA_TRY(check_ptr(v, "v", true));
+  MALA_TRY(check_ptr(o, "o", rows));
+  MALA_TRY(check_ptr(lse, "lse", rows));
+  MALA_TRY(check_ptr(d_o, "d_o", rows));
+  MALA_TRY(check_ptr(dq, "dq", rows));
+  MALA_TRY(check_ptr(dk, "dk", true));
+  MALA_TRY(check_ptr(dv, "dv", true));
+  const size_t need = bwd_ws_bytes(s);
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(MALA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
+                workspace ? ws_bytes : 0, need);
+  if (!aligned(workspace, kWsAlign))
+    return fail(MALA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  float* ws_d = (float*)workspace;
+  uint32_t* ws_bits =
+      (uint32_t*)((char*)workspace + round_up(mala::bwd_ws_d_floats(s) * sizeof(float)));
+  hipError_t e;
+  if (s.dtype_is_bf16())
+    e = mala::launch_bwd_bf16(s, q, k, v, o, lse, d_o, dq, dk, dv, ws_d, ws_bits, tile_mask,
+                              kept_tiles, st, stages);
+  else
+    e = mala::launch_bwd_f32(s, (const float*)q, (const float*)k, (const float*)v,
+                             (const float*)o, lse, (const float*)d_o, (float*)dq, (float*)dk,
+                             (float*)dv, ws_d, ws_bits, tile_mask, kept_tiles, st, stages);
+  return finish(e, st, "mala_bwd launch");
+}
+
+mala_status decode_impl(int stages, const mala_decode_problem* p, const void* q,
+                        const void* k_cache, const void* v_cache, const int32_t* seqlens_k,
+                        void* o, float* lse, void* workspace, size_t ws_bytes, int8_t* tile_mask,
+                        int32_t* kept_tiles, void* stream) {
+  mala::DecodeShape s;
+  MALA_TRY(check_decode(p, &s));
+  MALA_TRY(check_ptr(q, "q", true));
+  MALA_TRY(check_ptr(k_cache, "k_cache", true));
+  MALA_TRY(check_ptr(v_cache, "v_cache", true));
+  MALA_TRY(check_ptr(o, "o", true));
+  MALA_TRY(check_ptr(lse, "lse", true));
+  if (seqlens_k == nullptr) return fail(MALA_ERR_INVALID_ARG, "seqlens_k is NULL");
+  const size_t need = round_up(mala::decode_ws_floats(s) * sizeof(float));
+  if (workspace == nullptr || ws_bytes < need)
+    return fail(MALA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
+                workspace ? ws_bytes : 0, need);
+  if (!aligned(workspace, kWsAlign))
+    return fail(MALA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if (p->dtype == MALA_BF16)
+    e = mala::launch_decode_bf16(s, q, k_cache, v_cache, seqlens_k, o, lse, (float*)workspace,
+                                 tile_mask, kept_tiles, st, stages);
+  else
+    e = mala::launch_decode_f32(s, (const float*)q, (const float*)k_cache,
+                                (const float*)v_cache, seqlens_k, (float*)o, lse,
+                                (float*)workspace, tile_mask, kept_tiles, st, stages);
+  return finish(e, st, "mala_decode launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -196,37 +263,18 @@ mala_status mala_bwd(const mala_problem* p, const void* q, const void* k, const 
                      const void* o, const float* lse, const void* d_o, void* dq, void* dk,
                      void* dv, void* workspace, size_t ws_bytes, int8_t* tile_mask,
                      int32_t* kept_tiles, void* stream) {
-  mala::Shape s;
-  MALA_TRY(check_problem(p, &s));
-  const bool rows = s.nq > 0;
-  MALA_TRY(check_ptr(q, "q", rows));
-  MALA_TRY(check_ptr(k, "k", true));
-  MALA_TRY(check_ptr(v, "v", true));
-  MALA_TRY(check_ptr(o, "o", rows));
-  MALA_TRY(check_ptr(lse, "lse", rows));
-  MALA_TRY(check_ptr(d_o, "d_o", rows));
-  MALA_TRY(check_ptr(dq, "dq", rows));
-  MALA_TRY(check_ptr(dk, "dk", true));
-  MALA_TRY(check_ptr(dv, "dv", true));
-  const size_t need = bwd_ws_bytes(s);
-  if (workspace == nullptr || ws_bytes < need)
-    return fail(MALA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
-                workspace ? ws_bytes : 0, need);
-  if (!aligned(workspace, kWsAlign))
-    return fail(MALA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-  hipStream_t st = (hipStream_t)stream;
-  float* ws_d = (float*)workspace;
-  uint32_t* ws_bits =
-      (uint32_t*)((char*)workspace + round_up(mala::bwd_ws_d_floats(s) * sizeof(float)));
-  hipError_t e;
-  if (s.dtype_is_bf16())
-    e = mala::launch_bwd_bf16(s, q, k, v, o, lse, d_o, dq, dk, dv, ws_d, ws_bits, tile_mask,
-                              kept_tiles, st);
-  else
-    e = mala::launch_bwd_f32(s, (const float*)q, (const float*)k, (const float*)v,
-                             (const float*)o, lse, (const float*)d_o, (float*)dq, (float*)dk,
-                             (float*)dv, ws_d, ws_bits, tile_mask, kept_tiles, st);
-  return finish(e, st, "mala_bwd launch");
+  return bwd_impl(mala::kStagesAll, p, q, k, v, o, lse, d_o, dq, dk, dv, workspace, ws_bytes,
+                  tile_mask, kept_tiles, stream);
+}
+
+mala_status mala_bwd_stage(int32_t stage, const mala_problem* p, const void* q, const void* k,
+                           const void* v, const void* o, const float* lse, const void* d_o,
+                           void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                           int8_t* tile_mask, int32_t* kept_tiles, void* stream) {
+  if (stage < MALA_BWD_PREP || stage > MALA_BWD_DQ)
+    return fail(MALA_ERR_INVALID_ARG, "unknown backward stage %d", stage);
+  return bwd_impl(1 << stage, p, q, k, v, o, lse, d_o, dq, dk, dv, workspace, ws_bytes,
+                  tile_mask, kept_tiles, stream);
 }
 
 size_t mala_decode_workspace_size(const mala_decode_problem* p) {
@@ -239,30 +287,19 @@ mala_status mala_decode(const mala_decode_problem* p, const void* q, const void*
                         const void* v_cache, const int32_t* seqlens_k, void* o, float* lse,
                         void* workspace, size_t ws_bytes, int8_t* tile_mask, int32_t* kept_tiles,
                         void* stream) {
-  mala::DecodeShape s;
-  MALA_TRY(check_decode(p, &s));
-  MALA_TRY(check_ptr(q, "q", true));
-  MALA_TRY(check_ptr(k_cache, "k_cache", true));
-  MALA_TRY(check_ptr(v_cache, "v_cache", true));
-  MALA_TRY(check_ptr(o, "o", true));
-  MALA_TRY(check_ptr(lse, "lse", true));
-  if (seqlens_k == nullptr) return fail(MALA_ERR_INVALID_ARG, "seqlens_k is NULL");
-  const size_t need = round_up(mala::decode_ws_floats(s) * sizeof(float));
-  if (workspace == nullptr || ws_bytes < need)
-    return fail(MALA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
-                workspace ? ws_bytes : 0, need);
-  if (!aligned(workspace, kWsAlign))
-    return fail(MALA_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e;
-  if (p->dtype == MALA_BF16)
-    e = mala::launch_decode_bf16(s, q, k_cache, v_cache, seqlens_k, o, lse, (float*)workspace,
-                                 tile_mask, kept_tiles, st);
-  else
-    e = mala::launch_decode_f32(s, (const float*)q, (const float*)k_cache,
-                                (const float*)v_cache, seqlens_k, (float*)o, lse,
-                                (float*)workspace, tile_mask, kept_tiles, st);
-  return finish(e, st, "mala_decode launch");
+  return decode_impl(mala::kStageMain | mala::kStageCombine, p, q, k_cache, v_cache, seqlens_k, o,
+                     lse, workspace, ws_bytes, tile_mask, kept_tiles, stream);
+}
+
+mala_status mala_decode_stage(int32_t stage, const mala_decode_problem* p, const void* q,
+                              const void* k_cache, const void* v_cache, const int32_t* seqlens_k,
+                              void* o, float* lse, void* workspace, size_t ws_bytes,
+                              int8_t* tile_mask, int32_t* kept_tiles, void* stream) {
+  if (stage != MALA_DECODE_SPLIT && stage != MALA_DECODE_COMBINE)
+    return fail(MALA_ERR_INVALID_ARG, "unknown decode stage %d", stage);
+  return decode_impl(stage == MALA_DECODE_SPLIT ? mala::kStageMain : mala::kStageCombine, p, q,
+                     k_cache, v_cache, seqlens_k, o, lse, workspace, ws_bytes, tile_mask,
+                     kept_tiles, stream);
 }
 
 const char* mala_last_error(void) { return g_err; }

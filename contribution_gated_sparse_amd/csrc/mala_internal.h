@@ -38,6 +38,13 @@ struct DecodeShape {
   double log_tau;
 };
 
+// Stage masks of the multi-kernel operations.
+constexpr int kStagePrep = 1;      // backward: D = rowsum(O o dO), clear bits/counters
+constexpr int kStageMain = 2;      // backward: dK/dV kernel; decode: split kernel
+constexpr int kStageDq = 4;        // backward: dQ kernel
+constexpr int kStageCombine = 4;   // decode: merge kernel
+constexpr int kStagesAll = 7;
+
 // Launchers (return hipGetLastError() of the launch).
 hipError_t launch_fwd_bf16(const Shape& s, const void* q, const void* k, const void* v, void* o,
                            float* lse, int8_t* mask, int32_t* kept, hipStream_t st);
@@ -47,18 +54,18 @@ hipError_t launch_fwd_f32(const Shape& s, const float* q, const float* k, const 
 hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* d_o, void* dq, void* dk,
                            void* dv, float* ws_d, uint32_t* ws_bits, int8_t* mask, int32_t* kept,
-                           hipStream_t st);
+                           hipStream_t st, int stages);
 hipError_t launch_bwd_f32(const Shape& s, const float* q, const float* k, const float* v,
                           const float* o, const float* lse, const float* d_o, float* dq, float* dk,
                           float* dv, float* ws_d, uint32_t* ws_bits, int8_t* mask, int32_t* kept,
-                          hipStream_t st);
+                          hipStream_t st, int stages);
 
 hipError_t launch_decode_bf16(const DecodeShape& s, const void* q, const void* kc, const void* vc,
                               const int32_t* seqlens, void* o, float* lse, float* ws,
-                              int8_t* mask, int32_t* kept, hipStream_t st);
+                              int8_t* mask, int32_t* kept, hipStream_t st, int stages);
 hipError_t launch_decode_f32(const DecodeShape& s, const float* q, const float* kc,
                              const float* vc, const int32_t* seqlens, float* o, float* lse,
-                             float* ws, int8_t* mask, int32_t* kept, hipStream_t st);
+                             float* ws, int8_t* mask, int32_t* kept, hipStream_t st, int stages);
 
 // Small helpers (fill kernels instead of memsets, so the calls stay capturable).
 hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t st);

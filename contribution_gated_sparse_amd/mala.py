@@ -50,7 +50,10 @@ class DecodeProblem(ctypes.Structure):
 
 
 EXPORTS = ("mala_get_tiling", "mala_fwd", "mala_bwd_workspace_size", "mala_bwd",
-           "mala_decode_workspace_size", "mala_decode", "mala_last_error", "mala_version")
+           "mala_bwd_stage", "mala_decode_workspace_size", "mala_decode", "mala_decode_stage",
+           "mala_last_error", "mala_version")
+BWD_PREP, BWD_DKDV, BWD_DQ = 0, 1, 2
+DECODE_SPLIT, DECODE_COMBINE = 0, 1
 
 _lib = None
 
@@ -78,6 +81,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mala_bwd_workspace_size.restype = sz
     lib.mala_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
     lib.mala_bwd.restype = i32
+    lib.mala_bwd_stage.argtypes = [i32, P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    lib.mala_bwd_stage.restype = i32
+    lib.mala_decode_stage.argtypes = [i32, DP, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    lib.mala_decode_stage.restype = i32
     lib.mala_decode_workspace_size.argtypes = [DP]
     lib.mala_decode_workspace_size.restype = sz
     lib.mala_decode.argtypes = [DP, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
@@ -166,8 +173,11 @@ def mala_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float, caus
 
 def mala_bwd(q, k, v, o, lse, d_o, tau: float, causal: bool = True,
              softmax_scale: Optional[float] = None, want_mask: bool = False,
-             want_kept: bool = True, out: Optional[dict] = None, fast_grad: bool = False) -> dict:
-    """Backward -> dict(dq, dk, dv, mask, kept)."""
+             want_kept: bool = True, out: Optional[dict] = None, fast_grad: bool = False,
+             stages=None, events=None) -> dict:
+    """Backward -> dict(dq, dk, dv, mask, kept). ``stages``: run only these
+    stages (BWD_PREP, BWD_DKDV, BWD_DQ) through mala_bwd_stage; ``events``:
+    optional list of torch.cuda.Event, one recorded after each stage run."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (d_o, "d_o")):
         _dev(t, n)
     p = make_problem(q, k, tau, causal, softmax_scale,
@@ -192,9 +202,15 @@ def mala_bwd(q, k, v, o, lse, d_o, tau: float, causal: bool = True,
     kept = out.get("kept") if want_kept else None
     if want_kept and kept is None:
         kept = torch.empty((p.batch, p.n_q_heads, tr), dtype=torch.int32, device=q.device)
-    _check(lib.mala_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o),
-                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _ptr(mask), _ptr(kept),
-                        _stream()))
+    args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq),
+            _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _ptr(mask), _ptr(kept), _stream())
+    if stages is None and events is None:
+        _check(lib.mala_bwd(*args))
+    else:
+        for n, stg in enumerate(stages if stages is not None else (BWD_PREP, BWD_DKDV, BWD_DQ)):
+            _check(lib.mala_bwd_stage(stg, *args))
+            if events is not None:
+                events[n].record()
     return dict(dq=dq, dk=dk, dv=dv, mask=mask, kept=kept, ws=ws)
 
 
@@ -209,7 +225,7 @@ def make_decode_problem(q, k_cache, tau: float, max_n_k: int,
 def mala_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                 seqlens_k: torch.Tensor, tau: float, max_n_k: Optional[int] = None,
                 softmax_scale: Optional[float] = None, want_mask: bool = False,
-                want_kept: bool = True, out: Optional[dict] = None) -> dict:
+                want_kept: bool = True, out: Optional[dict] = None, events=None) -> dict:
     """One split-KV decode step. q [B,Hq,d]; caches [B,Hkv,cap,d]; seqlens_k
     int32 [B] on the device (N_k including the current token)."""
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seqlens_k, "seqlens_k")):
@@ -239,9 +255,14 @@ def mala_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if want_kept and kept is None:
         kept = torch.empty((p.batch, p.n_q_heads + p.n_kv_heads), dtype=torch.int32,
                            device=q.device)
-    _check(lib.mala_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                           _ptr(seqlens_k), _ptr(o), _ptr(lse), _ptr(ws), ws.numel(), _ptr(mask),
-                           _ptr(kept), _stream()))
+    args = (ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k), _ptr(o),
+            _ptr(lse), _ptr(ws), ws.numel(), _ptr(mask), _ptr(kept), _stream())
+    if events is None:
+        _check(lib.mala_decode(*args))
+    else:
+        for n, stg in enumerate((DECODE_SPLIT, DECODE_COMBINE)):
+            _check(lib.mala_decode_stage(stg, *args))
+            events[n].record()
     return dict(o=o, lse=lse, mask=mask, kept=kept, ws=ws)
 
 

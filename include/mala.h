@@ -147,6 +147,24 @@ mala_status mala_bwd(const mala_problem* p, const void* q, const void* k, const 
                      void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
                      int8_t* tile_mask, int32_t* kept_tiles, void* stream);
 
+/*
+ * The backward as three stages, for callers that schedule or time them
+ * separately. Calling MALA_BWD_PREP, MALA_BWD_DKDV, MALA_BWD_DQ in this order
+ * on one stream with the same arguments and workspace is mala_bwd.
+ *   PREP: D = rowsum(O o dO) into the workspace; clears the decision bits and
+ *         kept_tiles, and sets tile_mask to -1.
+ *   DKDV: key-major pass: recomputes S, applies the offline gate (Eq. 4),
+ *         writes the decisions (bits, tile_mask, kept_tiles), dK and dV.
+ *   DQ:   query-major pass over the kept tiles recorded by DKDV: writes dQ.
+ * Same argument checks and errors as mala_bwd; an unknown stage is
+ * MALA_ERR_INVALID_ARG.
+ */
+enum { MALA_BWD_PREP = 0, MALA_BWD_DKDV = 1, MALA_BWD_DQ = 2 };
+mala_status mala_bwd_stage(int32_t stage, const mala_problem* p, const void* q, const void* k,
+                           const void* v, const void* o, const float* lse, const void* d_o,
+                           void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                           int8_t* tile_mask, int32_t* kept_tiles, void* stream);
+
 /* Bytes of device workspace mala_decode needs (per-split partial states). */
 size_t mala_decode_workspace_size(const mala_decode_problem* p);
 
@@ -171,6 +189,18 @@ mala_status mala_decode(const mala_decode_problem* p, const void* q, const void*
                         const void* v_cache, const int32_t* seqlens_k, void* o, float* lse,
                         void* workspace, size_t ws_bytes, int8_t* tile_mask,
                         int32_t* kept_tiles, void* stream);
+
+/*
+ * Split-KV decode as two stages (MALA_DECODE_SPLIT then MALA_DECODE_COMBINE,
+ * same arguments and workspace, one stream) is mala_decode. SPLIT scores every
+ * key, gates the tiles of each split and writes the partial states (and the
+ * diagnostics); COMBINE merges them into o and lse.
+ */
+enum { MALA_DECODE_SPLIT = 0, MALA_DECODE_COMBINE = 1 };
+mala_status mala_decode_stage(int32_t stage, const mala_decode_problem* p, const void* q,
+                              const void* k_cache, const void* v_cache, const int32_t* seqlens_k,
+                              void* o, float* lse, void* workspace, size_t ws_bytes,
+                              int8_t* tile_mask, int32_t* kept_tiles, void* stream);
 
 /* Description of the last error on the calling thread ("" if none). */
 const char* mala_last_error(void);
