@@ -31,16 +31,7 @@ namespace mala {
 namespace {
 
 constexpr int kBQ = 32;     // query rows per backward decision tile
-constexpr int kBK = 32;     // keys per backward decision tile
-
-// Same permutation as the forward's V^T layout: position of row x (0..63) in
-// a transposed tile so that 8 consecutive bf16 match the order of one 16-wide
-// k-step of an S accumulator (row 8(r/4) + 4(l/32) + r%4).
-__device__ __forceinline__ int perm16(int x) {
-  const int u = (x >> 2) & 3;
-  const int pu = (u == 1) ? 2 : (u == 2 ? 1 : u);
-  return (x & ~15) + 4 * pu + (x & 3);
-}
+constexpr int kBK = 16;     // keys per backward decision tile
 
 // ---------------------------------------------------------------- prep
 __global__ __launch_bounds__(256) void bwd_prep_kernel(int rows, int d, const bf16* __restrict__ O,
@@ -69,37 +60,38 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int rows, int d, const bf
 }
 
 // ---------------------------------------------------------------- dK, dV
-// LDS: the block's K and V rows (B operands of S = Q K^T and dP = dO V^T,
-// staged once), and one 64-row query tile: Q and dO rows (A operands of S and
-// dP) plus their transposes (A operands of dK^T = Q^T dS and dV^T = dO^T P).
-// Single-buffered: the next tile is prefetched into registers during the
-// current one and stored between two barriers.
+// A workgroup owns 128 keys of one KV head: 8 waves x 16 keys. Each wave keeps
+// its K and V rows in registers as the B operands of S = Q K^T and
+// dP = dO V^T (16x16x32 MFMA) and accumulates dK^T, dV^T (64 registers).
+// The query side streams through LDS in 32-row steps: Q and dO rows,
+// double-buffered; their transposes, the A operands of dK^T = Q^T dS and
+// dV^T = dO^T P, come from the same row-major tiles through transposing LDS
+// reads. One backward decision covers 32 query rows x 16 keys: the wave's
+// whole step.
 template <int D>
 struct alignas(16) DkdvSmem {
-  bf16 k[128][D + 8];
-  bf16 v[128][D + 8];
-  bf16 q[64][D + 8];
-  bf16 dout[64][D + 8];
-  bf16 qt[D][64 + 8];         // rows permuted within groups of 16
-  bf16 dot[D][64 + 8];
-  alignas(16) float z2[64];   // z_q * log2 e
-  float u2[64];               // z_q * log2 e + log2(tau / L_q): skip iff s2 < u2 everywhere
-  float dd[64];               // D_q
+  static constexpr int kStride = D + (D == 128 ? 24 : 40);   // conflict-free b128 and tr reads
+  bf16 q[2][32][kStride];
+  bf16 dout[2][32][kStride];
+  alignas(16) float z2[2][32];  // z_q * log2 e
+  float u2[2][32];              // z_q * log2 e + log2(tau / L_q): skip iff s2 < u2 everywhere
+  float dd[2][32];              // D_q
 };
 
 template <int D, bool kSplit>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     Shape s, const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dq,
     bf16* __restrict__ dK, bf16* __restrict__ dV, uint32_t* __restrict__ bits,
     int8_t* __restrict__ mask, int32_t* __restrict__ kept, int n_kb) {
   __shared__ DkdvSmem<D> sm;
-  constexpr int KT = D / 16;      // k-steps over d
-  constexpr int DB = D / 32;      // 32-row blocks of dK^T / dV^T
+  constexpr int ST = DkdvSmem<D>::kStride;
+  constexpr int KS = D / 32;      // 32-wide k-steps over d (16x16x32 MFMA)
+  constexpr int DB = D / 16;      // 16-row blocks of dK^T / dV^T
   constexpr int CPR = D / 8;      // 16-byte chunks per row
-  constexpr int QPT = 64 * CPR / 256;   // consecutive rows per thread when staging a tile
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
   const int bk_count = s.batch * s.hkv;
   const int J = (int)(blockIdx.x / bk_count);          // key block (0 = longest)
   const int bkv = (int)(blockIdx.x % bk_count);
@@ -107,214 +99,197 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int kw0 = J * 128 + w * kBK;                   // this wave's first key
   const size_t krow0 = ((size_t)b * s.hkv + hk) * (size_t)s.nk;
   const int tr32 = (s.nq + kBQ - 1) / kBQ;
-  const int tc32 = (s.nk + kBK - 1) / kBK;
-  const int words = (tc32 + 31) / 32;
-  const int tr64 = (s.nq + 63) / 64;
-  const int key = kw0 + l32;
+  const int tc16 = (s.nk + kBK - 1) / kBK;
+  const int words = (tc16 + 31) / 32;
+  const int key = kw0 + l16;
 
-  // stage the block's K and V rows (zero past N_k)
+  // K and V rows of this wave as B operands: lane (key l16, group g) holds
+  // row[32 t + 8 g .. + 7]; rows past N_k read as zeros.
+  bf16x8 kr[KS], vr[KS];
   {
     const auto krs = make_rsrc(K + krow0 * D, (uint32_t)((size_t)s.nk * D * 2));
     const auto vrs = make_rsrc(V + krow0 * D, (uint32_t)((size_t)s.nk * D * 2));
-    for (int idx = tid; idx < 128 * CPR; idx += 256) {
-      const int r = idx / CPR, c = idx % CPR;
-      const uint32_t off = (uint32_t)((J * 128 + r) * D + 8 * c) * 2;
-      store16(&sm.k[r][8 * c], buf_load16(krs, off));
-      store16(&sm.v[r][8 * c], buf_load16(vrs, off));
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      kr[t] = buf_load16(krs, (uint32_t)(key * D + 32 * t + 8 * g) * 2);
+      vr[t] = buf_load16(vrs, (uint32_t)(key * D + 32 * t + 8 * g) * 2);
     }
   }
-  f32x16 dk[DB], dv[DB];
+  f32x4 dk[DB], dv[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { dk[db][r] = 0.f; dv[db][r] = 0.f; }
+    for (int r = 0; r < 4; ++r) { dk[db][r] = 0.f; dv[db][r] = 0.f; }
 
-  // first query tile (64 rows) with a legal entry for the block's first key
+  // first 32-row step with a legal entry for the block's first key
   int i_start = 0;
   if (s.causal) {
-    const int need = J * 128 - s.offset;              // smallest legal row of key J*128
-    i_start = need <= 0 ? 0 : need / 64;
+    const int need = J * 128 - s.offset;
+    i_start = need <= 0 ? 0 : need / 32;
   }
-  const int n_i = tr64 - i_start;
-  const int total = s.group * n_i;                    // (head, query tile) iterations
+  const int n_i = tr32 - i_start;
+  const int total = s.group * n_i;                     // (head, 32-row step) pairs
 
-  // staging: thread owns QPT consecutive rows x one 16-byte column chunk
-  const int sc = tid % CPR, srow = (tid / CPR) * QPT;
-  bf16x8 qreg[QPT], oreg[QPT];
+  // staging: 32 rows x CPR chunks of Q and of dO, one chunk each per thread
+  const int srow = tid / CPR, sc = tid % CPR;
+  const bool stager = tid < 32 * CPR;
+  bf16x8 qreg = zero8(), oreg = zero8();
   float zreg = 0.f, dreg = 0.f;
-  auto load_tile = [&](int it) {
+  auto load_step = [&](int it) {
     const int h = hk * s.group + it / n_i;
     const int i = i_start + it % n_i;
     const size_t qrow0 = ((size_t)b * s.hq + h) * (size_t)s.nq;
-    const auto qrs = make_rsrc(Q + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
-    const auto ors = make_rsrc(dO + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
-#pragma unroll
-    for (int p = 0; p < QPT; ++p) {
-      const uint32_t off = (uint32_t)((i * 64 + srow + p) * D + 8 * sc) * 2;
-      qreg[p] = buf_load16(qrs, off);
-      oreg[p] = buf_load16(ors, off);
+    if (stager) {
+      const auto qrs = make_rsrc(Q + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
+      const auto ors = make_rsrc(dO + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
+      const uint32_t off = (uint32_t)((i * 32 + srow) * D + 8 * sc) * 2;
+      qreg = buf_load16(qrs, off);
+      oreg = buf_load16(ors, off);
     }
-    if (tid < 64) {
-      const int q = i * 64 + tid;
+    if (tid < 32) {
+      const int q = i * 32 + tid;
       zreg = q < s.nq ? LSE[qrow0 + q] : 0.f;
       dreg = q < s.nq ? Dq[qrow0 + q] : 0.f;
     }
   };
-  auto store_tile = [&](int it) {
+  auto store_step = [&](int buf, int it) {
     const int i = i_start + it % n_i;
-#pragma unroll
-    for (int p = 0; p < QPT; ++p) {
-      store16(&sm.q[srow + p][8 * sc], qreg[p]);
-      store16(&sm.dout[srow + p][8 * sc], oreg[p]);
+    if (stager) {
+      store16(&sm.q[buf][srow][8 * sc], qreg);
+      store16(&sm.dout[buf][srow][8 * sc], oreg);
     }
-    const int pos = perm16(srow);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (QPT == 4) {
-        bf16x4 a = {qreg[0][e], qreg[1][e], qreg[2][e], qreg[3][e]};
-        bf16x4 c = {oreg[0][e], oreg[1][e], oreg[2][e], oreg[3][e]};
-        *reinterpret_cast<bf16x4*>(&sm.qt[8 * sc + e][pos]) = a;
-        *reinterpret_cast<bf16x4*>(&sm.dot[8 * sc + e][pos]) = c;
-      } else {
-        bf16x2 a = {qreg[0][e], qreg[1][e]};
-        bf16x2 c = {oreg[0][e], oreg[1][e]};
-        *reinterpret_cast<bf16x2*>(&sm.qt[8 * sc + e][pos]) = a;
-        *reinterpret_cast<bf16x2*>(&sm.dot[8 * sc + e][pos]) = c;
-      }
-    }
-    if (tid < 64) {
-      const int q = i * 64 + tid;
+    if (tid < 32) {
+      const int q = i * 32 + tid;
       const float L = s.causal ? (float)(q + s.offset + 1) : (float)s.nk;
       const float z2 = zreg * 1.4426950408889634f;
-      sm.z2[tid] = z2;
-      sm.u2[tid] = z2 + (s.log2_tau - fast_log2(L));
-      sm.dd[tid] = dreg;
+      sm.z2[buf][tid] = z2;
+      sm.u2[buf][tid] = z2 + (s.log2_tau - fast_log2(L));
+      sm.dd[buf][tid] = dreg;
     }
   };
 
   if (total > 0) {
-    load_tile(0);
-    store_tile(0);
+    load_step(0);
+    store_step(0, 0);
   }
   __syncthreads();
 
   for (int it = 0; it < total; ++it) {
+    const int buf = it & 1;
     const int h = hk * s.group + it / n_i;
-    const int i = i_start + it % n_i;
-    if (it + 1 < total) load_tile(it + 1);
-    const int qt0 = i * 64;                 // first row of the tile
+    const int r0 = (i_start + it % n_i) * 32;          // first query row of the step
+    if (it + 1 < total) load_step(it + 1);
     const size_t bh = (size_t)b * s.hq + h;
-
-#pragma unroll 1
-    for (int qb = 0; qb < 2; ++qb) {
-      // does this 32-row half have a legal entry for this wave's keys
-      const int r0 = qt0 + 32 * qb;
-      const bool legal =
-          r0 < s.nq && kw0 < s.nk && (!s.causal || kw0 <= min(r0 + 31, s.nq - 1) + s.offset);
-      if (!legal) continue;
-      // ---- recompute S = Q K^T: lane (key l32, half hf), regs = queries
-      f32x16 sacc;
+    const bool legal =
+        r0 < s.nq && kw0 < s.nk && (!s.causal || kw0 <= min(r0 + 31, s.nq - 1) + s.offset);
+    if (legal) {
+      // ---- recompute S = Q K^T: lane (key l16, group g), regs = queries 16qb + 4g + r
+      f32x4 sacc[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int t = 0; t < KT; ++t)
-        sacc = mfma32(load16(&sm.q[32 * qb + l32][16 * t + 8 * hf]),
-                      load16(&sm.k[32 * w + l32][16 * t + 8 * hf]), sacc);
+        for (int r = 0; r < 4; ++r) sacc[qb][r] = 0.f;
+#pragma unroll
+      for (int t = 0; t < KS; ++t)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          sacc[qb] = mfma16(load16(&sm.q[buf][16 * qb + l16][32 * t + 8 * g]), kr[t], sacc[qb]);
       const bool boundary = (r0 + 32 > s.nq) || (kw0 + kBK > s.nk) ||
                             (s.causal && kw0 + kBK - 1 > r0 + s.offset);
       // ---- offline gate, Eq. 4: skip iff S - z < log(tau / L) on every legal entry
       float x = kNegInf;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.u2[32 * qb + 8 * g + 4 * hf]);
+      for (int qb = 0; qb < 2; ++qb) {
+        const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.u2[buf][16 * qb + 4 * g]);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int r = 4 * g + c;
-          const int q = r0 + 8 * g + 4 * hf + c;
+        for (int r = 0; r < 4; ++r) {
+          const int q = r0 + 16 * qb + 4 * g + r;
           const bool ok = !boundary || ((q < s.nq) & (key < s.nk) &
                                         ((key <= q + s.offset) | !s.causal));
-          sacc[r] = ok ? sacc[r] : kNegInf;
-          x = fmaxf(x, ok ? fmaf(sacc[r], s.scale_log2, -u[c]) : kNegInf);
+          sacc[qb][r] = ok ? sacc[qb][r] : kNegInf;
+          x = fmaxf(x, ok ? fmaf(sacc[qb][r], s.scale_log2, -u[r]) : kNegInf);
         }
       }
       const bool keep = wave_any(x >= 0.f);
-      // decisions: one bit per (query head, 32-row tile, 32-key tile)
       if (lane == 0) {
-        const int j32 = kw0 / kBK;
-        const int i32 = r0 / kBQ;
-        if (keep) atomicOr(&bits[(bh * tr32 + i32) * words + (j32 >> 5)], 1u << (j32 & 31));
-        if (mask != nullptr) mask[(bh * tr32 + i32) * tc32 + j32] = keep ? 1 : 0;
+        const int j16 = kw0 / kBK, i32 = r0 / kBQ;
+        if (keep) atomicOr(&bits[(bh * tr32 + i32) * words + (j16 >> 5)], 1u << (j16 & 31));
+        if (mask != nullptr) mask[(bh * tr32 + i32) * tc16 + j16] = keep ? 1 : 0;
         if (kept != nullptr && keep) atomicAdd(&kept[bh * tr32 + i32], 1);
       }
-      if (!keep) continue;
-      // ---- P = exp(S - z), dP = dO V^T, dS = P o (dP - D)
-      f32x16 dp;
+      if (keep) {
+        // ---- P = exp(S - z), dP = dO V^T, dS = P o (dP - D)
+        f32x4 dp[2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] = 0.f;
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int t = 0; t < KT; ++t)
-        dp = mfma32(load16(&sm.dout[32 * qb + l32][16 * t + 8 * hf]),
-                    load16(&sm.v[32 * w + l32][16 * t + 8 * hf]), dp);
-      bf16x8 pb[2], dsb[2], dsl[2];
+          for (int r = 0; r < 4; ++r) dp[qb][r] = 0.f;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 z = *reinterpret_cast<const f32x4*>(&sm.z2[32 * qb + 8 * g + 4 * hf]);
-        const f32x4 ddv = *reinterpret_cast<const f32x4*>(&sm.dd[32 * qb + 8 * g + 4 * hf]);
+        for (int t = 0; t < KS; ++t)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int r = 4 * g + c;
-          const float p = fast_exp2(fmaf(sacc[r], s.scale_log2, -z[c]));
-          const float ds = p * (dp[r] - ddv[c]);
-          pb[r >> 3][r & 7] = (bf16)p;
-          const bf16 hi = (bf16)ds;
-          dsb[r >> 3][r & 7] = hi;
-          if constexpr (kSplit) dsl[r >> 3][r & 7] = (bf16)(ds - (float)hi);
+          for (int qb = 0; qb < 2; ++qb)
+            dp[qb] = mfma16(load16(&sm.dout[buf][16 * qb + l16][32 * t + 8 * g]), vr[t], dp[qb]);
+        // B operands over the 32 query rows: element e < 4 is row 4g + e,
+        // e >= 4 is row 16 + 4g + (e - 4), matching the transposing reads below
+        bf16x8 pb, dsb, dsl;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const f32x4 z = *reinterpret_cast<const f32x4*>(&sm.z2[buf][16 * qb + 4 * g]);
+          const f32x4 ddv = *reinterpret_cast<const f32x4*>(&sm.dd[buf][16 * qb + 4 * g]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = fast_exp2(fmaf(sacc[qb][r], s.scale_log2, -z[r]));
+            const float ds = p * (dp[qb][r] - ddv[r]);
+            pb[4 * qb + r] = (bf16)p;
+            const bf16 hi = (bf16)ds;
+            dsb[4 * qb + r] = hi;
+            if constexpr (kSplit) dsl[4 * qb + r] = (bf16)(ds - (float)hi);
+          }
         }
-      }
-      // ---- dV^T += dO^T P and dK^T += Q^T dS over the half's two 16-row k-steps
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int col = 32 * qb + 16 * t + 8 * hf;
+        // ---- dV^T += dO^T P and dK^T += Q^T dS (A operands by transposing reads)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dv[db] = mfma32(load16(&sm.dot[32 * db + l32][col]), pb[t], dv[db]);
-          const bf16x8 qa = load16(&sm.qt[32 * db + l32][col]);
-          dk[db] = mfma32(qa, dsb[t], dk[db]);
-          if constexpr (kSplit) dk[db] = mfma32(qa, dsl[t], dk[db]);
+          const bf16x8 oa = cat8(lds_read_tr(&sm.dout[buf][0][0], ST, 4 * g, 16 * db, l16),
+                                 lds_read_tr(&sm.dout[buf][0][0], ST, 16 + 4 * g, 16 * db, l16));
+          dv[db] = mfma16(oa, pb, dv[db]);
+          const bf16x8 qa = cat8(lds_read_tr(&sm.q[buf][0][0], ST, 4 * g, 16 * db, l16),
+                                 lds_read_tr(&sm.q[buf][0][0], ST, 16 + 4 * g, 16 * db, l16));
+          dk[db] = mfma16(qa, dsb, dk[db]);
+          if constexpr (kSplit) dk[db] = mfma16(qa, dsl, dk[db]);
         }
       }
     }
-    __syncthreads();                       // every wave is done with tile it
-    if (it + 1 < total) store_tile(it + 1);
-    __syncthreads();                       // tile it + 1 is visible
+    if (it + 1 < total) store_step(buf ^ 1, it + 1);
+    __syncthreads();
   }
 
-  // ---- store dK = scale * sum dS^T Q and dV (summed over the group's heads)
+  // ---- store dK = scale * sum dS^T Q and dV (summed over the group's heads):
+  // lane (key l16, group g) holds d = 16 db + 4 g + r
   if (key >= s.nk) return;
   bf16* dkr = dK + (krow0 + key) * D;
   bf16* dvr = dV + (krow0 + key) * D;
   const float sc_nat = s.scale_log2 * 0.69314718055994531f;   // softmax scale
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4 a = {(bf16)(dk[db][4 * g] * sc_nat), (bf16)(dk[db][4 * g + 1] * sc_nat),
-                  (bf16)(dk[db][4 * g + 2] * sc_nat), (bf16)(dk[db][4 * g + 3] * sc_nat)};
-      bf16x4 c = {(bf16)dv[db][4 * g], (bf16)dv[db][4 * g + 1], (bf16)dv[db][4 * g + 2],
-                  (bf16)dv[db][4 * g + 3]};
-      *reinterpret_cast<bf16x4*>(dkr + 32 * db + 8 * g + 4 * hf) = a;
-      *reinterpret_cast<bf16x4*>(dvr + 32 * db + 8 * g + 4 * hf) = c;
-    }
+  for (int db = 0; db < DB; ++db) {
+    bf16x4 a = {(bf16)(dk[db][0] * sc_nat), (bf16)(dk[db][1] * sc_nat),
+                (bf16)(dk[db][2] * sc_nat), (bf16)(dk[db][3] * sc_nat)};
+    bf16x4 c = {(bf16)dv[db][0], (bf16)dv[db][1], (bf16)dv[db][2], (bf16)dv[db][3]};
+    *reinterpret_cast<bf16x4*>(dkr + 16 * db + 4 * g) = a;
+    *reinterpret_cast<bf16x4*>(dvr + 16 * db + 4 * g) = c;
+  }
   (void)n_kb;
 }
 
 // ---------------------------------------------------------------- dQ
+// A workgroup owns 256 query rows (8 waves x 32) of one (batch, query head).
+// Key tiles of 64 rows (K and V, row-major, double-buffered) stream through
+// LDS, only those that some wave of the block keeps; K^T, the A operand of
+// dQ^T = K^T dS^T, comes from the K tile through transposing reads.
 template <int D>
-struct DqSmem {
-  bf16 k[2][64][D + 8];       // K_j rows (A operand of S^T = K Q^T)
-  bf16 v[2][64][D + 8];       // V_j rows (A operand of dP^T = V dO^T)
-  bf16 kt[2][D][64 + 8];      // K_j^T, keys permuted (A operand of dQ^T = K^T dS^T)
-  uint32_t need[2];           // does any wave of the block keep a half of tile j
+struct alignas(16) DqSmem {
+  static constexpr int kStride = D + (D == 128 ? 24 : 40);
+  bf16 k[2][64][kStride];
+  bf16 v[2][64][kStride];
 };
 
 template <int D, bool kSplit>
@@ -323,12 +298,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dq,
     bf16* __restrict__ dQ, const uint32_t* __restrict__ bits, int n_qb) {
   __shared__ DqSmem<D> sm;
+  constexpr int ST = DqSmem<D>::kStride;
   constexpr int KT = D / 16, DB = D / 32, CPR = D / 8;
   constexpr int RPP = 512 / CPR;            // rows per load pass
   constexpr int KPASS = 64 / RPP;
-  constexpr int KPT = 64 / RPP;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int gg = lane >> 4, i16 = lane & 15;
   const int bh_count = s.batch * s.hq;
   const int I = n_qb - 1 - (int)(blockIdx.x / bh_count);
   const int bh = (int)(blockIdx.x % bh_count);
@@ -336,8 +312,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   const size_t qrow0 = (size_t)bh * (size_t)s.nq;
   const size_t krow0 = ((size_t)b * s.hkv + hk) * (size_t)s.nk;
   const int tr32 = (s.nq + kBQ - 1) / kBQ;
-  const int tc32 = (s.nk + kBK - 1) / kBK;
-  const int words = (tc32 + 31) / 32;
+  const int tc16 = (s.nk + kBK - 1) / kBK;
+  const int words = (tc16 + 31) / 32;
   const int q0 = I * 256 + w * 32;
   const bool active = q0 < s.nq;
   const int q = q0 + l32;
@@ -372,8 +348,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   auto load_tile = [&](int j) {
 #pragma unroll
     for (int p = 0; p < KPASS; ++p) {
-      // rows kr*KPT + p: consecutive per thread so K^T writes are packed
-      const uint32_t off = (uint32_t)((j * 64 + kr * KPT + p) * D + 8 * kc) * 2;
+      const uint32_t off = (uint32_t)((j * 64 + p * RPP + kr) * D + 8 * kc) * 2;
       kreg[p] = buf_load16(krs, off);
       vreg[p] = buf_load16(vrs, off);
     }
@@ -381,28 +356,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < KPASS; ++p) {
-      store16(&sm.k[buf][kr * KPT + p][8 * kc], kreg[p]);
-      store16(&sm.v[buf][kr * KPT + p][8 * kc], vreg[p]);
-    }
-    const int pos = perm16(kr * KPT);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (KPT == 2) {
-        bf16x2 x = {kreg[0][e], kreg[1][e]};
-        *reinterpret_cast<bf16x2*>(&sm.kt[buf][8 * kc + e][pos]) = x;
-      } else {
-        sm.kt[buf][8 * kc + e][pos] = kreg[0][e];
-      }
+      store16(&sm.k[buf][p * RPP + kr][8 * kc], kreg[p]);
+      store16(&sm.v[buf][p * RPP + kr][8 * kc], vreg[p]);
     }
   };
-  // Is either 32-key half of tile j kept by some wave of the block?
+  // decision bits of tile j (64 keys = four 16-key columns) for one 32-row block
+  auto tile_bits = [&](const uint32_t* row_bits, int j) -> uint32_t {
+    return (row_bits[(4 * j) >> 5] >> ((4 * j) & 31)) & 15u;
+  };
+  // Is any column of tile j kept by some wave of the block?
   auto block_needs = [&](int j) -> uint32_t {
     uint32_t any = 0;
     for (int ww = 0; ww < 8; ++ww) {
       const int qq = I * 256 + ww * 32;
       if (qq >= s.nq) break;
-      const uint32_t wd = bits[((size_t)bh * tr32 + qq / kBQ) * words + ((2 * j) >> 5)];
-      any |= (wd >> ((2 * j) & 31)) & 3u;
+      any |= tile_bits(bits + ((size_t)bh * tr32 + qq / kBQ) * words, j);
     }
     return any;
   };
@@ -424,12 +392,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     if (jn >= 0) load_tile(jn);
 
     if (active) {
-      const uint32_t wd = mybits[(2 * j) >> 5] >> ((2 * j) & 31);
+      const uint32_t wd = tile_bits(mybits, j);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        if (!((wd >> half) & 1u)) continue;       // skipped (or not legal) tile
+        const uint32_t cols = (wd >> (2 * half)) & 3u;   // the half's two 16-key columns
+        if (cols == 0) continue;
         const int key0 = j * 64 + 32 * half;
-        // ---- S^T = K Q^T: lane (query l32, half hf), regs = keys
+        // ---- S^T = K Q^T and dP^T = V dO^T: lane (query l32, half hf), regs = keys
         f32x16 sacc, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; dp[r] = 0.f; }
@@ -443,22 +412,26 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
         bf16x8 dsb[2], dsl[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
+          // key offset 8(r/4) + 4hf + r%4 lies in column r / 8 of the half
           const int kk = key0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const bool ok = !boundary || ((kk < s.nk) & (q < s.nq) &
-                                        ((kk <= q + s.offset) | !s.causal));
+          const bool ok = ((cols >> (r >> 3)) & 1u) &&
+                          (!boundary || ((kk < s.nk) & (q < s.nq) &
+                                         ((kk <= q + s.offset) | !s.causal)));
           const float p = ok ? fast_exp2(fmaf(sacc[r], s.scale_log2, -z2)) : 0.f;
           const float ds = p * (dp[r] - dd);
           const bf16 hi = (bf16)ds;
           dsb[r >> 3][r & 7] = hi;
           if constexpr (kSplit) dsl[r >> 3][r & 7] = (bf16)(ds - (float)hi);
         }
-        // ---- dQ^T += K^T dS^T
+        // ---- dQ^T += K^T dS^T; K^T element e of lane (d, hf) is key
+        // 16t + 4hf + e (e < 4) or 16t + 8 + 4hf + (e - 4)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
-          {
-            const bf16x8 ka = load16(&sm.kt[buf][32 * db + l32][32 * half + 16 * t + 8 * hf]);
+          for (int db = 0; db < DB; ++db) {
+            const int r0 = 32 * half + 16 * t + 4 * hf, c0 = 32 * db + 16 * (gg & 1);
+            const bf16x8 ka = cat8(lds_read_tr(&sm.k[buf][0][0], ST, r0, c0, i16),
+                                   lds_read_tr(&sm.k[buf][0][0], ST, r0 + 8, c0, i16));
             dq[db] = mfma32(ka, dsb[t], dq[db]);
             if constexpr (kSplit) dq[db] = mfma32(ka, dsl[t], dq[db]);
           }
@@ -488,8 +461,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
 size_t bwd_ws_d_floats(const Shape& s) { return (size_t)s.batch * s.hq * s.nq; }
 
 size_t bwd_bits_words(const Shape& s) {
-  const size_t tr32 = (s.nq + kBQ - 1) / kBQ, tc32 = (s.nk + kBK - 1) / kBK;
-  return (size_t)s.batch * s.hq * tr32 * ((tc32 + 31) / 32);
+  const size_t tr = (s.nq + kBQ - 1) / kBQ, tc = (s.nk + kBK - 1) / kBK;
+  return (size_t)s.batch * s.hq * tr * ((tc + 31) / 32);
 }
 
 hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const void* v,
@@ -517,7 +490,7 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
   const dim3 g2((unsigned)(n_qb * s.batch * s.hq));
   auto launch = [&](auto dkdv, auto dqk) {
     if (g1.x && (stages & kStageMain))
-      hipLaunchKernelGGL(dkdv, g1, dim3(256), 0, st, s, (const bf16*)q, (const bf16*)k,
+      hipLaunchKernelGGL(dkdv, g1, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
                          (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dk, (bf16*)dv,
                          ws_bits, mask, kept, n_kb);
     if (g2.x && (stages & kStageDq))

@@ -28,6 +28,12 @@ __device__ __forceinline__ bool half_any(bool p) {
   const int half = (threadIdx.x & 63) >> 5;
   return ((m >> (32 * half)) & 0xffffffffull) != 0;
 }
+// ballot restricted to the 16 lanes of this lane's quarter
+__device__ __forceinline__ bool quarter_any(bool p) {
+  const uint64_t m = __builtin_amdgcn_ballot_w64(p);
+  const int qtr = (threadIdx.x & 63) >> 4;
+  return ((m >> (16 * qtr)) & 0xffffull) != 0;
+}
 
 // ---------------------------------------------------------------- forward
 // Block = 64 lanes = 64 query rows = two 32-row decision blocks (lanes 0-31,
@@ -148,7 +154,7 @@ __global__ __launch_bounds__(256) void bwd_prep_f32_kernel(int rows, int d, cons
   }
 }
 
-// Key-major dK/dV: block = 64 lanes = 64 keys = two 32-key decision columns.
+// Key-major dK/dV: block = 64 lanes = 64 keys = four 16-key decision columns.
 template <int D>
 __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
     Shape s, const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
@@ -160,14 +166,14 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
   __shared__ float qs[32][D];
   __shared__ float os[32][D];
   __shared__ double zz[32], uu[32], dd[32];
-  const int t = threadIdx.x, half = t >> 5;
+  const int t = threadIdx.x, qtr = t >> 4;
   const int bk_count = s.batch * s.hkv;
   const int J = (int)(blockIdx.x / bk_count);
   const int bkv = (int)(blockIdx.x % bk_count);
   const int b = bkv / s.hkv, hk = bkv % s.hkv;
   const size_t krow0 = ((size_t)b * s.hkv + hk) * (size_t)s.nk;
   const int key = J * 64 + t;
-  const int tr = (s.nq + 31) / 32, tc = (s.nk + 31) / 32, words = (tc + 31) / 32;
+  const int tr = (s.nq + 31) / 32, tc = (s.nk + 15) / 16, words = (tc + 31) / 32;
   for (int e = 0; e < D; ++e) {
     kv[0][t][e] = key < s.nk ? K[(krow0 + key) * D + e] : 0.f;
     kv[1][t][e] = key < s.nk ? V[(krow0 + key) * D + e] : 0.f;
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
   Acc dk[D], dv[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) { dk[e] = 0; dv[e] = 0; }
-  const int kc0 = J * 64 + 32 * half;          // first key of this lane's column
+  const int kc0 = J * 64 + 16 * qtr;           // first key of this lane's column
   int i_start = 0;
   if (s.causal) {
     const int need = J * 64 - s.offset;
@@ -214,11 +220,11 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
         sc[qq] = ok ? acc * s.scale : -HUGE_VAL;
         if (ok) x = fmax(x, sc[qq] - uu[qq]);
       }
-      const bool keep = legal_tile && half_any(x >= 0.0);
-      if (legal_tile && (t & 31) == 0) {
-        const int j32 = kc0 / 32;
-        if (keep) atomicOr(&bits[(bh * tr + i) * words + (j32 >> 5)], 1u << (j32 & 31));
-        if (mask != nullptr) mask[(bh * tr + i) * tc + j32] = keep ? 1 : 0;
+      const bool keep = legal_tile && quarter_any(x >= 0.0);
+      if (legal_tile && (t & 15) == 0) {
+        const int j16 = kc0 / 16;
+        if (keep) atomicOr(&bits[(bh * tr + i) * words + (j16 >> 5)], 1u << (j16 & 31));
+        if (mask != nullptr) mask[(bh * tr + i) * tc + j16] = keep ? 1 : 0;
         if (keep && kept != nullptr) atomicAdd(&kept[bh * tr + i], 1);
       }
       if (keep) {
@@ -254,8 +260,8 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
     float* __restrict__ dQ, const uint32_t* __restrict__ bits) {
   using Acc = typename std::conditional<D == 64, double, float>::type;
   __shared__ float dorow[64][D + 1];
-  __shared__ float ks[32][D];
-  __shared__ float vs[32][D];
+  __shared__ float ks[16][D];
+  __shared__ float vs[16][D];
   const int t = threadIdx.x, half = t >> 5;
   const int bh_count = s.batch * s.hq;
   const int blk = (int)(blockIdx.x / bh_count);
@@ -264,7 +270,7 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
   const size_t qrow0 = (size_t)bh * s.nq, krow0 = ((size_t)b * s.hkv + hk) * (size_t)s.nk;
   const int q = blk * 64 + t;
   const bool valid = q < s.nq;
-  const int tr = (s.nq + 31) / 32, tc = (s.nk + 31) / 32, words = (tc + 31) / 32;
+  const int tr = (s.nq + 31) / 32, tc = (s.nk + 15) / 16, words = (tc + 31) / 32;
   float qr[D];
   Acc dq[D];
 #pragma unroll
@@ -279,17 +285,17 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
   const uint32_t* mybits = bits + ((size_t)bh * tr + i32) * words;
   for (int j = 0; j < tc; ++j) {
     __syncthreads();
-    const int r = t & 31, c0 = (t >> 5) * (D / 2);
-    const int kk = j * 32 + r;
-    for (int e = c0; e < c0 + D / 2; ++e) {
+    const int r = t & 15, c0 = (t >> 4) * (D / 4);
+    const int kk = j * 16 + r;
+    for (int e = c0; e < c0 + D / 4; ++e) {
       ks[r][e] = kk < s.nk ? K[(krow0 + kk) * D + e] : 0.f;
       vs[r][e] = kk < s.nk ? V[(krow0 + kk) * D + e] : 0.f;
     }
     __syncthreads();
     const bool keep = valid && ((mybits[j >> 5] >> (j & 31)) & 1u);
     if (!keep) continue;
-    for (int k = 0; k < 32; ++k) {
-      const int key = j * 32 + k;
+    for (int k = 0; k < 16; ++k) {
+      const int key = j * 16 + k;
       if (!(key < s.nk && (!s.causal || key <= q + s.offset))) continue;
       double acc = 0.0, dp = 0.0;
 #pragma unroll 16
@@ -479,7 +485,7 @@ hipError_t launch_bwd_f32(const Shape& s, const float* q, const float* k, const 
                           hipStream_t st, int stages) {
   const int rows = s.batch * s.hq * s.nq;
   const size_t nwords = bwd_bits_words(s);
-  const size_t tr = (s.nq + 31) / 32, tc = (s.nk + 31) / 32;
+  const size_t tr = (s.nq + 31) / 32, tc = (s.nk + 15) / 16;
   const size_t nkept = (size_t)s.batch * s.hq * tr;
   const size_t nmask = mask ? (size_t)s.batch * s.hq * tr * tc : 0;
   size_t work = (size_t)rows;

@@ -12,7 +12,7 @@ namespace mala {
 constexpr int kFwdBq = 32;      // query rows per forward decision block (one wave)
 constexpr int kFwdBk = 64;      // keys per forward tile
 constexpr int kBwdBq = 32;      // query rows per backward tile
-constexpr int kBwdBk = 32;      // keys per backward tile (refines the forward tile)
+constexpr int kBwdBk = 16;      // keys per backward tile (refines the forward tile)
 constexpr int kDecBk = 64;      // keys per decode tile
 constexpr int kDecChunk = 256;  // keys per decode split
 

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_tiling(lib):
     assert M.mala_get_tiling(M.OP_FWD) == (32, 64, 0)
-    assert M.mala_get_tiling(M.OP_BWD) == (32, 32, 0)
+    assert M.mala_get_tiling(M.OP_BWD) == (32, 16, 0)
     assert M.mala_get_tiling(M.OP_DECODE) == (1, 64, 256)
     fb = M.mala_get_tiling(M.OP_FWD)
     bb = M.mala_get_tiling(M.OP_BWD)
@@ -105,7 +105,7 @@ def test_backward_workspace(lib):
     p = prob()
     need = lib.mala_bwd_workspace_size(ctypes.byref(p))
     # D (B*Hq*Nq fp32) + decision bits, each rounded up to 256 bytes
-    tr, tc = -(-100 // 32), -(-100 // 32)
+    tr, tc = -(-100 // 32), -(-100 // 16)
     expect = -(-(4 * 100 * 4) // 256) * 256 + -(-(4 * tr * -(-tc // 32) * 4) // 256) * 256
     assert need == expect
     assert lib.mala_bwd_workspace_size(ctypes.byref(prob(head_dim=80))) == 0
