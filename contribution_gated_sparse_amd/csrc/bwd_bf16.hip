@@ -79,7 +79,7 @@ struct alignas(16) DkdvSmem {
 };
 
 template <int D, bool kSplit>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
     Shape s, const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dq,
     bf16* __restrict__ dK, bf16* __restrict__ dV, uint32_t* __restrict__ bits,
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
   constexpr int DB = D / 16;      // 16-row blocks of dK^T / dV^T
   constexpr int CPR = D / 8;      // 16-byte chunks per row
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int bk_count = s.batch * s.hkv;
   const int J = (int)(blockIdx.x / bk_count);          // key block (0 = longest)
@@ -172,6 +172,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     load_step(0);
     store_step(0, 0);
   }
+#pragma unroll
+  for (int t = 0; t < KS; ++t) {
+    settle(kr[t]);
+    settle(vr[t]);
+  }
   __syncthreads();
 
   for (int it = 0; it < total; ++it) {
@@ -183,6 +188,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
     const bool legal =
         r0 < s.nq && kw0 < s.nk && (!s.causal || kw0 <= min(r0 + 31, s.nq - 1) + s.offset);
     if (legal) {
+      // Every LDS operand of a phase is read before the phase's products so
+      // that the reads overlap the matrix work instead of waiting one by one.
+      // Row-major Q and dO rows (A operands of S and dP): row 16 qb + l16,
+      // columns 32 t + 8 g .. + 7.
+      bf16x8 qrow[KS][2], orow[KS][2];
+#pragma unroll
+      for (int t = 0; t < KS; ++t)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          qrow[t][qb] = load16(&sm.q[buf][16 * qb + l16][32 * t + 8 * g]);
+          orow[t][qb] = load16(&sm.dout[buf][16 * qb + l16][32 * t + 8 * g]);
+        }
       // ---- recompute S = Q K^T: lane (key l16, group g), regs = queries 16qb + 4g + r
       f32x4 sacc[2];
 #pragma unroll
@@ -192,8 +209,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 #pragma unroll
       for (int t = 0; t < KS; ++t)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          sacc[qb] = mfma16(load16(&sm.q[buf][16 * qb + l16][32 * t + 8 * g]), kr[t], sacc[qb]);
+        for (int qb = 0; qb < 2; ++qb) sacc[qb] = mfma16(qrow[t][qb], kr[t], sacc[qb]);
       const bool boundary = (r0 + 32 > s.nq) || (kw0 + kBK > s.nk) ||
                             (s.causal && kw0 + kBK - 1 > r0 + s.offset);
       // ---- offline gate, Eq. 4: skip iff S - z < log(tau / L) on every legal entry
@@ -218,6 +234,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
         if (kept != nullptr && keep) atomicAdd(&kept[bh * tr32 + i32], 1);
       }
       if (keep) {
+        // dO^T and Q^T, the A operands of dV^T = dO^T P and dK^T = Q^T dS,
+        // through transposing reads: element e < 4 is query row 4g + e,
+        // e >= 4 is row 16 + 4g + (e - 4), for column 16 db + l16.
+        bf16x8 ocol[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          ocol[db] = cat8(lds_read_tr(&sm.dout[buf][0][0], ST, 4 * g, 16 * db, l16),
+                          lds_read_tr(&sm.dout[buf][0][0], ST, 16 + 4 * g, 16 * db, l16));
         // ---- P = exp(S - z), dP = dO V^T, dS = P o (dP - D)
         f32x4 dp[2];
 #pragma unroll
@@ -227,10 +251,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int t = 0; t < KS; ++t)
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            dp[qb] = mfma16(load16(&sm.dout[buf][16 * qb + l16][32 * t + 8 * g]), vr[t], dp[qb]);
-        // B operands over the 32 query rows: element e < 4 is row 4g + e,
-        // e >= 4 is row 16 + 4g + (e - 4), matching the transposing reads below
+          for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma16(orow[t][qb], vr[t], dp[qb]);
+        bf16x8 qcol[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          qcol[db] = cat8(lds_read_tr(&sm.q[buf][0][0], ST, 4 * g, 16 * db, l16),
+                          lds_read_tr(&sm.q[buf][0][0], ST, 16 + 4 * g, 16 * db, l16));
+        // B operands over the 32 query rows, in the row order of the
+        // transposing reads
         bf16x8 pb, dsb, dsl;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -246,16 +274,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(
             if constexpr (kSplit) dsl[4 * qb + r] = (bf16)(ds - (float)hi);
           }
         }
-        // ---- dV^T += dO^T P and dK^T += Q^T dS (A operands by transposing reads)
+        // ---- dV^T += dO^T P and dK^T += Q^T dS
+#pragma unroll
+        for (int db = 0; db < DB; ++db) dv[db] = mfma16(ocol[db], pb, dv[db]);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 oa = cat8(lds_read_tr(&sm.dout[buf][0][0], ST, 4 * g, 16 * db, l16),
-                                 lds_read_tr(&sm.dout[buf][0][0], ST, 16 + 4 * g, 16 * db, l16));
-          dv[db] = mfma16(oa, pb, dv[db]);
-          const bf16x8 qa = cat8(lds_read_tr(&sm.q[buf][0][0], ST, 4 * g, 16 * db, l16),
-                                 lds_read_tr(&sm.q[buf][0][0], ST, 16 + 4 * g, 16 * db, l16));
-          dk[db] = mfma16(qa, dsb, dk[db]);
-          if constexpr (kSplit) dk[db] = mfma16(qa, dsl, dk[db]);
+          dk[db] = mfma16(qcol[db], dsb, dk[db]);
+          if constexpr (kSplit) dk[db] = mfma16(qcol[db], dsl, dk[db]);
         }
       }
     }
@@ -303,7 +328,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   constexpr int RPP = 512 / CPR;            // rows per load pass
   constexpr int KPASS = 64 / RPP;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, hf = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int gg = lane >> 4, i16 = lane & 15;
   const int bh_count = s.batch * s.hq;
   const int I = n_qb - 1 - (int)(blockIdx.x / bh_count);
@@ -384,6 +410,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   if (j >= 0) {
     load_tile(j);
     store_tile(buf);
+  }
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    settle(qr[t]);
+    settle(orr[t]);
   }
   __syncthreads();
   while (j >= 0) {

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     int8_t* __restrict__ mask, int32_t* __restrict__ kept) {
   constexpr int D = 128;
   __shared__ DecSmem sm;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j16 = lane & 15, g = lane >> 4;
   const int c = blockIdx.x;
   const int b = blockIdx.y / s.hkv, hk = blockIdx.y % s.hkv;

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int l32 = lane & 31;
   const int hf = lane >> 5;
 
@@ -138,6 +138,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
     load_tile(top_b);
     store_tile(top_b & 1);
   }
+#pragma unroll
+  for (int t = 0; t < KT; ++t) settle(qr[t]);
   __syncthreads();
 
   for (int j = top_b; j >= 0; --j) {

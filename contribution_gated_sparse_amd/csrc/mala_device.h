@@ -52,6 +52,14 @@ __device__ __forceinline__ void store16(void* p, bf16x8 v) {
   *reinterpret_cast<bf16x8*>(p) = v;
 }
 
+// Registers loaded before a loop and read inside it: the waitcnt insertion
+// does not carry "already arrived" around the loop back edge, so every use in
+// the loop would wait on the vector-memory counter, which by then also counts
+// the loop's own prefetches. Touching the registers once here (an empty asm
+// that reads and redefines them) makes that wait happen once, before the loop.
+__device__ __forceinline__ void settle(bf16x8& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void settle(float& x) { asm volatile("" : "+v"(x)); }
+
 __device__ __forceinline__ bf16x8 zero8() {
   bf16x8 z;
 #pragma unroll
