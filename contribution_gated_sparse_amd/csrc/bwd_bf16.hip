@@ -4,18 +4,20 @@
 // Three kernels:
 //   1. bwd_prep:  D_q = rowsum(O o dO) in fp32, and clears the decision bits
 //                 and the kept-tile counters.
-//   2. bwd_dkdv:  key-major. A workgroup owns 128 keys of one KV head (4 waves
-//                 x 32 keys) and walks every query head of the group and every
-//                 64-row query tile from the diagonal down the sequence. Each
-//                 wave recomputes S = Q K^T for its 32 keys, applies the offline
-//                 gate (Eq. 4) per 32 x 32 tile against the saved z_q, and for
-//                 kept tiles forms P = exp(S - z), dP = dO V^T, dS = P o (dP - D)
-//                 and accumulates dV += P^T dO and dK += dS^T Q on chip. The
-//                 decisions are written as one bit per tile.
+//   2. bwd_dkdv:  key-major. A workgroup owns 128 keys of one KV head (8 waves
+//                 x 16 keys) and walks every query head of the group and every
+//                 32-row query step from the diagonal down the sequence. Each
+//                 wave recomputes S = Q K^T for its 16 keys, applies the
+//                 offline gate (Eq. 4) to its 32 x 16 tile against the saved
+//                 z_q, and for kept tiles forms P = exp(S - z), dP = dO V^T,
+//                 dS = P o (dP - D) and accumulates dV += P^T dO and
+//                 dK += dS^T Q on chip. The decisions are written as one bit
+//                 per tile.
 //   3. bwd_dq:    query-major. A workgroup owns 256 query rows (8 waves x 32);
 //                 each wave reads the decision bits of its rows and, for kept
 //                 tiles only, recomputes S, P, dP, dS and accumulates
-//                 dQ += dS K on chip. No atomics on dQ.
+//                 dQ += dS K on chip. No atomics on dQ. It also counts the
+//                 kept tiles of each 32-row block from the bits.
 // Both kernels see the same decisions, so dQ, dK and dV use one support.
 //
 // dS enters the dK and dQ products as a bf16 MFMA operand. By default it is
@@ -67,15 +69,20 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int rows, int d, const bf
 // double-buffered; their transposes, the A operands of dK^T = Q^T dS and
 // dV^T = dO^T P, come from the same row-major tiles through transposing LDS
 // reads. One backward decision covers 32 query rows x 16 keys: the wave's
-// whole step.
+// whole step. The 8 waves' decisions of a step form one byte of the decision
+// bit rows (the workgroup's 8 consecutive 16-key columns); it is gathered in
+// LDS and written with one plain store by the workgroup that owns it.
 template <int D>
 struct alignas(16) DkdvSmem {
-  static constexpr int kStride = D + (D == 128 ? 24 : 40);   // conflict-free b128 and tr reads
+  // row stride (bf16): 16-byte row reads and transposing reads of the
+  // 16x16x32 operand layouts both run without bank conflicts at 176 (D=128)
+  static constexpr int kStride = D == 128 ? 176 : 80;
   bf16 q[2][32][kStride];
   bf16 dout[2][32][kStride];
   alignas(16) float z2[2][32];  // z_q * log2 e
   float u2[2][32];              // z_q * log2 e + log2(tau / L_q): skip iff s2 < u2 everywhere
   float dd[2][32];              // D_q
+  uint32_t keep[2];             // bit w: wave w kept its tile in this step
 };
 
 template <int D, bool kSplit>
@@ -83,7 +90,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     Shape s, const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dq,
     bf16* __restrict__ dK, bf16* __restrict__ dV, uint32_t* __restrict__ bits,
-    int8_t* __restrict__ mask, int32_t* __restrict__ kept, int n_kb) {
+    int8_t* __restrict__ mask, int n_kb) {
   __shared__ DkdvSmem<D> sm;
   constexpr int ST = DkdvSmem<D>::kStride;
   constexpr int KS = D / 32;      // 32-wide k-steps over d (16x16x32 MFMA)
@@ -102,6 +109,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int tc16 = (s.nk + kBK - 1) / kBK;
   const int words = (tc16 + 31) / 32;
   const int key = kw0 + l16;
+  uint8_t* const bit_bytes = reinterpret_cast<uint8_t*>(bits);
 
   // K and V rows of this wave as B operands: lane (key l16, group g) holds
   // row[32 t + 8 g .. + 7]; rows past N_k read as zeros.
@@ -127,17 +135,14 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const int need = J * 128 - s.offset;
     i_start = need <= 0 ? 0 : need / 32;
   }
-  const int n_i = tr32 - i_start;
-  const int total = s.group * n_i;                     // (head, 32-row step) pairs
+  const int total = s.group * (tr32 - i_start);        // (head, 32-row step) pairs
 
   // staging: 32 rows x CPR chunks of Q and of dO, one chunk each per thread
   const int srow = tid / CPR, sc = tid % CPR;
   const bool stager = tid < 32 * CPR;
   bf16x8 qreg = zero8(), oreg = zero8();
   float zreg = 0.f, dreg = 0.f;
-  auto load_step = [&](int it) {
-    const int h = hk * s.group + it / n_i;
-    const int i = i_start + it % n_i;
+  auto load_step = [&](int h, int i) {
     const size_t qrow0 = ((size_t)b * s.hq + h) * (size_t)s.nq;
     if (stager) {
       const auto qrs = make_rsrc(Q + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
@@ -152,8 +157,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       dreg = q < s.nq ? Dq[qrow0 + q] : 0.f;
     }
   };
-  auto store_step = [&](int buf, int it) {
-    const int i = i_start + it % n_i;
+  auto store_step = [&](int buf, int i) {
     if (stager) {
       store16(&sm.q[buf][srow][8 * sc], qreg);
       store16(&sm.dout[buf][srow][8 * sc], oreg);
@@ -167,10 +171,19 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       sm.dd[buf][tid] = dreg;
     }
   };
+  // the previous step's decision byte -> bit row (bh, i32), byte J
+  auto flush_keep = [&](int buf, size_t bh, int i32) {
+    if (tid == 0) {
+      bit_bytes[(bh * tr32 + i32) * (size_t)words * 4 + J] = (uint8_t)sm.keep[buf];
+      sm.keep[buf] = 0u;
+    }
+  };
 
+  if (tid < 2) sm.keep[tid] = 0u;
+  int h = hk * s.group, i = i_start;                   // current step
   if (total > 0) {
-    load_step(0);
-    store_step(0, 0);
+    load_step(h, i);
+    store_step(0, i);
   }
 #pragma unroll
   for (int t = 0; t < KS; ++t) {
@@ -179,12 +192,16 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
   __syncthreads();
 
+  size_t prev_bh = 0;
+  int prev_i = -1;
   for (int it = 0; it < total; ++it) {
     const int buf = it & 1;
-    const int h = hk * s.group + it / n_i;
-    const int r0 = (i_start + it % n_i) * 32;          // first query row of the step
-    if (it + 1 < total) load_step(it + 1);
+    int hn = h, in = i + 1;                            // next step
+    if (in == tr32) { in = i_start; ++hn; }
+    if (it + 1 < total) load_step(hn, in);
+    if (prev_i >= 0) flush_keep(buf ^ 1, prev_bh, prev_i);
     const size_t bh = (size_t)b * s.hq + h;
+    const int r0 = i * 32;                             // first query row of the step
     const bool legal =
         r0 < s.nq && kw0 < s.nk && (!s.causal || kw0 <= min(r0 + 31, s.nq - 1) + s.offset);
     if (legal) {
@@ -228,10 +245,8 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       }
       const bool keep = wave_any(x >= 0.f);
       if (lane == 0) {
-        const int j16 = kw0 / kBK, i32 = r0 / kBQ;
-        if (keep) atomicOr(&bits[(bh * tr32 + i32) * words + (j16 >> 5)], 1u << (j16 & 31));
-        if (mask != nullptr) mask[(bh * tr32 + i32) * tc16 + j16] = keep ? 1 : 0;
-        if (kept != nullptr && keep) atomicAdd(&kept[bh * tr32 + i32], 1);
+        if (keep) atomicOr(&sm.keep[buf], 1u << w);
+        if (mask != nullptr) mask[(bh * tr32 + i) * tc16 + kw0 / kBK] = keep ? 1 : 0;
       }
       if (keep) {
         // dO^T and Q^T, the A operands of dV^T = dO^T P and dK^T = Q^T dS,
@@ -284,9 +299,14 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         }
       }
     }
-    if (it + 1 < total) store_step(buf ^ 1, it + 1);
+    prev_bh = bh;
+    prev_i = i;
+    if (it + 1 < total) store_step(buf ^ 1, in);
+    h = hn;
+    i = in;
     __syncthreads();
   }
+  if (prev_i >= 0) flush_keep((total - 1) & 1, prev_bh, prev_i);
 
   // ---- store dK = scale * sum dS^T Q and dV (summed over the group's heads):
   // lane (key l16, group g) holds d = 16 db + 4 g + r
@@ -310,20 +330,31 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 // Key tiles of 64 rows (K and V, row-major, double-buffered) stream through
 // LDS, only those that some wave of the block keeps; K^T, the A operand of
 // dQ^T = K^T dS^T, comes from the K tile through transposing reads.
+//
+// The K tile is read both as rows (16-byte reads, S^T = K Q^T) and through
+// transposing reads (K^T). No single row stride serves both without bank
+// conflicts, so K uses a stride of 160 (transposing reads conflict-free) and
+// permutes the 16-byte chunks of each row: chunk c of row r is stored at
+// chunk c ^ ((r / 4) % 4), which spreads 16 consecutive rows of one chunk
+// over all 64 banks. V is only read as rows (stride 136).
 template <int D>
 struct alignas(16) DqSmem {
-  static constexpr int kStride = D + (D == 128 ? 24 : 40);
-  bf16 k[2][64][kStride];
-  bf16 v[2][64][kStride];
+  static constexpr int kStrideK = D + 32;
+  static constexpr int kStrideV = D + 8;
+  bf16 k[2][64][kStrideK];
+  bf16 v[2][64][kStrideV];
 };
+// column (bf16 index) of element chunk `c` of K tile row `r`, after the swizzle
+__device__ __forceinline__ int kswz(int r, int c) { return 8 * (c ^ ((r >> 2) & 3)); }
 
 template <int D, bool kSplit>
 __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     Shape s, const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dq,
-    bf16* __restrict__ dQ, const uint32_t* __restrict__ bits, int n_qb) {
+    bf16* __restrict__ dQ, const uint32_t* __restrict__ bits, int32_t* __restrict__ kept,
+    int n_qb) {
   __shared__ DqSmem<D> sm;
-  constexpr int ST = DqSmem<D>::kStride;
+  constexpr int SK = DqSmem<D>::kStrideK, SV = DqSmem<D>::kStrideV;
   constexpr int KT = D / 16, DB = D / 32, CPR = D / 8;
   constexpr int RPP = 512 / CPR;            // rows per load pass
   constexpr int KPASS = 64 / RPP;
@@ -369,6 +400,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   const int ntiles = lastkey < 0 ? 0 : lastkey / 64 + 1;
   const uint32_t* mybits = bits + ((size_t)bh * tr32 + (active ? q0 / kBQ : 0)) * words;
 
+  // kept backward tiles of this wave's 32-row block: the population count of
+  // its decision bits
+  if (kept != nullptr && active) {
+    int cnt = 0;
+    for (int x = lane; x < words; x += 64) cnt += __popc(mybits[x]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+    if (lane == 0) kept[(size_t)bh * tr32 + q0 / kBQ] = cnt;
+  }
+
   bf16x8 kreg[KPASS], vreg[KPASS];
   const int kc = tid % CPR, kr = tid / CPR;
   auto load_tile = [&](int j) {
@@ -382,8 +423,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < KPASS; ++p) {
-      store16(&sm.k[buf][p * RPP + kr][8 * kc], kreg[p]);
-      store16(&sm.v[buf][p * RPP + kr][8 * kc], vreg[p]);
+      const int row = p * RPP + kr;
+      store16(&sm.k[buf][row][kswz(row, kc)], kreg[p]);
+      store16(&sm.v[buf][row][8 * kc], vreg[p]);
     }
   };
   // decision bits of tile j (64 keys = four 16-key columns) for one 32-row block
@@ -430,13 +472,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
         if (cols == 0) continue;
         const int key0 = j * 64 + 32 * half;
         // ---- S^T = K Q^T and dP^T = V dO^T: lane (query l32, half hf), regs = keys
+        const int krow = 32 * half + l32;
         f32x16 sacc, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
-          sacc = mfma32(load16(&sm.k[buf][32 * half + l32][16 * t + 8 * hf]), qr[t], sacc);
-          dp = mfma32(load16(&sm.v[buf][32 * half + l32][16 * t + 8 * hf]), orr[t], dp);
+          sacc = mfma32(load16(&sm.k[buf][krow][kswz(krow, 2 * t + hf)]), qr[t], sacc);
+          dp = mfma32(load16(&sm.v[buf][krow][16 * t + 8 * hf]), orr[t], dp);
         }
         const bool boundary = (key0 + 32 > s.nk) || (q0 + 32 > s.nq) ||
                               (s.causal && key0 + 31 > q0 + s.offset);
@@ -455,14 +498,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
           if constexpr (kSplit) dsl[r >> 3][r & 7] = (bf16)(ds - (float)hi);
         }
         // ---- dQ^T += K^T dS^T; K^T element e of lane (d, hf) is key
-        // 16t + 4hf + e (e < 4) or 16t + 8 + 4hf + (e - 4)
+        // 16t + 4hf + e (e < 4) or 16t + 8 + 4hf + (e - 4). Lane i16 of a
+        // 16-lane group reads row r0 + i16 / 4, columns c0 + 4 (i16 % 4)..+3,
+        // where the chunk holding them is permuted by the swizzle.
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const int r0 = 32 * half + 16 * t + 4 * hf, c0 = 32 * db + 16 * (gg & 1);
-            const bf16x8 ka = cat8(lds_read_tr(&sm.k[buf][0][0], ST, r0, c0, i16),
-                                   lds_read_tr(&sm.k[buf][0][0], ST, r0 + 8, c0, i16));
+            const int r0 = 32 * half + 16 * t + 4 * hf;
+            const int c = 4 * db + 2 * (gg & 1) + ((i16 & 3) >> 1);   // 16-byte chunk
+            const int within = 4 * (i16 & 1);
+            const int ra = r0 + (i16 >> 2), rb = r0 + 8 + (i16 >> 2);
+            const bf16x8 ka = cat8(lds_read_tr_at(&sm.k[buf][ra][kswz(ra, c) + within]),
+                                   lds_read_tr_at(&sm.k[buf][rb][kswz(rb, c) + within]));
             dq[db] = mfma32(ka, dsb[t], dq[db]);
             if constexpr (kSplit) dq[db] = mfma32(ka, dsl[t], dq[db]);
           }
@@ -523,10 +571,11 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
     if (g1.x && (stages & kStageMain))
       hipLaunchKernelGGL(dkdv, g1, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
                          (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dk, (bf16*)dv,
-                         ws_bits, mask, kept, n_kb);
+                         ws_bits, mask, n_kb);
     if (g2.x && (stages & kStageDq))
       hipLaunchKernelGGL(dqk, g2, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
-                         (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dq, ws_bits, n_qb);
+                         (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dq, ws_bits, kept,
+                         n_qb);
   };
   const bool split = !(s.flags & MALA_FLAG_FAST_GRAD);
   if (s.d == 128) {

@@ -74,11 +74,13 @@ __device__ __forceinline__ bf16x8 zero8() {
 // order an MFMA A operand needs when the tile is stored the other way round.
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* tile, int stride, int r0, int c0, int j) {
-  const bf16* p = tile + (r0 + (j >> 2)) * stride + c0 + 4 * (j & 3);
+__device__ __forceinline__ bf16x4 lds_read_tr_at(const bf16* p) {   // p: this lane's 8 bytes
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (lds_i16x4*)(__attribute__((address_space(3))) void*)(p));
   return __builtin_bit_cast(bf16x4, v);
+}
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* tile, int stride, int r0, int c0, int j) {
+  return lds_read_tr_at(tile + (r0 + (j >> 2)) * stride + c0 + 4 * (j & 3));
 }
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
   return (bf16x8){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};

@@ -154,8 +154,9 @@ mala_status mala_bwd(const mala_problem* p, const void* q, const void* k, const 
  *   PREP: D = rowsum(O o dO) into the workspace; clears the decision bits and
  *         kept_tiles, and sets tile_mask to -1.
  *   DKDV: key-major pass: recomputes S, applies the offline gate (Eq. 4),
- *         writes the decisions (bits, tile_mask, kept_tiles), dK and dV.
- *   DQ:   query-major pass over the kept tiles recorded by DKDV: writes dQ.
+ *         writes the decisions (bits, tile_mask), dK and dV.
+ *   DQ:   query-major pass over the kept tiles recorded by DKDV: writes dQ;
+ *         kept_tiles is complete once this stage has run.
  * Same argument checks and errors as mala_bwd; an unknown stage is
  * MALA_ERR_INVALID_ARG.
  */
