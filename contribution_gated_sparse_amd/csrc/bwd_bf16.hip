@@ -231,16 +231,24 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                             (s.causal && kw0 + kBK - 1 > r0 + s.offset);
       // ---- offline gate, Eq. 4: skip iff S - z < log(tau / L) on every legal entry
       float x = kNegInf;
+      if (!boundary) {                                 // wave-uniform: every entry legal
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.u2[buf][16 * qb + 4 * g]);
+        for (int qb = 0; qb < 2; ++qb) {
+          const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.u2[buf][16 * qb + 4 * g]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = r0 + 16 * qb + 4 * g + r;
-          const bool ok = !boundary || ((q < s.nq) & (key < s.nk) &
-                                        ((key <= q + s.offset) | !s.causal));
-          sacc[qb][r] = ok ? sacc[qb][r] : kNegInf;
-          x = fmaxf(x, ok ? fmaf(sacc[qb][r], s.scale_log2, -u[r]) : kNegInf);
+          for (int r = 0; r < 4; ++r) x = fmaxf(x, fmaf(sacc[qb][r], s.scale_log2, -u[r]));
+        }
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.u2[buf][16 * qb + 4 * g]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int q = r0 + 16 * qb + 4 * g + r;
+            const bool ok = (q < s.nq) & (key < s.nk) & ((key <= q + s.offset) | (s.causal == 0));
+            sacc[qb][r] = ok ? sacc[qb][r] : kNegInf;   // P = 0 on illegal entries
+            x = fmaxf(x, ok ? fmaf(sacc[qb][r], s.scale_log2, -u[r]) : kNegInf);
+          }
         }
       }
       const bool keep = wave_any(x >= 0.f);
@@ -488,10 +496,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
         for (int r = 0; r < 16; ++r) {
           // key offset 8(r/4) + 4hf + r%4 lies in column r / 8 of the half
           const int kk = key0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const bool ok = ((cols >> (r >> 3)) & 1u) &&
-                          (!boundary || ((kk < s.nk) & (q < s.nq) &
-                                         ((kk <= q + s.offset) | !s.causal)));
-          const float p = ok ? fast_exp2(fmaf(sacc[r], s.scale_log2, -z2)) : 0.f;
+          bool ok = ((cols >> (r >> 3)) & 1u) != 0;
+          if (boundary)                                // wave-uniform
+            ok = ok & (kk < s.nk) & (q < s.nq) & ((kk <= q + s.offset) | (s.causal == 0));
+          const float e = fast_exp2(fmaf(sacc[r], s.scale_log2, -z2));
+          const float p = ok ? e : 0.f;
           const float ds = p * (dp[r] - dd);
           const bf16 hi = (bf16)ds;
           dsb[r >> 3][r & 7] = hi;
