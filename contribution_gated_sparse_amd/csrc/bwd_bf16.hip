@@ -65,24 +65,25 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int rows, int d, const bf
 // A workgroup owns 128 keys of one KV head: 8 waves x 16 keys. Each wave keeps
 // its K and V rows in registers as the B operands of S = Q K^T and
 // dP = dO V^T (16x16x32 MFMA) and accumulates dK^T, dV^T (64 registers).
-// The query side streams through LDS in 32-row steps: Q and dO rows,
-// double-buffered; their transposes, the A operands of dK^T = Q^T dS and
-// dV^T = dO^T P, come from the same row-major tiles through transposing LDS
-// reads. One backward decision covers 32 query rows x 16 keys: the wave's
-// whole step. The 8 waves' decisions of a step form one byte of the decision
-// bit rows (the workgroup's 8 consecutive 16-key columns); it is gathered in
-// LDS and written with one plain store by the workgroup that owns it.
+// The query side streams through LDS in 64-row steps (one barrier each): Q and
+// dO rows, double-buffered; their transposes, the A operands of dK^T = Q^T dS
+// and dV^T = dO^T P, come from the same row-major tiles through transposing
+// LDS reads. A step is two 32-row halves, and one backward decision covers a
+// half: 32 query rows x the wave's 16 keys. The 8 waves' decisions of a half
+// form one byte of the decision bit rows (the workgroup's 8 consecutive
+// 16-key columns); it is gathered in LDS and written with one plain store by
+// the workgroup that owns it.
 template <int D>
 struct alignas(16) DkdvSmem {
   // row stride (bf16): 16-byte row reads and transposing reads of the
   // 16x16x32 operand layouts both run without bank conflicts at 176 (D=128)
   static constexpr int kStride = D == 128 ? 176 : 80;
-  bf16 q[2][32][kStride];
-  bf16 dout[2][32][kStride];
-  alignas(16) float z2[2][32];  // z_q * log2 e
-  float u2[2][32];              // z_q * log2 e + log2(tau / L_q): skip iff s2 < u2 everywhere
-  float dd[2][32];              // D_q
-  uint32_t keep[2];             // bit w: wave w kept its tile in this step
+  bf16 q[2][64][kStride];
+  bf16 dout[2][64][kStride];
+  alignas(16) float z2[2][64];  // z_q * log2 e
+  float u2[2][64];              // z_q * log2 e + log2(tau / L_q): skip iff s2 < u2 everywhere
+  float dd[2][64];              // D_q
+  uint32_t keep[2][2];          // [buf][half] bit w: wave w kept its tile
 };
 
 template <int D, bool kSplit>
@@ -96,6 +97,8 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   constexpr int KS = D / 32;      // 32-wide k-steps over d (16x16x32 MFMA)
   constexpr int DB = D / 16;      // 16-row blocks of dK^T / dV^T
   constexpr int CPR = D / 8;      // 16-byte chunks per row
+  constexpr int RPP = 512 / CPR;  // staged rows per pass of the 512 threads
+  constexpr int NPASS = 64 / RPP;
 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
@@ -106,6 +109,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int kw0 = J * 128 + w * kBK;                   // this wave's first key
   const size_t krow0 = ((size_t)b * s.hkv + hk) * (size_t)s.nk;
   const int tr32 = (s.nq + kBQ - 1) / kBQ;
+  const int tr64 = (s.nq + 63) / 64;
   const int tc16 = (s.nk + kBK - 1) / kBK;
   const int words = (tc16 + 31) / 32;
   const int key = kw0 + l16;
@@ -129,41 +133,42 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
     for (int r = 0; r < 4; ++r) { dk[db][r] = 0.f; dv[db][r] = 0.f; }
 
-  // first 32-row step with a legal entry for the block's first key
+  // first 64-row step with a legal entry for the block's first key
   int i_start = 0;
   if (s.causal) {
     const int need = J * 128 - s.offset;
-    i_start = need <= 0 ? 0 : need / 32;
+    i_start = need <= 0 ? 0 : need / 64;
   }
-  const int total = s.group * (tr32 - i_start);        // (head, 32-row step) pairs
+  const int total = s.group * (tr64 - i_start);        // (head, 64-row step) pairs
 
-  // staging: 32 rows x CPR chunks of Q and of dO, one chunk each per thread
+  // staging: 64 rows x CPR chunks of Q and of dO, NPASS chunks each per thread
   const int srow = tid / CPR, sc = tid % CPR;
-  const bool stager = tid < 32 * CPR;
-  bf16x8 qreg = zero8(), oreg = zero8();
+  bf16x8 qreg[NPASS], oreg[NPASS];
   float zreg = 0.f, dreg = 0.f;
   auto load_step = [&](int h, int i) {
     const size_t qrow0 = ((size_t)b * s.hq + h) * (size_t)s.nq;
-    if (stager) {
-      const auto qrs = make_rsrc(Q + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
-      const auto ors = make_rsrc(dO + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
-      const uint32_t off = (uint32_t)((i * 32 + srow) * D + 8 * sc) * 2;
-      qreg = buf_load16(qrs, off);
-      oreg = buf_load16(ors, off);
+    const auto qrs = make_rsrc(Q + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
+    const auto ors = make_rsrc(dO + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      const uint32_t off = (uint32_t)((i * 64 + p * RPP + srow) * D + 8 * sc) * 2;
+      qreg[p] = buf_load16(qrs, off);
+      oreg[p] = buf_load16(ors, off);
     }
-    if (tid < 32) {
-      const int q = i * 32 + tid;
+    if (tid < 64) {
+      const int q = i * 64 + tid;
       zreg = q < s.nq ? LSE[qrow0 + q] : 0.f;
       dreg = q < s.nq ? Dq[qrow0 + q] : 0.f;
     }
   };
   auto store_step = [&](int buf, int i) {
-    if (stager) {
-      store16(&sm.q[buf][srow][8 * sc], qreg);
-      store16(&sm.dout[buf][srow][8 * sc], oreg);
+#pragma unroll
+    for (int p = 0; p < NPASS; ++p) {
+      store16(&sm.q[buf][p * RPP + srow][8 * sc], qreg[p]);
+      store16(&sm.dout[buf][p * RPP + srow][8 * sc], oreg[p]);
     }
-    if (tid < 32) {
-      const int q = i * 32 + tid;
+    if (tid < 64) {
+      const int q = i * 64 + tid;
       const float L = s.causal ? (float)(q + s.offset + 1) : (float)s.nk;
       const float z2 = zreg * 1.4426950408889634f;
       sm.z2[buf][tid] = z2;
@@ -171,15 +176,15 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       sm.dd[buf][tid] = dreg;
     }
   };
-  // the previous step's decision byte -> bit row (bh, i32), byte J
-  auto flush_keep = [&](int buf, size_t bh, int i32) {
-    if (tid == 0) {
-      bit_bytes[(bh * tr32 + i32) * (size_t)words * 4 + J] = (uint8_t)sm.keep[buf];
-      sm.keep[buf] = 0u;
+  // the previous step's two decision bytes -> bit rows (bh, 2 i + half), byte J
+  auto flush_keep = [&](int buf, size_t bh, int i) {
+    if (tid < 2 && 2 * i + tid < tr32) {
+      bit_bytes[(bh * tr32 + 2 * i + tid) * (size_t)words * 4 + J] = (uint8_t)sm.keep[buf][tid];
+      sm.keep[buf][tid] = 0u;
     }
   };
 
-  if (tid < 2) sm.keep[tid] = 0u;
+  if (tid < 4) sm.keep[tid >> 1][tid & 1] = 0u;
   int h = hk * s.group, i = i_start;                   // current step
   if (total > 0) {
     load_step(h, i);
@@ -197,14 +202,17 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   for (int it = 0; it < total; ++it) {
     const int buf = it & 1;
     int hn = h, in = i + 1;                            // next step
-    if (in == tr32) { in = i_start; ++hn; }
+    if (in == tr64) { in = i_start; ++hn; }
     if (it + 1 < total) load_step(hn, in);
     if (prev_i >= 0) flush_keep(buf ^ 1, prev_bh, prev_i);
     const size_t bh = (size_t)b * s.hq + h;
-    const int r0 = i * 32;                             // first query row of the step
-    const bool legal =
-        r0 < s.nq && kw0 < s.nk && (!s.causal || kw0 <= min(r0 + 31, s.nq - 1) + s.offset);
-    if (legal) {
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+      const int r0 = i * 64 + 32 * half;               // first query row of the half
+      const int lr = 32 * half;                        // its first row in the LDS tile
+      const bool legal =
+          r0 < s.nq && kw0 < s.nk && (!s.causal || kw0 <= min(r0 + 31, s.nq - 1) + s.offset);
+      if (!legal) continue;
       // Every LDS operand of a phase is read before the phase's products so
       // that the reads overlap the matrix work instead of waiting one by one.
       // Row-major Q and dO rows (A operands of S and dP): row 16 qb + l16,
@@ -214,8 +222,8 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       for (int t = 0; t < KS; ++t)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          qrow[t][qb] = load16(&sm.q[buf][16 * qb + l16][32 * t + 8 * g]);
-          orow[t][qb] = load16(&sm.dout[buf][16 * qb + l16][32 * t + 8 * g]);
+          qrow[t][qb] = load16(&sm.q[buf][lr + 16 * qb + l16][32 * t + 8 * g]);
+          orow[t][qb] = load16(&sm.dout[buf][lr + 16 * qb + l16][32 * t + 8 * g]);
         }
       // ---- recompute S = Q K^T: lane (key l16, group g), regs = queries 16qb + 4g + r
       f32x4 sacc[2];
@@ -234,14 +242,14 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       if (!boundary) {                                 // wave-uniform: every entry legal
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.u2[buf][16 * qb + 4 * g]);
+          const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.u2[buf][lr + 16 * qb + 4 * g]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) x = fmaxf(x, fmaf(sacc[qb][r], s.scale_log2, -u[r]));
         }
       } else {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.u2[buf][16 * qb + 4 * g]);
+          const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.u2[buf][lr + 16 * qb + 4 * g]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int q = r0 + 16 * qb + 4 * g + r;
@@ -253,58 +261,57 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       }
       const bool keep = wave_any(x >= 0.f);
       if (lane == 0) {
-        if (keep) atomicOr(&sm.keep[buf], 1u << w);
-        if (mask != nullptr) mask[(bh * tr32 + i) * tc16 + kw0 / kBK] = keep ? 1 : 0;
+        if (keep) atomicOr(&sm.keep[buf][half], 1u << w);
+        if (mask != nullptr) mask[(bh * tr32 + 2 * i + half) * tc16 + kw0 / kBK] = keep ? 1 : 0;
       }
-      if (keep) {
-        // dO^T and Q^T, the A operands of dV^T = dO^T P and dK^T = Q^T dS,
-        // through transposing reads: element e < 4 is query row 4g + e,
-        // e >= 4 is row 16 + 4g + (e - 4), for column 16 db + l16.
-        bf16x8 ocol[DB];
+      if (!keep) continue;
+      // dO^T and Q^T, the A operands of dV^T = dO^T P and dK^T = Q^T dS,
+      // through transposing reads: element e < 4 is query row 4g + e,
+      // e >= 4 is row 16 + 4g + (e - 4), for column 16 db + l16.
+      bf16x8 ocol[DB];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          ocol[db] = cat8(lds_read_tr(&sm.dout[buf][0][0], ST, 4 * g, 16 * db, l16),
-                          lds_read_tr(&sm.dout[buf][0][0], ST, 16 + 4 * g, 16 * db, l16));
-        // ---- P = exp(S - z), dP = dO V^T, dS = P o (dP - D)
-        f32x4 dp[2];
+      for (int db = 0; db < DB; ++db)
+        ocol[db] = cat8(lds_read_tr(&sm.dout[buf][lr][0], ST, 4 * g, 16 * db, l16),
+                        lds_read_tr(&sm.dout[buf][lr][0], ST, 16 + 4 * g, 16 * db, l16));
+      // ---- P = exp(S - z), dP = dO V^T, dS = P o (dP - D)
+      f32x4 dp[2];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) dp[qb][r] = 0.f;
+        for (int r = 0; r < 4; ++r) dp[qb][r] = 0.f;
 #pragma unroll
-        for (int t = 0; t < KS; ++t)
+      for (int t = 0; t < KS; ++t)
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma16(orow[t][qb], vr[t], dp[qb]);
-        bf16x8 qcol[DB];
+        for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma16(orow[t][qb], vr[t], dp[qb]);
+      bf16x8 qcol[DB];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          qcol[db] = cat8(lds_read_tr(&sm.q[buf][0][0], ST, 4 * g, 16 * db, l16),
-                          lds_read_tr(&sm.q[buf][0][0], ST, 16 + 4 * g, 16 * db, l16));
-        // B operands over the 32 query rows, in the row order of the
-        // transposing reads
-        bf16x8 pb, dsb, dsl;
+      for (int db = 0; db < DB; ++db)
+        qcol[db] = cat8(lds_read_tr(&sm.q[buf][lr][0], ST, 4 * g, 16 * db, l16),
+                        lds_read_tr(&sm.q[buf][lr][0], ST, 16 + 4 * g, 16 * db, l16));
+      // B operands over the 32 query rows, in the row order of the
+      // transposing reads
+      bf16x8 pb, dsb, dsl;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const f32x4 z = *reinterpret_cast<const f32x4*>(&sm.z2[buf][16 * qb + 4 * g]);
-          const f32x4 ddv = *reinterpret_cast<const f32x4*>(&sm.dd[buf][16 * qb + 4 * g]);
+      for (int qb = 0; qb < 2; ++qb) {
+        const f32x4 z = *reinterpret_cast<const f32x4*>(&sm.z2[buf][lr + 16 * qb + 4 * g]);
+        const f32x4 ddv = *reinterpret_cast<const f32x4*>(&sm.dd[buf][lr + 16 * qb + 4 * g]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = fast_exp2(fmaf(sacc[qb][r], s.scale_log2, -z[r]));
-            const float ds = p * (dp[qb][r] - ddv[r]);
-            pb[4 * qb + r] = (bf16)p;
-            const bf16 hi = (bf16)ds;
-            dsb[4 * qb + r] = hi;
-            if constexpr (kSplit) dsl[4 * qb + r] = (bf16)(ds - (float)hi);
-          }
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(fmaf(sacc[qb][r], s.scale_log2, -z[r]));
+          const float ds = p * (dp[qb][r] - ddv[r]);
+          pb[4 * qb + r] = (bf16)p;
+          const bf16 hi = (bf16)ds;
+          dsb[4 * qb + r] = hi;
+          if constexpr (kSplit) dsl[4 * qb + r] = (bf16)(ds - (float)hi);
         }
-        // ---- dV^T += dO^T P and dK^T += Q^T dS
+      }
+      // ---- dV^T += dO^T P and dK^T += Q^T dS
 #pragma unroll
-        for (int db = 0; db < DB; ++db) dv[db] = mfma16(ocol[db], pb, dv[db]);
+      for (int db = 0; db < DB; ++db) dv[db] = mfma16(ocol[db], pb, dv[db]);
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dk[db] = mfma16(qcol[db], dsb, dk[db]);
-          if constexpr (kSplit) dk[db] = mfma16(qcol[db], dsl, dk[db]);
-        }
+      for (int db = 0; db < DB; ++db) {
+        dk[db] = mfma16(qcol[db], dsb, dk[db]);
+        if constexpr (kSplit) dk[db] = mfma16(qcol[db], dsl, dk[db]);
       }
     }
     prev_bh = bh;
