@@ -6,10 +6,13 @@
 //     wave w owns query rows [q0, q0 + 32), which is one decision block
 //     (B_q = 32), so the keep/skip vote of a tile is a wave ballot;
 //   - key tiles of B_k = 64 keys are visited from the diagonal down to tile 0;
-//     K_j (row-major) and V_j (transposed) are staged in double-buffered LDS
-//     and shared by the 8 waves; the next tile is prefetched into registers
-//     with buffer loads (zero past the end of the sequence) while the current
-//     one is consumed, so one barrier per tile suffices;
+//     K_j and V_j (both row-major) are staged in double-buffered LDS and
+//     shared by the 8 waves; the next tile is prefetched into registers with
+//     buffer loads (zero past the end of the sequence) while the current one
+//     is consumed, so one barrier per tile suffices;
+//   - V^T, the A operand of O^T += V^T P^T, comes from the row-major V tile
+//     through transposing LDS reads (ds_read_b64_tr_b16), so V is written to
+//     LDS with plain 16-byte stores;
 //   - scores are formed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA,
 //     so each lane owns one query column: the row max and row sum are in-lane
 //     reductions plus one permlane32 swap;
@@ -35,19 +38,12 @@ constexpr float kLazy = 8.0f;
 
 template <int D>
 struct FwdSmem {
-  bf16 k[2][kBK][D + 8];      // +8 bf16: 16-byte row skew, conflict-free 16 B reads
-  bf16 vt[2][D][kBK + 8];     // V transposed; keys permuted inside each group of 16
+  // row strides (bf16): 16-byte reads of K rows (32x32x16 A layout) are
+  // conflict-free at D + 8; transposing reads of V (the same layout, taken
+  // down the columns) are conflict-free at D + 32
+  bf16 k[2][kBK][D + 8];
+  bf16 v[2][kBK][D + 32];
 };
-
-// Position of key x (0..63) inside a V^T row. Quads 1 and 2 of every group of
-// 16 keys are swapped so that the 8 consecutive bf16 a lane reads as the MFMA
-// A operand are the 8 keys it holds for one 16-key step of P^T, whose order is
-// fixed by the accumulator layout of S^T (row 8(r/4) + 4(l/32) + r%4).
-__device__ __forceinline__ int vt_pos(int x) {
-  const int u = (x >> 2) & 3;
-  const int pu = (u == 1) ? 2 : (u == 2 ? 1 : u);
-  return (x & ~15) + 4 * pu + (x & 3);
-}
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
@@ -60,7 +56,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int RPP = kThreads / CPR;     // K rows per load pass
   constexpr int KPASS = kBK / RPP;
-  constexpr int KPT = kBK / RPP;          // consecutive V keys per thread
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -105,31 +100,23 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
 
-  bf16x8 kreg[KPASS], vreg[KPT];
+  constexpr int SV = D + 32;
+  const int i16 = lane & 15, gg = lane >> 4;
+  bf16x8 kreg[KPASS], vreg[KPASS];
   const int kc = tid % CPR, kr = tid / CPR;
   auto load_tile = [&](int j) {
 #pragma unroll
     for (int p = 0; p < KPASS; ++p)
       kreg[p] = buf_load16(krs, (uint32_t)((j * kBK + p * RPP + kr) * D + 8 * kc) * 2);
 #pragma unroll
-    for (int p = 0; p < KPT; ++p)
-      vreg[p] = buf_load16(vrs, (uint32_t)((j * kBK + kr * KPT + p) * D + 8 * kc) * 2);
+    for (int p = 0; p < KPASS; ++p)
+      vreg[p] = buf_load16(vrs, (uint32_t)((j * kBK + p * RPP + kr) * D + 8 * kc) * 2);
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int p = 0; p < KPASS; ++p) store16(&sm.k[buf][p * RPP + kr][8 * kc], kreg[p]);
-    const int pos = vt_pos(kr * KPT);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (KPT == 4) {
-        bf16x4 x = {vreg[0][e], vreg[1][e], vreg[2][e], vreg[3][e]};
-        *reinterpret_cast<bf16x4*>(&sm.vt[buf][8 * kc + e][pos]) = x;
-      } else if constexpr (KPT == 2) {
-        bf16x2 x = {vreg[0][e], vreg[1][e]};
-        *reinterpret_cast<bf16x2*>(&sm.vt[buf][8 * kc + e][pos]) = x;
-      } else {
-        sm.vt[buf][8 * kc + e][pos] = vreg[0][e];
-      }
+    for (int p = 0; p < KPASS; ++p) {
+      store16(&sm.k[buf][p * RPP + kr][8 * kc], kreg[p]);
+      store16(&sm.v[buf][p * RPP + kr][8 * kc], vreg[p]);
     }
   };
 
@@ -206,11 +193,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
             pb[2 * kb + (r >> 3)][r & 7] = (bf16)p;
           }
         lsum += sum_halves(rs);
+        // V^T element e of lane (d, hf) is key 16t + 4hf + e (e < 4) or
+        // 16t + 8 + 4hf + (e - 4): the key order in which pb[t] holds P^T
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
-            oacc[db] = mfma32(load16(&sm.vt[buf][32 * db + l32][16 * t + 8 * hf]), pb[t], oacc[db]);
+          for (int db = 0; db < DB; ++db) {
+            const int r0 = 16 * t + 4 * hf, c0 = 32 * db + 16 * (gg & 1);
+            const bf16x8 va = cat8(lds_read_tr(&sm.v[buf][0][0], SV, r0, c0, i16),
+                                   lds_read_tr(&sm.v[buf][0][0], SV, r0 + 8, c0, i16));
+            oacc[db] = mfma32(va, pb[t], oacc[db]);
+          }
         ++nkept;
       }
       if (mask != nullptr && lane == 0)
