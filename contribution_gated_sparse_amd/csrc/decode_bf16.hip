@@ -10,11 +10,14 @@
 //      then replays the split's gate sequence (newest tile first, state
 //      starting empty, L = N_k) from those statistics, which is exactly the
 //      forward rule of Eq. 3 on a one-row block per head;
-//   3. only a tile kept by at least one head loads its V tile (transposed
-//      through a wave-private LDS slab) and runs P V on the MFMA; heads that
-//      skipped it contribute P = 0;
+//   3. only a tile kept by at least one head loads its V tile; each 32-key
+//      half of it is staged row-major in a wave-private LDS slab and read back
+//      transposed (ds_read_b64_tr_b16) as the A operand of O^T += V^T P^T;
+//      heads that skipped the tile contribute P = 0;
 //   4. the four waves' partial outputs are summed in LDS and the split writes
-//      its partial state (m, l, O) in base 2.
+//      its partial state (m, S, O) in base 2.
+// The small LDS footprint (37 KB) lets four workgroups share a CU, so the K
+// and V streams of several splits are in flight at once.
 // A second kernel merges the splits with the normalizer-aware reduction.
 #include "mala_device.h"
 #include "mala_internal.h"
@@ -25,17 +28,11 @@ namespace {
 constexpr int kChunk = 256;
 constexpr int kTile = 64;
 constexpr int kMaxGroup = 16;
-
-// Position of key x inside a 32-key group of the V^T slab: matches the order
-// in which one 32-key k-step of P^T is held (keys 4g..4g+3 then 16+4g..16+4g+3
-// for lane group g), given by the 16x16 accumulator layout of S^T.
-__device__ __forceinline__ int dec_pos(int x) {
-  return (x & ~31) + 8 * ((x & 15) >> 2) + 4 * ((x >> 4) & 1) + (x & 3);
-}
+constexpr int kSlabStride = 144;      // bf16; conflict-free transposing reads (16x16x32 layout)
 
 union alignas(16) DecSlab {
-  bf16 vt[128][kTile + 8];            // V^T of the wave's tile
-  float ored[128][kMaxGroup];         // then the wave's partial O^T
+  bf16 v[32][kSlabStride];            // one 32-key half of the wave's V tile, row-major
+  float o[kMaxGroup][128 + 4];        // then the wave's partial O, [head][d]
 };
 struct alignas(16) DecSmem {
   DecSlab slab[4];                    // one per wave
@@ -43,10 +40,10 @@ struct alignas(16) DecSmem {
   float tsum[4][kMaxGroup];           // per (tile, head) sum of 2^(s - max)
 };
 
-__global__ __launch_bounds__(256, 2) void decode_split_kernel(
+__global__ __launch_bounds__(256, 4) void decode_split_kernel(
     DecodeShape s, const bf16* __restrict__ Qd, const bf16* __restrict__ Kc,
     const bf16* __restrict__ Vc, const int32_t* __restrict__ seqlens, float* __restrict__ ws,
-    int8_t* __restrict__ mask, int32_t* __restrict__ kept) {
+    int8_t* __restrict__ mask) {
   constexpr int D = 128;
   __shared__ DecSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -60,16 +57,20 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
 
   const int c0 = c * kChunk;
   const int ntile = c0 >= nk ? 0 : min(tpc, (nk - c0 + kTile - 1) / kTile);
-  const size_t part_stride = (size_t)s.n_chunks * (D + 2);
+  const size_t bh0 = (size_t)b * s.hq + hk * G;        // first query head of the group
   if (ntile == 0) {
     // split past the end of this sequence: no contribution
     if (tid < G) {
-      float* p = ws + ((size_t)b * s.hq + hk * G + tid) * part_stride + (size_t)c * (D + 2);
-      p[0] = kNegInf;
-      p[1] = 0.f;
+      float* pms = ws + dec_ms_at(s, bh0 + tid, c);
+      pms[0] = kNegInf;
+      pms[1] = 0.f;
     }
+    for (int idx = tid; idx < D * G; idx += 256) ws[dec_o_at(s, bh0 + idx / D, c) + idx % D] = 0.f;
     if (mask != nullptr && tid < G * tpc)
-      mask[(((size_t)b * s.hq + hk * G + tid / tpc) * s.n_chunks + c) * tpc + tid % tpc] = -1;
+      mask[((bh0 + tid / tpc) * s.n_chunks + c) * tpc + tid % tpc] = -1;
+    uint32_t* wbits = reinterpret_cast<uint32_t*>(ws);
+    if (tid < G) wbits[dec_kbits_at(s, bh0 + tid, c)] = 0u;
+    if (tid == 0) wbits[dec_vbits_at(s, blockIdx.y, c)] = 0u;
     return;
   }
 
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
     for (int r = 0; r < 4; ++r) sacc[kb][r] = 0.f;
   if (has_keys) {
     bf16x8 qb[D / 32];
-    const bf16* qrow = Qd + ((size_t)b * s.hq + hk * G + min(j16, G - 1)) * D;
+    const bf16* qrow = Qd + (bh0 + min(j16, G - 1)) * D;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) qb[t] = j16 < G ? load16(qrow + 32 * t + 8 * g) : zero8();
     bf16x8 ka[4][D / 32];
@@ -149,41 +150,37 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
   const uint64_t vote = __builtin_amdgcn_ballot_w64(mine);
   const bool tile_kept = has_keys && vote != 0;
 
+  // decisions: the head's kept-tile bits and the bits of V tiles read
+  // (counted by the merge kernel)
+  uint32_t* wbits = reinterpret_cast<uint32_t*>(ws);
   if (w == 0 && g == 0 && head_ok) {
-    const size_t bh = (size_t)b * s.hq + hk * G + j16;
+    const size_t bh = bh0 + j16;
     if (mask != nullptr)
       for (int t = 0; t < tpc; ++t)
         mask[(bh * s.n_chunks + c) * tpc + t] = t < ntile ? (int8_t)((keepbits >> t) & 1u) : (int8_t)-1;
-    if (kept != nullptr) atomicAdd(&kept[(size_t)b * (s.hq + s.hkv) + hk * G + j16], __popc(keepbits));
+    wbits[dec_kbits_at(s, bh, c)] = keepbits;
   }
-  if (kept != nullptr && lane == 0 && tile_kept)
-    atomicAdd(&kept[(size_t)b * (s.hq + s.hkv) + s.hq + hk], 1);
+  uint32_t vb = head_ok ? keepbits : 0u;   // tile t's V is read iff some head keeps it
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) vb |= __shfl_xor(vb, off, 64);
+  if (w == 0 && lane == 0) wbits[dec_vbits_at(s, blockIdx.y, c)] = vb;
 
-  // ---- kept tile: V load (HBM) -> transposed LDS slab -> P V on the MFMA
-  if (tile_kept) {
-    const int dc = lane & 15, kq = lane >> 4;        // 16-byte column chunk, 16-key group
-    bf16x8 vr[16];
-#pragma unroll
-    for (int p = 0; p < 16; ++p)
-      vr[p] = buf_load16(vrs, (uint32_t)((key0 + 16 * kq + p) * D + 8 * dc) * 2);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int pos = dec_pos(16 * kq + 4 * u);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16x4 x = {vr[4 * u][e], vr[4 * u + 1][e], vr[4 * u + 2][e], vr[4 * u + 3][e]};
-        *reinterpret_cast<bf16x4*>(&sm.slab[w].vt[8 * dc + e][pos]) = x;
-      }
-    }
-  }
-  __syncthreads();
+  // ---- kept tile: V load (HBM), then per 32-key half: row-major LDS slab ->
+  // transposing reads -> P V on the MFMA. Lane (chunk dc, group kq) loads key
+  // 32 (p / 8) + 8 kq + p % 8 into vr[p], 16 bytes at column chunk dc.
   f32x4 oacc[D / 16];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
 #pragma unroll
     for (int r = 0; r < 4; ++r) oacc[db][r] = 0.f;
   if (tile_kept) {
-    // P^T as the B operand: lane (head j16, group g) holds keys of one 32-key step
+    const int dc = lane & 15, kq = lane >> 4;
+    bf16x8 vr[16];
+#pragma unroll
+    for (int p = 0; p < 16; ++p)
+      vr[p] = buf_load16(vrs, (uint32_t)((key0 + 32 * (p >> 3) + 8 * kq + (p & 7)) * D + 8 * dc) * 2);
+    // P^T as the B operand of 32-key step ks: element e < 4 is key
+    // 32 ks + 4 g + e, e >= 4 is key 32 ks + 16 + 4 g + (e - 4)
     bf16x8 pb[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -192,104 +189,145 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(
         const float sv = sacc[2 * ks + (e >> 2)][e & 3];
         pb[ks][e] = (bf16)(mine ? fast_exp2(sv - M) : 0.f);
       }
+    bf16* slab = &sm.slab[w].v[0][0];
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db)
+    for (int ks = 0; ks < 2; ++ks) {
+      // the slab is private to the wave, and a wave's LDS operations complete
+      // in order: the previous half's reads are done before these writes land
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        oacc[db] = mfma16(load16(&sm.slab[w].vt[16 * db + j16][32 * ks + 8 * g]), pb[ks], oacc[db]);
+      for (int p = 0; p < 8; ++p) store16(slab + (8 * kq + p) * kSlabStride + 8 * dc, vr[8 * ks + p]);
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const bf16x8 va = cat8(lds_read_tr(slab, kSlabStride, 4 * g, 16 * db, j16),
+                               lds_read_tr(slab, kSlabStride, 16 + 4 * g, 16 * db, j16));
+        oacc[db] = mfma16(va, pb[ks], oacc[db]);
+      }
+    }
   }
-  __syncthreads();
-  // O^T[d = 16db + 4g + r][head j16]
+  __syncthreads();                  // every wave is done with its slab's V rows
+  // O^T[d = 16db + 4g + r][head j16] -> slab as O[head][d]
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sm.slab[w].ored[16 * db + 4 * g + r][j16] = oacc[db][r];
+    *reinterpret_cast<f32x4*>(&sm.slab[w].o[j16][16 * db + 4 * g]) = oacc[db];
   __syncthreads();
 
   // ---- sum the four waves and write the split's partial state
   for (int idx = tid; idx < D * G; idx += 256) {
     const int hh = idx / D, d = idx % D;
-    const float o = sm.slab[0].ored[d][hh] + sm.slab[1].ored[d][hh] + sm.slab[2].ored[d][hh] +
-                    sm.slab[3].ored[d][hh];
-    float* p = ws + ((size_t)b * s.hq + hk * G + hh) * part_stride + (size_t)c * (D + 2);
-    p[2 + d] = o;
+    const float o = sm.slab[0].o[hh][d] + sm.slab[1].o[hh][d] + sm.slab[2].o[hh][d] +
+                    sm.slab[3].o[hh][d];
+    ws[dec_o_at(s, bh0 + hh, c) + d] = o;
   }
   if (w == 0 && g == 0 && head_ok) {
-    float* p = ws + ((size_t)b * s.hq + hk * G + j16) * part_stride + (size_t)c * (D + 2);
-    p[0] = M;
-    p[1] = S;
+    float* pms = ws + dec_ms_at(s, bh0 + j16, c);
+    pms[0] = M;
+    pms[1] = S;
   }
 }
 
-// Merge the split partial states of one (sequence, head): z = log sum_c Z_c,
-// O = sum_c Z_c O_c / sum_c Z_c (the standard online-softmax reduction).
+// Merge the split partial states of one (sequence, head), 32 output columns
+// per workgroup: z = log sum_c Z_c, O = sum_c Z_c O_c / sum_c Z_c (the
+// standard online-softmax reduction). The splits' weights 2^(m_c - M) are
+// computed once into LDS, then 8 groups of 32 threads sum the weighted
+// partial rows (coalesced 128-byte reads), a block of splits at a time.
 template <typename OutT>
-__global__ __launch_bounds__(256) void decode_combine_kernel(int hq, int d, int n_chunks,
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeShape s,
                                                              const float* __restrict__ ws,
                                                              OutT* __restrict__ o,
-                                                             float* __restrict__ lse) {
-  const int bh = blockIdx.x;
-  const float* part = ws + (size_t)bh * n_chunks * (d + 2);
-  __shared__ float red[256];
+                                                             float* __restrict__ lse,
+                                                             int32_t* __restrict__ kept) {
+  constexpr int kBlk = 1024;            // splits per LDS block of weights
+  __shared__ float wts[kBlk];
+  __shared__ float red[8];
   __shared__ float acc[8][32];
-  const int tid = threadIdx.x;
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nc = s.n_chunks;
+  const float* ms = ws + dec_ms_at(s, bh, 0);
+  // M = max_c m_c
   float mx = kNegInf;
-  for (int c = tid; c < n_chunks; c += 256) mx = fmaxf(mx, part[(size_t)c * (d + 2)]);
-  red[tid] = mx;
+  for (int c = tid; c < nc; c += 256) mx = fmaxf(mx, ms[2 * c]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if (lane == 0) red[wv] = mx;
   __syncthreads();
-  for (int st = 128; st > 0; st >>= 1) {
-    if (tid < st) red[tid] = fmaxf(red[tid], red[tid + st]);
-    __syncthreads();
-  }
-  const float M = red[0];
+  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
-  float den = 0.f;
-  for (int c = tid; c < n_chunks; c += 256) {
-    const float m = part[(size_t)c * (d + 2)];
-    if (m > kNegInf) den += part[(size_t)c * (d + 2) + 1] * fast_exp2(m - M);
-  }
-  red[tid] = den;
-  __syncthreads();
-  for (int st = 128; st > 0; st >>= 1) {
-    if (tid < st) red[tid] += red[tid + st];
-    __syncthreads();
-  }
-  const float Z = red[0];
-  const int dd = blockIdx.y * 32 + (tid & 31), cl = tid >> 5;
-  float num = 0.f;
-  if (dd < d)
-    for (int c = cl; c < n_chunks; c += 8) {
-      const float m = part[(size_t)c * (d + 2)];
-      if (m > kNegInf) num += part[(size_t)c * (d + 2) + 2 + dd] * fast_exp2(m - M);
+  const int dl = tid & 31, cl = tid >> 5;
+  const int d = blockIdx.y * 32 + dl;
+  float den = 0.f, num = 0.f;
+  for (int cb = 0; cb < nc; cb += kBlk) {
+    const int n = min(kBlk, nc - cb);
+    for (int k = tid; k < n; k += 256) {
+      const float m = ms[2 * (cb + k)];
+      const float wgt = (M == kNegInf || m == kNegInf) ? 0.f : fast_exp2(m - M);
+      wts[k] = wgt;
+      den += wgt * ms[2 * (cb + k) + 1];
     }
-  acc[cl][tid & 31] = num;
+    __syncthreads();
+    if (d < s.d) {
+      const float* po = ws + dec_o_at(s, bh, cb) + d;
+      int k = cl;
+      for (; k + 24 < n; k += 32) {       // four splits in flight per thread
+        const float a0 = po[(size_t)k * s.d], a1 = po[(size_t)(k + 8) * s.d];
+        const float a2 = po[(size_t)(k + 16) * s.d], a3 = po[(size_t)(k + 24) * s.d];
+        num += wts[k] * a0 + wts[k + 8] * a1 + wts[k + 16] * a2 + wts[k + 24] * a3;
+      }
+      for (; k < n; k += 8) num += wts[k] * po[(size_t)k * s.d];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
+  if (lane == 0) red[4 + wv] = den;
+  acc[cl][dl] = num;
   __syncthreads();
-  if (tid < 32 && dd < d) {
+  const float Z = red[4] + red[5] + red[6] + red[7];
+  if (tid < 32 && d < s.d) {
     float t = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) t += acc[k][tid];
-    o[(size_t)bh * d + dd] = (OutT)(Z > 0.f ? t / Z : 0.f);
+    o[(size_t)bh * s.d + d] = (OutT)(Z > 0.f ? t / Z : 0.f);
   }
   if (blockIdx.y == 0 && tid == 0) lse[bh] = Z > 0.f ? (M + fast_log2(Z)) * kLn2 : kNegInf;
-  (void)hq;
+
+  // kept-tile counters from the splits' decision bits: [b][h] for the head,
+  // [b][Hq + g] (by the group's first head) for the V tiles of KV head g
+  if (kept != nullptr && blockIdx.y == 0 && tid < 64) {
+    const uint32_t* wbits = reinterpret_cast<const uint32_t*>(ws);
+    const int b = bh / s.hq, h = bh % s.hq, hk = h / s.group;
+    int nh = 0, nv = 0;
+    for (int c = tid; c < nc; c += 64) {
+      nh += __popc(wbits[dec_kbits_at(s, bh, c)]);
+      if (h % s.group == 0) nv += __popc(wbits[dec_vbits_at(s, (size_t)b * s.hkv + hk, c)]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      nh += __shfl_xor(nh, off, 64);
+      nv += __shfl_xor(nv, off, 64);
+    }
+    if (tid == 0) {
+      kept[(size_t)b * (s.hq + s.hkv) + h] = nh;
+      if (h % s.group == 0) kept[(size_t)b * (s.hq + s.hkv) + s.hq + hk] = nv;
+    }
+  }
 }
 
 }  // namespace
 
 size_t decode_ws_floats(const DecodeShape& s) {
-  return (size_t)s.batch * s.hq * s.n_chunks * (s.d + 2);
+  return (size_t)s.batch * s.hq * s.n_chunks * (s.d + 3) + (size_t)s.batch * s.hkv * s.n_chunks;
 }
 
 hipError_t launch_decode_combine_bf16(const DecodeShape& s, const float* ws, void* o, float* lse,
-                                      hipStream_t st) {
+                                      int32_t* kept, hipStream_t st) {
   hipLaunchKernelGGL(decode_combine_kernel<bf16>, dim3(s.batch * s.hq, (s.d + 31) / 32),
-                     dim3(256), 0, st, s.hq, s.d, s.n_chunks, ws, (bf16*)o, lse);
+                     dim3(256), 0, st, s, ws, (bf16*)o, lse, kept);
   return hipGetLastError();
 }
 hipError_t launch_decode_combine_f32(const DecodeShape& s, const float* ws, float* o, float* lse,
-                                     hipStream_t st) {
+                                     int32_t* kept, hipStream_t st) {
   hipLaunchKernelGGL(decode_combine_kernel<float>, dim3(s.batch * s.hq, (s.d + 31) / 32),
-                     dim3(256), 0, st, s.hq, s.d, s.n_chunks, ws, o, lse);
+                     dim3(256), 0, st, s, ws, o, lse, kept);
   return hipGetLastError();
 }
 
@@ -297,17 +335,12 @@ hipError_t launch_decode_bf16(const DecodeShape& s, const void* q, const void* k
                               const int32_t* seqlens, void* o, float* lse, float* ws,
                               int8_t* mask, int32_t* kept, hipStream_t st, int stages) {
   if (stages & kStageMain) {
-    if (kept != nullptr) {
-      hipError_t e = launch_fill_i32(kept, 0, (size_t)s.batch * (s.hq + s.hkv), st);
-      if (e != hipSuccess) return e;
-    }
     hipLaunchKernelGGL(decode_split_kernel, dim3(s.n_chunks, s.batch * s.hkv), dim3(256), 0, st,
-                       s, (const bf16*)q, (const bf16*)kc, (const bf16*)vc, seqlens, ws, mask,
-                       kept);
+                       s, (const bf16*)q, (const bf16*)kc, (const bf16*)vc, seqlens, ws, mask);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (stages & kStageCombine) return launch_decode_combine_bf16(s, ws, o, lse, st);
+  if (stages & kStageCombine) return launch_decode_combine_bf16(s, ws, o, lse, kept, st);
   return hipSuccess;
 }
 

@@ -334,7 +334,7 @@ template <int D>
 __global__ __launch_bounds__(64) void decode_split_f32_kernel(
     DecodeShape s, const float* __restrict__ Qd, const float* __restrict__ Kc,
     const float* __restrict__ Vc, const int32_t* __restrict__ seqlens, float* __restrict__ ws,
-    int8_t* __restrict__ mask, int32_t* __restrict__ kept) {
+    int8_t* __restrict__ mask) {
   constexpr int kMaxG = 16;
   __shared__ float qs[kMaxG][D];
   __shared__ double ps[kMaxG][64];
@@ -346,7 +346,6 @@ __global__ __launch_bounds__(64) void decode_split_f32_kernel(
   nk = max(1, min(nk, min(s.max_nk, s.cap)));
   const int c0 = c * 256;
   const int ntile = c0 >= nk ? 0 : min(4, (nk - c0 + 63) / 64);
-  const size_t pstride = (size_t)s.n_chunks * (D + 2);
   const size_t crow0 = ((size_t)b * s.hkv + hk) * (size_t)s.cap;
   for (int hh = 0; hh < G; ++hh)
     for (int e = t; e < D; e += 64) qs[hh][e] = Qd[((size_t)b * s.hq + hk * G + hh) * D + e];
@@ -356,7 +355,7 @@ __global__ __launch_bounds__(64) void decode_split_f32_kernel(
   double o0[kMaxG], o1[kMaxG];
 #pragma unroll
   for (int hh = 0; hh < kMaxG; ++hh) { o0[hh] = 0.0; o1[hh] = 0.0; }
-  int vtiles = 0;
+  uint32_t vbits = 0;               // bit tt: tile tt's V was read
   for (int tt = ntile - 1; tt >= 0; --tt) {
     const int key = c0 + 64 * tt + t;
     const bool ok = key < nk;
@@ -391,7 +390,7 @@ __global__ __launch_bounds__(64) void decode_split_f32_kernel(
       __syncthreads();
     }
     if (any_keep) {
-      ++vtiles;
+      vbits |= 1u << tt;
 #pragma unroll
       for (int hh = 0; hh < kMaxG; ++hh) { o0[hh] *= alpha[hh]; o1[hh] *= alpha[hh]; }
       for (int k = 0; k < 64; ++k) {
@@ -414,24 +413,23 @@ __global__ __launch_bounds__(64) void decode_split_f32_kernel(
   for (int hh = 0; hh < kMaxG; ++hh) {
     if (hh >= G) continue;
     const size_t bhh = (size_t)b * s.hq + hk * G + hh;
-    float* p = ws + bhh * pstride + (size_t)c * (D + 2);
+    float* pms = ws + dec_ms_at(s, bhh, c);
+    float* po = ws + dec_o_at(s, bhh, c);
     // base-2 partial state with the scale folded in: m2 = m*log2e, O and S
     // unnormalized relative to 2^m2 (the combine kernel's format)
     if (t == 0) {
-      p[0] = ntile ? (float)(st_m[hh] * log2e) : kNegInf;
-      p[1] = ntile ? (float)st_s[hh] : 0.f;
+      pms[0] = ntile ? (float)(st_m[hh] * log2e) : kNegInf;
+      pms[1] = ntile ? (float)st_s[hh] : 0.f;
       if (mask != nullptr)
         for (int tt = 0; tt < 4; ++tt)
           mask[(bhh * s.n_chunks + c) * 4 + tt] =
               tt < ntile ? (int8_t)((st_bits[hh] >> tt) & 1u) : (int8_t)-1;
-      if (kept != nullptr && ntile)
-        atomicAdd(&kept[(size_t)b * (s.hq + s.hkv) + hk * G + hh], __popc(st_bits[hh]));
+      reinterpret_cast<uint32_t*>(ws)[dec_kbits_at(s, bhh, c)] = ntile ? st_bits[hh] : 0u;
     }
-    if (t < D) p[2 + t] = (float)o0[hh];
-    if (t + 64 < D) p[2 + t + 64] = (float)o1[hh];
+    if (t < D) po[t] = (float)o0[hh];
+    if (t + 64 < D) po[t + 64] = (float)o1[hh];
   }
-  if (t == 0 && kept != nullptr && vtiles)
-    atomicAdd(&kept[(size_t)b * (s.hq + s.hkv) + s.hq + hk], vtiles);
+  if (t == 0) reinterpret_cast<uint32_t*>(ws)[dec_vbits_at(s, blockIdx.y, c)] = vbits;
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int32_t v, size_t n) {
@@ -520,21 +518,17 @@ hipError_t launch_decode_f32(const DecodeShape& s, const float* q, const float* 
                              const float* vc, const int32_t* seqlens, float* o, float* lse,
                              float* ws, int8_t* mask, int32_t* kept, hipStream_t st, int stages) {
   if (stages & kStageMain) {
-  if (kept != nullptr) {
-    hipError_t e = launch_fill_i32(kept, 0, (size_t)s.batch * (s.hq + s.hkv), st);
-    if (e != hipSuccess) return e;
-  }
   const dim3 grid(s.n_chunks, s.batch * s.hkv);
   if (s.d == 128)
     hipLaunchKernelGGL(decode_split_f32_kernel<128>, grid, dim3(64), 0, st, s, q, kc, vc, seqlens,
-                       ws, mask, kept);
+                       ws, mask);
   else
     hipLaunchKernelGGL(decode_split_f32_kernel<64>, grid, dim3(64), 0, st, s, q, kc, vc, seqlens,
-                       ws, mask, kept);
+                       ws, mask);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   }
-  if (stages & kStageCombine) return launch_decode_combine_f32(s, ws, o, lse, st);
+  if (stages & kStageCombine) return launch_decode_combine_f32(s, ws, o, lse, kept, st);
   return hipSuccess;
 }
 

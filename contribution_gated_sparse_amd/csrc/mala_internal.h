@@ -38,6 +38,26 @@ struct DecodeShape {
   double log_tau;
 };
 
+// Split-KV decode workspace, in 4-byte words: the partial states (base 2,
+// scale folded in) as the (m, S) pairs of every (sequence * query head,
+// split), then the unnormalized outputs O of every (sequence * query head,
+// split); then the split's decisions: per (sequence * query head, split) the
+// kept-tile bits of the head, per (sequence * KV head, split) the bits of the
+// tiles whose V was read. The merge kernel turns the bits into the kept-tile
+// counters, so the split kernel needs no atomics.
+__host__ __device__ inline size_t dec_ms_at(const DecodeShape& s, size_t bh, int c) {
+  return (bh * (size_t)s.n_chunks + c) * 2;
+}
+__host__ __device__ inline size_t dec_o_at(const DecodeShape& s, size_t bh, int c) {
+  return (size_t)s.batch * s.hq * s.n_chunks * 2 + (bh * (size_t)s.n_chunks + c) * s.d;
+}
+__host__ __device__ inline size_t dec_kbits_at(const DecodeShape& s, size_t bh, int c) {
+  return (size_t)s.batch * s.hq * s.n_chunks * (2 + s.d) + bh * (size_t)s.n_chunks + c;
+}
+__host__ __device__ inline size_t dec_vbits_at(const DecodeShape& s, size_t bkv, int c) {
+  return (size_t)s.batch * s.hq * s.n_chunks * (3 + s.d) + bkv * (size_t)s.n_chunks + c;
+}
+
 // Stage masks of the multi-kernel operations.
 constexpr int kStagePrep = 1;      // backward: D = rowsum(O o dO), clear bits/counters
 constexpr int kStageMain = 2;      // backward: dK/dV kernel; decode: split kernel
@@ -71,9 +91,9 @@ hipError_t launch_decode_f32(const DecodeShape& s, const float* q, const float* 
 hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t st);
 hipError_t launch_fill_i8(int8_t* p, int8_t value, size_t n, hipStream_t st);
 hipError_t launch_decode_combine_bf16(const DecodeShape& s, const float* ws, void* o, float* lse,
-                                      hipStream_t st);
+                                      int32_t* kept, hipStream_t st);
 hipError_t launch_decode_combine_f32(const DecodeShape& s, const float* ws, float* o, float* lse,
-                                     hipStream_t st);
+                                     int32_t* kept, hipStream_t st);
 
 // Workspace layouts.
 size_t bwd_ws_d_floats(const Shape& s);    // D = rowsum(O o dO), fp32 [B, Hq, Nq]

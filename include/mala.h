@@ -166,7 +166,8 @@ mala_status mala_bwd_stage(int32_t stage, const mala_problem* p, const void* q, 
                            void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
                            int8_t* tile_mask, int32_t* kept_tiles, void* stream);
 
-/* Bytes of device workspace mala_decode needs (per-split partial states). */
+/* Bytes of device workspace mala_decode needs (per-split partial states and
+ * decision bits). */
 size_t mala_decode_workspace_size(const mala_decode_problem* p);
 
 /*
@@ -194,8 +195,9 @@ mala_status mala_decode(const mala_decode_problem* p, const void* q, const void*
 /*
  * Split-KV decode as two stages (MALA_DECODE_SPLIT then MALA_DECODE_COMBINE,
  * same arguments and workspace, one stream) is mala_decode. SPLIT scores every
- * key, gates the tiles of each split and writes the partial states (and the
- * diagnostics); COMBINE merges them into o and lse.
+ * key, gates the tiles of each split and writes the partial states, the
+ * decision bits and tile_mask; COMBINE merges the partial states into o and
+ * lse and counts the decision bits into kept_tiles.
  */
 enum { MALA_DECODE_SPLIT = 0, MALA_DECODE_COMBINE = 1 };
 mala_status mala_decode_stage(int32_t stage, const mala_decode_problem* p, const void* q,
