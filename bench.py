@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="time budget of the CPU oracle baseline sample (0 = skip)")
     ap.add_argument("--no-128k", action="store_true", help="skip the 128K prefill extra")
+    ap.add_argument("--no-structured", action="store_true",
+                    help="skip the structured-logit extra (skip speedups against tau = 0)")
     ap.add_argument("--fast-grad", action="store_true", help="single-bf16 dS in the backward")
     ap.add_argument("--only", default="", help="profiling: 'fwd', 'bwd' or 'decode' alone")
     ap.add_argument("--profile", action="store_true",
@@ -70,6 +72,94 @@ def bwd_tiles(nq, nk, bq, bk):
         last = min(i * bq + bq - 1, nq - 1)
         tot += min(last + off, nk - 1) // bk + 1
     return tot
+
+
+def structured_section(args, m, W, torch, dev, tiling):
+    """Extra, not part of ``value``: the same kernels on structured-logit inputs
+    (sink keys, a local band, sparse retrieval keys), where the tolerance does
+    skip tiles, timed against tau = 0. Prefill: 32K, 32/8 heads; decode: 8
+    sequences of 131072 keys, 8/1 heads, the query of each sequence being the
+    sequence's last row."""
+    (fbq, fbk), (bbq, bbk), (dbk, dchunk) = tiling
+    taus = (0.0, 1e-4, 1e-2, 1.0)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    res = {"inputs": "workloads.make_structured (bf16)"}
+
+    x = W.make_structured(32768, hq=32, hkv=8, d=128, device=dev, dtype="bf16")
+    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    B, HQ, N, D = q.shape
+    fo = dict(o=torch.empty_like(q), lse=torch.empty(q.shape[:3], device=dev),
+              kept=torch.empty((B, HQ, -(-N // fbq)), dtype=torch.int32, device=dev))
+    bo = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+              kept=torch.empty((B, HQ, -(-N // bbq)), dtype=torch.int32, device=dev))
+    vis_f = fwd_tiles(N, N, fbq, fbk) * B * HQ
+    vis_b = bwd_tiles(N, N, bbq, bbk) * B * HQ
+    pre = {}
+    for tau_ in taus:
+        def run():
+            m.mala_fwd(q, k, v, tau_, softmax_scale=x["scale"], out=fo)
+            ev[1].record()
+            m.mala_bwd(q, k, v, fo["o"], fo["lse"], do, tau_, softmax_scale=x["scale"], out=bo,
+                       fast_grad=args.fast_grad)
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        tf = tb = 0.0
+        for _ in range(args.steps):
+            ev[0].record()
+            run()
+            ev[2].record()
+            torch.cuda.synchronize()
+            tf += ev[0].elapsed_time(ev[1])
+            tb += ev[1].elapsed_time(ev[2])
+        pre[tau_] = dict(fwd_ms=round(tf / args.steps, 3), bwd_ms=round(tb / args.steps, 3),
+                         fwd_kept_frac=round(int(fo["kept"].sum()) / vis_f, 4),
+                         bwd_kept_frac=round(int(bo["kept"].sum()) / vis_b, 4))
+    for tau_ in taus:
+        pre[tau_]["speedup_vs_tau0"] = round(
+            (pre[0.0]["fwd_ms"] + pre[0.0]["bwd_ms"]) / (pre[tau_]["fwd_ms"] + pre[tau_]["bwd_ms"]), 4)
+        pre[tau_]["fwd_speedup"] = round(pre[0.0]["fwd_ms"] / pre[tau_]["fwd_ms"], 4)
+        pre[tau_]["bwd_speedup"] = round(pre[0.0]["bwd_ms"] / pre[tau_]["bwd_ms"], 4)
+    res["prefill_32k"] = {f"tau={t:g}": pre[t] for t in taus}
+    del x, q, k, v, do, fo, bo
+    torch.cuda.empty_cache()
+
+    n = 131072
+    y = W.make_structured(n, hq=8, hkv=1, d=128, batch=8, device=dev, dtype="bf16", with_do=False)
+    kc, vc = y["k"], y["v"]
+    qd = y["q"][:, :, n - 1].contiguous()
+    del y
+    torch.cuda.empty_cache()
+    DB, DHQ, DHKV = kc.shape[0], qd.shape[1], kc.shape[1]
+    seq = torch.full((DB,), n, dtype=torch.int32, device=dev)
+    out = dict(o=torch.empty_like(qd), lse=torch.empty(qd.shape[:2], device=dev),
+               kept=torch.empty((DB, DHQ + DHKV), dtype=torch.int32, device=dev))
+    tiles = DB * DHKV * (-(-n // dbk))
+    dec = {}
+    for tau_ in taus:
+        for _ in range(args.warmup + 2):
+            m.mala_decode(qd, kc, vc, seq, tau_, max_n_k=n, softmax_scale=x_scale(128), out=out)
+        torch.cuda.synchronize()
+        reps = 20
+        ev[0].record()
+        for _ in range(reps):
+            m.mala_decode(qd, kc, vc, seq, tau_, max_n_k=n, softmax_scale=x_scale(128), out=out)
+        ev[1].record()
+        torch.cuda.synchronize()
+        kept = out["kept"].cpu()
+        vt = int(kept[:, DHQ:].sum())
+        dec[tau_] = dict(us_per_step=round(ev[0].elapsed_time(ev[1]) / reps * 1e3, 2),
+                         head_kept_frac=round(int(kept[:, :DHQ].sum()) / (tiles * DHQ // DHKV), 4),
+                         v_tiles_kept_frac=round(vt / tiles, 4),
+                         bytes_per_step=DB * DHKV * n * 128 * 2 + vt * dbk * 128 * 2)
+    for tau_ in taus:
+        dec[tau_]["speedup_vs_tau0"] = round(dec[0.0]["us_per_step"] / dec[tau_]["us_per_step"], 4)
+    res["decode_128k"] = {f"tau={t:g}": dec[t] for t in taus}
+    return res
+
+
+def x_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
 
 
 def main():
@@ -337,6 +427,16 @@ def main():
         torch.cuda.empty_cache()
         x = W.make_prefill(cfg, device=dev)   # for the CPU sample below
         q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+
+    # ------------------------------------------------------------ structured-logit extra
+    if not args.no_structured:
+        keep_cpu = (q.cpu(), k.cpu(), v.cpu(), do.cpu()) if args.cpu_seconds > 0 else None
+        del x, q, k, v, do
+        torch.cuda.empty_cache()
+        out["structured"] = structured_section(args, m, W, torch, dev,
+                                               ((fbq, fbk), (bbq, bbk), (dbk, dchunk)))
+        if keep_cpu is not None:
+            q, k, v, do = (t.to(dev) for t in keep_cpu)
 
     # ------------------------------------------------------------ CPU oracle baseline
     if args.cpu_seconds > 0:
