@@ -20,12 +20,15 @@
 //                 kept tiles of each 32-row block from the bits.
 // Both kernels see the same decisions, so dQ, dK and dV use one support.
 //
-// dS enters the dK and dQ products as a bf16 MFMA operand. By default it is
-// split into hi = bf16(dS) and lo = bf16(dS - hi) and both halves are
-// multiplied (two MFMAs), which carries dS to ~16 significant bits: dK and
-// dQ are sums of many terms that largely cancel (sum_k dS_qk = 0 for the
-// full support), and a single bf16 rounding of dS leaves errors of ~2^-9 of
-// the terms rather than of the result. MALA_FLAG_FAST_GRAD skips the lo half.
+// dS enters the dK and dQ products as a bf16 MFMA operand. dK takes it as one
+// bf16 operand. For dQ it is by default split into hi = bf16(dS) and
+// lo = bf16(dS - hi) and both halves are multiplied (two MFMAs), which
+// carries dS to ~16 significant bits: a row of dS sums to zero over the full
+// support (sum_k dS_qk = 0), so dQ_q = sum_k dS_qk k_k is a sum of terms that
+// largely cancel, and a single bf16 rounding of dS would leave errors of ~2^-9
+// of the terms rather than of the result. A column of dS has no such
+// identity, and dK keeps its error well inside the same bound with one
+// rounding. MALA_FLAG_FAST_GRAD skips the lo half in dQ as well.
 #include "mala_device.h"
 #include "mala_internal.h"
 
@@ -86,7 +89,7 @@ struct alignas(16) DkdvSmem {
   uint32_t keep[2][2];          // [buf][half] bit w: wave w kept its tile
 };
 
-template <int D, bool kSplit>
+template <int D>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
     Shape s, const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dq,
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
                         lds_read_tr(&sm.q[buf][lr][0], ST, 16 + 4 * g, 16 * db, l16));
       // B operands over the 32 query rows, in the row order of the
       // transposing reads
-      bf16x8 pb, dsb, dsl;
+      bf16x8 pb, dsb;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const f32x4 z = *reinterpret_cast<const f32x4*>(&sm.z2[buf][lr + 16 * qb + 4 * g]);
@@ -300,19 +303,14 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
           const float p = fast_exp2(fmaf(sacc[qb][r], s.scale_log2, -z[r]));
           const float ds = p * (dp[qb][r] - ddv[r]);
           pb[4 * qb + r] = (bf16)p;
-          const bf16 hi = (bf16)ds;
-          dsb[4 * qb + r] = hi;
-          if constexpr (kSplit) dsl[4 * qb + r] = (bf16)(ds - (float)hi);
+          dsb[4 * qb + r] = (bf16)ds;
         }
       }
       // ---- dV^T += dO^T P and dK^T += Q^T dS
 #pragma unroll
       for (int db = 0; db < DB; ++db) dv[db] = mfma16(ocol[db], pb, dv[db]);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        dk[db] = mfma16(qcol[db], dsb, dk[db]);
-        if constexpr (kSplit) dk[db] = mfma16(qcol[db], dsl, dk[db]);
-      }
+      for (int db = 0; db < DB; ++db) dk[db] = mfma16(qcol[db], dsb, dk[db]);
     }
     prev_bh = bh;
     prev_i = i;
@@ -595,11 +593,11 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
   };
   const bool split = !(s.flags & MALA_FLAG_FAST_GRAD);
   if (s.d == 128) {
-    if (split) launch(bwd_dkdv_kernel<128, true>, bwd_dq_kernel<128, true>);
-    else launch(bwd_dkdv_kernel<128, false>, bwd_dq_kernel<128, false>);
+    if (split) launch(bwd_dkdv_kernel<128>, bwd_dq_kernel<128, true>);
+    else launch(bwd_dkdv_kernel<128>, bwd_dq_kernel<128, false>);
   } else {
-    if (split) launch(bwd_dkdv_kernel<64, true>, bwd_dq_kernel<64, true>);
-    else launch(bwd_dkdv_kernel<64, false>, bwd_dq_kernel<64, false>);
+    if (split) launch(bwd_dkdv_kernel<64>, bwd_dq_kernel<64, true>);
+    else launch(bwd_dkdv_kernel<64>, bwd_dq_kernel<64, false>);
   }
   return hipGetLastError();
 }

@@ -61,10 +61,11 @@ typedef enum { MALA_OP_FWD = 0, MALA_OP_BWD = 1, MALA_OP_DECODE = 2 } mala_op;
 
 /* Problem flags. */
 enum {
-  /* bf16 backward: multiply dS into dK and dQ as one bf16 operand instead of
-   * a hi + lo pair of bf16 operands. Faster (two fewer matrix products per
-   * kept tile) and less accurate: gradient errors grow to ~2^-9 of the
-   * summed terms, which exceeds 1% of the result where they cancel. */
+  /* bf16 backward: multiply dS into dQ as one bf16 operand (as dK always
+   * takes it) instead of a hi + lo pair of bf16 operands. Faster (one fewer
+   * matrix product per kept tile and key column) and less accurate: dQ errors
+   * grow to ~2^-9 of the summed terms, which can exceed 1% of the result
+   * where the terms of a row cancel. */
   MALA_FLAG_FAST_GRAD = 1
 };
 
