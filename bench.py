@@ -158,6 +158,33 @@ def structured_section(args, m, W, torch, dev, tiling):
     return res
 
 
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "mala_kernels_prefill32k_decode128k_hbm_traffic.md")
+KERNEL_ROWS = {"fwd": ("fwd_bf16_kernel<128>", "fwd_bf16.hip"),
+               "bwd_dkdv": ("bwd_dkdv_kernel<128>", "bwd_bf16.hip"),
+               "bwd_dq": ("bwd_dq_kernel<128, true>", "bwd_bf16.hip")}
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of ``kernel`` from the committed FETCH_SIZE /
+    WRITE_SIZE summary (copy-calibrated), or None when the kernel's sources
+    have changed since those counters were taken."""
+    import hashlib
+    import re
+    if kernel not in KERNEL_ROWS or not os.path.exists(TRAFFIC_MD):
+        return None
+    row, src = KERNEL_ROWS[kernel]
+    csrc = os.path.join(ROOT, "contribution_gated_sparse_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (src, "mala_device.h", "mala_internal.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    for line in open(TRAFFIC_MD):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 7 and cells[0] == row and re.fullmatch(r"[0-9a-f]{16}", cells[6]):
+            return float(cells[5]) * 1e9 if cells[6] == h.hexdigest()[:16] else None
+    return None
+
+
 def x_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
@@ -343,7 +370,7 @@ def main():
             "achieved": alg[dominant] / (tms[dominant] * 1e-3) / 1e12,
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dominant)      # HBM bytes per launch (rocprofv3)
     roof["algorithmic_per_launch"] = alg[dominant]
 
     out = {
