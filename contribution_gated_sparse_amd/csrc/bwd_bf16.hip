@@ -445,22 +445,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   auto tile_bits = [&](const uint32_t* row_bits, int j) -> uint32_t {
     return (row_bits[(4 * j) >> 5] >> ((4 * j) & 31)) & 15u;
   };
-  // Is any column of tile j kept by some wave of the block?
-  auto block_needs = [&](int j) -> uint32_t {
-    uint32_t any = 0;
-    for (int ww = 0; ww < 8; ++ww) {
-      const int qq = I * 256 + ww * 32;
-      if (qq >= s.nq) break;
-      any |= tile_bits(bits + ((size_t)bh * tr32 + qq / kBQ) * words, j);
-    }
-    return any;
+  // Is any column of tile j kept by some wave of the block? Lane ww < 8 reads
+  // the bits of the block's 32-row block ww (one vector load for all eight),
+  // and four ballots OR them together.
+  const int nrb = min(8, (s.nq - I * 256 + 31) / 32);   // valid 32-row blocks
+  const uint32_t* blockbits = bits + ((size_t)bh * tr32 + I * 8) * words;
+  auto block_probe = [&](int j) -> uint32_t {       // this lane's share of block_needs(j)
+    return lane < nrb ? tile_bits(blockbits + (size_t)lane * words, j) : 0u;
   };
+  auto block_any = [&](uint32_t v) -> bool { return wave_any(v != 0u); };
+  auto block_needs = [&](int j) -> bool { return block_any(block_probe(j)); };
 
   // walk only the tiles some wave needs; stage each one in LDS. The staging
   // buffer alternates per staged tile (not per tile index: skipped tiles are
   // jumped over, so index parity would reuse the buffer being read).
   int j = ntiles - 1;
-  while (j >= 0 && block_needs(j) == 0) --j;
+  while (j >= 0 && !block_needs(j)) --j;
+  int jn = j - 1;                                      // next needed tile
+  while (jn >= 0 && !block_needs(jn)) --jn;
   int buf = 0;
   if (j >= 0) {
     load_tile(j);
@@ -472,13 +474,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     settle(orr[t]);
   }
   __syncthreads();
+  uint32_t wd = j >= 0 && active ? tile_bits(mybits, j) : 0u;   // this wave's columns of tile j
   while (j >= 0) {
-    int jn = j - 1;
-    while (jn >= 0 && block_needs(jn) == 0) --jn;
+    // prefetch tile jn, its column bits for this wave, and the probe of the
+    // tile after it; all are consumed at the end of this iteration
     if (jn >= 0) load_tile(jn);
+    const uint32_t wd_next = jn >= 0 && active ? tile_bits(mybits, jn) : 0u;
+    const uint32_t probe = jn >= 1 ? block_probe(jn - 1) : 0u;
 
     if (active) {
-      const uint32_t wd = tile_bits(mybits, j);
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const uint32_t cols = (wd >> (2 * half)) & 3u;   // the half's two 16-key columns
@@ -496,16 +500,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
         }
         const bool boundary = (key0 + 32 > s.nk) || (q0 + 32 > s.nq) ||
                               (s.causal && key0 + 31 > q0 + s.offset);
+        if (boundary) {                                // wave-uniform: mask illegal entries
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = key0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const bool ok = (kk < s.nk) & (q < s.nq) & ((kk <= q + s.offset) | (s.causal == 0));
+            sacc[r] = ok ? sacc[r] : kNegInf;
+          }
+        }
+        // key offset 8(r/4) + 4hf + r%4 lies in column r / 8 of the half: a
+        // skipped column contributes P = 0
+        const float colw[2] = {(cols & 1u) ? 1.f : 0.f, (cols & 2u) ? 1.f : 0.f};
         bf16x8 dsb[2], dsl[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          // key offset 8(r/4) + 4hf + r%4 lies in column r / 8 of the half
-          const int kk = key0 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          bool ok = ((cols >> (r >> 3)) & 1u) != 0;
-          if (boundary)                                // wave-uniform
-            ok = ok & (kk < s.nk) & (q < s.nq) & ((kk <= q + s.offset) | (s.causal == 0));
-          const float e = fast_exp2(fmaf(sacc[r], s.scale_log2, -z2));
-          const float p = ok ? e : 0.f;
+          const float p = fast_exp2(fmaf(sacc[r], s.scale_log2, -z2)) * colw[r >> 3];
           const float ds = p * (dp[r] - dd);
           const bf16 hi = (bf16)ds;
           dsb[r >> 3][r & 7] = hi;
@@ -531,9 +540,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
       }
     }
     if (jn >= 0) store_tile(buf ^ 1);
+    int jnn = jn - 1;                                  // the tile after jn
+    if (jnn >= 0 && !block_any(probe)) {
+      --jnn;
+      while (jnn >= 0 && !block_needs(jnn)) --jnn;
+    }
     __syncthreads();
     buf ^= 1;
     j = jn;
+    jn = jnn < 0 ? -1 : jnn;
+    wd = wd_next;
   }
 
   if (!active || q >= s.nq) return;
