@@ -1,0 +1,135 @@
+"""GPU parity at the full sizes of the benchmark workloads (8K, 32K and 128K
+causal prefill + backward; 128K split-KV decode), run through the same entry
+points and flags as bench.py, against the CPU fp64 oracle on sampled outputs.
+
+The oracle cannot redo a whole 32K or 128K problem in seconds, so each test
+checks outputs it can compute one by one:
+  - forward: O, LSE and every tile decision of sampled 32-row query blocks of
+    one query head (first, early, middle, late and last blocks);
+  - backward dQ and the backward decisions of the same blocks;
+  - backward dK and dV of the last 64 keys of one KV head: causally only the
+    last 64 query rows of the group's heads reach them, so the oracle runs on
+    those rows alone (bottom-right alignment keeps their positions);
+  - decode: whole steps (every head, every split) of the 128K decode batch.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import mala_oracle as O
+from parity_util import BAND, compare_values, np64, tiling
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():   # collected on CPU only to be deselected
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+DEV = "cuda"
+TAU = 1e-4
+
+
+def lib():
+    import contribution_gated_sparse_amd as m
+    return m
+
+
+def _agree(gm, om, margin, what):
+    """Decisions agree wherever the oracle visited and the margin is clear of
+    the near-tie band."""
+    seen = om != O.NOT_VISITED
+    clear = seen & ~(np.abs(np.nan_to_num(margin, nan=np.inf)) < BAND["bf16"])
+    bad = int((gm[clear] != om[clear]).sum())
+    assert bad == 0, f"{what}: {bad} decisions differ outside the near-tie band"
+    return int((seen & ~clear).sum())
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4])
+def test_prefill_full_size_sampled(cid):
+    m = lib()
+    cfg = W.CONFIGS[cid]
+    x = W.make_prefill(cfg, device=DEV)
+    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    scale = x["scale"]
+    B, HQ, N, D = q.shape
+    HKV = k.shape[1]
+    G = HQ // HKV
+    (fbq, fbk, _), (bbq, bbk, _), _ = tiling()
+    assert N % 64 == 0 and fbq == bbq
+    print(f"[full-size] config {cid}: B={B} Hq={HQ} Hkv={HKV} N={N} d={D}", flush=True)
+
+    g = m.mala_fwd(q, k, v, TAU, softmax_scale=scale, want_mask=True)
+    gb = m.mala_bwd(q, k, v, g["o"], g["lse"], do, TAU, softmax_scale=scale, want_mask=True)
+    torch.cuda.synchronize()
+
+    kh = HKV - 1
+    heads = list(range(kh * G, (kh + 1) * G))
+    h = heads[-1]
+    tr = N // fbq
+    blocks = sorted({0, 1, tr // 3, tr // 2 + 1, tr - 3, tr - 1})
+
+    # ---- forward and dQ on sampled blocks of head h
+    kn, vn = np64(k[:, kh:kh + 1]), np64(v[:, kh:kh + 1])
+    qh, doh = np64(q[:, h:h + 1]), np64(do[:, h:h + 1])
+    fmask = g["mask"][:, h:h + 1].cpu().numpy()
+    r = O.mala_fwd(qh, kn, vn, TAU, scale, True, fbq, fbk,
+                   blocks=[(0, 0, i) for i in blocks], replay=fmask, band=BAND["bf16"])
+    _agree(fmask, r["mask"], r["margin"], "forward")
+    kept = g["kept"][:, h:h + 1].cpu().numpy()
+    for i in blocks:
+        assert kept[0, 0, i] == int((r["mask"][0, 0, i] == O.KEPT).sum())
+    rows = np.zeros((1, 1, N), bool)
+    for i in blocks:
+        rows[..., i * fbq:(i + 1) * fbq] = True
+    compare_values("O", np64(g["o"][:, h:h + 1]), r["o"], "bf16", rows)
+    dl = float(np.abs(np64(g["lse"][:, h:h + 1])[rows] - r["lse"][rows]).max())
+    assert dl <= 2e-3, f"LSE error {dl:.3e}"
+
+    bmask = gb["mask"][:, h:h + 1].cpu().numpy()
+    rb = O.mala_bwd(qh, kn, vn, r["o"], r["lse"], doh, TAU, scale, True, bbq, bbk,
+                    qblocks=blocks, replay=bmask, band=BAND["bf16"], o_storage="bf16")
+    _agree(bmask, rb["mask"], rb["margin"], "backward")
+    compare_values("dQ", np64(gb["dq"][:, h:h + 1]), rb["dq"], "bf16", rows)
+
+    # ---- dK, dV of the last 64 keys of KV head kh: only the group's last 64
+    # query rows see them
+    t = 64
+    qt, dot = np64(q[:, heads, N - t:]), np64(do[:, heads, N - t:])
+    ft = g["mask"][:, heads, -(t // fbq):].cpu().numpy()
+    rt = O.mala_fwd(qt, kn, vn, TAU, scale, True, fbq, fbk, replay=ft, band=BAND["bf16"])
+    _agree(ft, rt["mask"], rt["margin"], "forward (tail)")
+    compare_values("O tail", np64(g["o"][:, heads, N - t:]), rt["o"], "bf16")
+    bt = gb["mask"][:, heads, -(t // bbq):].cpu().numpy()
+    rbt = O.mala_bwd(qt, kn, vn, rt["o"], rt["lse"], dot, TAU, scale, True, bbq, bbk,
+                     replay=bt, band=BAND["bf16"], o_storage="bf16")
+    _agree(bt, rbt["mask"], rbt["margin"], "backward (tail)")
+    compare_values("dQ tail", np64(gb["dq"][:, heads, N - t:]), rbt["dq"], "bf16")
+    compare_values("dK tail", np64(gb["dk"][:, kh:kh + 1, N - t:]), rbt["dk"][:, :, N - t:], "bf16")
+    compare_values("dV tail", np64(gb["dv"][:, kh:kh + 1, N - t:]), rbt["dv"][:, :, N - t:], "bf16")
+
+
+@pytest.mark.parametrize("step", [0, 63])
+def test_decode_full_size(step):
+    m = lib()
+    x = W.make_decode(W.CONFIGS[5], device=DEV)
+    kc, vc, qs = x["k_cache"], x["v_cache"], x["q_steps"]
+    cache0 = x["cache"]
+    B, HQ = qs.shape[1], qs.shape[2]
+    n = cache0 + step + 1
+    print(f"[full-size] decode step {step}: B={B} Hq={HQ} N_k={n}", flush=True)
+    _, _, (_, dbk, chunk) = tiling()
+    q = qs[step].contiguous()
+    lens = [n] * B
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    g = m.mala_decode(q, kc, vc, seq, TAU, max_n_k=n, softmax_scale=x["scale"], want_mask=True)
+    torch.cuda.synchronize()
+    gmask = g["mask"].cpu().numpy()
+    r = O.mala_decode(np64(q), np64(kc[:, :, :n]), np64(vc[:, :, :n]), lens, TAU, x["scale"],
+                      chunk, dbk, replay=gmask, band=BAND["bf16"])
+    assert np.array_equal(gmask, r["mask"]), "decode decisions differ outside the near-tie band"
+    kept = g["kept"].cpu().numpy()
+    assert np.array_equal(kept[:, :HQ], (r["mask"] == O.KEPT).sum((-1, -2)))
+    assert np.array_equal(kept[:, HQ:], r["v_tiles"].sum((-1, -2)))
+    compare_values("decode O", np64(g["o"]), r["o"], "bf16")
+    dl = float(np.abs(np64(g["lse"]) - r["lse"]).max())
+    assert dl <= 2e-3, f"LSE error {dl:.3e}"
