@@ -115,6 +115,22 @@ def structured_section(args, m, W, torch, dev, tiling):
         pre[tau_] = dict(fwd_ms=round(tf / args.steps, 3), bwd_ms=round(tb / args.steps, 3),
                          fwd_kept_frac=round(int(fo["kept"].sum()) / vis_f, 4),
                          bwd_kept_frac=round(int(bo["kept"].sum()) / vis_b, 4))
+        # fidelity against tau = 0 (App. C.1/C.3 quantities): omitted normalized
+        # mass per row, 1 - Z_R / Z = 1 - exp(z_tau - z_0), bounded by
+        # tau / (1 + tau) (Prop. 1), and the relative L2 error of each output row
+        if tau_ == 0.0:
+            lse0, o0 = fo["lse"].clone(), fo["o"].float()
+        eps = (1.0 - torch.exp(fo["lse"] - lse0)).flatten().double()
+        rl2 = ((fo["o"].float() - o0).norm(dim=-1) / o0.norm(dim=-1).clamp_min(1e-30)).flatten()
+        bound = tau_ / (1.0 + tau_)
+        pre[tau_]["omitted_mass"] = {
+            "mean": float(eps.mean()), "p95": float(eps.sort().values[int(0.95 * (eps.numel() - 1))]),
+            "max": float(eps.max()), "bound": bound,
+            # fp32 LSEs resolve the mass to ~1e-5
+            "rows_over_bound": int((eps > bound + 1e-5).sum())}
+        pre[tau_]["o_rel_l2"] = {"mean": float(rl2.mean()),
+                                 "p95": float(rl2.sort().values[int(0.95 * (rl2.numel() - 1))]),
+                                 "max": float(rl2.max())}
     for tau_ in taus:
         pre[tau_]["speedup_vs_tau0"] = round(
             (pre[0.0]["fwd_ms"] + pre[0.0]["bwd_ms"]) / (pre[tau_]["fwd_ms"] + pre[tau_]["bwd_ms"]), 4)

@@ -7,3 +7,4 @@ does, and fails loudly if it has not been built.
 """
 from .mala import (MalaError, mala_bwd, mala_decode, mala_fwd, mala_get_tiling,  # noqa: F401
                    load_library, version)
+from .autograd import MalaAttentionFunction, mala_attention  # noqa: F401
