@@ -493,11 +493,27 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
         f32x16 sacc, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; dp[r] = 0.f; }
+        // K and V row operands, read four ahead of their products: the
+        // schedule is pinned to four LDS reads, then alternating product and
+        // read, so the two product chains (S^T, dP^T) hide the read latency
+        bf16x8 ka_[KT], va_[KT];
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
-          sacc = mfma32(load16(&sm.k[buf][krow][kswz(krow, 2 * t + hf)]), qr[t], sacc);
-          dp = mfma32(load16(&sm.v[buf][krow][16 * t + 8 * hf]), orr[t], dp);
+          ka_[t] = load16(&sm.k[buf][krow][kswz(krow, 2 * t + hf)]);
+          va_[t] = load16(&sm.v[buf][krow][16 * t + 8 * hf]);
         }
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+          sacc = mfma32(ka_[t], qr[t], sacc);
+          dp = mfma32(va_[t], orr[t], dp);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);       // 4 LDS reads
+#pragma unroll
+        for (int u = 0; u < 2 * KT - 4; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // 1 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // 1 LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);       // last 4 MFMAs
         const bool boundary = (key0 + 32 > s.nk) || (q0 + 32 > s.nq) ||
                               (s.causal && key0 + 31 > q0 + s.offset);
         if (boundary) {                                // wave-uniform: mask illegal entries
