@@ -227,95 +227,107 @@ __global__ __launch_bounds__(256, 4) void decode_split_kernel(
 
 // Merge the split partial states of one (sequence, head), 32 output columns
 // per workgroup: z = log sum_c Z_c, O = sum_c Z_c O_c / sum_c Z_c (the
-// standard online-softmax reduction). The splits' weights 2^(m_c - M) are
-// computed once into LDS, then 8 groups of 32 threads sum the weighted
-// partial rows (coalesced 128-byte reads), a block of splits at a time.
+// standard online-softmax reduction), in one pass over the partials. Thread
+// (split lane cl, column quad dq) folds splits cl, cl + 32, ... into a
+// running (max, normalizer, output) with rescaling, sixteen splits in
+// flight per thread; the 32 split lanes are then merged the same way in LDS.
 template <typename OutT>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeShape s,
                                                              const float* __restrict__ ws,
                                                              OutT* __restrict__ o,
                                                              float* __restrict__ lse,
                                                              int32_t* __restrict__ kept) {
-  constexpr int kBlk = 1024;            // splits per LDS block of weights
-  __shared__ float wts[kBlk];
-  __shared__ float red[8];
-  __shared__ float acc[8][32];
-  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ float sm_m[32], sm_z[32];
+  __shared__ f32x4 sm_o[32][8];
+  __shared__ int sm_cnt[4][2];
+  const int bh = blockIdx.x, tid = threadIdx.x;
   const int nc = s.n_chunks;
   const float* ms = ws + dec_ms_at(s, bh, 0);
-  // M = max_c m_c
-  float mx = kNegInf;
-  for (int c = tid; c < nc; c += 256) mx = fmaxf(mx, ms[2 * c]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  if (lane == 0) red[wv] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  const int dl = tid & 31, cl = tid >> 5;
-  const int d = blockIdx.y * 32 + dl;
-  float den = 0.f, num = 0.f;
-  for (int cb = 0; cb < nc; cb += kBlk) {
-    const int n = min(kBlk, nc - cb);
-    for (int k = tid; k < n; k += 256) {
-      const float m = ms[2 * (cb + k)];
-      const float wgt = (M == kNegInf || m == kNegInf) ? 0.f : fast_exp2(m - M);
-      wts[k] = wgt;
-      den += wgt * ms[2 * (cb + k) + 1];
-    }
-    __syncthreads();
-    if (d < s.d) {
-      const float* po = ws + dec_o_at(s, bh, cb) + d;
-      int k = cl;
-      for (; k + 24 < n; k += 32) {       // four splits in flight per thread
-        const float a0 = po[(size_t)k * s.d], a1 = po[(size_t)(k + 8) * s.d];
-        const float a2 = po[(size_t)(k + 16) * s.d], a3 = po[(size_t)(k + 24) * s.d];
-        num += wts[k] * a0 + wts[k + 8] * a1 + wts[k + 16] * a2 + wts[k + 24] * a3;
-      }
-      for (; k < n; k += 8) num += wts[k] * po[(size_t)k * s.d];
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
-  if (lane == 0) red[4 + wv] = den;
-  acc[cl][dl] = num;
-  __syncthreads();
-  const float Z = red[4] + red[5] + red[6] + red[7];
-  if (tid < 32 && d < s.d) {
-    float t = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) t += acc[k][tid];
-    o[(size_t)bh * s.d + d] = (OutT)(Z > 0.f ? t / Z : 0.f);
-  }
-  if (blockIdx.y == 0 && tid == 0) lse[bh] = Z > 0.f ? (M + fast_log2(Z)) * kLn2 : kNegInf;
-
-  // kept-tile counters from the splits' decision bits: [b][h] for the head,
-  // [b][Hq + g] (by the group's first head) for the V tiles of KV head g
-  if (kept != nullptr && blockIdx.y == 0 && tid < 64) {
+  const int cl = tid >> 3, dq = tid & 7;
+  const int d0 = blockIdx.y * 32 + 4 * dq;            // this thread's 4 columns
+  const bool dok = d0 < s.d;                            // d is a multiple of 32
+  const float* po = ws + dec_o_at(s, bh, 0) + (dok ? d0 : 0);
+  // kept-tile counters from the splits' decision bits, counted by every
+  // thread of the first column block and issued ahead of the merge loads:
+  // [b][h] for the head, [b][Hq + g] (by the group's first head) for the V
+  // tiles of KV head g
+  const bool count = kept != nullptr && blockIdx.y == 0;
+  const int cb_ = bh / s.hq, ch_ = bh % s.hq, chk_ = ch_ / s.group;
+  const bool vhead = ch_ % s.group == 0;
+  int nh = 0, nv = 0;
+  if (count) {
     const uint32_t* wbits = reinterpret_cast<const uint32_t*>(ws);
-    const int b = bh / s.hq, h = bh % s.hq, hk = h / s.group;
-    int nh = 0, nv = 0;
-    for (int c = tid; c < nc; c += 64) {
+    for (int c = tid; c < nc; c += 256) {
       nh += __popc(wbits[dec_kbits_at(s, bh, c)]);
-      if (h % s.group == 0) nv += __popc(wbits[dec_vbits_at(s, (size_t)b * s.hkv + hk, c)]);
+      if (vhead) nv += __popc(wbits[dec_vbits_at(s, (size_t)cb_ * s.hkv + chk_, c)]);
     }
+  }
+  float mrun = kNegInf, zrun = 0.f;
+  f32x4 orun = {0.f, 0.f, 0.f, 0.f};
+  auto fold = [&](float m, float z, f32x4 x) {
+    const float mn = fmaxf(mrun, m);
+    const float a = mrun == kNegInf ? 0.f : fast_exp2(mrun - mn);
+    const float w = m == kNegInf ? 0.f : fast_exp2(m - mn);
+    zrun = zrun * a + z * w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) orun[e] = orun[e] * a + x[e] * w;
+    mrun = mn;
+  };
+  constexpr int kU = 16;                               // splits in flight per thread
+  int k = cl;
+  for (; k + (kU - 1) * 32 < nc; k += kU * 32) {
+    float2 mz[kU];
+    f32x4 x[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      mz[u] = *reinterpret_cast<const float2*>(ms + 2 * (k + 32 * u));
+      x[u] = *reinterpret_cast<const f32x4*>(po + (size_t)(k + 32 * u) * s.d);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) fold(mz[u].x, mz[u].y, x[u]);
+  }
+  for (; k < nc; k += 32) {
+    const float2 mz = *reinterpret_cast<const float2*>(ms + 2 * k);
+    fold(mz.x, mz.y, *reinterpret_cast<const f32x4*>(po + (size_t)k * s.d));
+  }
+  if (dq == 0) { sm_m[cl] = mrun; sm_z[cl] = zrun; }
+  sm_o[cl][dq] = orun;
+  if (count) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       nh += __shfl_xor(nh, off, 64);
       nv += __shfl_xor(nv, off, 64);
     }
-    if (tid == 0) {
-      kept[(size_t)b * (s.hq + s.hkv) + h] = nh;
-      if (h % s.group == 0) kept[(size_t)b * (s.hq + s.hkv) + s.hq + hk] = nv;
+    if ((tid & 63) == 0) { sm_cnt[tid >> 6][0] = nh; sm_cnt[tid >> 6][1] = nv; }
+  }
+  __syncthreads();
+  if (count && tid == 0) {
+    const size_t base = (size_t)cb_ * (s.hq + s.hkv);
+    kept[base + ch_] = sm_cnt[0][0] + sm_cnt[1][0] + sm_cnt[2][0] + sm_cnt[3][0];
+    if (vhead) kept[base + s.hq + chk_] = sm_cnt[0][1] + sm_cnt[1][1] + sm_cnt[2][1] + sm_cnt[3][1];
+  }
+  if (tid < 32) {
+    float M = kNegInf;
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) M = fmaxf(M, sm_m[j]);
+    float Z = 0.f, t = 0.f;
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) {
+      const float w = sm_m[j] == kNegInf ? 0.f : fast_exp2(sm_m[j] - M);
+      Z += sm_z[j] * w;
+      t += sm_o[j][tid >> 2][tid & 3] * w;
     }
+    const int d = blockIdx.y * 32 + tid;
+    if (d < s.d) o[(size_t)bh * s.d + d] = (OutT)(Z > 0.f ? t / Z : 0.f);
+    if (blockIdx.y == 0 && tid == 0) lse[bh] = Z > 0.f ? (M + fast_log2(Z)) * kLn2 : kNegInf;
   }
 }
 
 }  // namespace
 
 size_t decode_ws_floats(const DecodeShape& s) {
-  return (size_t)s.batch * s.hq * s.n_chunks * (s.d + 3) + (size_t)s.batch * s.hkv * s.n_chunks;
+  return dec_ms_words(s) + (size_t)s.batch * s.hq * s.n_chunks * (s.d + 1) +
+         (size_t)s.batch * s.hkv * s.n_chunks;
 }
 
 hipError_t launch_decode_combine_bf16(const DecodeShape& s, const float* ws, void* o, float* lse,

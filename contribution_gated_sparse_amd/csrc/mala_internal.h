@@ -45,17 +45,23 @@ struct DecodeShape {
 // kept-tile bits of the head, per (sequence * KV head, split) the bits of the
 // tiles whose V was read. The merge kernel turns the bits into the kept-tile
 // counters, so the split kernel needs no atomics.
+// The (m, S) region is padded to 256 bytes so that the partial outputs are
+// 16-byte aligned.
+__host__ __device__ inline size_t dec_ms_words(const DecodeShape& s) {
+  return ((size_t)s.batch * s.hq * s.n_chunks * 2 + 63) / 64 * 64;
+}
 __host__ __device__ inline size_t dec_ms_at(const DecodeShape& s, size_t bh, int c) {
   return (bh * (size_t)s.n_chunks + c) * 2;
 }
 __host__ __device__ inline size_t dec_o_at(const DecodeShape& s, size_t bh, int c) {
-  return (size_t)s.batch * s.hq * s.n_chunks * 2 + (bh * (size_t)s.n_chunks + c) * s.d;
+  return dec_ms_words(s) + (bh * (size_t)s.n_chunks + c) * s.d;
 }
 __host__ __device__ inline size_t dec_kbits_at(const DecodeShape& s, size_t bh, int c) {
-  return (size_t)s.batch * s.hq * s.n_chunks * (2 + s.d) + bh * (size_t)s.n_chunks + c;
+  return dec_ms_words(s) + (size_t)s.batch * s.hq * s.n_chunks * s.d + bh * (size_t)s.n_chunks + c;
 }
 __host__ __device__ inline size_t dec_vbits_at(const DecodeShape& s, size_t bkv, int c) {
-  return (size_t)s.batch * s.hq * s.n_chunks * (3 + s.d) + bkv * (size_t)s.n_chunks + c;
+  return dec_ms_words(s) + (size_t)s.batch * s.hq * s.n_chunks * (s.d + 1) +
+         bkv * (size_t)s.n_chunks + c;
 }
 
 // Stage masks of the multi-kernel operations.

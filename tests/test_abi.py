@@ -130,9 +130,11 @@ def dprob(**kw):
 def test_decode_validation_and_workspace(lib):
     p = dprob()
     n = lib.mala_decode_workspace_size(ctypes.byref(p))
-    # 4 splits of 256 keys: (m, S, O, kept bits) per (sequence, query head, split)
-    # plus V-read bits per (sequence, KV head, split), 4 bytes each
-    assert n == -(-((2 * 8 * 4 * 131 + 2 * 1 * 4) * 4) // 256) * 256
+    # 4 splits of 256 keys: (m, S) pairs padded to 64 words, then (O, kept
+    # bits) per (sequence, query head, split) and V-read bits per (sequence,
+    # KV head, split), 4 bytes each
+    ms = -(-(2 * 8 * 4 * 2) // 64) * 64
+    assert n == -(-((ms + 2 * 8 * 4 * 129 + 2 * 1 * 4) * 4) // 256) * 256
     for kw, word in [(dict(n_q_heads=34, n_kv_heads=2), "16"), (dict(max_n_k=2000), "max_n_k"),
                      (dict(head_dim=64), "head_dim"), (dict(tau=-2.0), "tau"),
                      (dict(n_q_heads=7, n_kv_heads=2), "multiple")]:
