@@ -271,12 +271,29 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       // dO^T and Q^T, the A operands of dV^T = dO^T P and dK^T = Q^T dS,
       // through transposing reads: element e < 4 is query row 4g + e,
       // e >= 4 is row 16 + 4g + (e - 4), for column 16 db + l16.
-      bf16x8 ocol[DB];
+      bf16x8 ocol[DB], qcol[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         ocol[db] = cat8(lds_read_tr(&sm.dout[buf][lr][0], ST, 4 * g, 16 * db, l16),
                         lds_read_tr(&sm.dout[buf][lr][0], ST, 16 + 4 * g, 16 * db, l16));
-      // ---- P = exp(S - z), dP = dO V^T, dS = P o (dP - D)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        qcol[db] = cat8(lds_read_tr(&sm.q[buf][lr][0], ST, 4 * g, 16 * db, l16),
+                        lds_read_tr(&sm.q[buf][lr][0], ST, 16 + 4 * g, 16 * db, l16));
+      // ---- P = exp(S - z) (B operand over the 32 query rows, in the row
+      // order of the transposing reads); it does not wait for dP
+      bf16x8 pb, dsb;
+      float pv[2][4];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const f32x4 z = *reinterpret_cast<const f32x4*>(&sm.z2[buf][lr + 16 * qb + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pv[qb][r] = fast_exp2(fmaf(sacc[qb][r], s.scale_log2, -z[r]));
+          pb[4 * qb + r] = (bf16)pv[qb][r];
+        }
+      }
+      // ---- dP = dO V^T and dV^T += dO^T P, independent products
       f32x4 dp[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
@@ -286,29 +303,15 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       for (int t = 0; t < KS; ++t)
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma16(orow[t][qb], vr[t], dp[qb]);
-      bf16x8 qcol[DB];
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        qcol[db] = cat8(lds_read_tr(&sm.q[buf][lr][0], ST, 4 * g, 16 * db, l16),
-                        lds_read_tr(&sm.q[buf][lr][0], ST, 16 + 4 * g, 16 * db, l16));
-      // B operands over the 32 query rows, in the row order of the
-      // transposing reads
-      bf16x8 pb, dsb;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const f32x4 z = *reinterpret_cast<const f32x4*>(&sm.z2[buf][lr + 16 * qb + 4 * g]);
-        const f32x4 ddv = *reinterpret_cast<const f32x4*>(&sm.dd[buf][lr + 16 * qb + 4 * g]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(fmaf(sacc[qb][r], s.scale_log2, -z[r]));
-          const float ds = p * (dp[qb][r] - ddv[r]);
-          pb[4 * qb + r] = (bf16)p;
-          dsb[4 * qb + r] = (bf16)ds;
-        }
-      }
-      // ---- dV^T += dO^T P and dK^T += Q^T dS
 #pragma unroll
       for (int db = 0; db < DB; ++db) dv[db] = mfma16(ocol[db], pb, dv[db]);
+      // ---- dS = P o (dP - D), then dK^T += Q^T dS
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const f32x4 ddv = *reinterpret_cast<const f32x4*>(&sm.dd[buf][lr + 16 * qb + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dsb[4 * qb + r] = (bf16)(pv[qb][r] * (dp[qb][r] - ddv[r]));
+      }
 #pragma unroll
       for (int db = 0; db < DB; ++db) dk[db] = mfma16(qcol[db], dsb, dk[db]);
     }
