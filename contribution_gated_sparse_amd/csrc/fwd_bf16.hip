@@ -140,11 +140,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+      // K row operands four reads ahead of their products (pinned interleave:
+      // four LDS reads, then alternating product and read)
+      bf16x8 ka[KT][2];
 #pragma unroll
       for (int t = 0; t < KT; ++t)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          sacc[kb] = mfma32(load16(&sm.k[buf][32 * kb + l32][16 * t + 8 * hf]), qr[t], sacc[kb]);
+        for (int kb = 0; kb < 2; ++kb) ka[t][kb] = load16(&sm.k[buf][32 * kb + l32][16 * t + 8 * hf]);
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(ka[t][kb], qr[t], sacc[kb]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int u = 0; u < 2 * KT - 4; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       // ---- causal mask at the diagonal and the ragged key tail
       const int key0 = j * kBK;
       if ((key0 + kBK > s.nk) || (s.causal && key0 + kBK - 1 > q0 + s.offset)) {
