@@ -370,6 +370,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     bf16* __restrict__ dQ, const uint32_t* __restrict__ bits, int32_t* __restrict__ kept,
     int n_qb) {
   __shared__ DqSmem<D> sm;
+  extern __shared__ uint32_t need[];   // ceil(tiles / 32) words, sized at launch
   constexpr int SK = DqSmem<D>::kStrideK, SV = DqSmem<D>::kStrideV;
   constexpr int KT = D / 16, DB = D / 32, CPR = D / 8;
   constexpr int RPP = 512 / CPR;            // rows per load pass
@@ -448,24 +449,38 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   auto tile_bits = [&](const uint32_t* row_bits, int j) -> uint32_t {
     return (row_bits[(4 * j) >> 5] >> ((4 * j) & 31)) & 15u;
   };
-  // Is any column of tile j kept by some wave of the block? Lane ww < 8 reads
-  // the bits of the block's 32-row block ww (one vector load for all eight),
-  // and four ballots OR them together.
+  // Tiles some wave of the block keeps, as a bitmap in LDS (bit t: some
+  // 32-row block of the workgroup keeps a column of 64-key tile t), built
+  // once by all threads so that skipped tiles cost no memory round trip.
   const int nrb = min(8, (s.nq - I * 256 + 31) / 32);   // valid 32-row blocks
   const uint32_t* blockbits = bits + ((size_t)bh * tr32 + I * 8) * words;
-  auto block_probe = [&](int j) -> uint32_t {       // this lane's share of block_needs(j)
-    return lane < nrb ? tile_bits(blockbits + (size_t)lane * words, j) : 0u;
+  const int nneed = (ntiles + 31) / 32;
+  for (int x = tid; x < nneed; x += 512) need[x] = 0u;
+  __syncthreads();
+  for (int t = tid; t < ntiles; t += 512) {
+    uint32_t any = 0;
+#pragma unroll
+    for (int ww = 0; ww < 8; ++ww)
+      if (ww < nrb) any |= tile_bits(blockbits + (size_t)ww * words, t);
+    if (any) atomicOr(&need[t >> 5], 1u << (t & 31));
+  }
+  __syncthreads();
+  // largest needed tile index <= j, or -1
+  auto next_needed = [&](int j) -> int {
+    while (j >= 0) {
+      const uint32_t w = __builtin_amdgcn_readfirstlane(need[j >> 5]) &
+                         (0xffffffffu >> (31 - (j & 31)));
+      if (w != 0u) return (j & ~31) + 31 - __clz(w);
+      j = (j & ~31) - 1;
+    }
+    return -1;
   };
-  auto block_any = [&](uint32_t v) -> bool { return wave_any(v != 0u); };
-  auto block_needs = [&](int j) -> bool { return block_any(block_probe(j)); };
 
   // walk only the tiles some wave needs; stage each one in LDS. The staging
   // buffer alternates per staged tile (not per tile index: skipped tiles are
   // jumped over, so index parity would reuse the buffer being read).
-  int j = ntiles - 1;
-  while (j >= 0 && !block_needs(j)) --j;
-  int jn = j - 1;                                      // next needed tile
-  while (jn >= 0 && !block_needs(jn)) --jn;
+  int j = next_needed(ntiles - 1);
+  int jn = j < 0 ? -1 : next_needed(j - 1);            // next needed tile
   int buf = 0;
   if (j >= 0) {
     load_tile(j);
@@ -479,11 +494,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   __syncthreads();
   uint32_t wd = j >= 0 && active ? tile_bits(mybits, j) : 0u;   // this wave's columns of tile j
   while (j >= 0) {
-    // prefetch tile jn, its column bits for this wave, and the probe of the
-    // tile after it; all are consumed at the end of this iteration
+    // prefetch tile jn and its column bits for this wave; both are consumed
+    // at the end of this iteration
     if (jn >= 0) load_tile(jn);
     const uint32_t wd_next = jn >= 0 && active ? tile_bits(mybits, jn) : 0u;
-    const uint32_t probe = jn >= 1 ? block_probe(jn - 1) : 0u;
 
     if (active) {
 #pragma unroll
@@ -559,15 +573,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
       }
     }
     if (jn >= 0) store_tile(buf ^ 1);
-    int jnn = jn - 1;                                  // the tile after jn
-    if (jnn >= 0 && !block_any(probe)) {
-      --jnn;
-      while (jnn >= 0 && !block_needs(jnn)) --jnn;
-    }
+    const int jnn = jn < 1 ? -1 : next_needed(jn - 1);   // the needed tile after jn
     __syncthreads();
     buf ^= 1;
     j = jn;
-    jn = jnn < 0 ? -1 : jnn;
+    jn = jnn;
     wd = wd_next;
   }
 
@@ -621,8 +631,10 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
       hipLaunchKernelGGL(dkdv, g1, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
                          (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dk, (bf16*)dv,
                          ws_bits, mask, n_kb);
+    // dynamic LDS: the needed-tile bitmap, one bit per 64-key tile
+    const size_t need_bytes = (size_t)((s.nk + 64 * 32 - 1) / (64 * 32)) * 4;
     if (g2.x && (stages & kStageDq))
-      hipLaunchKernelGGL(dqk, g2, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
+      hipLaunchKernelGGL(dqk, g2, dim3(512), need_bytes, st, s, (const bf16*)q, (const bf16*)k,
                          (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dq, ws_bits, kept,
                          n_qb);
   };
