@@ -256,3 +256,41 @@ def test_autograd_chunked_prefill_matches_direct_calls():
     assert torch.equal(o.detach(), f["o"])
     assert torch.equal(base.grad, b["dq"].float())
     assert torch.equal(k.grad, b["dk"]) and torch.equal(v.grad, b["dv"])
+
+
+# ------------------------------------------------------------- staged entry points
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_staged_entry_points_match_single_calls(dtype):
+    """mala_bwd_stage (PREP, DKDV, DQ) and mala_decode_stage (SPLIT, COMBINE),
+    the calls bench.py times one by one, give bit-identical results to
+    mala_bwd and mala_decode, including the decisions and the counters."""
+    m = lib()
+    cfg = W.CONFIGS[2] if dtype == torch.bfloat16 else W.CONFIGS[1]
+    x = W.make_prefill(cfg, n=300, hq=4, hkv=2, d=128 if dtype == torch.bfloat16 else 64,
+                       planted=4, seed=21)
+    x = to_dev({k: (v.to(dtype) if isinstance(v, torch.Tensor) else v) for k, v in x.items()})
+    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    f = m.mala_fwd(q, k, v, 1e-2, softmax_scale=x["scale"])
+    a = m.mala_bwd(q, k, v, f["o"], f["lse"], do, 1e-2, softmax_scale=x["scale"], want_mask=True)
+    b = m.mala_bwd(q, k, v, f["o"], f["lse"], do, 1e-2, softmax_scale=x["scale"], want_mask=True,
+                   stages=(m.mala.BWD_PREP, m.mala.BWD_DKDV, m.mala.BWD_DQ))
+    torch.cuda.synchronize()
+    for name in ("dq", "dk", "dv", "mask", "kept"):
+        assert torch.equal(a[name], b[name]), name
+
+    y = W.make_decode(W.CONFIGS[5], cache=700, steps=1, batch=2, planted=4)
+    y = to_dev({k: (v.to(dtype) if isinstance(v, torch.Tensor) and v.is_floating_point() else v)
+                for k, v in y.items()})
+    if dtype == torch.float32:
+        y["k_cache"], y["v_cache"] = y["k_cache"][..., :64].contiguous(), y["v_cache"][..., :64].contiguous()
+        y["q_steps"] = y["q_steps"][..., :64].contiguous()
+    qd = y["q_steps"][0].contiguous()
+    seq = torch.tensor([701, 300], dtype=torch.int32, device=DEV)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    c = m.mala_decode(qd, y["k_cache"], y["v_cache"], seq, 1e-2, max_n_k=701, want_mask=True)
+    e = m.mala_decode(qd, y["k_cache"], y["v_cache"], seq, 1e-2, max_n_k=701, want_mask=True,
+                      events=ev)
+    torch.cuda.synchronize()
+    for name in ("o", "lse", "mask", "kept"):
+        assert torch.equal(c[name], e[name]), name
