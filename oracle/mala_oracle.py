@@ -20,9 +20,11 @@ tolerance rules in the design notes of this repository):
   causal); this gives L_q = q + 1 for equal lengths and L_0 = N_k for a
   single decode row (Sec. 2.1);
 * tau = 0 makes log(tau / L_q) = -inf, so nothing is skipped (Sec. 2.3);
-* a decision whose margin lies within a near-tie band may be replayed from
-  another implementation's choice (forward only: the forward rule is
-  path dependent); every other decision is the oracle's own;
+* a decision whose margin lies within a near-tie band (a decision that sits
+  on the threshold within rounding) may be replayed from another
+  implementation's choice, in the forward (whose rule is path dependent, so
+  later decisions stay comparable) and in the backward; every other decision
+  is the oracle's own;
 * split-KV decode: chunks aligned to absolute position 0, tiles aligned to
   the chunk start, newest tile first inside each chunk, one decision per
   query head (Sec. 2.4 and App. A.1, "Fused decoding execution").
@@ -384,24 +386,9 @@ def mala_decode(q, k_cache, v_cache, seqlens, tau: float, scale: float,
 
 
 # --------------------------------------------------------------------------
-# Work accounting and fidelity measures (Sec. 2.3, App. C.1-C.3)
+# Fidelity measure (App. C.2)
 # --------------------------------------------------------------------------
-
-def slots_per_query(mask: np.ndarray, nq: int, bq: int, bk: int) -> np.ndarray:
-    """Post-score key slots per query row (Eq. 11 summand): a kept B_q x B_k
-    tile adds B_k slots to each of its rows, masked slots included.
-    mask: [B,H,T_r,T_c] -> [B,H,N_q]."""
-    kept = (mask == KEPT).sum(axis=-1) * bk           # [B,H,T_r]
-    return np.repeat(kept, bq, axis=-1)[..., :nq]
-
 
 def omitted_mass(lse_screened, lse_reference):
     """1 - exp(z_screened - z_reference) (App. C.2)."""
     return 1.0 - np.exp(_f64(lse_screened) - _f64(lse_reference))
-
-
-def rel_l2(x, ref) -> float:
-    """||x - ref||_2 / ||ref||_2 (App. C.3)."""
-    x, ref = _f64(x), _f64(ref)
-    den = np.linalg.norm(ref.ravel())
-    return float(np.linalg.norm((x - ref).ravel()) / (den if den > 0 else 1.0))
