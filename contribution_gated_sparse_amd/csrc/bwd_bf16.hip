@@ -542,12 +542,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
           }
         }
         // key offset 8(r/4) + 4hf + r%4 lies in column r / 8 of the half: a
-        // skipped column contributes P = 0
-        const float colw[2] = {(cols & 1u) ? 1.f : 0.f, (cols & 2u) ? 1.f : 0.f};
+        // skipped column contributes P = 0 (wave-uniform, rare when dense)
+        if (cols != 3u) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!((cols >> (r >> 3)) & 1u)) sacc[r] = kNegInf;
+        }
         bf16x8 dsb[2], dsl[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(sacc[r], s.scale_log2, -z2)) * colw[r >> 3];
+          const float p = fast_exp2(fmaf(sacc[r], s.scale_log2, -z2));
           const float ds = p * (dp[r] - dd);
           const bf16 hi = (bf16)ds;
           dsb[r >> 3][r & 7] = hi;
