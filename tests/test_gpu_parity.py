@@ -88,6 +88,9 @@ SHAPES = [
     (1, 8, 2, 777, 777, 128),
     (1, 2, 2, 300, 300, 64),
     (1, 4, 4, 100, 356, 128),     # chunked prefill: bottom-right causal alignment
+    (1, 2, 2, 1, 700, 128),       # one query row against a long prefix
+    (1, 16, 1, 130, 130, 128),    # a 16-head GQA group on one KV head
+    (3, 4, 2, 33, 97, 64),        # d = 64, batch 3, ragged tiles, chunked
 ]
 
 
