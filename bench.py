@@ -171,6 +171,33 @@ def structured_section(args, m, W, torch, dev, tiling):
     for tau_ in taus:
         dec[tau_]["speedup_vs_tau0"] = round(dec[0.0]["us_per_step"] / dec[tau_]["us_per_step"], 4)
     res["decode_128k"] = {f"tau={t:g}": dec[t] for t in taus}
+
+    # split length: each split tests its tiles against its own partial
+    # normalizer, so longer splits skip more tiles but leave fewer splits to
+    # run in parallel (App. A.1 "Fused decoding execution")
+    sweep = {}
+    for label, sk in (("256", 0), ("auto", m.DECODE_SPLIT_AUTO), ("4096", 4096),
+                      ("unsplit", n)):
+        row = {}
+        for tau_ in (0.0, 1e-4, 1.0):
+            reps = 3 if label == "unsplit" else 20
+            for _ in range(2):
+                r = m.mala_decode(qd, kc, vc, seq, tau_, max_n_k=n, softmax_scale=x_scale(128),
+                                  out=out, split_keys=sk)
+                out["ws"] = r["ws"]         # reused by the timed calls
+            torch.cuda.synchronize()
+            ev[0].record()
+            for _ in range(reps):
+                m.mala_decode(qd, kc, vc, seq, tau_, max_n_k=n, softmax_scale=x_scale(128),
+                              out=out, split_keys=sk)
+            ev[1].record()
+            torch.cuda.synchronize()
+            vt = int(out["kept"][:, DHQ:].sum())
+            row[f"tau={tau_:g}"] = dict(us_per_step=round(ev[0].elapsed_time(ev[1]) / reps * 1e3, 2),
+                                        v_tiles_kept_frac=round(vt / tiles, 4))
+        row["split_keys"] = r["split"]
+        sweep[label] = row
+    res["decode_128k_split_length"] = sweep
     return res
 
 

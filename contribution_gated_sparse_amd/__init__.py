@@ -5,6 +5,7 @@ The operator lives in libmala.so (hand-written HIP kernels behind a C ABI,
 binding. Importing this package does not load the library; the first call
 does, and fails loudly if it has not been built.
 """
-from .mala import (MalaError, mala_bwd, mala_decode, mala_fwd, mala_get_tiling,  # noqa: F401
-                   load_library, version)
+from .mala import (DECODE_SPLIT_AUTO, MalaError, decode_split_keys, mala_bwd,  # noqa: F401
+                   mala_decode, mala_fwd, mala_get_tiling, load_library, make_decode_problem,
+                   version)
 from .autograd import MalaAttentionFunction, mala_attention  # noqa: F401

@@ -1,23 +1,28 @@
 // MALA split-KV decode for bf16 caches on gfx950 (Sec. 2.4; App. A.1
 // "Fused decoding execution").
 //
-// One workgroup handles one 256-key split of one (sequence, KV head) for all
-// query heads of the group (up to 16, packed as MFMA columns). Wave w owns the
-// split's tile w (64 keys):
-//   1. it reads its K tile straight from HBM in the 16x16x32 MFMA operand
-//      layout and scores it against every head (score discovery: all keys);
+// One workgroup handles one split of one (sequence, KV head) for all query
+// heads of the group (up to 16, packed as MFMA columns). The split's tiles
+// (64 keys each) are visited newest first in groups of four, one tile per
+// wave, with the split's running state (M, S) carried from group to group:
+//   1. each wave reads its K tile straight from HBM in the 16x16x32 MFMA
+//      operand layout and scores it against every head (score discovery:
+//      all keys);
 //   2. per-head tile max and tile sum are exchanged through LDS; every wave
-//      then replays the split's gate sequence (newest tile first, state
-//      starting empty, L = N_k) from those statistics, which is exactly the
-//      forward rule of Eq. 3 on a one-row block per head;
+//      then replays the group's gate sequence (newest tile first) from those
+//      statistics and the running state, which is exactly the forward rule of
+//      Eq. 3 on a one-row block per head with L = N_k;
 //   3. only a tile kept by at least one head loads its V tile; each 32-key
 //      half of it is staged row-major in a wave-private LDS slab and read back
 //      transposed (ds_read_b64_tr_b16) as the A operand of O^T += V^T P^T;
-//      heads that skipped the tile contribute P = 0;
+//      heads that skipped the tile contribute P = 0. P is taken against the
+//      running maximum, and a wave's partial output is rescaled when a group
+//      raises it (the online-softmax update);
 //   4. the four waves' partial outputs are summed in LDS and the split writes
 //      its partial state (m, S, O) in base 2.
-// The small LDS footprint (37 KB) lets four workgroups share a CU, so the K
-// and V streams of several splits are in flight at once.
+// With the default 256-key split a workgroup is one group. The small LDS
+// footprint (37 KB) lets four workgroups share a CU, so the K and V streams
+// of several splits are in flight at once.
 // A second kernel merges the splits with the normalizer-aware reduction.
 #include "mala_device.h"
 #include "mala_internal.h"
@@ -25,7 +30,6 @@
 namespace mala {
 namespace {
 
-constexpr int kChunk = 256;
 constexpr int kTile = 64;
 constexpr int kMaxGroup = 16;
 constexpr int kSlabStride = 144;      // bf16; conflict-free transposing reads (16x16x32 layout)
@@ -36,8 +40,8 @@ union alignas(16) DecSlab {
 };
 struct alignas(16) DecSmem {
   DecSlab slab[4];                    // one per wave
-  float tmax[4][kMaxGroup];           // per (tile, head) max, base 2
-  float tsum[4][kMaxGroup];           // per (tile, head) sum of 2^(s - max)
+  float tmax[4][kMaxGroup];           // per (tile of the group, head) max, base 2
+  float tsum[4][kMaxGroup];           // per (tile of the group, head) sum of 2^(s - max)
 };
 
 __global__ __launch_bounds__(256, 4) void decode_split_kernel(
@@ -53,11 +57,25 @@ __global__ __launch_bounds__(256, 4) void decode_split_kernel(
   const int G = s.group;
   int nk = seqlens[b];
   nk = max(1, min(nk, min(s.max_nk, s.cap)));
-  const int tpc = kChunk / kTile;
-
-  const int c0 = c * kChunk;
+  const int tpc = s.chunk / kTile;                     // tiles per split
+  const int c0 = c * s.chunk;
   const int ntile = c0 >= nk ? 0 : min(tpc, (nk - c0 + kTile - 1) / kTile);
+  const int ngroup = (ntile + 3) / 4;
   const size_t bh0 = (size_t)b * s.hq + hk * G;        // first query head of the group
+  uint32_t* wbits = reinterpret_cast<uint32_t*>(ws);
+  const bool head_ok = j16 < G;
+
+  // decision words and mask entries no group of this split visits: tiles
+  // from 4 * ngroup on (all of them for a split past the end of the sequence)
+  for (int x = (4 * ngroup) / 32 + tid; x < s.wps; x += 256) {
+    for (int hh = 0; hh < G; ++hh) wbits[dec_kbits_at(s, bh0 + hh, c) + x] = 0u;
+    wbits[dec_vbits_at(s, blockIdx.y, c) + x] = 0u;
+  }
+  if (mask != nullptr)
+    for (int x = tid; x < G * (tpc - 4 * ngroup); x += 256) {
+      const int hh = x / (tpc - 4 * ngroup), t = 4 * ngroup + x % (tpc - 4 * ngroup);
+      mask[((bh0 + hh) * s.n_chunks + c) * tpc + t] = -1;
+    }
   if (ntile == 0) {
     // split past the end of this sequence: no contribution
     if (tid < G) {
@@ -66,11 +84,6 @@ __global__ __launch_bounds__(256, 4) void decode_split_kernel(
       pms[1] = 0.f;
     }
     for (int idx = tid; idx < D * G; idx += 256) ws[dec_o_at(s, bh0 + idx / D, c) + idx % D] = 0.f;
-    if (mask != nullptr && tid < G * tpc)
-      mask[((bh0 + tid / tpc) * s.n_chunks + c) * tpc + tid % tpc] = -1;
-    uint32_t* wbits = reinterpret_cast<uint32_t*>(ws);
-    if (tid < G) wbits[dec_kbits_at(s, bh0 + tid, c)] = 0u;
-    if (tid == 0) wbits[dec_vbits_at(s, blockIdx.y, c)] = 0u;
     return;
   }
 
@@ -78,129 +91,171 @@ __global__ __launch_bounds__(256, 4) void decode_split_kernel(
   const size_t crow0 = ((size_t)b * s.hkv + hk) * (size_t)s.cap;
   const auto krs = make_rsrc(Kc + crow0 * D, (uint32_t)((size_t)nk * D * 2));
   const auto vrs = make_rsrc(Vc + crow0 * D, (uint32_t)((size_t)nk * D * 2));
-  const int key0 = c0 + w * kTile;
-  const bool has_keys = key0 < nk;
-
-  // ---- score discovery for this wave's tile: S^T[key][head], 4 blocks of 16 keys
-  f32x4 sacc[4];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sacc[kb][r] = 0.f;
-  if (has_keys) {
-    bf16x8 qb[D / 32];
-    const bf16* qrow = Qd + (bh0 + min(j16, G - 1)) * D;
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) qb[t] = j16 < G ? load16(qrow + 32 * t + 8 * g) : zero8();
-    bf16x8 ka[4][D / 32];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-        ka[kb][t] = buf_load16(krs, (uint32_t)((key0 + 16 * kb + j16) * D + 32 * t + 8 * g) * 2);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) sacc[kb] = mfma16(ka[kb][t], qb[t], sacc[kb]);
-  }
-  // lane (head j16, group g) holds keys key0 + 16kb + 4g + r
-  float mx = kNegInf;
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = key0 + 16 * kb + 4 * g + r;
-      const float v = key < nk ? sacc[kb][r] * s.scale_log2 : kNegInf;
-      sacc[kb][r] = v;
-      mx = fmaxf(mx, v);
-    }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  float sm_ = 0.f;
-  if (mx > kNegInf) {
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sm_ += fast_exp2(sacc[kb][r] - mx);
-  }
-  sm_ += __shfl_xor(sm_, 16, 64);
-  sm_ += __shfl_xor(sm_, 32, 64);
-  if (g == 0) {
-    sm.tmax[w][j16] = mx;
-    sm.tsum[w][j16] = sm_;
-  }
-  __syncthreads();
-
-  // ---- the split's gate: newest tile first, empty state, L = N_k (Eq. 3)
+  const bf16* qrow = Qd + (bh0 + min(j16, G - 1)) * D;
   const float c2 = s.log2_tau - fast_log2((float)nk);
-  float M = kNegInf, S = 0.f;
-  uint32_t keepbits = 0;            // bit t: this lane's head keeps tile t
-  for (int t = ntile - 1; t >= 0; --t) {
-    const float tm = sm.tmax[t][j16], ts = sm.tsum[t][j16];
-    const bool keep = (S == 0.f) || (tm - (M + fast_log2(S)) >= c2);
-    if (keep) {
-      const float mn = fmaxf(M, tm);
-      S = S * fast_exp2(M - mn) + ts * fast_exp2(tm - mn);
-      M = mn;
-      keepbits |= 1u << t;
-    }
-  }
-  const bool head_ok = j16 < G;
-  const bool mine = head_ok && ((keepbits >> w) & 1u);
-  const uint64_t vote = __builtin_amdgcn_ballot_w64(mine);
-  const bool tile_kept = has_keys && vote != 0;
-
-  // decisions: the head's kept-tile bits and the bits of V tiles read
-  // (counted by the merge kernel)
-  uint32_t* wbits = reinterpret_cast<uint32_t*>(ws);
-  if (w == 0 && g == 0 && head_ok) {
-    const size_t bh = bh0 + j16;
-    if (mask != nullptr)
-      for (int t = 0; t < tpc; ++t)
-        mask[(bh * s.n_chunks + c) * tpc + t] = t < ntile ? (int8_t)((keepbits >> t) & 1u) : (int8_t)-1;
-    wbits[dec_kbits_at(s, bh, c)] = keepbits;
-  }
-  uint32_t vb = head_ok ? keepbits : 0u;   // tile t's V is read iff some head keeps it
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) vb |= __shfl_xor(vb, off, 64);
-  if (w == 0 && lane == 0) wbits[dec_vbits_at(s, blockIdx.y, c)] = vb;
-
-  // ---- kept tile: V load (HBM), then per 32-key half: row-major LDS slab ->
-  // transposing reads -> P V on the MFMA. Lane (chunk dc, group kq) loads key
-  // 32 (p / 8) + 8 kq + p % 8 into vr[p], 16 bytes at column chunk dc.
+  float M = kNegInf, S = 0.f;       // the split's running state for head j16
+  uint32_t kword = 0u, vword = 0u;  // decision bits of the current 32-tile word
   f32x4 oacc[D / 16];
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
 #pragma unroll
     for (int r = 0; r < 4; ++r) oacc[db][r] = 0.f;
-  if (tile_kept) {
-    const int dc = lane & 15, kq = lane >> 4;
-    bf16x8 vr[16];
+
+  for (int grp = ngroup - 1; grp >= 0; --grp) {
+    const int tw = 4 * grp + w;                        // this wave's tile
+    const int key0 = c0 + tw * kTile;
+    const bool has_keys = tw < ntile;
+
+    // ---- score discovery for this wave's tile: S^T[key][head], 4 blocks of 16 keys
+    f32x4 sacc[4];
 #pragma unroll
-    for (int p = 0; p < 16; ++p)
-      vr[p] = buf_load16(vrs, (uint32_t)((key0 + 32 * (p >> 3) + 8 * kq + (p & 7)) * D + 8 * dc) * 2);
-    // P^T as the B operand of 32-key step ks: element e < 4 is key
-    // 32 ks + 4 g + e, e >= 4 is key 32 ks + 16 + 4 g + (e - 4)
-    bf16x8 pb[2];
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+      for (int r = 0; r < 4; ++r) sacc[kb][r] = 0.f;
+    if (has_keys) {
+      // the group's queries as the B operand: lane (head j16, group g) holds
+      // q[32 t + 8 g .. + 7] (read again per group: cache-resident, and not
+      // held in registers across the V phase)
+      bf16x8 qb[D / 32];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float sv = sacc[2 * ks + (e >> 2)][e & 3];
-        pb[ks][e] = (bf16)(mine ? fast_exp2(sv - M) : 0.f);
+      for (int t = 0; t < D / 32; ++t) qb[t] = head_ok ? load16(qrow + 32 * t + 8 * g) : zero8();
+      // two 32-key halves, so the K operands and the partial output fit the
+      // register budget of four workgroups per CU together
+#pragma unroll
+      for (int hk2 = 0; hk2 < 2; ++hk2) {
+        bf16x8 ka[2][D / 32];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int t = 0; t < D / 32; ++t)
+            ka[kb][t] = buf_load16(
+                krs, (uint32_t)((key0 + 16 * (2 * hk2 + kb) + j16) * D + 32 * t + 8 * g) * 2);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int t = 0; t < D / 32; ++t)
+            sacc[2 * hk2 + kb] = mfma16(ka[kb][t], qb[t], sacc[2 * hk2 + kb]);
       }
-    bf16* slab = &sm.slab[w].v[0][0];
+    }
+    // lane (head j16, group g) holds keys key0 + 16kb + 4g + r
+    float mx = kNegInf;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      // the slab is private to the wave, and a wave's LDS operations complete
-      // in order: the previous half's reads are done before these writes land
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int p = 0; p < 8; ++p) store16(slab + (8 * kq + p) * kSlabStride + 8 * dc, vr[8 * ks + p]);
+      for (int r = 0; r < 4; ++r) {
+        const int key = key0 + 16 * kb + 4 * g + r;
+        const float v = key < nk ? sacc[kb][r] * s.scale_log2 : kNegInf;
+        sacc[kb][r] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float sm_ = 0.f;
+    if (mx > kNegInf) {
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const bf16x8 va = cat8(lds_read_tr(slab, kSlabStride, 4 * g, 16 * db, j16),
-                               lds_read_tr(slab, kSlabStride, 16 + 4 * g, 16 * db, j16));
-        oacc[db] = mfma16(va, pb[ks], oacc[db]);
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm_ += fast_exp2(sacc[kb][r] - mx);
+    }
+    sm_ += __shfl_xor(sm_, 16, 64);
+    sm_ += __shfl_xor(sm_, 32, 64);
+    __syncthreads();                // the previous group's statistics have been read
+    if (g == 0) {
+      sm.tmax[w][j16] = mx;
+      sm.tsum[w][j16] = sm_;
+    }
+    __syncthreads();
+
+    // ---- the group's gate, newest tile first, continuing the split's state (Eq. 3)
+    const float m_prev = M;
+    uint32_t keepbits = 0;          // bit tt: head j16 keeps tile 4 grp + tt
+    for (int tt = 3; tt >= 0; --tt) {
+      if (4 * grp + tt >= ntile) continue;
+      const float tm = sm.tmax[tt][j16], ts = sm.tsum[tt][j16];
+      const bool keep = (S == 0.f) || (tm - (M + fast_log2(S)) >= c2);
+      if (keep) {
+        const float mn = fmaxf(M, tm);
+        S = S * fast_exp2(M - mn) + ts * fast_exp2(tm - mn);
+        M = mn;
+        keepbits |= 1u << tt;
+      }
+    }
+    const bool mine = head_ok && ((keepbits >> w) & 1u);
+    const uint64_t vote = __builtin_amdgcn_ballot_w64(mine);
+    const bool tile_kept = has_keys && vote != 0;
+
+    // decisions: the head's kept-tile bits and the bits of V tiles read
+    // (counted by the merge kernel), one 32-tile word at a time
+    const int sh = (4 * grp) & 31;
+    kword |= (head_ok ? keepbits : 0u) << sh;
+    uint32_t vb = head_ok ? keepbits : 0u;   // tile tt's V is read iff some head keeps it
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) vb |= __shfl_xor(vb, off, 64);
+    vword |= vb << sh;
+    // (addresses as a wave-uniform base plus a 32-bit lane offset)
+    if (w == 0 && g == 0 && head_ok && mask != nullptr) {
+      int8_t* mrow = mask + (bh0 * s.n_chunks + c) * tpc;
+      for (int tt = 0; tt < 4; ++tt) {
+        const int t = 4 * grp + tt;
+        if (t < tpc)
+          mrow[(uint32_t)(j16 * s.n_chunks * tpc + t)] =
+              t < ntile ? (int8_t)((keepbits >> tt) & 1u) : (int8_t)-1;
+      }
+    }
+    if (sh == 0) {                  // the lowest group of its word: flush the word
+      const int word = (4 * grp) >> 5;
+      if (w == 0 && g == 0 && head_ok) {
+        int jh = j16;               // formed here, not kept live across the loop
+        asm volatile("" : "+v"(jh));
+        (wbits + dec_kbits_at(s, bh0, c))[(uint32_t)(jh * s.n_chunks * s.wps + word)] = kword;
+      }
+      if (w == 0 && lane == 0) wbits[dec_vbits_at(s, blockIdx.y, c) + word] = vword;
+      kword = 0u;
+      vword = 0u;
+    }
+
+    // a group that raised the running maximum rescales the partial output
+    if (M != m_prev) {
+      const float a = fast_exp2(m_prev - M);        // 0 while the state was empty
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) oacc[db][r] *= a;
+    }
+
+    // ---- kept tile: V load (HBM), then per 32-key half: row-major LDS slab ->
+    // transposing reads -> P V on the MFMA. Lane (chunk dc, group kq) loads key
+    // 32 (p / 8) + 8 kq + p % 8 into vr[p], 16 bytes at column chunk dc.
+    if (tile_kept) {
+      // P^T as the B operand of 32-key step ks: element e < 4 is key
+      // 32 ks + 4 g + e, e >= 4 is key 32 ks + 16 + 4 g + (e - 4); formed
+      // before the V loads so that the scores are dead during the V phase
+      bf16x8 pb[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float sv = sacc[2 * ks + (e >> 2)][e & 3];
+          pb[ks][e] = (bf16)(mine ? fast_exp2(sv - M) : 0.f);
+        }
+      const int dc = lane & 15, kq = lane >> 4;
+      bf16x8 vr[16];
+#pragma unroll
+      for (int p = 0; p < 16; ++p)
+        vr[p] = buf_load16(vrs, (uint32_t)((key0 + 32 * (p >> 3) + 8 * kq + (p & 7)) * D + 8 * dc) * 2);
+      bf16* slab = &sm.slab[w].v[0][0];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        // the slab is private to the wave, and a wave's LDS operations complete
+        // in order: the previous half's reads are done before these writes land
+#pragma unroll
+        for (int p = 0; p < 8; ++p) store16(slab + (8 * kq + p) * kSlabStride + 8 * dc, vr[8 * ks + p]);
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+          const bf16x8 va = cat8(lds_read_tr(slab, kSlabStride, 4 * g, 16 * db, j16),
+                                 lds_read_tr(slab, kSlabStride, 16 + 4 * g, 16 * db, j16));
+          oacc[db] = mfma16(va, pb[ks], oacc[db]);
+        }
       }
     }
   }
@@ -257,9 +312,12 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeShape s,
   int nh = 0, nv = 0;
   if (count) {
     const uint32_t* wbits = reinterpret_cast<const uint32_t*>(ws);
-    for (int c = tid; c < nc; c += 256) {
-      nh += __popc(wbits[dec_kbits_at(s, bh, c)]);
-      if (vhead) nv += __popc(wbits[dec_vbits_at(s, (size_t)cb_ * s.hkv + chk_, c)]);
+    // a head's (and a KV head's) words of all splits are contiguous
+    const uint32_t* hb = wbits + dec_kbits_at(s, bh, 0);
+    const uint32_t* vbw = wbits + dec_vbits_at(s, (size_t)cb_ * s.hkv + chk_, 0);
+    for (int x = tid; x < nc * s.wps; x += 256) {
+      nh += __popc(hb[x]);
+      if (vhead) nv += __popc(vbw[x]);
     }
   }
   float mrun = kNegInf, zrun = 0.f;
@@ -326,8 +384,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeShape s,
 }  // namespace
 
 size_t decode_ws_floats(const DecodeShape& s) {
-  return dec_ms_words(s) + (size_t)s.batch * s.hq * s.n_chunks * (s.d + 1) +
-         (size_t)s.batch * s.hkv * s.n_chunks;
+  return dec_ms_words(s) + (size_t)s.batch * s.hq * s.n_chunks * (s.d + s.wps) +
+         (size_t)s.batch * s.hkv * s.n_chunks * s.wps;
 }
 
 hipError_t launch_decode_combine_bf16(const DecodeShape& s, const float* ws, void* o, float* lse,

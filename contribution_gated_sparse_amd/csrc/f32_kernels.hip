@@ -344,12 +344,23 @@ __global__ __launch_bounds__(64) void decode_split_f32_kernel(
   const int b = blockIdx.y / s.hkv, hk = blockIdx.y % s.hkv, G = s.group;
   int nk = seqlens[b];
   nk = max(1, min(nk, min(s.max_nk, s.cap)));
-  const int c0 = c * 256;
-  const int ntile = c0 >= nk ? 0 : min(4, (nk - c0 + 63) / 64);
+  const int tpc = s.chunk / 64;    // tiles per split
+  const int c0 = c * s.chunk;
+  const int ntile = c0 >= nk ? 0 : min(tpc, (nk - c0 + 63) / 64);
   const size_t crow0 = ((size_t)b * s.hkv + hk) * (size_t)s.cap;
+  const size_t bh0 = (size_t)b * s.hq + hk * G;
+  uint32_t* wbits = reinterpret_cast<uint32_t*>(ws);
   for (int hh = 0; hh < G; ++hh)
-    for (int e = t; e < D; e += 64) qs[hh][e] = Qd[((size_t)b * s.hq + hk * G + hh) * D + e];
+    for (int e = t; e < D; e += 64) qs[hh][e] = Qd[(bh0 + hh) * D + e];
   if (t < kMaxG) { st_m[t] = -HUGE_VAL; st_s[t] = 0.0; st_bits[t] = 0u; }
+  // decision words and mask entries of tiles past the sequence's end
+  for (int x = (ntile + 31) / 32 + t; x < s.wps; x += 64) {
+    for (int hh = 0; hh < G; ++hh) wbits[dec_kbits_at(s, bh0 + hh, c) + x] = 0u;
+    wbits[dec_vbits_at(s, blockIdx.y, c) + x] = 0u;
+  }
+  if (mask != nullptr)
+    for (int x = t; x < G * (tpc - ntile); x += 64)
+      mask[((bh0 + x / (tpc - ntile)) * s.n_chunks + c) * tpc + ntile + x % (tpc - ntile)] = -1;
   __syncthreads();
   const double cth = s.log_tau - log((double)nk);
   double o0[kMaxG], o1[kMaxG];
@@ -382,15 +393,17 @@ __global__ __launch_bounds__(64) void decode_split_f32_kernel(
         if (t == 0) {
           st_s[hh] = S * alpha[hh] + tot;
           st_m[hh] = mn;
-          st_bits[hh] |= 1u << tt;
+          st_bits[hh] |= 1u << (tt & 31);
         }
         any_keep = true;
       }
+      if (t == 0 && mask != nullptr)
+        mask[((bh0 + hh) * s.n_chunks + c) * tpc + tt] = keep ? 1 : 0;
       ps[hh][t] = p;
       __syncthreads();
     }
     if (any_keep) {
-      vbits |= 1u << tt;
+      vbits |= 1u << (tt & 31);
 #pragma unroll
       for (int hh = 0; hh < kMaxG; ++hh) { o0[hh] *= alpha[hh]; o1[hh] *= alpha[hh]; }
       for (int k = 0; k < 64; ++k) {
@@ -407,6 +420,15 @@ __global__ __launch_bounds__(64) void decode_split_f32_kernel(
       }
     }
     __syncthreads();
+    if ((tt & 31) == 0) {           // the lowest tile of a 32-tile word: flush it
+      if (t < G) {
+        wbits[dec_kbits_at(s, bh0 + t, c) + tt / 32] = st_bits[t];
+        st_bits[t] = 0u;
+      }
+      if (t == 0) wbits[dec_vbits_at(s, blockIdx.y, c) + tt / 32] = vbits;
+      vbits = 0u;
+    }
+    __syncthreads();
   }
   const double log2e = 1.4426950408889634;
 #pragma unroll
@@ -420,16 +442,10 @@ __global__ __launch_bounds__(64) void decode_split_f32_kernel(
     if (t == 0) {
       pms[0] = ntile ? (float)(st_m[hh] * log2e) : kNegInf;
       pms[1] = ntile ? (float)st_s[hh] : 0.f;
-      if (mask != nullptr)
-        for (int tt = 0; tt < 4; ++tt)
-          mask[(bhh * s.n_chunks + c) * 4 + tt] =
-              tt < ntile ? (int8_t)((st_bits[hh] >> tt) & 1u) : (int8_t)-1;
-      reinterpret_cast<uint32_t*>(ws)[dec_kbits_at(s, bhh, c)] = ntile ? st_bits[hh] : 0u;
     }
     if (t < D) po[t] = (float)o0[hh];
     if (t + 64 < D) po[t + 64] = (float)o1[hh];
   }
-  if (t == 0) reinterpret_cast<uint32_t*>(ws)[dec_vbits_at(s, blockIdx.y, c)] = vbits;
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int32_t v, size_t n) {

@@ -111,6 +111,23 @@ size_t bwd_ws_bytes(const mala::Shape& s) {
          round_up(mala::bwd_bits_words(s) * sizeof(uint32_t));
 }
 
+// Keys per split for a checked decode problem (the rule mala_decode_split_keys
+// documents).
+int split_keys(const mala_decode_problem* p) {
+  int64_t split = mala::kDecChunk;
+  if (p->split_keys > 0) {
+    split = p->split_keys;
+  } else if (p->split_keys == MALA_DECODE_SPLIT_AUTO) {
+    const int64_t heads = (int64_t)p->batch * p->n_kv_heads;
+    const int64_t target = heads >= 1024 ? 1 : 1024 / heads;   // splits per (sequence, KV head)
+    const int64_t unit = (int64_t)mala::kDecChunk * target;
+    split = (int64_t)mala::kDecChunk * ((p->max_n_k + unit - 1) / unit);
+    if (split < mala::kDecChunk) split = mala::kDecChunk;
+  }
+  const int64_t whole = ((int64_t)p->max_n_k + mala::kDecBk - 1) / mala::kDecBk * mala::kDecBk;
+  return (int)(split < whole ? split : whole);
+}
+
 mala_status check_decode(const mala_decode_problem* p, mala::DecodeShape* s) {
   if (p == nullptr) return fail(MALA_ERR_INVALID_ARG, "problem is NULL");
   if (p->batch < 1 || p->n_q_heads < 1 || p->n_kv_heads < 1)
@@ -131,6 +148,10 @@ mala_status check_decode(const mala_decode_problem* p, mala::DecodeShape* s) {
     return fail(MALA_ERR_INVALID_ARG, "tau must be finite and >= 0");
   if (!std::isfinite(p->softmax_scale) || p->softmax_scale <= 0.f)
     return fail(MALA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if (p->split_keys < MALA_DECODE_SPLIT_AUTO || (p->split_keys > 0 && p->split_keys % mala::kDecBk))
+    return fail(MALA_ERR_INVALID_ARG,
+                "split_keys must be 0, MALA_DECODE_SPLIT_AUTO or a positive multiple of %d",
+                mala::kDecBk);
   s->batch = p->batch;
   s->hq = p->n_q_heads;
   s->hkv = p->n_kv_heads;
@@ -138,7 +159,9 @@ mala_status check_decode(const mala_decode_problem* p, mala::DecodeShape* s) {
   s->group = p->n_q_heads / p->n_kv_heads;
   s->cap = p->cache_capacity;
   s->max_nk = p->max_n_k;
-  s->n_chunks = (p->max_n_k + mala::kDecChunk - 1) / mala::kDecChunk;
+  s->chunk = split_keys(p);
+  s->n_chunks = (p->max_n_k + s->chunk - 1) / s->chunk;
+  s->wps = (s->chunk / mala::kDecBk + 31) / 32;
   s->scale_log2 = p->softmax_scale * 1.4426950408889634f;
   s->log2_tau = p->tau > 0.f ? std::log2(p->tau) : -INFINITY;
   s->scale = (double)p->softmax_scale;
@@ -275,6 +298,12 @@ mala_status mala_bwd_stage(int32_t stage, const mala_problem* p, const void* q, 
     return fail(MALA_ERR_INVALID_ARG, "unknown backward stage %d", stage);
   return bwd_impl(1 << stage, p, q, k, v, o, lse, d_o, dq, dk, dv, workspace, ws_bytes,
                   tile_mask, kept_tiles, stream);
+}
+
+int32_t mala_decode_split_keys(const mala_decode_problem* p) {
+  mala::DecodeShape s;
+  if (check_decode(p, &s) != MALA_OK) return 0;
+  return s.chunk;
 }
 
 size_t mala_decode_workspace_size(const mala_decode_problem* p) {

@@ -14,7 +14,7 @@ constexpr int kFwdBk = 64;      // keys per forward tile
 constexpr int kBwdBq = 32;      // query rows per backward tile
 constexpr int kBwdBk = 16;      // keys per backward tile (refines the forward tile)
 constexpr int kDecBk = 64;      // keys per decode tile
-constexpr int kDecChunk = 256;  // keys per decode split
+constexpr int kDecChunk = 256;  // default keys per decode split
 
 // Everything a kernel needs about one prefill/training problem.
 struct Shape {
@@ -31,7 +31,10 @@ struct Shape {
 };
 
 struct DecodeShape {
-  int batch, hq, hkv, d, group, cap, max_nk, n_chunks;
+  int batch, hq, hkv, d, group, cap, max_nk;
+  int chunk;         // keys per split, a multiple of kDecBk
+  int n_chunks;      // ceil(max_nk / chunk)
+  int wps;           // decision-bit words per split: ceil(chunk / kDecBk / 32)
   float scale_log2;
   float log2_tau;
   double scale;
@@ -41,9 +44,10 @@ struct DecodeShape {
 // Split-KV decode workspace, in 4-byte words: the partial states (base 2,
 // scale folded in) as the (m, S) pairs of every (sequence * query head,
 // split), then the unnormalized outputs O of every (sequence * query head,
-// split); then the split's decisions: per (sequence * query head, split) the
-// kept-tile bits of the head, per (sequence * KV head, split) the bits of the
-// tiles whose V was read. The merge kernel turns the bits into the kept-tile
+// split); then the split's decisions, wps words each (bit t of word i: tile
+// 32 i + t of the split): per (sequence * query head, split) the kept-tile
+// bits of the head, per (sequence * KV head, split) the bits of the tiles
+// whose V was read. The merge kernel turns the bits into the kept-tile
 // counters, so the split kernel needs no atomics.
 // The (m, S) region is padded to 256 bytes so that the partial outputs are
 // 16-byte aligned.
@@ -57,11 +61,12 @@ __host__ __device__ inline size_t dec_o_at(const DecodeShape& s, size_t bh, int 
   return dec_ms_words(s) + (bh * (size_t)s.n_chunks + c) * s.d;
 }
 __host__ __device__ inline size_t dec_kbits_at(const DecodeShape& s, size_t bh, int c) {
-  return dec_ms_words(s) + (size_t)s.batch * s.hq * s.n_chunks * s.d + bh * (size_t)s.n_chunks + c;
+  return dec_ms_words(s) + (size_t)s.batch * s.hq * s.n_chunks * s.d +
+         (bh * (size_t)s.n_chunks + c) * s.wps;
 }
 __host__ __device__ inline size_t dec_vbits_at(const DecodeShape& s, size_t bkv, int c) {
-  return dec_ms_words(s) + (size_t)s.batch * s.hq * s.n_chunks * (s.d + 1) +
-         bkv * (size_t)s.n_chunks + c;
+  return dec_ms_words(s) + (size_t)s.batch * s.hq * s.n_chunks * (s.d + s.wps) +
+         (bkv * (size_t)s.n_chunks + c) * s.wps;
 }
 
 // Stage masks of the multi-kernel operations.

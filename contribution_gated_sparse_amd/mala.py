@@ -46,12 +46,14 @@ class DecodeProblem(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("cache_capacity", ctypes.c_int32), ("max_n_k", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("tau", ctypes.c_float),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("split_keys", ctypes.c_int32)]
 
+
+DECODE_SPLIT_AUTO = -1
 
 EXPORTS = ("mala_get_tiling", "mala_fwd", "mala_bwd_workspace_size", "mala_bwd",
-           "mala_bwd_stage", "mala_decode_workspace_size", "mala_decode", "mala_decode_stage",
-           "mala_last_error", "mala_version")
+           "mala_bwd_stage", "mala_decode_workspace_size", "mala_decode_split_keys", "mala_decode",
+           "mala_decode_stage", "mala_last_error", "mala_version")
 BWD_PREP, BWD_DKDV, BWD_DQ = 0, 1, 2
 DECODE_SPLIT, DECODE_COMBINE = 0, 1
 
@@ -87,6 +89,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mala_decode_stage.restype = i32
     lib.mala_decode_workspace_size.argtypes = [DP]
     lib.mala_decode_workspace_size.restype = sz
+    lib.mala_decode_split_keys.argtypes = [DP]
+    lib.mala_decode_split_keys.restype = i32
     lib.mala_decode.argtypes = [DP, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
     lib.mala_decode.restype = i32
     lib.mala_last_error.argtypes = []
@@ -215,28 +219,44 @@ def mala_bwd(q, k, v, o, lse, d_o, tau: float, causal: bool = True,
 
 
 def make_decode_problem(q, k_cache, tau: float, max_n_k: int,
-                        softmax_scale: Optional[float] = None) -> DecodeProblem:
+                        softmax_scale: Optional[float] = None,
+                        split_keys: int = 0) -> DecodeProblem:
     b, hq, d = q.shape
     hkv, cap = k_cache.shape[1], k_cache.shape[2]
     scale = 1.0 / math.sqrt(d) if softmax_scale is None else softmax_scale
-    return DecodeProblem(b, hq, hkv, d, cap, int(max_n_k), _dtype_code(q), float(tau), float(scale))
+    return DecodeProblem(b, hq, hkv, d, cap, int(max_n_k), _dtype_code(q), float(tau), float(scale),
+                         int(split_keys))
+
+
+def decode_split_keys(p: DecodeProblem) -> int:
+    """Keys per split that mala_decode uses for problem ``p`` (raises if
+    ``p`` is invalid)."""
+    lib = load_library()
+    n = lib.mala_decode_split_keys(ctypes.byref(p))
+    if n <= 0:
+        raise MalaError(MALA_ERR_INVALID_ARG, lib.mala_last_error().decode())
+    return n
 
 
 def mala_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                 seqlens_k: torch.Tensor, tau: float, max_n_k: Optional[int] = None,
                 softmax_scale: Optional[float] = None, want_mask: bool = False,
-                want_kept: bool = True, out: Optional[dict] = None, events=None) -> dict:
+                want_kept: bool = True, out: Optional[dict] = None, events=None,
+                split_keys: int = 0) -> dict:
     """One split-KV decode step. q [B,Hq,d]; caches [B,Hkv,cap,d]; seqlens_k
-    int32 [B] on the device (N_k including the current token)."""
+    int32 [B] on the device (N_k including the current token). ``split_keys``:
+    0 for the default split, DECODE_SPLIT_AUTO, or a multiple of 64; the
+    returned ``split`` is the length used (the mask is [B,Hq,n_chunks,split/64])."""
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seqlens_k, "seqlens_k")):
         _dev(t, n)
     if seqlens_k.dtype != torch.int32:
         raise TypeError("seqlens_k must be int32")
     if max_n_k is None:
         max_n_k = k_cache.shape[2]
-    p = make_decode_problem(q, k_cache, tau, max_n_k, softmax_scale)
+    p = make_decode_problem(q, k_cache, tau, max_n_k, softmax_scale, split_keys)
     lib = load_library()
-    _, bk, chunk = mala_get_tiling(OP_DECODE)
+    _, bk, _ = mala_get_tiling(OP_DECODE)
+    chunk = decode_split_keys(p)
     nch = -(-int(max_n_k) // chunk)
     out = {} if out is None else out
     o = out.get("o")
@@ -263,7 +283,7 @@ def mala_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         for n, stg in enumerate((DECODE_SPLIT, DECODE_COMBINE)):
             _check(lib.mala_decode_stage(stg, *args))
             events[n].record()
-    return dict(o=o, lse=lse, mask=mask, kept=kept, ws=ws)
+    return dict(o=o, lse=lse, mask=mask, kept=kept, ws=ws, split=chunk)
 
 
 def version() -> str:

@@ -95,7 +95,15 @@ typedef struct {
   int32_t dtype;           /* mala_dtype                                     */
   float tau;
   float softmax_scale;
+  int32_t split_keys;      /* keys per split: 0 = the default (256),
+                              MALA_DECODE_SPLIT_AUTO = chosen from the problem
+                              size, else a positive multiple of 64; a split
+                              longer than max_n_k is one split per sequence.
+                              mala_decode_split_keys() reports the value used. */
 } mala_decode_problem;
+
+/* split_keys: pick the split length from the problem (see mala_decode_split_keys). */
+enum { MALA_DECODE_SPLIT_AUTO = -1 };
 
 /*
  * Decision partition used by an operation (the pages leave B_q and B_k open,
@@ -104,9 +112,11 @@ typedef struct {
  *   op = MALA_OP_BWD:    *bq x *bk tiles; they refine the forward tiles, so a
  *                        forward-skipped tile is backward-skipped (Sec. 2.2).
  *   op = MALA_OP_DECODE: *bq = 1 (one decision per query head), *bk keys per
- *                        tile, *chunk keys per split; splits are aligned to
- *                        position 0 and tiles to the split start; the newest
- *                        tile of a split is tested first.
+ *                        tile, *chunk the default keys per split (a problem
+ *                        may choose another length: mala_decode_split_keys);
+ *                        splits are aligned to position 0 and tiles to the
+ *                        split start; the newest tile of a split is tested
+ *                        first.
  * *chunk is 0 for FWD/BWD. Returns MALA_ERR_INVALID_ARG for an unknown op or
  * a null output pointer.
  */
@@ -172,6 +182,23 @@ mala_status mala_bwd_stage(int32_t stage, const mala_problem* p, const void* q, 
 size_t mala_decode_workspace_size(const mala_decode_problem* p);
 
 /*
+ * Keys per split that mala_decode uses for problem p, or 0 if p is invalid.
+ * Each split starts with an empty running state and tests its tiles against
+ * its own partial normalizer (Sec. 2.2, split-KV decoding; App. A.1 "Fused
+ * decoding execution"), so the retained support depends on this length:
+ * longer splits test more tiles against a more complete normalizer (fewer
+ * forced first tiles) but leave fewer splits to run in parallel.
+ *   split_keys = 0:                      256
+ *   split_keys = MALA_DECODE_SPLIT_AUTO: the shortest multiple of 256 (at
+ *       least 256) that gives at most 1024 splits over batch x KV heads:
+ *       256 * ceil(max_n_k / (256 * max(1, 1024 / (batch * n_kv_heads))))
+ *   split_keys > 0:                      split_keys (a multiple of 64)
+ * The result is then capped at max_n_k rounded up to 64 (one split per
+ * sequence). n_chunks = ceil(max_n_k / split) splits of split / 64 tiles.
+ */
+int32_t mala_decode_split_keys(const mala_decode_problem* p);
+
+/*
  * Split-KV decode (Sec. 2.4; App. A.1 "Fused decoding execution").
  *   q [B,Hq,d]                     the query token of each sequence, at
  *                                  position seqlens_k[b] - 1
@@ -182,8 +209,9 @@ size_t mala_decode_workspace_size(const mala_decode_problem* p);
  *                                  out-of-range lengths are clamped)
  *   o [B,Hq,d], lse [B,Hq] fp32    outputs
  *   workspace, ws_bytes            >= mala_decode_workspace_size(p)
- *   tile_mask  int8 [B,Hq,n_chunks,chunk/bk] or NULL (n_chunks =
- *              ceil(max_n_k/chunk)); entries past a sequence's end are -1
+ *   tile_mask  int8 [B,Hq,n_chunks,split/bk] or NULL (split =
+ *              mala_decode_split_keys(p), n_chunks = ceil(max_n_k/split));
+ *              entries past a sequence's end are -1
  *   kept_tiles int32 [B,Hq+Hkv] or NULL: [b][h] kept tiles of query head h,
  *              [b][Hq+g] tiles of KV head g whose V was read (kept by at least
  *              one query head of the group)

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
     assert set(names) == set(M.EXPORTS)
@@ -122,7 +122,7 @@ def test_backward_workspace(lib):
 
 def dprob(**kw):
     base = dict(batch=2, n_q_heads=8, n_kv_heads=1, head_dim=128, cache_capacity=1000,
-                max_n_k=900, dtype=M.MALA_BF16, tau=1e-4, softmax_scale=0.088)
+                max_n_k=900, dtype=M.MALA_BF16, tau=1e-4, softmax_scale=0.088, split_keys=0)
     base.update(kw)
     return M.DecodeProblem(*[base[f] for f, _ in M.DecodeProblem._fields_])
 
@@ -148,6 +148,32 @@ def test_decode_validation_and_workspace(lib):
         assert st != 0 and word in lib.mala_last_error().decode()
     # fp32 decode supports head_dim 64
     assert lib.mala_decode_workspace_size(ctypes.byref(dprob(head_dim=64, dtype=M.MALA_F32))) > 0
+
+
+def test_decode_split_keys_rule(lib):
+    """The split length each split_keys setting selects (the rule the header
+    states), its validation, and the workspace of multi-word decision bits."""
+    def split(**kw):
+        return lib.mala_decode_split_keys(ctypes.byref(dprob(**kw)))
+    assert split() == 256
+    assert split(split_keys=64) == 64
+    assert split(split_keys=512) == 512
+    # longer than the sequence: one split, max_n_k rounded up to 64
+    assert split(split_keys=4096) == 960
+    for bad in (100, -2, 63):
+        assert split(split_keys=bad) == 0
+        assert "split_keys" in lib.mala_last_error().decode()
+    # AUTO: 256 * ceil(max_n_k / (256 * max(1, 1024 // (batch * n_kv_heads))))
+    assert split(split_keys=M.DECODE_SPLIT_AUTO) == 256                    # 2 x 1 heads, 900 keys
+    big = dict(batch=8, max_n_k=131073, cache_capacity=131073, split_keys=M.DECODE_SPLIT_AUTO)
+    assert split(**big) == 1280                  # 128 splits per sequence: 256 * ceil(131073 / 32768)
+    assert split(**dict(big, n_kv_heads=2, n_q_heads=16)) == 2304        # 64: 256 * ceil(131073 / 16384)
+    assert split(batch=1024, split_keys=M.DECODE_SPLIT_AUTO) == 960       # one split, capped
+    # 2 splits of 40 tiles: two bit words per (head, split)
+    p = dprob(max_n_k=5000, cache_capacity=5000, split_keys=2560)
+    ms = -(-(2 * 8 * 2 * 2) // 64) * 64
+    words = ms + 2 * 8 * 2 * (128 + 2) + 2 * 1 * 2 * 2
+    assert lib.mala_decode_workspace_size(ctypes.byref(p)) == -(-(words * 4) // 256) * 256
 
 
 def test_version(lib):

@@ -10,7 +10,8 @@ checks outputs it can compute one by one:
   - backward dK and dV of the last 64 keys of one KV head: causally only the
     last 64 query rows of the group's heads reach them, so the oracle runs on
     those rows alone (bottom-right alignment keeps their positions);
-  - decode: whole steps (every head, every split) of the 128K decode batch.
+  - decode: whole steps (every head, every split) of the 128K decode batch,
+    with the default 256-key splits and with the automatic split length.
 """
 import numpy as np
 import pytest
@@ -108,21 +109,24 @@ def test_prefill_full_size_sampled(cid):
     compare_values("dV tail", np64(gb["dv"][:, kh:kh + 1, N - t:]), rbt["dv"][:, :, N - t:], "bf16")
 
 
-@pytest.mark.parametrize("step", [0, 63])
-def test_decode_full_size(step):
+@pytest.mark.parametrize("step,split_keys", [(0, 0), (63, 0), (0, -1)])
+def test_decode_full_size(step, split_keys):
     m = lib()
     x = W.make_decode(W.CONFIGS[5], device=DEV)
     kc, vc, qs = x["k_cache"], x["v_cache"], x["q_steps"]
     cache0 = x["cache"]
     B, HQ = qs.shape[1], qs.shape[2]
     n = cache0 + step + 1
-    print(f"[full-size] decode step {step}: B={B} Hq={HQ} N_k={n}", flush=True)
+    print(f"[full-size] decode step {step}: B={B} Hq={HQ} N_k={n} split_keys={split_keys}",
+          flush=True)
     _, _, (_, dbk, chunk) = tiling()
     q = qs[step].contiguous()
     lens = [n] * B
     seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
-    g = m.mala_decode(q, kc, vc, seq, TAU, max_n_k=n, softmax_scale=x["scale"], want_mask=True)
+    g = m.mala_decode(q, kc, vc, seq, TAU, max_n_k=n, softmax_scale=x["scale"], want_mask=True,
+                      split_keys=split_keys)
     torch.cuda.synchronize()
+    chunk = g["split"]
     gmask = g["mask"].cpu().numpy()
     r = O.mala_decode(np64(q), np64(kc[:, :, :n]), np64(vc[:, :, :n]), lens, TAU, x["scale"],
                       chunk, dbk, replay=gmask, band=BAND["bf16"])

@@ -149,16 +149,20 @@ def test_structured_skipping_fwd_bwd(dtype, tau):
 
 # ------------------------------------------------------------- decode
 
-def check_decode(x, lens, tau, steps_q, max_ties=4):
+def check_decode(x, lens, tau, steps_q, max_ties=4, split_keys=0):
     m = lib()
     kc, vc = x["k_cache"], x["v_cache"]
     kind = dtype_name(kc)
     _, _, (_, dbk, chunk) = tiling()
     q = steps_q
     seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    print(f"[decode] {kind} lens={lens} tau={tau} split_keys={split_keys}", flush=True)
     g = m.mala_decode(q, kc, vc, seq, tau, max_n_k=max(lens), softmax_scale=x["scale"],
-                      want_mask=True)
+                      want_mask=True, split_keys=split_keys)
     torch.cuda.synchronize()
+    if split_keys == 0:
+        assert g["split"] == chunk
+    chunk = g["split"]
     gmask = g["mask"].cpu().numpy()
     r = O.mala_decode(np64(q), np64(kc), np64(vc), lens, tau, x["scale"], chunk, dbk,
                       replay=gmask, band=BAND[kind])
@@ -189,6 +193,29 @@ def test_decode_f32_small(tau):
     x = {k: (v.float() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
     x = to_dev(x)
     check_decode(x, [602, 65], tau, x["q_steps"][1].contiguous())
+
+
+# split lengths other than the default: one tile per split, splits that are
+# not whole groups of four tiles, several 32-tile decision words per split,
+# the automatic rule, and one split per sequence (App. A.1 "Fused decoding
+# execution": each split tests its tiles against its own partial normalizer)
+@pytest.mark.parametrize("split_keys", [64, 192, 512, 2560, -1, 8192])
+@pytest.mark.parametrize("tau", [1e-4, 1.0])
+def test_decode_bf16_split_lengths(split_keys, tau):
+    x = W.make_decode(W.CONFIGS[5], cache=4100, steps=1, batch=3, planted=24)
+    x = to_dev(x)
+    g, r = check_decode(x, [4101, 3001, 257], tau, x["q_steps"][0].contiguous(),
+                        split_keys=split_keys)
+    if split_keys == 8192:
+        assert g["split"] == 4160 and g["mask"].shape[2] == 1
+
+
+@pytest.mark.parametrize("split_keys", [64, 320, 2560])
+def test_decode_f32_split_lengths(split_keys):
+    x = W.make_decode(W.CONFIGS[5], cache=2200, steps=1, batch=2, hq=4, hkv=2, planted=8)
+    x = {k: (v.float() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    x = to_dev(x)
+    check_decode(x, [2201, 130], 1e-4, x["q_steps"][0].contiguous(), split_keys=split_keys)
 
 
 def test_decode_group16_and_single_key():
