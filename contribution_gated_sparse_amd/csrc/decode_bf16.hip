@@ -280,6 +280,321 @@ __global__ __launch_bounds__(256, 4) void decode_split_kernel(
   }
 }
 
+// ---------------------------------------------------------------- long splits
+// A split longer than 1024 keys would leave one workgroup walking many tile
+// groups in sequence (and few workgroups in all). Such splits run as three
+// parallel passes that take the same decisions:
+//   1. decode_stats_kernel: one wave per tile scores the tile against every
+//      head of the group and stores each head's tile maximum and tile sum
+//      (exactly the statistics the one-kernel path exchanges through LDS);
+//   2. decode_gate_kernel: one wave per (query head, split) replays the
+//      split's gate, newest tile first, from those statistics. A 64-lane
+//      ballot over the next 64 tiles finds the newest tile the current state
+//      keeps, so a run of skipped tiles costs one step; a prefix log-sum-exp
+//      scan over the window finds where a run of kept tiles ends, so such a
+//      run costs one step too. The state is updated only by kept tiles, as in
+//      Eq. 3. It writes the decision bits, the mask and the split's final
+//      (M, S);
+//   3. decode_pv_kernel: parts of tpart tiles in parallel; a wave takes a
+//      tile that some head keeps, scores it again, forms P against the
+//      split's final maximum and accumulates P V. Every part of a split holds
+//      the split's maximum and the first part its sum, so the merge kernel
+//      sums the parts without rescaling.
+
+__global__ __launch_bounds__(256, 4) void decode_stats_kernel(
+    DecodeShape s, const bf16* __restrict__ Qd, const bf16* __restrict__ Kc,
+    const int32_t* __restrict__ seqlens, float* __restrict__ ws) {
+  constexpr int D = 128;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j16 = lane & 15, g = lane >> 4;
+  const int b = blockIdx.y / s.hkv, hk = blockIdx.y % s.hkv;
+  const int G = s.group;
+  int nk = seqlens[b];
+  nk = max(1, min(nk, min(s.max_nk, s.cap)));
+  const int tpc = s.chunk / kTile;
+  const int ta = 4 * blockIdx.x + w;                   // tile index from position 0
+  const int c = ta / tpc, t = ta % tpc;
+  const int key0 = ta * kTile;
+  if (c >= s.n_chunks || key0 >= nk) return;           // wave-uniform; no barrier below
+  const size_t bh0 = (size_t)b * s.hq + hk * G;
+  const size_t crow0 = ((size_t)b * s.hkv + hk) * (size_t)s.cap;
+  const auto krs = make_rsrc(Kc + crow0 * D, (uint32_t)((size_t)nk * D * 2));
+  bf16x8 qb[D / 32];
+  const bf16* qrow = Qd + (bh0 + min(j16, G - 1)) * D;
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u) qb[u] = j16 < G ? load16(qrow + 32 * u + 8 * g) : zero8();
+  f32x4 sacc[4];
+  bf16x8 ka[4][D / 32];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u) {
+      ka[kb][u] = buf_load16(krs, (uint32_t)((key0 + 16 * kb + j16) * D + 32 * u + 8 * g) * 2);
+    }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u) sacc[kb] = mfma16(ka[kb][u], qb[u], sacc[kb]);
+  }
+  float mx = kNegInf;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int key = key0 + 16 * kb + 4 * g + r;
+      const float v = key < nk ? sacc[kb][r] * s.scale_log2 : kNegInf;
+      sacc[kb][r] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  float sm_ = 0.f;
+  if (mx > kNegInf) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm_ += fast_exp2(sacc[kb][r] - mx);
+  }
+  sm_ += __shfl_xor(sm_, 16, 64);
+  sm_ += __shfl_xor(sm_, 32, 64);
+  if (g == 0 && j16 < G)
+    *reinterpret_cast<float2*>(ws + dec_stats_at(s, bh0 + j16, c, t)) = make_float2(mx, sm_);
+}
+
+constexpr int kGateWords = 256;       // decision words per head a gate workgroup holds
+constexpr int kGateWin = 8;           // 64-tile windows of statistics loaded per batch
+
+__global__ __launch_bounds__(1024) void decode_gate_kernel(DecodeShape s,
+                                                           const int32_t* __restrict__ seqlens,
+                                                           float* __restrict__ ws,
+                                                           int8_t* __restrict__ mask) {
+  __shared__ uint32_t kb[kMaxGroup][kGateWords];
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = blockIdx.x;
+  const int b = blockIdx.y / s.hkv, hk = blockIdx.y % s.hkv;
+  const int G = s.group;
+  int nk = seqlens[b];
+  nk = max(1, min(nk, min(s.max_nk, s.cap)));
+  const int tpc = s.chunk / kTile;
+  const int c0 = c * s.chunk;
+  const int ntile = c0 >= nk ? 0 : min(tpc, (nk - c0 + kTile - 1) / kTile);
+  const size_t bh0 = (size_t)b * s.hq + hk * G;
+  const size_t bh = bh0 + w;                           // wave w: query head w of the group
+  uint32_t* wbits = reinterpret_cast<uint32_t*>(ws);
+  for (int x = lane; x < s.wps; x += 64) kb[w][x] = 0u;
+
+  // ---- replay the split's gate (Eq. 3, newest tile first, empty state)
+  float M = kNegInf, S = 0.f;
+  const float2* st = reinterpret_cast<const float2*>(ws + dec_stats_at(s, bh, c, 0));
+  const float c2 = s.log2_tau - fast_log2((float)nk);
+  for (int base = ntile - 1; base >= 0; base -= 64 * kGateWin) {
+    // lane i of window k holds tile base - 64 k - i
+    float2 win[kGateWin];
+#pragma unroll
+    for (int k = 0; k < kGateWin; ++k) {
+      const int t = base - 64 * k - lane;
+      win[k] = t >= 0 ? st[t] : make_float2(kNegInf, 0.f);
+    }
+#pragma unroll
+    for (int k = 0; k < kGateWin; ++k) {
+      const int wb = base - 64 * k;                    // tile of lane 0
+      if (wb < 0) break;
+      const int last = min(63, wb);                    // last lane holding a tile
+      const float tmv = win[k].x, tsv = win[k].y;
+      int off = 0;                                     // lanes below off are decided
+      while (off <= last) {
+        // the newest undecided tile, tested against the state exactly as in
+        // the one-kernel path
+        const float tm0 = __shfl(tmv, off, 64);
+        const bool keep0 = S == 0.f || tm0 - (M + fast_log2(S)) >= c2;
+        if (keep0) {
+          // A run of kept tiles: if every tile before lane i is kept, the state
+          // lane i is tested against is the state combined with those tiles,
+          // an exclusive prefix of the window. The first lane that fails that
+          // test is the first tile of the run that is skipped.
+          const bool cand = lane >= off && lane <= last;
+          float m = cand ? tmv : kNegInf, z = cand ? tsv : 0.f;
+#pragma unroll
+          for (int d = 1; d < 64; d <<= 1) {           // inclusive log-sum-exp scan
+            const float mu = __shfl_up(m, d, 64), zu = __shfl_up(z, d, 64);
+            if (lane >= d) {
+              const float mn = fmaxf(m, mu);
+              z = (mu == kNegInf ? 0.f : zu * fast_exp2(mu - mn)) +
+                  (m == kNegInf ? 0.f : z * fast_exp2(m - mn));
+              m = mn;
+            }
+          }
+          float me = __shfl_up(m, 1, 64), ze = __shfl_up(z, 1, 64);   // exclusive
+          if (lane == 0) { me = kNegInf; ze = 0.f; }
+          const float um = fmaxf(M, me);
+          const float us = (M == kNegInf ? 0.f : S * fast_exp2(M - um)) +
+                           (me == kNegInf ? 0.f : ze * fast_exp2(me - um));
+          const bool pass = us == 0.f || tmv - (um + fast_log2(us)) >= c2;
+          const uint64_t bal = __builtin_amdgcn_ballot_w64(cand && !pass);
+          const int j = bal ? (int)__builtin_ctzll(bal) : last + 1;   // first skipped lane
+          if (cand && lane < j) {
+            const int t = wb - lane;
+            atomicOr(&kb[w][t >> 5], 1u << (t & 31));
+          }
+          if (j <= last) {                             // lane j is skipped: its state carries on
+            M = __shfl(um, j, 64);
+            S = __shfl(us, j, 64);
+          } else {                                     // the whole rest of the window is kept
+            const float ml = __shfl(m, last, 64), zl = __shfl(z, last, 64);
+            const float mn = fmaxf(M, ml);
+            S = (M == kNegInf ? 0.f : S * fast_exp2(M - mn)) + zl * fast_exp2(ml - mn);
+            M = mn;
+          }
+          off = j + 1;
+        } else {
+          // a run of skipped tiles: the newest later tile the state keeps
+          const bool cand = lane > off && lane <= last;
+          const bool keep = cand && tmv - (M + fast_log2(S)) >= c2;
+          const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+          if (bal == 0) break;                         // the rest of the window is skipped
+          const int i = (int)__builtin_ctzll(bal);
+          const float tm = __shfl(tmv, i, 64), ts = __shfl(tsv, i, 64);
+          const float mn = fmaxf(M, tm);
+          S = S * fast_exp2(M - mn) + ts * fast_exp2(tm - mn);
+          M = mn;
+          const int t = wb - i;
+          if (lane == 0) kb[w][t >> 5] |= 1u << (t & 31);
+          off = i + 1;
+        }
+      }
+    }
+  }
+  // the split's state: its maximum in every part, its sum in the first
+  for (int p = lane; p < s.ppc; p += 64) {
+    float* pms = ws + dec_ms_at(s, bh, c * s.ppc + p);
+    pms[0] = M;
+    pms[1] = p == 0 ? S : 0.f;
+  }
+  __syncthreads();
+  // decision words of every head, the V-read words (some head keeps the
+  // tile) and the mask
+  for (int x = tid; x < s.wps; x += blockDim.x) {
+    uint32_t v = 0u;
+    for (int hh = 0; hh < G; ++hh) {
+      const uint32_t k = kb[hh][x];
+      wbits[dec_kbits_at(s, bh0 + hh, c) + x] = k;
+      v |= k;
+    }
+    wbits[dec_vbits_at(s, blockIdx.y, c) + x] = v;
+  }
+  if (mask != nullptr)
+    for (int x = tid; x < G * tpc; x += blockDim.x) {
+      const int hh = x / tpc, t = x % tpc;
+      mask[((bh0 + hh) * s.n_chunks + c) * tpc + t] =
+          t < ntile ? (int8_t)((kb[hh][t >> 5] >> (t & 31)) & 1u) : (int8_t)-1;
+    }
+}
+
+__global__ __launch_bounds__(256, 4) void decode_pv_kernel(
+    DecodeShape s, const bf16* __restrict__ Qd, const bf16* __restrict__ Kc,
+    const bf16* __restrict__ Vc, const int32_t* __restrict__ seqlens, float* __restrict__ ws) {
+  constexpr int D = 128;
+  __shared__ DecSlab slab[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j16 = lane & 15, g = lane >> 4;
+  const int part = blockIdx.x, c = part / s.ppc, p = part % s.ppc;
+  const int b = blockIdx.y / s.hkv, hk = blockIdx.y % s.hkv;
+  const int G = s.group;
+  int nk = seqlens[b];
+  nk = max(1, min(nk, min(s.max_nk, s.cap)));
+  const int tpc = s.chunk / kTile;
+  const int c0 = c * s.chunk;
+  const int ntile = c0 >= nk ? 0 : min(tpc, (nk - c0 + kTile - 1) / kTile);
+  const int t_lo = p * s.tpart, t_hi = min(t_lo + s.tpart, ntile);
+  const size_t bh0 = (size_t)b * s.hq + hk * G;
+  const bool head_ok = j16 < G;
+  const uint32_t* wbits = reinterpret_cast<const uint32_t*>(ws);
+  const uint32_t* vw = wbits + dec_vbits_at(s, blockIdx.y, c);
+  const uint32_t* kw = wbits + dec_kbits_at(s, bh0 + min(j16, G - 1), c);
+  const float Mh = ws[dec_ms_at(s, bh0 + min(j16, G - 1), part)];   // the split's maximum
+  const size_t crow0 = ((size_t)b * s.hkv + hk) * (size_t)s.cap;
+  const auto krs = make_rsrc(Kc + crow0 * D, (uint32_t)((size_t)nk * D * 2));
+  const auto vrs = make_rsrc(Vc + crow0 * D, (uint32_t)((size_t)nk * D * 2));
+  const bf16* qrow = Qd + (bh0 + min(j16, G - 1)) * D;
+  f32x4 oacc[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) oacc[db][r] = 0.f;
+
+  for (int t = t_lo + w; t < t_hi; t += 4) {           // wave-uniform; no barrier inside
+    if (!((vw[t >> 5] >> (t & 31)) & 1u)) continue;    // no head keeps the tile
+    const bool mine = head_ok && ((kw[t >> 5] >> (t & 31)) & 1u);
+    const int key0 = c0 + t * kTile;
+    // ---- the tile's scores again (as pass 1), then P against the split's maximum
+    f32x4 sacc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sacc[kb][r] = 0.f;
+    {
+      bf16x8 qb[D / 32];
+#pragma unroll
+      for (int u = 0; u < D / 32; ++u) qb[u] = head_ok ? load16(qrow + 32 * u + 8 * g) : zero8();
+#pragma unroll
+      for (int hk2 = 0; hk2 < 2; ++hk2) {
+        bf16x8 ka[2][D / 32];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int u = 0; u < D / 32; ++u)
+            ka[kb][u] = buf_load16(
+                krs, (uint32_t)((key0 + 16 * (2 * hk2 + kb) + j16) * D + 32 * u + 8 * g) * 2);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int u = 0; u < D / 32; ++u)
+            sacc[2 * hk2 + kb] = mfma16(ka[kb][u], qb[u], sacc[2 * hk2 + kb]);
+      }
+    }
+    bf16x8 pb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kb = 2 * ks + (e >> 2), r = e & 3;
+        const int key = key0 + 16 * kb + 4 * g + r;
+        const float sv = key < nk ? sacc[kb][r] * s.scale_log2 : kNegInf;
+        pb[ks][e] = (bf16)(mine ? fast_exp2(sv - Mh) : 0.f);
+      }
+    // ---- V (HBM) -> wave-private slab -> transposing reads -> P V
+    const int dc = lane & 15, kq = lane >> 4;
+    bf16x8 vr[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      vr[q] = buf_load16(vrs, (uint32_t)((key0 + 32 * (q >> 3) + 8 * kq + (q & 7)) * D + 8 * dc) * 2);
+    bf16* sl = &slab[w].v[0][0];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) store16(sl + (8 * kq + q) * kSlabStride + 8 * dc, vr[8 * ks + q]);
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const bf16x8 va = cat8(lds_read_tr(sl, kSlabStride, 4 * g, 16 * db, j16),
+                               lds_read_tr(sl, kSlabStride, 16 + 4 * g, 16 * db, j16));
+        oacc[db] = mfma16(va, pb[ks], oacc[db]);
+      }
+    }
+  }
+  __syncthreads();                  // every wave is done with its slab's V rows
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+    *reinterpret_cast<f32x4*>(&slab[w].o[j16][16 * db + 4 * g]) = oacc[db];
+  __syncthreads();
+  for (int idx = tid; idx < D * G; idx += 256) {
+    const int hh = idx / D, d = idx % D;
+    ws[dec_o_at(s, bh0 + hh, part) + d] =
+        slab[0].o[hh][d] + slab[1].o[hh][d] + slab[2].o[hh][d] + slab[3].o[hh][d];
+  }
+}
+
 // Merge the split partial states of one (sequence, head), 32 output columns
 // per workgroup: z = log sum_c Z_c, O = sum_c Z_c O_c / sum_c Z_c (the
 // standard online-softmax reduction), in one pass over the partials. Thread
@@ -296,7 +611,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeShape s,
   __shared__ f32x4 sm_o[32][8];
   __shared__ int sm_cnt[4][2];
   const int bh = blockIdx.x, tid = threadIdx.x;
-  const int nc = s.n_chunks;
+  const int nc = s.n_parts;                            // partial states per head
   const float* ms = ws + dec_ms_at(s, bh, 0);
   const int cl = tid >> 3, dq = tid & 7;
   const int d0 = blockIdx.y * 32 + 4 * dq;            // this thread's 4 columns
@@ -315,7 +630,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeShape s,
     // a head's (and a KV head's) words of all splits are contiguous
     const uint32_t* hb = wbits + dec_kbits_at(s, bh, 0);
     const uint32_t* vbw = wbits + dec_vbits_at(s, (size_t)cb_ * s.hkv + chk_, 0);
-    for (int x = tid; x < nc * s.wps; x += 256) {
+    for (int x = tid; x < s.n_chunks * s.wps; x += 256) {
       nh += __popc(hb[x]);
       if (vhead) nv += __popc(vbw[x]);
     }
@@ -384,8 +699,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeShape s,
 }  // namespace
 
 size_t decode_ws_floats(const DecodeShape& s) {
-  return dec_ms_words(s) + (size_t)s.batch * s.hq * s.n_chunks * (s.d + s.wps) +
-         (size_t)s.batch * s.hkv * s.n_chunks * s.wps;
+  return s.staged ? dec_stats_at(s, (size_t)s.batch * s.hq, 0, 0)
+                  : dec_vbits_at(s, (size_t)s.batch * s.hkv, 0);
 }
 
 hipError_t launch_decode_combine_bf16(const DecodeShape& s, const float* ws, void* o, float* lse,
@@ -405,8 +720,19 @@ hipError_t launch_decode_bf16(const DecodeShape& s, const void* q, const void* k
                               const int32_t* seqlens, void* o, float* lse, float* ws,
                               int8_t* mask, int32_t* kept, hipStream_t st, int stages) {
   if (stages & kStageMain) {
-    hipLaunchKernelGGL(decode_split_kernel, dim3(s.n_chunks, s.batch * s.hkv), dim3(256), 0, st,
-                       s, (const bf16*)q, (const bf16*)kc, (const bf16*)vc, seqlens, ws, mask);
+    const unsigned bkv = (unsigned)(s.batch * s.hkv);
+    if (s.staged) {
+      const int tiles = s.n_chunks * (s.chunk / kTile);
+      hipLaunchKernelGGL(decode_stats_kernel, dim3((tiles + 3) / 4, bkv), dim3(256), 0, st, s,
+                         (const bf16*)q, (const bf16*)kc, seqlens, ws);
+      hipLaunchKernelGGL(decode_gate_kernel, dim3(s.n_chunks, bkv), dim3(64 * s.group), 0, st, s,
+                         seqlens, ws, mask);
+      hipLaunchKernelGGL(decode_pv_kernel, dim3(s.n_parts, bkv), dim3(256), 0, st, s,
+                         (const bf16*)q, (const bf16*)kc, (const bf16*)vc, seqlens, ws);
+    } else {
+      hipLaunchKernelGGL(decode_split_kernel, dim3(s.n_chunks, bkv), dim3(256), 0, st, s,
+                         (const bf16*)q, (const bf16*)kc, (const bf16*)vc, seqlens, ws, mask);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -162,6 +162,24 @@ mala_status check_decode(const mala_decode_problem* p, mala::DecodeShape* s) {
   s->chunk = split_keys(p);
   s->n_chunks = (p->max_n_k + s->chunk - 1) / s->chunk;
   s->wps = (s->chunk / mala::kDecBk + 31) / 32;
+  // long splits (bf16) that would leave fewer split workgroups than the
+  // chip's 256 compute units run as three parallel passes, when a group's
+  // decision words fit the gate kernel's LDS (16 heads x 256 words)
+  const int tpc = s->chunk / mala::kDecBk;
+  s->staged = p->dtype == MALA_BF16 && s->chunk > 1024 &&
+              (int64_t)s->n_chunks * p->batch * p->n_kv_heads < 256 && s->wps <= 256;
+  s->tpart = tpc;
+  s->ppc = 1;
+  if (s->staged) {
+    // parts of tpart tiles (a multiple of 4, one tile per wave), about 2048
+    // P V workgroups in all
+    const int64_t tiles = (int64_t)s->n_chunks * tpc * p->batch * p->n_kv_heads;
+    int64_t tp = (tiles + 2047) / 2048;
+    tp = (tp + 3) / 4 * 4;
+    s->tpart = (int)(tp < 4 ? 4 : tp > tpc ? (tpc + 3) / 4 * 4 : tp);
+    s->ppc = (tpc + s->tpart - 1) / s->tpart;
+  }
+  s->n_parts = s->n_chunks * s->ppc;
   s->scale_log2 = p->softmax_scale * 1.4426950408889634f;
   s->log2_tau = p->tau > 0.f ? std::log2(p->tau) : -INFINITY;
   s->scale = (double)p->softmax_scale;

@@ -35,6 +35,13 @@ struct DecodeShape {
   int chunk;         // keys per split, a multiple of kDecBk
   int n_chunks;      // ceil(max_nk / chunk)
   int wps;           // decision-bit words per split: ceil(chunk / kDecBk / 32)
+  // Long splits (bf16) run as three parallel passes instead of one workgroup
+  // walking the whole split: tile statistics, the gate replay per head, and
+  // P V over the kept tiles in parts of tpart tiles (ppc parts per split).
+  // The merge then sees n_parts = n_chunks * ppc partial states per head
+  // (n_parts = n_chunks for the one-kernel path).
+  int staged;        // nonzero: the three-pass path
+  int tpart, ppc, n_parts;
   float scale_log2;
   float log2_tau;
   double scale;
@@ -51,22 +58,30 @@ struct DecodeShape {
 // counters, so the split kernel needs no atomics.
 // The (m, S) region is padded to 256 bytes so that the partial outputs are
 // 16-byte aligned.
+// Partial states are indexed by part (split c, part p: c * ppc + p); the
+// decision bits by split.
 __host__ __device__ inline size_t dec_ms_words(const DecodeShape& s) {
-  return ((size_t)s.batch * s.hq * s.n_chunks * 2 + 63) / 64 * 64;
+  return ((size_t)s.batch * s.hq * s.n_parts * 2 + 63) / 64 * 64;
 }
-__host__ __device__ inline size_t dec_ms_at(const DecodeShape& s, size_t bh, int c) {
-  return (bh * (size_t)s.n_chunks + c) * 2;
+__host__ __device__ inline size_t dec_ms_at(const DecodeShape& s, size_t bh, int part) {
+  return (bh * (size_t)s.n_parts + part) * 2;
 }
-__host__ __device__ inline size_t dec_o_at(const DecodeShape& s, size_t bh, int c) {
-  return dec_ms_words(s) + (bh * (size_t)s.n_chunks + c) * s.d;
+__host__ __device__ inline size_t dec_o_at(const DecodeShape& s, size_t bh, int part) {
+  return dec_ms_words(s) + (bh * (size_t)s.n_parts + part) * s.d;
 }
 __host__ __device__ inline size_t dec_kbits_at(const DecodeShape& s, size_t bh, int c) {
-  return dec_ms_words(s) + (size_t)s.batch * s.hq * s.n_chunks * s.d +
+  return dec_ms_words(s) + (size_t)s.batch * s.hq * s.n_parts * s.d +
          (bh * (size_t)s.n_chunks + c) * s.wps;
 }
 __host__ __device__ inline size_t dec_vbits_at(const DecodeShape& s, size_t bkv, int c) {
-  return dec_ms_words(s) + (size_t)s.batch * s.hq * s.n_chunks * (s.d + s.wps) +
-         (bkv * (size_t)s.n_chunks + c) * s.wps;
+  return dec_ms_words(s) + (size_t)s.batch * s.hq * s.n_parts * s.d +
+         (size_t)s.batch * s.hq * s.n_chunks * s.wps + (bkv * (size_t)s.n_chunks + c) * s.wps;
+}
+// three-pass path only: (tile max, tile sum) per (sequence * query head,
+// split, tile), base 2, as float2 (the offset is even)
+__host__ __device__ inline size_t dec_stats_at(const DecodeShape& s, size_t bh, int c, int t) {
+  const size_t base = (dec_vbits_at(s, (size_t)s.batch * s.hkv, 0) + 1) / 2 * 2;
+  return base + ((bh * (size_t)s.n_chunks + c) * (s.chunk / kDecBk) + t) * 2;
 }
 
 // Stage masks of the multi-kernel operations.

@@ -169,10 +169,19 @@ def test_decode_split_keys_rule(lib):
     assert split(**big) == 1280                  # 128 splits per sequence: 256 * ceil(131073 / 32768)
     assert split(**dict(big, n_kv_heads=2, n_q_heads=16)) == 2304        # 64: 256 * ceil(131073 / 16384)
     assert split(batch=1024, split_keys=M.DECODE_SPLIT_AUTO) == 960       # one split, capped
-    # 2 splits of 40 tiles: two bit words per (head, split)
-    p = dprob(max_n_k=5000, cache_capacity=5000, split_keys=2560)
+    # fp32, 2 splits of 40 tiles: two bit words per (head, split)
+    p = dprob(max_n_k=5000, cache_capacity=5000, split_keys=2560, dtype=M.MALA_F32)
     ms = -(-(2 * 8 * 2 * 2) // 64) * 64
     words = ms + 2 * 8 * 2 * (128 + 2) + 2 * 1 * 2 * 2
+    assert lib.mala_decode_workspace_size(ctypes.byref(p)) == -(-(words * 4) // 256) * 256
+    # bf16 splits longer than 1024 keys run as three passes: the partial states
+    # are per part of tpart tiles (here 160 tiles in all -> tpart 4, 10 parts
+    # per split), and the per-(head, tile) statistics follow the bits
+    p = dprob(max_n_k=5000, cache_capacity=5000, split_keys=2560)
+    parts = 2 * 10
+    ms = -(-(2 * 8 * parts * 2) // 64) * 64
+    bits_end = ms + 2 * 8 * parts * 128 + 2 * 8 * 2 * 2 + 2 * 1 * 2 * 2
+    words = bits_end + bits_end % 2 + 2 * 8 * 2 * 40 * 2
     assert lib.mala_decode_workspace_size(ctypes.byref(p)) == -(-(words * 4) // 256) * 256
 
 

@@ -200,7 +200,7 @@ def test_decode_f32_small(tau):
 # the automatic rule, and one split per sequence (App. A.1 "Fused decoding
 # execution": each split tests its tiles against its own partial normalizer)
 @pytest.mark.parametrize("split_keys", [64, 192, 512, 2560, -1, 8192])
-@pytest.mark.parametrize("tau", [1e-4, 1.0])
+@pytest.mark.parametrize("tau", [0.0, 1e-4, 1.0])
 def test_decode_bf16_split_lengths(split_keys, tau):
     x = W.make_decode(W.CONFIGS[5], cache=4100, steps=1, batch=3, planted=24)
     x = to_dev(x)
