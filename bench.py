@@ -74,6 +74,70 @@ def bwd_tiles(nq, nk, bq, bk):
     return tot
 
 
+def head_rel_l2(x, x0):
+    """||x - x0|| / ||x0|| per (batch, head) over that head's [N, d] block."""
+    num = (x.float() - x0.float()).pow(2).sum((-1, -2)).sqrt()
+    den = x0.float().pow(2).sum((-1, -2)).sqrt().clamp_min(1e-30)
+    return (num / den).flatten()
+
+
+def mean_p95(t):
+    t = t.flatten().double()
+    return {"mean": float(t.mean()), "p95": float(t.sort().values[int(0.95 * (t.numel() - 1))])}
+
+
+def matched_work(m, W, torch, dev, fbq, fbk, n=8192):
+    """Allocation at matched work (Sec. 3, Table 1; App. C.2) on structured
+    inputs: MALA's forward support against a per-instance reference-mass
+    control that keeps, for every decision (head x query block), exactly as
+    many key tiles as MALA kept there, chosen by their mass under the
+    unscreened softmax. Both supports are scored the same way in fp32 from
+    the unscreened scores: omitted mass per row and the relative L2 error of
+    the output they imply, so the comparison isolates the allocation.
+    Measurement only: the supports come from the library, the scoring is
+    plain torch on the GPU."""
+    z = W.make_structured(n, hq=32, hkv=8, d=128, device=dev, dtype="bf16", with_do=False)
+    q, k, v, scale = z["q"], z["k"], z["v"], z["scale"]
+    _, HQ, N, _ = q.shape
+    G = HQ // k.shape[1]
+    lse0 = m.mala_fwd(q, k, v, 0.0, softmax_scale=scale)["lse"]
+    causal = torch.ones(N, N, dtype=torch.bool, device=dev).tril()
+    res = {"n": n, "heads": HQ, "decision": f"{fbq} query rows x {fbk} keys"}
+    for tau_ in (1e-4, 1.0):
+        mask = m.mala_fwd(q, k, v, tau_, softmax_scale=scale, want_mask=True)["mask"]
+        Tr, Tc = mask.shape[2], mask.shape[3]
+        acc = {"mala": ([], []), "control": ([], [])}
+        slots = 0
+        for h in range(HQ):
+            kh, vh = k[0, h // G].float(), v[0, h // G].float()
+            p = torch.exp((q[0, h].float() @ kh.T) * scale - lse0[0, h, :, None].float())
+            p = p.masked_fill(~causal, 0.0)                    # unscreened probabilities
+            o_ref = (p @ vh) / p.sum(-1, keepdim=True)
+            pt = p.view(N, Tc, fbk).sum(-1)                    # row mass per key tile
+            blk = pt.view(Tr, fbq, Tc).sum(1)                  # decision mass per key tile
+            keep = mask[0, h] == 1
+            cnt = keep.sum(-1)
+            slots += int(cnt.sum())
+            order = torch.argsort(blk, dim=-1, descending=True, stable=True)
+            rank = torch.empty_like(order)
+            rank.scatter_(1, order, torch.arange(Tc, device=dev).expand(Tr, Tc).contiguous())
+            ctrl = rank < cnt[:, None]                         # the same count, highest mass
+            for name, sup in (("mala", keep), ("control", ctrl)):
+                rows = sup.repeat_interleave(fbq, 0)[:N]       # [N, Tc]
+                om = 1.0 - (pt * rows).sum(-1) / p.sum(-1)
+                pk = p * rows.repeat_interleave(fbk, 1)[:, :N]
+                o = (pk @ vh) / pk.sum(-1, keepdim=True)
+                rl2 = (o - o_ref).norm(dim=-1) / o_ref.norm(dim=-1).clamp_min(1e-30)
+                acc[name][0].append(om)
+                acc[name][1].append(rl2)
+        row = {"slots_per_query": round(slots * fbk * fbq / (HQ * N), 1)}
+        for name, (om, rl2) in acc.items():
+            row[name] = {"omitted_mass": mean_p95(torch.cat(om)),
+                         "o_rel_l2": mean_p95(torch.cat(rl2))}
+        res[f"tau={tau_:g}"] = row
+    return res
+
+
 def structured_section(args, m, W, torch, dev, tiling):
     """Extra, not part of ``value``: the same kernels on structured-logit inputs
     (sink keys, a local band, sparse retrieval keys), where the tolerance does
@@ -85,8 +149,10 @@ def structured_section(args, m, W, torch, dev, tiling):
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     res = {"inputs": "workloads.make_structured (bf16)"}
 
-    x = W.make_structured(32768, hq=32, hkv=8, d=128, device=dev, dtype="bf16")
-    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    x = W.make_structured(32768, hq=32, hkv=8, d=128, device=dev, dtype="bf16", with_do=False)
+    q, k, v = x["q"], x["k"], x["v"]
+    # dO: a deterministic Rademacher probe (App. C.3)
+    do = W.rademacher(q.shape, seed=20269002, device=dev, dtype="bf16")
     B, HQ, N, D = q.shape
     fo = dict(o=torch.empty_like(q), lse=torch.empty(q.shape[:3], device=dev),
               kept=torch.empty((B, HQ, -(-N // fbq)), dtype=torch.int32, device=dev))
@@ -120,6 +186,7 @@ def structured_section(args, m, W, torch, dev, tiling):
         # tau / (1 + tau) (Prop. 1), and the relative L2 error of each output row
         if tau_ == 0.0:
             lse0, o0 = fo["lse"].clone(), fo["o"].float()
+            g0 = {n_: bo[n_].clone() for n_ in ("dq", "dk", "dv")}
         eps = (1.0 - torch.exp(fo["lse"] - lse0)).flatten().double()
         rl2 = ((fo["o"].float() - o0).norm(dim=-1) / o0.norm(dim=-1).clamp_min(1e-30)).flatten()
         bound = tau_ / (1.0 + tau_)
@@ -131,13 +198,25 @@ def structured_section(args, m, W, torch, dev, tiling):
         pre[tau_]["o_rel_l2"] = {"mean": float(rl2.mean()),
                                  "p95": float(rl2.sort().values[int(0.95 * (rl2.numel() - 1))]),
                                  "max": float(rl2.max())}
+        # head-level relative L2 errors (App. C.3): output and dQ per query
+        # head, dK and dV per KV head
+        pre[tau_]["head_rel_l2"] = {"o": mean_p95(head_rel_l2(fo["o"], o0))}
+        for n_ in ("dq", "dk", "dv"):
+            pre[tau_]["head_rel_l2"][n_] = mean_p95(head_rel_l2(bo[n_], g0[n_]))
+        # mean post-score key slots per query (Eq. 11): kept tiles x B_k over
+        # the block's rows
+        pre[tau_]["slots_per_query"] = {
+            "fwd": round(float(fo["kept"].double().sum()) * fbk * fbq / (B * HQ * N), 1),
+            "bwd": round(float(bo["kept"].double().sum()) * bbk * bbq / (B * HQ * N), 1)}
     for tau_ in taus:
         pre[tau_]["speedup_vs_tau0"] = round(
             (pre[0.0]["fwd_ms"] + pre[0.0]["bwd_ms"]) / (pre[tau_]["fwd_ms"] + pre[tau_]["bwd_ms"]), 4)
         pre[tau_]["fwd_speedup"] = round(pre[0.0]["fwd_ms"] / pre[tau_]["fwd_ms"], 4)
         pre[tau_]["bwd_speedup"] = round(pre[0.0]["bwd_ms"] / pre[tau_]["bwd_ms"], 4)
     res["prefill_32k"] = {f"tau={t:g}": pre[t] for t in taus}
-    del x, q, k, v, do, fo, bo
+    del x, q, k, v, do, fo, bo, g0
+    torch.cuda.empty_cache()
+    res["matched_work_8k"] = matched_work(m, W, torch, dev, fbq, fbk)
     torch.cuda.empty_cache()
 
     n = 131072

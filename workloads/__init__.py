@@ -8,7 +8,7 @@ Recipe (the same on every device; the numbers differ between a CPU and a GPU
 generator, so a test always hands the oracle the exact tensors the GPU saw):
 
 * one ``torch.Generator`` per drawn tensor, seeded with ``seed * 64 + tag``
-  (tags: Q=1, K=2, V=3, dO=4, temperature=5, planting=6), seed defaulting to
+  (tags: Q=1, K=2, V=3, dO=4, temperature=5, planting=6, Rademacher probe=7), seed defaulting to
   ``20260000 + config id``; decode sequence ``b`` adds ``1000 * b`` to the seed;
 * Q, K, V, dO ~ N(0, 1), layout [B, H, N, d] with d contiguous, drawn in fp32;
 * a per-query-head temperature T_h ~ U(lo, hi) is folded into Q before rounding
@@ -29,7 +29,7 @@ from typing import Optional, Sequence
 
 import torch
 
-TAG_Q, TAG_K, TAG_V, TAG_DO, TAG_T, TAG_PLANT = 1, 2, 3, 4, 5, 6
+TAG_Q, TAG_K, TAG_V, TAG_DO, TAG_T, TAG_PLANT, TAG_PROBE = 1, 2, 3, 4, 5, 6, 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -173,6 +173,15 @@ def make_prefill(cfg: PrefillConfig, *, seed: Optional[int] = None, device="cpu"
                do=_cast(do, cfg.dtype) if do is not None else None,
                scale=1.0 / math.sqrt(d), temps=temps, dtype=cfg.dtype)
     return out
+
+
+def rademacher(shape, *, seed: int, device="cpu", dtype: str = "bf16") -> torch.Tensor:
+    """A deterministic Rademacher probe: entries -1 or +1 with probability 1/2
+    each, from their own stream (tag 7). It is the dO direction of the
+    gradient-fidelity measurements (App. C.3 uses such a probe)."""
+    u = torch.rand(shape, generator=_gen(device, seed, TAG_PROBE), device=device,
+                   dtype=torch.float32)
+    return _cast(torch.where(u < 0.5, -1.0, 1.0), dtype)
 
 
 def make_decode(cfg: DecodeConfig, *, seed: Optional[int] = None, device="cpu",
