@@ -42,3 +42,14 @@ def test_decode_inputs():
     assert x["q_steps"].shape == (3, 2, 8, 128)
     y = W.make_decode(cfg, cache=500, steps=3, batch=2, planted=4)
     assert torch.equal(x["k_cache"], y["k_cache"]) and torch.equal(x["q_steps"], y["q_steps"])
+
+
+def test_rademacher_probe():
+    """The dO probe of the fidelity measurements: only -1 and +1, about half
+    each, the same for the same seed and different for another seed."""
+    a = W.rademacher((4, 1000), seed=7, dtype="f32")
+    assert set(a.unique().tolist()) == {-1.0, 1.0}
+    assert abs(float(a.mean())) < 0.05
+    assert torch.equal(a, W.rademacher((4, 1000), seed=7, dtype="f32"))
+    assert not torch.equal(a, W.rademacher((4, 1000), seed=8, dtype="f32"))
+    assert W.rademacher((3, 5), seed=7).dtype == torch.bfloat16
