@@ -295,11 +295,12 @@ __global__ __launch_bounds__(256, 4) void decode_split_kernel(
 //      run costs one step too. The state is updated only by kept tiles, as in
 //      Eq. 3. It writes the decision bits, the mask and the split's final
 //      (M, S);
-//   3. decode_pv_kernel: parts of tpart tiles in parallel; a wave takes a
+//   3. decode_pv_kernel: parts of four tiles in parallel; a wave takes a
 //      tile that some head keeps, scores it again, forms P against the
-//      split's final maximum and accumulates P V. Every part of a split holds
-//      the split's maximum and the first part its sum, so the merge kernel
-//      sums the parts without rescaling.
+//      split's final maximum and accumulates P V. The first part of a split
+//      holds the split's maximum and sum, every other part with a kept tile
+//      the maximum, so the merge kernel sums those parts without rescaling;
+//      it skips the empty ones, which write nothing.
 
 __global__ __launch_bounds__(256, 4) void decode_stats_kernel(
     DecodeShape s, const bf16* __restrict__ Qd, const bf16* __restrict__ Kc,
@@ -366,11 +367,17 @@ __global__ __launch_bounds__(256, 4) void decode_stats_kernel(
 constexpr int kGateWords = 256;       // decision words per head a gate workgroup holds
 constexpr int kGateWin = 8;           // 64-tile windows of statistics loaded per batch
 
+// lane i's value of x, i wave-uniform (v_readlane: no LDS round trip)
+__device__ __forceinline__ float lane_of(float x, int i) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), i));
+}
+
 __global__ __launch_bounds__(1024) void decode_gate_kernel(DecodeShape s,
                                                            const int32_t* __restrict__ seqlens,
                                                            float* __restrict__ ws,
                                                            int8_t* __restrict__ mask) {
   __shared__ uint32_t kb[kMaxGroup][kGateWords];
+  __shared__ float2 stl[kMaxGroup][kGateWin][64];     // each wave's current batch of statistics
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = blockIdx.x;
   const int b = blockIdx.y / s.hkv, hk = blockIdx.y % s.hkv;
@@ -389,25 +396,35 @@ __global__ __launch_bounds__(1024) void decode_gate_kernel(DecodeShape s,
   float M = kNegInf, S = 0.f;
   const float2* st = reinterpret_cast<const float2*>(ws + dec_stats_at(s, bh, c, 0));
   const float c2 = s.log2_tau - fast_log2((float)nk);
+  // Lane i of window k of a batch holds tile base - 64 k - i. A batch is
+  // parked in the wave's slice of LDS (a wave's LDS accesses complete in
+  // order, so no barrier), the next one is loaded into registers meanwhile,
+  // and the windows are replayed by a loop that reads them back.
+  float2 nxt[kGateWin];
+#pragma unroll
+  for (int k = 0; k < kGateWin; ++k) {
+    const int t = ntile - 1 - 64 * k - lane;
+    nxt[k] = t >= 0 ? st[t] : make_float2(kNegInf, 0.f);
+  }
   for (int base = ntile - 1; base >= 0; base -= 64 * kGateWin) {
-    // lane i of window k holds tile base - 64 k - i
-    float2 win[kGateWin];
 #pragma unroll
     for (int k = 0; k < kGateWin; ++k) {
-      const int t = base - 64 * k - lane;
-      win[k] = t >= 0 ? st[t] : make_float2(kNegInf, 0.f);
+      stl[w][k][lane] = nxt[k];
+      const int t = base - 64 * (kGateWin + k) - lane;
+      nxt[k] = t >= 0 ? st[t] : make_float2(kNegInf, 0.f);
     }
-#pragma unroll
+#pragma unroll 1
     for (int k = 0; k < kGateWin; ++k) {
       const int wb = base - 64 * k;                    // tile of lane 0
       if (wb < 0) break;
       const int last = min(63, wb);                    // last lane holding a tile
-      const float tmv = win[k].x, tsv = win[k].y;
+      const float2 wv = stl[w][k][lane];
+      const float tmv = wv.x, tsv = wv.y;
       int off = 0;                                     // lanes below off are decided
       while (off <= last) {
         // the newest undecided tile, tested against the state exactly as in
         // the one-kernel path
-        const float tm0 = __shfl(tmv, off, 64);
+        const float tm0 = lane_of(tmv, off);
         const bool keep0 = S == 0.f || tm0 - (M + fast_log2(S)) >= c2;
         if (keep0) {
           // A run of kept tiles: if every tile before lane i is kept, the state
@@ -439,10 +456,10 @@ __global__ __launch_bounds__(1024) void decode_gate_kernel(DecodeShape s,
             atomicOr(&kb[w][t >> 5], 1u << (t & 31));
           }
           if (j <= last) {                             // lane j is skipped: its state carries on
-            M = __shfl(um, j, 64);
-            S = __shfl(us, j, 64);
+            M = lane_of(um, j);
+            S = lane_of(us, j);
           } else {                                     // the whole rest of the window is kept
-            const float ml = __shfl(m, last, 64), zl = __shfl(z, last, 64);
+            const float ml = lane_of(m, last), zl = lane_of(z, last);
             const float mn = fmaxf(M, ml);
             S = (M == kNegInf ? 0.f : S * fast_exp2(M - mn)) + zl * fast_exp2(ml - mn);
             M = mn;
@@ -455,7 +472,7 @@ __global__ __launch_bounds__(1024) void decode_gate_kernel(DecodeShape s,
           const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
           if (bal == 0) break;                         // the rest of the window is skipped
           const int i = (int)__builtin_ctzll(bal);
-          const float tm = __shfl(tmv, i, 64), ts = __shfl(tsv, i, 64);
+          const float tm = lane_of(tmv, i), ts = lane_of(tsv, i);
           const float mn = fmaxf(M, tm);
           S = S * fast_exp2(M - mn) + ts * fast_exp2(tm - mn);
           M = mn;
@@ -466,13 +483,18 @@ __global__ __launch_bounds__(1024) void decode_gate_kernel(DecodeShape s,
       }
     }
   }
-  // the split's state: its maximum in every part, its sum in the first
+  // the split's state: its sum in the first part, its maximum in the first
+  // part and in every part that holds a tile the head keeps; a later part
+  // without one is empty (m = -inf: the merge reads nothing of it)
+  __syncthreads();
   for (int p = lane; p < s.ppc; p += 64) {
+    bool any = p == 0;
+    for (int t = p * s.tpart; t < min((p + 1) * s.tpart, ntile) && !any; ++t)
+      any = (kb[w][t >> 5] >> (t & 31)) & 1u;
     float* pms = ws + dec_ms_at(s, bh, c * s.ppc + p);
-    pms[0] = M;
+    pms[0] = any ? M : kNegInf;
     pms[1] = p == 0 ? S : 0.f;
   }
-  __syncthreads();
   // decision words of every head, the V-read words (some head keeps the
   // tile) and the mask
   for (int x = tid; x < s.wps; x += blockDim.x) {
@@ -524,62 +546,84 @@ __global__ __launch_bounds__(256, 4) void decode_pv_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) oacc[db][r] = 0.f;
 
-  for (int t = t_lo + w; t < t_hi; t += 4) {           // wave-uniform; no barrier inside
-    if (!((vw[t >> 5] >> (t & 31)) & 1u)) continue;    // no head keeps the tile
-    const bool mine = head_ok && ((kw[t >> 5] >> (t & 31)) & 1u);
-    const int key0 = c0 + t * kTile;
-    // ---- the tile's scores again (as pass 1), then P against the split's maximum
-    f32x4 sacc[4];
+  // the part's V-read words, each loaded once: bits t_lo .. t_hi - 1
+  auto part_bits = [&](int x) -> uint32_t {
+    const int lo = max(t_lo - 32 * x, 0), hi = min(t_hi - 32 * x, 32);
+    const uint32_t m = (hi >= 32 ? ~0u : (1u << hi) - 1u) & ~((1u << lo) - 1u);
+    return vw[x] & m;
+  };
+  const int x_lo = t_lo >> 5, x_hi = t_hi > t_lo ? (t_hi - 1) >> 5 : x_lo - 1;
+  if (p > 0) {
+    // an empty later part (no head keeps a tile of it) is skipped by the merge
+    uint32_t any = 0u;
+    for (int x = x_lo; x <= x_hi; ++x) any |= part_bits(x);
+    if (any == 0u) return;                             // uniform over the workgroup
+  }
+  // wave w takes the part's tiles t_lo + w, t_lo + w + 4, ...: in every word
+  // the bits congruent to t_lo + w modulo 4
+  const uint32_t mine_mod4 = 0x11111111u << ((t_lo + w) & 3);
+  for (int x = x_lo; x <= x_hi; ++x) {
+    uint32_t todo = part_bits(x) & mine_mod4;
+    if (todo == 0u) continue;
+    const uint32_t kword = kw[x];                      // this lane's head
+    while (todo != 0u) {                               // wave-uniform; no barrier inside
+      const int t = 32 * x + __builtin_ctz(todo);
+      todo &= todo - 1u;
+      const bool mine = head_ok && ((kword >> (t & 31)) & 1u);
+      const int key0 = c0 + t * kTile;
+      // ---- the tile's scores again (as pass 1), then P against the split's maximum
+      f32x4 sacc[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sacc[kb][r] = 0.f;
-    {
-      bf16x8 qb[D / 32];
+        for (int r = 0; r < 4; ++r) sacc[kb][r] = 0.f;
+      {
+        bf16x8 qb[D / 32];
 #pragma unroll
-      for (int u = 0; u < D / 32; ++u) qb[u] = head_ok ? load16(qrow + 32 * u + 8 * g) : zero8();
+        for (int u = 0; u < D / 32; ++u) qb[u] = head_ok ? load16(qrow + 32 * u + 8 * g) : zero8();
 #pragma unroll
-      for (int hk2 = 0; hk2 < 2; ++hk2) {
-        bf16x8 ka[2][D / 32];
+        for (int hk2 = 0; hk2 < 2; ++hk2) {
+          bf16x8 ka[2][D / 32];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int u = 0; u < D / 32; ++u)
-            ka[kb][u] = buf_load16(
-                krs, (uint32_t)((key0 + 16 * (2 * hk2 + kb) + j16) * D + 32 * u + 8 * g) * 2);
+            for (int u = 0; u < D / 32; ++u)
+              ka[kb][u] = buf_load16(
+                  krs, (uint32_t)((key0 + 16 * (2 * hk2 + kb) + j16) * D + 32 * u + 8 * g) * 2);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+          for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int u = 0; u < D / 32; ++u)
-            sacc[2 * hk2 + kb] = mfma16(ka[kb][u], qb[u], sacc[2 * hk2 + kb]);
+            for (int u = 0; u < D / 32; ++u)
+              sacc[2 * hk2 + kb] = mfma16(ka[kb][u], qb[u], sacc[2 * hk2 + kb]);
+        }
       }
-    }
-    bf16x8 pb[2];
+      bf16x8 pb[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kb = 2 * ks + (e >> 2), r = e & 3;
-        const int key = key0 + 16 * kb + 4 * g + r;
-        const float sv = key < nk ? sacc[kb][r] * s.scale_log2 : kNegInf;
-        pb[ks][e] = (bf16)(mine ? fast_exp2(sv - Mh) : 0.f);
-      }
-    // ---- V (HBM) -> wave-private slab -> transposing reads -> P V
-    const int dc = lane & 15, kq = lane >> 4;
-    bf16x8 vr[16];
+        for (int e = 0; e < 8; ++e) {
+          const int kb = 2 * ks + (e >> 2), r = e & 3;
+          const int key = key0 + 16 * kb + 4 * g + r;
+          const float sv = key < nk ? sacc[kb][r] * s.scale_log2 : kNegInf;
+          pb[ks][e] = (bf16)(mine ? fast_exp2(sv - Mh) : 0.f);
+        }
+      // ---- V (HBM) -> wave-private slab -> transposing reads -> P V
+      const int dc = lane & 15, kq = lane >> 4;
+      bf16x8 vr[16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q)
-      vr[q] = buf_load16(vrs, (uint32_t)((key0 + 32 * (q >> 3) + 8 * kq + (q & 7)) * D + 8 * dc) * 2);
-    bf16* sl = &slab[w].v[0][0];
+      for (int q = 0; q < 16; ++q)
+        vr[q] = buf_load16(vrs, (uint32_t)((key0 + 32 * (q >> 3) + 8 * kq + (q & 7)) * D + 8 * dc) * 2);
+      bf16* sl = &slab[w].v[0][0];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) store16(sl + (8 * kq + q) * kSlabStride + 8 * dc, vr[8 * ks + q]);
+        for (int q = 0; q < 8; ++q) store16(sl + (8 * kq + q) * kSlabStride + 8 * dc, vr[8 * ks + q]);
 #pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const bf16x8 va = cat8(lds_read_tr(sl, kSlabStride, 4 * g, 16 * db, j16),
-                               lds_read_tr(sl, kSlabStride, 16 + 4 * g, 16 * db, j16));
-        oacc[db] = mfma16(va, pb[ks], oacc[db]);
+        for (int db = 0; db < D / 16; ++db) {
+          const bf16x8 va = cat8(lds_read_tr(sl, kSlabStride, 4 * g, 16 * db, j16),
+                                 lds_read_tr(sl, kSlabStride, 16 + 4 * g, 16 * db, j16));
+          oacc[db] = mfma16(va, pb[ks], oacc[db]);
+        }
       }
     }
   }
@@ -652,16 +696,22 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeShape s,
     float2 mz[kU];
     f32x4 x[kU];
 #pragma unroll
+    for (int u = 0; u < kU; ++u) mz[u] = *reinterpret_cast<const float2*>(ms + 2 * (k + 32 * u));
+#pragma unroll
     for (int u = 0; u < kU; ++u) {
-      mz[u] = *reinterpret_cast<const float2*>(ms + 2 * (k + 32 * u));
-      x[u] = *reinterpret_cast<const f32x4*>(po + (size_t)(k + 32 * u) * s.d);
+      // the three-pass path leaves the output of an empty part unwritten
+      const bool rd = !s.staged || mz[u].x != kNegInf;
+      x[u] = rd ? *reinterpret_cast<const f32x4*>(po + (size_t)(k + 32 * u) * s.d)
+                : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) fold(mz[u].x, mz[u].y, x[u]);
   }
   for (; k < nc; k += 32) {
     const float2 mz = *reinterpret_cast<const float2*>(ms + 2 * k);
-    fold(mz.x, mz.y, *reinterpret_cast<const f32x4*>(po + (size_t)k * s.d));
+    const bool rd = !s.staged || mz.x != kNegInf;
+    fold(mz.x, mz.y, rd ? *reinterpret_cast<const f32x4*>(po + (size_t)k * s.d)
+                        : f32x4{0.f, 0.f, 0.f, 0.f});
   }
   if (dq == 0) { sm_m[cl] = mrun; sm_z[cl] = zrun; }
   sm_o[cl][dq] = orun;

@@ -171,13 +171,11 @@ mala_status check_decode(const mala_decode_problem* p, mala::DecodeShape* s) {
   s->tpart = tpc;
   s->ppc = 1;
   if (s->staged) {
-    // parts of tpart tiles (a multiple of 4, one tile per wave), about 2048
-    // P V workgroups in all
-    const int64_t tiles = (int64_t)s->n_chunks * tpc * p->batch * p->n_kv_heads;
-    int64_t tp = (tiles + 2047) / 2048;
-    tp = (tp + 3) / 4 * 4;
-    s->tpart = (int)(tp < 4 ? 4 : tp > tpc ? (tpc + 3) / 4 * 4 : tp);
-    s->ppc = (tpc + s->tpart - 1) / s->tpart;
+    // parts of four tiles, one per wave of the P V workgroup: kept tiles
+    // cluster (sinks, the recent band), and a part never walks more than
+    // one of them per wave; empty parts exit at once and the merge skips them
+    s->tpart = 4;
+    s->ppc = (tpc + 3) / 4;
   }
   s->n_parts = s->n_chunks * s->ppc;
   s->scale_log2 = p->softmax_scale * 1.4426950408889634f;

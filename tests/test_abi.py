@@ -175,8 +175,8 @@ def test_decode_split_keys_rule(lib):
     words = ms + 2 * 8 * 2 * (128 + 2) + 2 * 1 * 2 * 2
     assert lib.mala_decode_workspace_size(ctypes.byref(p)) == -(-(words * 4) // 256) * 256
     # bf16 splits longer than 1024 keys run as three passes: the partial states
-    # are per part of tpart tiles (here 160 tiles in all -> tpart 4, 10 parts
-    # per split), and the per-(head, tile) statistics follow the bits
+    # are per part of 4 tiles (10 parts per 40-tile split), and the
+    # per-(head, tile) statistics follow the bits
     p = dprob(max_n_k=5000, cache_capacity=5000, split_keys=2560)
     parts = 2 * 10
     ms = -(-(2 * 8 * parts * 2) // 64) * 64
