@@ -645,7 +645,7 @@ __global__ __launch_bounds__(256, 4) void decode_pv_kernel(
 // (split lane cl, column quad dq) folds splits cl, cl + 32, ... into a
 // running (max, normalizer, output) with rescaling, sixteen splits in
 // flight per thread; the 32 split lanes are then merged the same way in LDS.
-template <typename OutT>
+template <typename OutT, bool kSkipEmpty>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeShape s,
                                                              const float* __restrict__ ws,
                                                              OutT* __restrict__ o,
@@ -700,7 +700,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeShape s,
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       // the three-pass path leaves the output of an empty part unwritten
-      const bool rd = !s.staged || mz[u].x != kNegInf;
+      const bool rd = !kSkipEmpty || mz[u].x != kNegInf;
       x[u] = rd ? *reinterpret_cast<const f32x4*>(po + (size_t)(k + 32 * u) * s.d)
                 : f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -709,7 +709,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeShape s,
   }
   for (; k < nc; k += 32) {
     const float2 mz = *reinterpret_cast<const float2*>(ms + 2 * k);
-    const bool rd = !s.staged || mz.x != kNegInf;
+    const bool rd = !kSkipEmpty || mz.x != kNegInf;
     fold(mz.x, mz.y, rd ? *reinterpret_cast<const f32x4*>(po + (size_t)k * s.d)
                         : f32x4{0.f, 0.f, 0.f, 0.f});
   }
@@ -755,13 +755,18 @@ size_t decode_ws_floats(const DecodeShape& s) {
 
 hipError_t launch_decode_combine_bf16(const DecodeShape& s, const float* ws, void* o, float* lse,
                                       int32_t* kept, hipStream_t st) {
-  hipLaunchKernelGGL(decode_combine_kernel<bf16>, dim3(s.batch * s.hq, (s.d + 31) / 32),
-                     dim3(256), 0, st, s, ws, (bf16*)o, lse, kept);
+  const dim3 grid(s.batch * s.hq, (s.d + 31) / 32);
+  if (s.staged)
+    hipLaunchKernelGGL((decode_combine_kernel<bf16, true>), grid, dim3(256), 0, st, s, ws,
+                       (bf16*)o, lse, kept);
+  else
+    hipLaunchKernelGGL((decode_combine_kernel<bf16, false>), grid, dim3(256), 0, st, s, ws,
+                       (bf16*)o, lse, kept);
   return hipGetLastError();
 }
 hipError_t launch_decode_combine_f32(const DecodeShape& s, const float* ws, float* o, float* lse,
                                      int32_t* kept, hipStream_t st) {
-  hipLaunchKernelGGL(decode_combine_kernel<float>, dim3(s.batch * s.hq, (s.d + 31) / 32),
+  hipLaunchKernelGGL((decode_combine_kernel<float, false>), dim3(s.batch * s.hq, (s.d + 31) / 32),
                      dim3(256), 0, st, s, ws, o, lse, kept);
   return hipGetLastError();
 }
