@@ -210,6 +210,18 @@ def test_decode_bf16_split_lengths(split_keys, tau):
         assert g["split"] == 4160 and g["mask"].shape[2] == 1
 
 
+# one split per sequence runs as three passes (tile statistics, per-head gate
+# replay, P V over kept tiles); other group shapes: 16 query heads per KV head
+# (a 1024-thread gate workgroup) and 4 per KV head with two KV heads
+@pytest.mark.parametrize("hq,hkv", [(16, 1), (8, 2)])
+@pytest.mark.parametrize("tau", [0.0, 1.0])
+def test_decode_bf16_unsplit_groups(hq, hkv, tau):
+    x = W.make_decode(W.CONFIGS[5], cache=3000, steps=1, batch=2, hq=hq, hkv=hkv, planted=12)
+    x = to_dev(x)
+    g, r = check_decode(x, [3001, 1500], tau, x["q_steps"][0].contiguous(), split_keys=8192)
+    assert g["split"] == 3008 and g["mask"].shape[2] == 1
+
+
 @pytest.mark.parametrize("split_keys", [64, 320, 2560])
 def test_decode_f32_split_lengths(split_keys):
     x = W.make_decode(W.CONFIGS[5], cache=2200, steps=1, batch=2, hq=4, hkv=2, planted=8)
