@@ -94,7 +94,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     Shape s, const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dq,
     bf16* __restrict__ dK, bf16* __restrict__ dV, uint32_t* __restrict__ bits,
-    int8_t* __restrict__ mask, int n_kb) {
+    int8_t* __restrict__ mask) {
   __shared__ DkdvSmem<D> sm;
   constexpr int ST = DkdvSmem<D>::kStride;
   constexpr int KS = D / 32;      // 32-wide k-steps over d (16x16x32 MFMA)
@@ -338,7 +338,6 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     *reinterpret_cast<bf16x4*>(dkr + 16 * db + 4 * g) = a;
     *reinterpret_cast<bf16x4*>(dvr + 16 * db + 4 * g) = c;
   }
-  (void)n_kb;
 }
 
 // ---------------------------------------------------------------- dQ
@@ -634,7 +633,7 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
     if (g1.x && (stages & kStageMain))
       hipLaunchKernelGGL(dkdv, g1, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
                          (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dk, (bf16*)dv,
-                         ws_bits, mask, n_kb);
+                         ws_bits, mask);
     // dynamic LDS: the needed-tile bitmap, one bit per 64-key tile
     const size_t need_bytes = (size_t)((s.nk + 64 * 32 - 1) / (64 * 32)) * 4;
     if (g2.x && (stages & kStageDq))

@@ -281,9 +281,11 @@ __global__ __launch_bounds__(256, 4) void decode_split_kernel(
 }
 
 // ---------------------------------------------------------------- long splits
-// A split longer than 1024 keys would leave one workgroup walking many tile
-// groups in sequence (and few workgroups in all). Such splits run as three
-// parallel passes that take the same decisions:
+// With splits longer than 1024 keys and fewer split workgroups than the
+// chip's 256 compute units (one split per sequence, say), each workgroup of
+// the one-kernel path would walk many tile groups in sequence on a mostly
+// idle chip. Such splits run as three parallel passes that take the same
+// decisions:
 //   1. decode_stats_kernel: one wave per tile scores the tile against every
 //      head of the group and stores each head's tile maximum and tile sum
 //      (exactly the statistics the one-kernel path exchanges through LDS);
