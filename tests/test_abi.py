@@ -185,5 +185,25 @@ def test_decode_split_keys_rule(lib):
     assert lib.mala_decode_workspace_size(ctypes.byref(p)) == -(-(words * 4) // 256) * 256
 
 
+def test_header_and_abi_from_c(lib, tmp_path):
+    """include/mala.h compiles as pedantic C99, and a C program linked
+    against libmala gets the documented tiling, workspace, split-length and
+    error behaviour (no GPU needed)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    libdir = os.path.dirname(M.LIB_PATH)
+    exe = str(tmp_path / "c_abi_check")
+    src = os.path.join(ROOT, "tests", "c_abi_check.c")
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                        "-I", os.path.join(ROOT, "include"), src, "-L", libdir, "-lmala",
+                        f"-Wl,-rpath,{libdir}", "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0 and "c abi ok" in r.stdout, r.stdout + r.stderr
+
+
 def test_version(lib):
     assert "gfx950" in M.version()
