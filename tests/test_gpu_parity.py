@@ -230,6 +230,24 @@ def test_decode_f32_split_lengths(split_keys):
     check_decode(x, [2201, 130], 1e-4, x["q_steps"][0].contiguous(), split_keys=split_keys)
 
 
+def test_decode_clamps_out_of_range_lengths():
+    """seqlens_k outside [1, max_n_k] is clamped on the device (the header's
+    contract): lengths 0 and 5000 with max_n_k = 701 give exactly the results
+    of lengths 1 and 701."""
+    m = lib()
+    x = to_dev(W.make_decode(W.CONFIGS[5], cache=700, steps=1, batch=2, planted=4))
+    q = x["q_steps"][0].contiguous()
+    outs = []
+    for lens in ([0, 5000], [1, 701]):
+        seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+        g = m.mala_decode(q, x["k_cache"], x["v_cache"], seq, 1e-4, max_n_k=701,
+                          softmax_scale=x["scale"], want_mask=True)
+        torch.cuda.synchronize()
+        outs.append({k_: g[k_].cpu() for k_ in ("o", "lse", "mask", "kept")})
+    for k_ in outs[0]:
+        assert torch.equal(outs[0][k_], outs[1][k_]), k_
+
+
 def test_decode_group16_and_single_key():
     x = W.make_decode(W.CONFIGS[5], cache=300, steps=1, batch=2, hq=16, hkv=1, planted=4)
     x = to_dev(x)
