@@ -148,6 +148,10 @@ mala_status check_decode(const mala_decode_problem* p, mala::DecodeShape* s) {
     return fail(MALA_ERR_INVALID_ARG, "tau must be finite and >= 0");
   if (!std::isfinite(p->softmax_scale) || p->softmax_scale <= 0.f)
     return fail(MALA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
+  if ((int64_t)p->batch * p->n_kv_heads > 65535)
+    return fail(MALA_ERR_UNSUPPORTED,
+                "batch x n_kv_heads (%lld) exceeds 65535, the launch grid's second dimension",
+                (long long)p->batch * p->n_kv_heads);
   if (p->split_keys < MALA_DECODE_SPLIT_AUTO || (p->split_keys > 0 && p->split_keys % mala::kDecBk))
     return fail(MALA_ERR_INVALID_ARG,
                 "split_keys must be 0, MALA_DECODE_SPLIT_AUTO or a positive multiple of %d",

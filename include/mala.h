@@ -84,7 +84,9 @@ typedef struct {
   int32_t flags;           /* MALA_FLAG_* (0 = defaults)                     */
 } mala_problem;
 
-/* One split-KV decode step: a single query token per sequence. */
+/* One split-KV decode step: a single query token per sequence.
+ * batch * n_kv_heads must not exceed 65535 (MALA_ERR_UNSUPPORTED), and a
+ * KV head groups at most 16 query heads. */
 typedef struct {
   int32_t batch;
   int32_t n_q_heads;

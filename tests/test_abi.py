@@ -136,6 +136,7 @@ def test_decode_validation_and_workspace(lib):
     ms = -(-(2 * 8 * 4 * 2) // 64) * 64
     assert n == -(-((ms + 2 * 8 * 4 * 129 + 2 * 1 * 4) * 4) // 256) * 256
     for kw, word in [(dict(n_q_heads=34, n_kv_heads=2), "16"), (dict(max_n_k=2000), "max_n_k"),
+                     (dict(batch=40000, n_q_heads=2, n_kv_heads=2), "65535"),
                      (dict(head_dim=64), "head_dim"), (dict(tau=-2.0), "tau"),
                      (dict(n_q_heads=7, n_kv_heads=2), "multiple")]:
         q = dprob(**kw)
