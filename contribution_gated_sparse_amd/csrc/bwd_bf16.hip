@@ -6,10 +6,11 @@
 //                 and the kept-tile counters.
 //   2. bwd_dkdv:  key-major. A workgroup owns 128 keys of one KV head (8 waves
 //                 x 16 keys) and walks every query head of the group and every
-//                 32-row query step from the diagonal down the sequence. Each
-//                 wave recomputes S = Q K^T for its 16 keys, applies the
-//                 offline gate (Eq. 4) to its 32 x 16 tile against the saved
-//                 z_q, and for kept tiles forms P = exp(S - z), dP = dO V^T,
+//                 64-row query step from the diagonal down the sequence. Each
+//                 wave recomputes S = Q K^T for its 16 keys and the step's 64
+//                 rows, applies the offline gate (Eq. 4) to each of its two
+//                 32 x 16 tiles against the saved z_q, and only for kept tiles
+//                 reads the staged dO rows and forms P = exp(S - z), dP = dO V^T,
 //                 dS = P o (dP - D) and accumulates dV += P^T dO and
 //                 dK += dS^T Q on chip. The decisions are written as one bit
 //                 per tile.
@@ -209,111 +210,130 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     if (it + 1 < total) load_step(hn, in);
     if (prev_i >= 0) flush_keep(buf ^ 1, prev_bh, prev_i);
     const size_t bh = (size_t)b * s.hq + h;
-#pragma unroll 1
+    // ---- S = Q K^T over the whole 64-row step and both halves' gates come
+    // first: a skipped half then costs its Q reads and score products only,
+    // and the products of the two halves overlap.
+    bool legal[2];
+#pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int r0 = i * 64 + 32 * half;               // first query row of the half
-      const int lr = 32 * half;                        // its first row in the LDS tile
-      const bool legal =
-          r0 < s.nq && kw0 < s.nk && (!s.causal || kw0 <= min(r0 + 31, s.nq - 1) + s.offset);
-      if (!legal) continue;
-      // Every LDS operand of a phase is read before the phase's products so
-      // that the reads overlap the matrix work instead of waiting one by one.
-      // Row-major Q and dO rows (A operands of S and dP): row 16 qb + l16,
-      // columns 32 t + 8 g .. + 7.
-      bf16x8 qrow[KS][2], orow[KS][2];
+      const int r0 = i * 64 + 32 * half;
+      legal[half] = r0 < s.nq && kw0 < s.nk && (!s.causal || kw0 <= min(r0 + 31, s.nq - 1) + s.offset);
+    }
+    if (legal[0] || legal[1]) {
+      // lane (key l16, group g), regs = queries 16 qb + 4 g + r of the step
+      f32x4 sacc[4], uu[4];
 #pragma unroll
-      for (int t = 0; t < KS; ++t)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          qrow[t][qb] = load16(&sm.q[buf][lr + 16 * qb + l16][32 * t + 8 * g]);
-          orow[t][qb] = load16(&sm.dout[buf][lr + 16 * qb + l16][32 * t + 8 * g]);
-        }
-      // ---- recompute S = Q K^T: lane (key l16, group g), regs = queries 16qb + 4g + r
-      f32x4 sacc[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 4; ++qb) {
+        uu[qb] = *reinterpret_cast<const f32x4*>(&sm.u2[buf][16 * qb + 4 * g]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) sacc[qb][r] = 0.f;
+      }
+      {
+        bf16x8 qrow[KS][4];
 #pragma unroll
-      for (int t = 0; t < KS; ++t)
+        for (int t = 0; t < KS; ++t)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) sacc[qb] = mfma16(qrow[t][qb], kr[t], sacc[qb]);
-      const bool boundary = (r0 + 32 > s.nq) || (kw0 + kBK > s.nk) ||
-                            (s.causal && kw0 + kBK - 1 > r0 + s.offset);
-      // ---- offline gate, Eq. 4: skip iff S - z < log(tau / L) on every legal entry
-      float x = kNegInf;
-      if (!boundary) {                                 // wave-uniform: every entry legal
+          for (int qb = 0; qb < 4; ++qb) qrow[t][qb] = load16(&sm.q[buf][16 * qb + l16][32 * t + 8 * g]);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.u2[buf][lr + 16 * qb + 4 * g]);
+        for (int t = 0; t < KS; ++t)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) x = fmaxf(x, fmaf(sacc[qb][r], s.scale_log2, -u[r]));
+          for (int qb = 0; qb < 4; ++qb) sacc[qb] = mfma16(qrow[t][qb], kr[t], sacc[qb]);
+      }
+      // ---- offline gate, Eq. 4, per half: skip iff S - z < log(tau / L) on
+      // every legal entry of its 32 x 16 tile
+      uint32_t kept_halves = 0u;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if (!legal[half]) continue;
+        const int r0 = i * 64 + 32 * half;
+        const bool boundary = (r0 + 32 > s.nq) || (kw0 + kBK > s.nk) ||
+                              (s.causal && kw0 + kBK - 1 > r0 + s.offset);
+        float x = kNegInf;
+        if (!boundary) {                               // wave-uniform: every entry legal
+#pragma unroll
+          for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              x = fmaxf(x, fmaf(sacc[2 * half + qh][r], s.scale_log2, -uu[2 * half + qh][r]));
+        } else {
+#pragma unroll
+          for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int qb = 2 * half + qh;
+              const int q = r0 + 16 * qh + 4 * g + r;
+              const bool ok = (q < s.nq) & (key < s.nk) & ((key <= q + s.offset) | (s.causal == 0));
+              sacc[qb][r] = ok ? sacc[qb][r] : kNegInf;   // P = 0 on illegal entries
+              x = fmaxf(x, ok ? fmaf(sacc[qb][r], s.scale_log2, -uu[qb][r]) : kNegInf);
+            }
         }
-      } else {
+        const bool keep = wave_any(x >= 0.f);
+        if (lane == 0) {
+          if (keep) atomicOr(&sm.keep[buf][half], 1u << w);
+          if (mask != nullptr) mask[(bh * tr32 + 2 * i + half) * tc16 + kw0 / kBK] = keep ? 1 : 0;
+        }
+        kept_halves |= keep ? (1u << half) : 0u;
+      }
+#pragma unroll 1
+      for (int half = 0; half < 2; ++half) {
+        if (!(kept_halves & (1u << half))) continue;
+        const int lr = 32 * half;                      // first row of the half in the LDS tile
+        f32x4 sh[2];
+        sh[0] = half ? sacc[2] : sacc[0];
+        sh[1] = half ? sacc[3] : sacc[1];
+        // Row-major dO rows (A operand of dP): row 16 qb + l16, columns 32 t + 8 g .. + 7.
+        bf16x8 orow[KS][2];
+#pragma unroll
+        for (int t = 0; t < KS; ++t)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) orow[t][qb] = load16(&sm.dout[buf][lr + 16 * qb + l16][32 * t + 8 * g]);
+        // dO^T and Q^T, the A operands of dV^T = dO^T P and dK^T = Q^T dS,
+        // through transposing reads: element e < 4 is query row 4g + e,
+        // e >= 4 is row 16 + 4g + (e - 4), for column 16 db + l16.
+        bf16x8 ocol[DB], qcol[DB];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          ocol[db] = cat8(lds_read_tr(&sm.dout[buf][lr][0], ST, 4 * g, 16 * db, l16),
+                          lds_read_tr(&sm.dout[buf][lr][0], ST, 16 + 4 * g, 16 * db, l16));
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          qcol[db] = cat8(lds_read_tr(&sm.q[buf][lr][0], ST, 4 * g, 16 * db, l16),
+                          lds_read_tr(&sm.q[buf][lr][0], ST, 16 + 4 * g, 16 * db, l16));
+        // ---- P = exp(S - z) (B operand over the 32 query rows, in the row
+        // order of the transposing reads); it does not wait for dP
+        bf16x8 pb, dsb;
+        float pv[2][4];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          const f32x4 u = *reinterpret_cast<const f32x4*>(&sm.u2[buf][lr + 16 * qb + 4 * g]);
+          const f32x4 z = *reinterpret_cast<const f32x4*>(&sm.z2[buf][lr + 16 * qb + 4 * g]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int q = r0 + 16 * qb + 4 * g + r;
-            const bool ok = (q < s.nq) & (key < s.nk) & ((key <= q + s.offset) | (s.causal == 0));
-            sacc[qb][r] = ok ? sacc[qb][r] : kNegInf;   // P = 0 on illegal entries
-            x = fmaxf(x, ok ? fmaf(sacc[qb][r], s.scale_log2, -u[r]) : kNegInf);
+            pv[qb][r] = fast_exp2(fmaf(sh[qb][r], s.scale_log2, -z[r]));
+            pb[4 * qb + r] = (bf16)pv[qb][r];
           }
         }
-      }
-      const bool keep = wave_any(x >= 0.f);
-      if (lane == 0) {
-        if (keep) atomicOr(&sm.keep[buf][half], 1u << w);
-        if (mask != nullptr) mask[(bh * tr32 + 2 * i + half) * tc16 + kw0 / kBK] = keep ? 1 : 0;
-      }
-      if (!keep) continue;
-      // dO^T and Q^T, the A operands of dV^T = dO^T P and dK^T = Q^T dS,
-      // through transposing reads: element e < 4 is query row 4g + e,
-      // e >= 4 is row 16 + 4g + (e - 4), for column 16 db + l16.
-      bf16x8 ocol[DB], qcol[DB];
+        // ---- dP = dO V^T and dV^T += dO^T P, independent products
+        f32x4 dp[2];
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        ocol[db] = cat8(lds_read_tr(&sm.dout[buf][lr][0], ST, 4 * g, 16 * db, l16),
-                        lds_read_tr(&sm.dout[buf][lr][0], ST, 16 + 4 * g, 16 * db, l16));
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        qcol[db] = cat8(lds_read_tr(&sm.q[buf][lr][0], ST, 4 * g, 16 * db, l16),
-                        lds_read_tr(&sm.q[buf][lr][0], ST, 16 + 4 * g, 16 * db, l16));
-      // ---- P = exp(S - z) (B operand over the 32 query rows, in the row
-      // order of the transposing reads); it does not wait for dP
-      bf16x8 pb, dsb;
-      float pv[2][4];
+          for (int r = 0; r < 4; ++r) dp[qb][r] = 0.f;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const f32x4 z = *reinterpret_cast<const f32x4*>(&sm.z2[buf][lr + 16 * qb + 4 * g]);
+        for (int t = 0; t < KS; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pv[qb][r] = fast_exp2(fmaf(sacc[qb][r], s.scale_log2, -z[r]));
-          pb[4 * qb + r] = (bf16)pv[qb][r];
+          for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma16(orow[t][qb], vr[t], dp[qb]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) dv[db] = mfma16(ocol[db], pb, dv[db]);
+        // ---- dS = P o (dP - D), then dK^T += Q^T dS
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const f32x4 ddv = *reinterpret_cast<const f32x4*>(&sm.dd[buf][lr + 16 * qb + 4 * g]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dsb[4 * qb + r] = (bf16)(pv[qb][r] * (dp[qb][r] - ddv[r]));
         }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) dk[db] = mfma16(qcol[db], dsb, dk[db]);
       }
-      // ---- dP = dO V^T and dV^T += dO^T P, independent products
-      f32x4 dp[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dp[qb][r] = 0.f;
-#pragma unroll
-      for (int t = 0; t < KS; ++t)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma16(orow[t][qb], vr[t], dp[qb]);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) dv[db] = mfma16(ocol[db], pb, dv[db]);
-      // ---- dS = P o (dP - D), then dK^T += Q^T dS
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const f32x4 ddv = *reinterpret_cast<const f32x4*>(&sm.dd[buf][lr + 16 * qb + 4 * g]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dsb[4 * qb + r] = (bf16)(pv[qb][r] * (dp[qb][r] - ddv[r]));
-      }
-#pragma unroll
-      for (int db = 0; db < DB; ++db) dk[db] = mfma16(qcol[db], dsb, dk[db]);
     }
     prev_bh = bh;
     prev_i = i;
