@@ -87,7 +87,7 @@ struct alignas(16) DkdvSmem {
   alignas(16) float z2[2][64];  // z_q * log2 e
   float u2[2][64];              // z_q * log2 e + log2(tau / L_q): skip iff s2 < u2 everywhere
   float dd[2][64];              // D_q
-  uint32_t keep[2][2];          // [buf][half] bit w: wave w kept its tile
+  uint32_t keep[2];             // [buf] bit w / 8 + w: wave w kept its first / second half
 };
 
 template <int D>
@@ -145,21 +145,25 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
   const int total = s.group * (tr64 - i_start);        // (head, 64-row step) pairs
 
-  // staging: 64 rows x CPR chunks of Q and of dO, NPASS chunks each per thread
+  // staging: 64 rows x CPR chunks of Q and of dO, NPASS chunks each per thread.
+  // The buffer resources span one query head (rows past N_q read as zeros)
+  // and are rebuilt only when the walk moves to the next head.
   const int srow = tid / CPR, sc = tid % CPR;
+  const uint32_t toff = (uint32_t)(srow * D + 8 * sc) * 2;   // this thread's chunk in a step
+  const uint32_t head_bytes = (uint32_t)((size_t)s.nq * D * 2);
+  auto head_row0 = [&](int h) { return ((size_t)b * s.hq + h) * (size_t)s.nq; };
   bf16x8 qreg[NPASS], oreg[NPASS];
   float zreg = 0.f, dreg = 0.f;
-  auto load_step = [&](int h, int i) {
-    const size_t qrow0 = ((size_t)b * s.hq + h) * (size_t)s.nq;
-    const auto qrs = make_rsrc(Q + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
-    const auto ors = make_rsrc(dO + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
+  auto load_step = [&](__amdgpu_buffer_rsrc_t qrs, __amdgpu_buffer_rsrc_t ors, int h, int i) {
+    const uint32_t off0 = toff + (uint32_t)(i * 64) * (uint32_t)(D * 2);
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
-      const uint32_t off = (uint32_t)((i * 64 + p * RPP + srow) * D + 8 * sc) * 2;
+      const uint32_t off = off0 + (uint32_t)(p * RPP * D * 2);
       qreg[p] = buf_load16(qrs, off);
       oreg[p] = buf_load16(ors, off);
     }
     if (tid < 64) {
+      const size_t qrow0 = head_row0(h);
       const int q = i * 64 + tid;
       zreg = q < s.nq ? LSE[qrow0 + q] : 0.f;
       dreg = q < s.nq ? Dq[qrow0 + q] : 0.f;
@@ -180,18 +184,34 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       sm.dd[buf][tid] = dreg;
     }
   };
-  // the previous step's two decision bytes -> bit rows (bh, 2 i + half), byte J
-  auto flush_keep = [&](int buf, size_t bh, int i) {
+  // the previous step's decision word (byte 0: first half, byte 1: second
+  // half) -> bit rows (b, h, 2 i + half), byte J
+  auto flush_keep = [&](int buf, int h, int i) {
     if (tid < 2 && 2 * i + tid < tr32) {
-      bit_bytes[(bh * tr32 + 2 * i + tid) * (size_t)words * 4 + J] = (uint8_t)sm.keep[buf][tid];
-      sm.keep[buf][tid] = 0u;
+      const size_t bh = (size_t)b * s.hq + h;
+      bit_bytes[(bh * tr32 + 2 * i + tid) * (size_t)words * 4 + J] = (uint8_t)(sm.keep[buf] >> (8 * tid));
+      if (tid == 0) sm.keep[buf] = 0u;
     }
   };
 
-  if (tid < 4) sm.keep[tid >> 1][tid & 1] = 0u;
+  // Steps on which both halves hold only legal entries for this wave's keys
+  // (all 64 rows below N_q, all 16 keys below N_k and, when causal, on or
+  // below the diagonal) skip the legality and boundary tests.
+  const bool keys_in = kw0 + kBK <= s.nk;
+  int i_lo = 0;
+  if (s.causal) {
+    const int need = kw0 + kBK - 1 - s.offset;
+    i_lo = need <= 0 ? 0 : (need + 63) / 64;
+  }
+  const int i_hi = s.nq / 64;
+
+  if (tid < 2) sm.keep[tid] = 0u;
   int h = hk * s.group, i = i_start;                   // current step
+  int hl = h;                                          // head of the staging resources
+  auto lq = make_rsrc(Q + head_row0(h) * D, head_bytes);
+  auto lo = make_rsrc(dO + head_row0(h) * D, head_bytes);
   if (total > 0) {
-    load_step(h, i);
+    load_step(lq, lo, h, i);
     store_step(0, i);
   }
 #pragma unroll
@@ -201,24 +221,30 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
   __syncthreads();
 
-  size_t prev_bh = 0;
-  int prev_i = -1;
+  int prev_h = 0, prev_i = -1;
   for (int it = 0; it < total; ++it) {
     const int buf = it & 1;
     int hn = h, in = i + 1;                            // next step
     if (in == tr64) { in = i_start; ++hn; }
-    if (it + 1 < total) load_step(hn, in);
-    if (prev_i >= 0) flush_keep(buf ^ 1, prev_bh, prev_i);
-    const size_t bh = (size_t)b * s.hq + h;
+    if (hn != hl && it + 1 < total) {
+      hl = hn;
+      lq = make_rsrc(Q + head_row0(hn) * D, head_bytes);
+      lo = make_rsrc(dO + head_row0(hn) * D, head_bytes);
+    }
+    if (it + 1 < total) load_step(lq, lo, hn, in);
+    if (prev_i >= 0) flush_keep(buf ^ 1, prev_h, prev_i);
+    bool legal[2] = {true, true}, bnd[2] = {false, false};
+    if (!(keys_in && i >= i_lo && i < i_hi)) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int r0 = i * 64 + 32 * half;
+        legal[half] = r0 < s.nq && kw0 < s.nk && (!s.causal || kw0 <= min(r0 + 31, s.nq - 1) + s.offset);
+        bnd[half] = (r0 + 32 > s.nq) || (kw0 + kBK > s.nk) || (s.causal && kw0 + kBK - 1 > r0 + s.offset);
+      }
+    }
     // ---- S = Q K^T over the whole 64-row step and both halves' gates come
     // first: a skipped half then costs its Q reads and score products only,
     // and the products of the two halves overlap.
-    bool legal[2];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int r0 = i * 64 + 32 * half;
-      legal[half] = r0 < s.nq && kw0 < s.nk && (!s.causal || kw0 <= min(r0 + 31, s.nq - 1) + s.offset);
-    }
     if (legal[0] || legal[1]) {
       // lane (key l16, group g), regs = queries 16 qb + 4 g + r of the step
       f32x4 sacc[4], uu[4];
@@ -245,17 +271,15 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         if (!legal[half]) continue;
-        const int r0 = i * 64 + 32 * half;
-        const bool boundary = (r0 + 32 > s.nq) || (kw0 + kBK > s.nk) ||
-                              (s.causal && kw0 + kBK - 1 > r0 + s.offset);
         float x = kNegInf;
-        if (!boundary) {                               // wave-uniform: every entry legal
+        if (!bnd[half]) {                              // wave-uniform: every entry legal
 #pragma unroll
           for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
               x = fmaxf(x, fmaf(sacc[2 * half + qh][r], s.scale_log2, -uu[2 * half + qh][r]));
         } else {
+          const int r0 = i * 64 + 32 * half;
 #pragma unroll
           for (int qh = 0; qh < 2; ++qh)
 #pragma unroll
@@ -267,12 +291,16 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
               x = fmaxf(x, ok ? fmaf(sacc[qb][r], s.scale_log2, -uu[qb][r]) : kNegInf);
             }
         }
-        const bool keep = wave_any(x >= 0.f);
-        if (lane == 0) {
-          if (keep) atomicOr(&sm.keep[buf][half], 1u << w);
-          if (mask != nullptr) mask[(bh * tr32 + 2 * i + half) * tc16 + kw0 / kBK] = keep ? 1 : 0;
-        }
-        kept_halves |= keep ? (1u << half) : 0u;
+        if (__builtin_amdgcn_ballot_w64(x >= 0.f) != 0) kept_halves |= 1u << half;
+      }
+      if (kept_halves != 0u && lane == 0)
+        atomicOr(&sm.keep[buf], ((kept_halves & 1u) << w) | ((kept_halves >> 1) << (8 + w)));
+      if (mask != nullptr && lane == 0) {
+        const size_t bh = (size_t)b * s.hq + h;
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+          if (legal[half])
+            mask[(bh * tr32 + 2 * i + half) * tc16 + kw0 / kBK] = (int8_t)((kept_halves >> half) & 1u);
       }
 #pragma unroll 1
       for (int half = 0; half < 2; ++half) {
@@ -335,14 +363,14 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         for (int db = 0; db < DB; ++db) dk[db] = mfma16(qcol[db], dsb, dk[db]);
       }
     }
-    prev_bh = bh;
+    prev_h = h;
     prev_i = i;
     if (it + 1 < total) store_step(buf ^ 1, in);
     h = hn;
     i = in;
     __syncthreads();
   }
-  if (prev_i >= 0) flush_keep((total - 1) & 1, prev_bh, prev_i);
+  if (prev_i >= 0) flush_keep((total - 1) & 1, prev_h, prev_i);
 
   // ---- store dK = scale * sum dS^T Q and dV (summed over the group's heads):
   // lane (key l16, group g) holds d = 16 db + 4 g + r
