@@ -226,13 +226,21 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const int buf = it & 1;
     int hn = h, in = i + 1;                            // next step
     if (in == tr64) { in = i_start; ++hn; }
-    if (hn != hl && it + 1 < total) {
+    const bool more = it + 1 < total;
+    if (hn != hl) {
+      // the next head, or past the group after the last step: then a
+      // zero-sized range, so the staging loads return zeros and touch nothing
       hl = hn;
-      lq = make_rsrc(Q + head_row0(hn) * D, head_bytes);
-      lo = make_rsrc(dO + head_row0(hn) * D, head_bytes);
+      lq = make_rsrc(Q + head_row0(more ? hn : h) * D, more ? head_bytes : 0u);
+      lo = make_rsrc(dO + head_row0(more ? hn : h) * D, more ? head_bytes : 0u);
     }
-    if (it + 1 < total) load_step(lq, lo, hn, in);
+    // the decision store goes out before the staging loads: the loads' wait
+    // at the end of the step then covers it, instead of the next step's
+    // loads waiting for it
     if (prev_i >= 0) flush_keep(buf ^ 1, prev_h, prev_i);
+    // unconditional, so that the wait for these loads at the end of the step
+    // is the only one (after the last step they stage zeros into the idle buffer)
+    load_step(lq, lo, more ? hn : h, more ? in : i);
     bool legal[2] = {true, true}, bnd[2] = {false, false};
     if (!(keys_in && i >= i_lo && i < i_hi)) {
 #pragma unroll
@@ -365,7 +373,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
     prev_h = h;
     prev_i = i;
-    if (it + 1 < total) store_step(buf ^ 1, in);
+    store_step(buf ^ 1, more ? in : i);
     h = hn;
     i = in;
     __syncthreads();
