@@ -90,12 +90,12 @@ struct alignas(16) DkdvSmem {
   uint32_t keep[2];             // [buf] bit w / 8 + w: wave w kept its first / second half
 };
 
-template <int D>
+template <int D, bool kGated>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
     Shape s, const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dq,
     bf16* __restrict__ dK, bf16* __restrict__ dV, uint32_t* __restrict__ bits,
-    int8_t* __restrict__ mask) {
+    int8_t* __restrict__ mask, float* __restrict__ part) {
   __shared__ DkdvSmem<D> sm;
   constexpr int ST = DkdvSmem<D>::kStride;
   constexpr int KS = D / 32;      // 32-wide k-steps over d (16x16x32 MFMA)
@@ -107,8 +107,12 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int bk_count = s.batch * s.hkv;
-  const int J = (int)(blockIdx.x / bk_count);          // key block (0 = longest)
-  const int bkv = (int)(blockIdx.x % bk_count);
+  // walks per key block: one over the whole group, or (gated) one per query
+  // head, whose fp32 partials the finalize kernel sums
+  const int nsub = kGated ? s.group : 1;
+  const int J = (int)(blockIdx.x / (bk_count * nsub));  // key block (0 = longest)
+  const int rem = (int)(blockIdx.x % (bk_count * nsub));
+  const int bkv = rem / nsub, hsub = rem % nsub;
   const int b = bkv / s.hkv, hk = bkv % s.hkv;
   const int kw0 = J * 128 + w * kBK;                   // this wave's first key
   const size_t krow0 = ((size_t)b * s.hkv + hk) * (size_t)s.nk;
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const int need = J * 128 - s.offset;
     i_start = need <= 0 ? 0 : need / 64;
   }
-  const int total = s.group * (tr64 - i_start);        // (head, 64-row step) pairs
+  const int total = (kGated ? 1 : s.group) * (tr64 - i_start);   // (head, 64-row step) pairs
 
   // staging: 64 rows x CPR chunks of Q and of dO, NPASS chunks each per thread.
   // The buffer resources span one query head (rows past N_q read as zeros)
@@ -194,6 +198,66 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     }
   };
 
+  // the post-score path of one kept 32 x 16 tile (rows 32 half .. + 31 of
+  // the step in LDS buffer bf; s0, s1: its scores, illegal entries -inf):
+  // P, dP, dS and the dV, dK products
+  auto kept_tile = [&](int bf, int half, f32x4 s0, f32x4 s1) {
+    const int lr = 32 * half;                        // first row of the half in the LDS tile
+    f32x4 sh[2] = {s0, s1};
+    // Row-major dO rows (A operand of dP): row 16 qb + l16, columns 32 t + 8 g .. + 7.
+    bf16x8 orow[KS][2];
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) orow[t][qb] = load16(&sm.dout[bf][lr + 16 * qb + l16][32 * t + 8 * g]);
+    // dO^T and Q^T, the A operands of dV^T = dO^T P and dK^T = Q^T dS,
+    // through transposing reads: element e < 4 is query row 4g + e,
+    // e >= 4 is row 16 + 4g + (e - 4), for column 16 db + l16.
+    bf16x8 ocol[DB], qcol[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      ocol[db] = cat8(lds_read_tr(&sm.dout[bf][lr][0], ST, 4 * g, 16 * db, l16),
+                      lds_read_tr(&sm.dout[bf][lr][0], ST, 16 + 4 * g, 16 * db, l16));
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      qcol[db] = cat8(lds_read_tr(&sm.q[bf][lr][0], ST, 4 * g, 16 * db, l16),
+                      lds_read_tr(&sm.q[bf][lr][0], ST, 16 + 4 * g, 16 * db, l16));
+    // ---- P = exp(S - z) (B operand over the 32 query rows, in the row
+    // order of the transposing reads); it does not wait for dP
+    bf16x8 pb, dsb;
+    float pv[2][4];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const f32x4 z = *reinterpret_cast<const f32x4*>(&sm.z2[bf][lr + 16 * qb + 4 * g]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pv[qb][r] = fast_exp2(fmaf(sh[qb][r], s.scale_log2, -z[r]));
+        pb[4 * qb + r] = (bf16)pv[qb][r];
+      }
+    }
+    // ---- dP = dO V^T and dV^T += dO^T P, independent products
+    f32x4 dp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dp[qb][r] = 0.f;
+#pragma unroll
+    for (int t = 0; t < KS; ++t)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma16(orow[t][qb], vr[t], dp[qb]);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dv[db] = mfma16(ocol[db], pb, dv[db]);
+    // ---- dS = P o (dP - D), then dK^T += Q^T dS
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const f32x4 ddv = *reinterpret_cast<const f32x4*>(&sm.dd[bf][lr + 16 * qb + 4 * g]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dsb[4 * qb + r] = (bf16)(pv[qb][r] * (dp[qb][r] - ddv[r]));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dk[db] = mfma16(qcol[db], dsb, dk[db]);
+  };
+
   // Steps on which both halves hold only legal entries for this wave's keys
   // (all 64 rows below N_q, all 16 keys below N_k and, when causal, on or
   // below the diagonal) skip the legality and boundary tests.
@@ -205,6 +269,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
   const int i_hi = s.nq / 64;
 
+  if constexpr (!kGated) {
   if (tid < 2) sm.keep[tid] = 0u;
   int h = hk * s.group, i = i_start;                   // current step
   int hl = h;                                          // head of the staging resources
@@ -313,62 +378,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll 1
       for (int half = 0; half < 2; ++half) {
         if (!(kept_halves & (1u << half))) continue;
-        const int lr = 32 * half;                      // first row of the half in the LDS tile
-        f32x4 sh[2];
-        sh[0] = half ? sacc[2] : sacc[0];
-        sh[1] = half ? sacc[3] : sacc[1];
-        // Row-major dO rows (A operand of dP): row 16 qb + l16, columns 32 t + 8 g .. + 7.
-        bf16x8 orow[KS][2];
-#pragma unroll
-        for (int t = 0; t < KS; ++t)
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) orow[t][qb] = load16(&sm.dout[buf][lr + 16 * qb + l16][32 * t + 8 * g]);
-        // dO^T and Q^T, the A operands of dV^T = dO^T P and dK^T = Q^T dS,
-        // through transposing reads: element e < 4 is query row 4g + e,
-        // e >= 4 is row 16 + 4g + (e - 4), for column 16 db + l16.
-        bf16x8 ocol[DB], qcol[DB];
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          ocol[db] = cat8(lds_read_tr(&sm.dout[buf][lr][0], ST, 4 * g, 16 * db, l16),
-                          lds_read_tr(&sm.dout[buf][lr][0], ST, 16 + 4 * g, 16 * db, l16));
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          qcol[db] = cat8(lds_read_tr(&sm.q[buf][lr][0], ST, 4 * g, 16 * db, l16),
-                          lds_read_tr(&sm.q[buf][lr][0], ST, 16 + 4 * g, 16 * db, l16));
-        // ---- P = exp(S - z) (B operand over the 32 query rows, in the row
-        // order of the transposing reads); it does not wait for dP
-        bf16x8 pb, dsb;
-        float pv[2][4];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const f32x4 z = *reinterpret_cast<const f32x4*>(&sm.z2[buf][lr + 16 * qb + 4 * g]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            pv[qb][r] = fast_exp2(fmaf(sh[qb][r], s.scale_log2, -z[r]));
-            pb[4 * qb + r] = (bf16)pv[qb][r];
-          }
-        }
-        // ---- dP = dO V^T and dV^T += dO^T P, independent products
-        f32x4 dp[2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dp[qb][r] = 0.f;
-#pragma unroll
-        for (int t = 0; t < KS; ++t)
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma16(orow[t][qb], vr[t], dp[qb]);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) dv[db] = mfma16(ocol[db], pb, dv[db]);
-        // ---- dS = P o (dP - D), then dK^T += Q^T dS
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const f32x4 ddv = *reinterpret_cast<const f32x4*>(&sm.dd[buf][lr + 16 * qb + 4 * g]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) dsb[4 * qb + r] = (bf16)(pv[qb][r] * (dp[qb][r] - ddv[r]));
-        }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) dk[db] = mfma16(qcol[db], dsb, dk[db]);
+        kept_tile(buf, half, half ? sacc[2] : sacc[0], half ? sacc[3] : sacc[1]);
       }
     }
     prev_h = h;
@@ -379,10 +389,146 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     __syncthreads();
   }
   if (prev_i >= 0) flush_keep((total - 1) & 1, prev_h, prev_i);
+  } else {
+    // ---- decisions from the gate pass: only steps that hold a kept tile of
+    // this workgroup are staged; a wave forms scores only for its kept tiles.
+    // Step t of the walk is head hk * group + t / nsteps, row step
+    // i_start + t % nsteps.
+    const int nsteps = tr64 - i_start;
+    auto step_hi = [&](int t, int& hh, int& ii) {
+      hh = hk * s.group + hsub + t / nsteps;
+      ii = i_start + t % nsteps;
+    };
+    // look-ahead over 64 steps at a time: lane k holds the two decision
+    // bytes of step la_base + k, and bit k of la says whether any is set
+    uint64_t la = 0u;
+    int la_base = -64;
+    uint32_t la_val = 0u;
+    auto la_fill = [&](int t0) {
+      const int t = t0 + lane;
+      uint32_t v = 0u;
+      if (t < total) {
+        int hh, ii;
+        step_hi(t, hh, ii);
+        const size_t row = ((size_t)b * s.hq + hh) * tr32 + 2 * ii;
+        v = bit_bytes[row * (size_t)words * 4 + J];
+        if (2 * ii + 1 < tr32) v |= (uint32_t)bit_bytes[(row + 1) * (size_t)words * 4 + J] << 8;
+      }
+      la_val = v;
+      la = __builtin_amdgcn_ballot_w64(v != 0u);
+      la_base = t0;
+    };
+    // the first step at or after t with a kept tile (total if none) and its bytes
+    auto next_kept = [&](int t, uint32_t& v) {
+      while (t < total) {
+        if (t >= la_base + 64) la_fill(t);
+        const uint64_t m = la >> (t - la_base);
+        if (m != 0u) {
+          t += (int)__builtin_ctzll(m);
+          v = __builtin_amdgcn_readlane(la_val, t - la_base);
+          return t;
+        }
+        t = la_base + 64;
+      }
+      v = 0u;
+      return total;
+    };
+
+    uint32_t v;
+    int t = next_kept(0, v);
+    int h = hk * s.group + hsub, i = i_start;
+    if (t < total) step_hi(t, h, i);
+    int hl = h;
+    auto lq = make_rsrc(Q + head_row0(h) * D, head_bytes);
+    auto lo = make_rsrc(dO + head_row0(h) * D, head_bytes);
+    load_step(lq, lo, h, i);
+    store_step(0, i);
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      settle(kr[k]);
+      settle(vr[k]);
+    }
+    __syncthreads();
+    int buf = 0;
+    while (t < total) {
+      uint32_t vn;
+      const int tn = next_kept(t + 1, vn);
+      int hn = h, in = i;                              // after the last: the current step again
+      if (tn < total) step_hi(tn, hn, in);
+      if (hn != hl) {
+        hl = hn;
+        lq = make_rsrc(Q + head_row0(hn) * D, head_bytes);
+        lo = make_rsrc(dO + head_row0(hn) * D, head_bytes);
+      }
+      load_step(lq, lo, hn, in);
+      // this wave's kept halves of step t
+      const uint32_t mine = ((v >> w) & 1u) | (((v >> (8 + w)) & 1u) << 1);
+      if (mine != 0u) {
+        bool bnd[2] = {false, false};
+        if (!(keys_in && i >= i_lo && i < i_hi)) {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int r0 = i * 64 + 32 * half;
+            bnd[half] = (r0 + 32 > s.nq) || (kw0 + kBK > s.nk) || (s.causal && kw0 + kBK - 1 > r0 + s.offset);
+          }
+        }
+        f32x4 sacc[4];
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sacc[qb][r] = 0.f;
+        {
+          bf16x8 qrow[KS][4];
+#pragma unroll
+          for (int k = 0; k < KS; ++k)
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb) qrow[k][qb] = load16(&sm.q[buf][16 * qb + l16][32 * k + 8 * g]);
+#pragma unroll
+          for (int k = 0; k < KS; ++k)
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb) sacc[qb] = mfma16(qrow[k][qb], kr[k], sacc[qb]);
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          if (!bnd[half]) continue;
+          const int r0 = i * 64 + 32 * half;
+#pragma unroll
+          for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int q = r0 + 16 * qh + 4 * g + r;
+              const bool ok = (q < s.nq) & (key < s.nk) & ((key <= q + s.offset) | (s.causal == 0));
+              sacc[2 * half + qh][r] = ok ? sacc[2 * half + qh][r] : kNegInf;   // P = 0 there
+            }
+        }
+        if (mine & 1u) kept_tile(buf, 0, sacc[0], sacc[1]);
+        if (mine & 2u) kept_tile(buf, 1, sacc[2], sacc[3]);
+      }
+      store_step(buf ^ 1, in);
+      t = tn;
+      v = vn;
+      h = hn;
+      i = in;
+      buf ^= 1;
+      __syncthreads();
+    }
+  }
 
   // ---- store dK = scale * sum dS^T Q and dV (summed over the group's heads):
   // lane (key l16, group g) holds d = 16 db + 4 g + r
   if (key >= s.nk) return;
+  if constexpr (kGated) {
+    // this walk's head only: fp32 partials [2][B][Hq][N_k][D] (dK unscaled)
+    const size_t prow = ((size_t)b * s.hq + hk * s.group + hsub) * (size_t)s.nk + key;
+    float* pk = part + prow * D;
+    float* pv = part + ((size_t)s.batch * s.hq * s.nk + prow) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      *reinterpret_cast<f32x4*>(pk + 16 * db + 4 * g) = dk[db];
+      *reinterpret_cast<f32x4*>(pv + 16 * db + 4 * g) = dv[db];
+    }
+    return;
+  }
   bf16* dkr = dK + (krow0 + key) * D;
   bf16* dvr = dV + (krow0 + key) * D;
   const float sc_nat = s.scale_log2 * 0.69314718055994531f;   // softmax scale
@@ -393,6 +539,182 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     bf16x4 c = {(bf16)dv[db][0], (bf16)dv[db][1], (bf16)dv[db][2], (bf16)dv[db][3]};
     *reinterpret_cast<bf16x4*>(dkr + 16 * db + 4 * g) = a;
     *reinterpret_cast<bf16x4*>(dvr + 16 * db + 4 * g) = c;
+  }
+}
+
+// The gated walks' partials summed over each KV head's group of query heads
+// (in head order, so the result does not depend on scheduling): dK = scale *
+// sum, dV = sum, in bf16.
+__global__ __launch_bounds__(256) void bwd_dkdv_finalize_kernel(Shape s, const float* __restrict__ part,
+                                                                bf16* __restrict__ dK,
+                                                                bf16* __restrict__ dV) {
+  const size_t per_head = (size_t)s.nk * s.d;                 // floats of one head's partial
+  const size_t n4 = (size_t)s.batch * s.hkv * per_head / 4;   // 4-element chunks of dK
+  const size_t dv_off = (size_t)s.batch * s.hq * per_head;
+  const float sc_nat = s.scale_log2 * 0.69314718055994531f;
+  const size_t nthr = (size_t)gridDim.x * blockDim.x;
+  for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < n4; c += nthr) {
+    const size_t e = 4 * c;                                   // element of [B][Hkv][N_k][D]
+    const size_t bk = e / per_head, within = e % per_head;
+    const size_t b = bk / s.hkv, hk = bk % s.hkv;
+    const size_t p0 = ((b * s.hq + hk * s.group) * per_head) + within;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, v = {0.f, 0.f, 0.f, 0.f};
+    for (int hs = 0; hs < s.group; ++hs) {
+      a += *reinterpret_cast<const f32x4*>(part + p0 + hs * per_head);
+      v += *reinterpret_cast<const f32x4*>(part + dv_off + p0 + hs * per_head);
+    }
+    const bf16x4 ka = {(bf16)(a[0] * sc_nat), (bf16)(a[1] * sc_nat), (bf16)(a[2] * sc_nat),
+                       (bf16)(a[3] * sc_nat)};
+    const bf16x4 va = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+    *reinterpret_cast<bf16x4*>(dK + e) = ka;
+    *reinterpret_cast<bf16x4*>(dV + e) = va;
+  }
+}
+
+// ---------------------------------------------------------------- gate pass
+// For inputs on which few tiles are kept (MALA_FLAG_GATE_PASS): the offline
+// gate (Eq. 4) of every legal 32 x 16 backward tile, taken in a query-major
+// pass before dK/dV, so that dK/dV stages and processes only the steps that
+// hold a kept tile (a skipped tile then costs no dO load, App. A.1). Every
+// legal score is still formed, here. The layout is the forward's: a
+// workgroup owns 256 query rows of one (batch, query head), wave w rows
+// [32 w, 32 w + 32), one backward decision row; K tiles of 64 keys are
+// double-buffered in LDS and shared by the 8 waves; S^T = K Q^T with the
+// 32x32x16 MFMA and Q^T in registers, so every lane owns one query row and
+// compares against its own z_q. The decisions of the wave's row go out as
+// whole 32-bit words of the bit rows, one plain store each.
+template <int D>
+struct alignas(16) GateSmem {
+  bf16 k[2][64][D + 8];   // conflict-free 16-byte row reads (32x32x16 A layout)
+};
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* __restrict__ Q,
+                                                          const bf16* __restrict__ K,
+                                                          const float* __restrict__ LSE,
+                                                          uint32_t* __restrict__ bits,
+                                                          int8_t* __restrict__ mask, int n_qb) {
+  __shared__ GateSmem<D> sm;
+  constexpr int KT = D / 16;              // 16-wide k-steps of the QK contraction
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int RPP = 512 / CPR;          // K rows per load pass
+  constexpr int KPASS = 64 / RPP;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int bh_count = s.batch * s.hq;
+  const int I = n_qb - 1 - (int)(blockIdx.x / bh_count);     // longest blocks first
+  const int bh = (int)(blockIdx.x % bh_count);
+  const int b = bh / s.hq, h = bh % s.hq, hk = h / s.group;
+  const size_t qrow0 = (size_t)bh * (size_t)s.nq;
+  const size_t krow0 = ((size_t)b * s.hkv + hk) * (size_t)s.nk;
+  const int tr32 = (s.nq + kBQ - 1) / kBQ;
+  const int tc16 = (s.nk + kBK - 1) / kBK;
+  const int words = (tc16 + 31) / 32;
+
+  const int q0 = I * 256 + 32 * w;
+  const bool active = q0 < s.nq;
+  auto top_tile = [&](int last_row) {
+    const int lastkey = s.causal ? min(last_row + s.offset, s.nk - 1) : s.nk - 1;
+    return lastkey / 64;
+  };
+  const int top_b = top_tile(min(I * 256 + 255, s.nq - 1));
+  const int top_w = active ? top_tile(min(q0 + 31, s.nq - 1)) : -1;
+
+  const auto qrs = make_rsrc(Q + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
+  const auto krs = make_rsrc(K + krow0 * D, (uint32_t)((size_t)s.nk * D * 2));
+  // Q^T as the B operand: lane (query l32, half hf) holds Q[q][16t + 8hf .. +7]
+  const int q = q0 + l32;
+  const bool rvalid = q < s.nq;
+  bf16x8 qr[KT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) qr[t] = buf_load16(qrs, (uint32_t)(q * D + 16 * t + 8 * hf) * 2);
+  // the row's threshold in base 2, as dK/dV forms it: skip iff s2 < u2 on
+  // every legal entry (u2 = +inf for rows past N_q: never kept)
+  float u2 = __builtin_inff();
+  if (rvalid) {
+    const float L = s.causal ? (float)(q + s.offset + 1) : (float)s.nk;
+    u2 = LSE[qrow0 + q] * 1.4426950408889634f + (s.log2_tau - fast_log2(L));
+  }
+
+  bf16x8 kreg[KPASS];
+  const int kc = tid % CPR, krr = tid / CPR;
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int p = 0; p < KPASS; ++p)
+      kreg[p] = buf_load16(krs, (uint32_t)((j * 64 + p * RPP + krr) * D + 8 * kc) * 2);
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < KPASS; ++p) store16(&sm.k[buf][p * RPP + krr][8 * kc], kreg[p]);
+  };
+  if (top_b >= 0) {
+    load_tile(top_b);
+    store_tile(top_b & 1);
+  }
+#pragma unroll
+  for (int t = 0; t < KT; ++t) settle(qr[t]);
+  settle(u2);
+  __syncthreads();
+
+  const size_t brow = (size_t)bh * tr32 + (active ? q0 / kBQ : 0);   // this wave's bit row
+  uint32_t word = 0u;            // decisions of columns 32 (j / 8) .. + 31 of this wave's row
+  for (int j = top_b; j >= 0; --j) {
+    const int buf = j & 1;
+    if (j > 0) load_tile(j - 1);
+    if (active && j <= top_w) {
+      // ---- S^T[key][query], 64 keys x 32 queries: register r of block kb is
+      // key 32 kb + 8 (r / 4) + 4 hf + r % 4
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+      bf16x8 ka[KT][2];
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) ka[t][kb] = load16(&sm.k[buf][32 * kb + l32][16 * t + 8 * hf]);
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(ka[t][kb], qr[t], sacc[kb]);
+      const int key0 = j * 64;
+      if ((key0 + 64 > s.nk) || (q0 + 32 > s.nq) || (s.causal && key0 + 63 > q0 + s.offset)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const bool ok = rvalid && key < s.nk && (!s.causal || key <= q + s.offset);
+            if (!ok) sacc[kb][r] = kNegInf;
+          }
+      }
+      // ---- offline gate, Eq. 4, per 16-key column c = keys 16 c .. + 15
+      // of the tile: registers 8 (c % 2) .. + 7 of block c / 2
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float x = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          x = fmaxf(x, fmaf(sacc[c >> 1][8 * (c & 1) + r], s.scale_log2, -u2));
+        const bool keep = __builtin_amdgcn_ballot_w64(x >= 0.f) != 0;
+        const int col = 4 * j + c;
+        if (keep) word |= 1u << (col & 31);
+        if (mask != nullptr && lane == 0 && col < tc16) {
+          const int kc0 = 16 * col;
+          const bool legal = kc0 < s.nk && (!s.causal || kc0 <= min(q0 + 31, s.nq - 1) + s.offset);
+          if (legal) mask[brow * tc16 + col] = keep ? 1 : 0;
+        }
+      }
+      if ((j & 7) == 0) {
+        if (lane == 0) bits[brow * words + (j >> 3)] = word;
+        word = 0u;
+      }
+    }
+    if (j > 0) store_tile((j - 1) & 1);
+    __syncthreads();
   }
 }
 
@@ -657,6 +979,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
 
 size_t bwd_ws_d_floats(const Shape& s) { return (size_t)s.batch * s.hq * s.nq; }
 
+size_t bwd_part_floats(const Shape& s) {
+  if (!s.dtype_is_bf16() || !(s.flags & MALA_FLAG_GATE_PASS)) return 0;
+  return 2 * (size_t)s.batch * s.hq * s.nk * s.d;
+}
+
 size_t bwd_bits_words(const Shape& s) {
   const size_t tr = (s.nq + kBQ - 1) / kBQ, tc = (s.nk + kBK - 1) / kBK;
   return (size_t)s.batch * s.hq * tr * ((tc + 31) / 32);
@@ -664,8 +991,8 @@ size_t bwd_bits_words(const Shape& s) {
 
 hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* d_o, void* dq, void* dk,
-                           void* dv, float* ws_d, uint32_t* ws_bits, int8_t* mask, int32_t* kept,
-                           hipStream_t st, int stages) {
+                           void* dv, float* ws_d, uint32_t* ws_bits, float* ws_part, int8_t* mask,
+                           int32_t* kept, hipStream_t st, int stages) {
   const int rows = s.batch * s.hq * s.nq;
   const size_t nwords = bwd_bits_words(s);
   const size_t nkept = (size_t)s.batch * s.hq * ((s.nq + kBQ - 1) / kBQ);
@@ -685,11 +1012,31 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
   const dim3 g1((unsigned)(n_kb * s.batch * s.hkv));
   const int n_qb = (s.nq + 255) / 256;
   const dim3 g2((unsigned)(n_qb * s.batch * s.hq));
-  auto launch = [&](auto dkdv, auto dqk) {
-    if (g1.x && (stages & kStageMain))
+  // MALA_FLAG_GATE_PASS: the gate pass writes the decisions, and dK/dV
+  // visits only the steps that hold a kept tile
+  const bool gated = (s.flags & MALA_FLAG_GATE_PASS) != 0;
+  auto launch = [&](auto gate, auto dkdv, auto dkdv_gated, auto dqk) {
+    if (gated && (stages & kStageMain)) {
+      // decisions, then one walk per (key block, query head), then the sums
+      if (g2.x)
+        hipLaunchKernelGGL(gate, g2, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k, lse,
+                           ws_bits, mask, n_qb);
+      const dim3 g1h((unsigned)(g1.x * s.group));
+      if (g1h.x)
+        hipLaunchKernelGGL(dkdv_gated, g1h, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
+                           (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dk, (bf16*)dv,
+                           ws_bits, mask, ws_part);
+      const size_t n4 = (size_t)s.batch * s.hkv * s.nk * s.d / 4;
+      size_t blocks = (n4 + 255) / 256;
+      if (blocks > 65536) blocks = 65536;
+      if (n4)
+        hipLaunchKernelGGL(bwd_dkdv_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, s,
+                           (const float*)ws_part, (bf16*)dk, (bf16*)dv);
+    } else if (g1.x && (stages & kStageMain)) {
       hipLaunchKernelGGL(dkdv, g1, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
                          (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dk, (bf16*)dv,
-                         ws_bits, mask);
+                         ws_bits, mask, (float*)nullptr);
+    }
     // dynamic LDS: the needed-tile bitmap, one bit per 64-key tile
     const size_t need_bytes = (size_t)((s.nk + 64 * 32 - 1) / (64 * 32)) * 4;
     if (g2.x && (stages & kStageDq))
@@ -699,11 +1046,19 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
   };
   const bool split = !(s.flags & MALA_FLAG_FAST_GRAD);
   if (s.d == 128) {
-    if (split) launch(bwd_dkdv_kernel<128>, bwd_dq_kernel<128, true>);
-    else launch(bwd_dkdv_kernel<128>, bwd_dq_kernel<128, false>);
+    if (split)
+      launch(bwd_gate_kernel<128>, bwd_dkdv_kernel<128, false>, bwd_dkdv_kernel<128, true>,
+             bwd_dq_kernel<128, true>);
+    else
+      launch(bwd_gate_kernel<128>, bwd_dkdv_kernel<128, false>, bwd_dkdv_kernel<128, true>,
+             bwd_dq_kernel<128, false>);
   } else {
-    if (split) launch(bwd_dkdv_kernel<64>, bwd_dq_kernel<64, true>);
-    else launch(bwd_dkdv_kernel<64>, bwd_dq_kernel<64, false>);
+    if (split)
+      launch(bwd_gate_kernel<64>, bwd_dkdv_kernel<64, false>, bwd_dkdv_kernel<64, true>,
+             bwd_dq_kernel<64, true>);
+    else
+      launch(bwd_gate_kernel<64>, bwd_dkdv_kernel<64, false>, bwd_dkdv_kernel<64, true>,
+             bwd_dq_kernel<64, false>);
   }
   return hipGetLastError();
 }

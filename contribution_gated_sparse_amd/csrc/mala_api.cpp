@@ -65,7 +65,7 @@ mala_status check_problem(const mala_problem* p, mala::Shape* s) {
     return fail(MALA_ERR_INVALID_ARG, "tau must be finite and >= 0");
   if (!std::isfinite(p->softmax_scale) || p->softmax_scale <= 0.f)
     return fail(MALA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
-  if (p->flags & ~MALA_FLAG_FAST_GRAD)
+  if (p->flags & ~(MALA_FLAG_FAST_GRAD | MALA_FLAG_GATE_PASS))
     return fail(MALA_ERR_INVALID_ARG, "unknown flags 0x%x", (unsigned)p->flags);
   const size_t es = elem_size(p->dtype);
   if ((size_t)p->n_q * p->head_dim * es >= (1ull << 31) ||
@@ -108,7 +108,8 @@ mala_status check_ptr(const void* ptr, const char* name, bool needed) {
 
 size_t bwd_ws_bytes(const mala::Shape& s) {
   return round_up(mala::bwd_ws_d_floats(s) * sizeof(float)) +
-         round_up(mala::bwd_bits_words(s) * sizeof(uint32_t));
+         round_up(mala::bwd_bits_words(s) * sizeof(uint32_t)) +
+         round_up(mala::bwd_part_floats(s) * sizeof(float));
 }
 
 // Keys per split for a checked decode problem (the rule mala_decode_split_keys
@@ -215,10 +216,11 @@ mala_status bwd_impl(int stages, const mala_problem* p, const void* q, const voi
   float* ws_d = (float*)workspace;
   uint32_t* ws_bits =
       (uint32_t*)((char*)workspace + round_up(mala::bwd_ws_d_floats(s) * sizeof(float)));
+  float* ws_part = (float*)((char*)ws_bits + round_up(mala::bwd_bits_words(s) * sizeof(uint32_t)));
   hipError_t e;
   if (s.dtype_is_bf16())
-    e = mala::launch_bwd_bf16(s, q, k, v, o, lse, d_o, dq, dk, dv, ws_d, ws_bits, tile_mask,
-                              kept_tiles, st, stages);
+    e = mala::launch_bwd_bf16(s, q, k, v, o, lse, d_o, dq, dk, dv, ws_d, ws_bits, ws_part,
+                              tile_mask, kept_tiles, st, stages);
   else
     e = mala::launch_bwd_f32(s, (const float*)q, (const float*)k, (const float*)v,
                              (const float*)o, lse, (const float*)d_o, (float*)dq, (float*)dk,

@@ -99,8 +99,8 @@ hipError_t launch_fwd_f32(const Shape& s, const float* q, const float* k, const 
 
 hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* d_o, void* dq, void* dk,
-                           void* dv, float* ws_d, uint32_t* ws_bits, int8_t* mask, int32_t* kept,
-                           hipStream_t st, int stages);
+                           void* dv, float* ws_d, uint32_t* ws_bits, float* ws_part, int8_t* mask,
+                           int32_t* kept, hipStream_t st, int stages);
 hipError_t launch_bwd_f32(const Shape& s, const float* q, const float* k, const float* v,
                           const float* o, const float* lse, const float* d_o, float* dq, float* dk,
                           float* dv, float* ws_d, uint32_t* ws_bits, int8_t* mask, int32_t* kept,
@@ -124,6 +124,7 @@ hipError_t launch_decode_combine_f32(const DecodeShape& s, const float* ws, floa
 // Workspace layouts.
 size_t bwd_ws_d_floats(const Shape& s);    // D = rowsum(O o dO), fp32 [B, Hq, Nq]
 size_t bwd_bits_words(const Shape& s);     // backward decisions, one bit per tile
+size_t bwd_part_floats(const Shape& s);    // gate pass: fp32 dK, dV partials [2, B, Hq, N_k, D]
 size_t decode_ws_floats(const DecodeShape& s);
 
 }  // namespace mala

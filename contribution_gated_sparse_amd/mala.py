@@ -39,6 +39,7 @@ class Problem(ctypes.Structure):
 
 
 MALA_FLAG_FAST_GRAD = 1
+MALA_FLAG_GATE_PASS = 2
 
 
 class DecodeProblem(ctypes.Structure):
@@ -178,14 +179,16 @@ def mala_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float, caus
 def mala_bwd(q, k, v, o, lse, d_o, tau: float, causal: bool = True,
              softmax_scale: Optional[float] = None, want_mask: bool = False,
              want_kept: bool = True, out: Optional[dict] = None, fast_grad: bool = False,
-             stages=None, events=None) -> dict:
-    """Backward -> dict(dq, dk, dv, mask, kept). ``stages``: run only these
-    stages (BWD_PREP, BWD_DKDV, BWD_DQ) through mala_bwd_stage; ``events``:
-    optional list of torch.cuda.Event, one recorded after each stage run."""
+             gate_pass: bool = False, stages=None, events=None) -> dict:
+    """Backward -> dict(dq, dk, dv, mask, kept). ``gate_pass``: take the
+    decisions in a separate score pass so that dK/dV visits only the steps
+    with a kept tile (MALA_FLAG_GATE_PASS). ``stages``: run only these stages
+    (BWD_PREP, BWD_DKDV, BWD_DQ) through mala_bwd_stage; ``events``: optional
+    list of torch.cuda.Event, one recorded after each stage run."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (d_o, "d_o")):
         _dev(t, n)
     p = make_problem(q, k, tau, causal, softmax_scale,
-                     MALA_FLAG_FAST_GRAD if fast_grad else 0)
+                     (MALA_FLAG_FAST_GRAD if fast_grad else 0) | (MALA_FLAG_GATE_PASS if gate_pass else 0))
     lib = load_library()
     bq, bk, _ = mala_get_tiling(OP_BWD)
     tr, tc = -(-p.n_q // bq), -(-p.n_k // bk)

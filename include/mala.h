@@ -66,7 +66,17 @@ enum {
    * matrix product per kept tile and key column) and less accurate: dQ errors
    * grow to ~2^-9 of the summed terms, which can exceed 1% of the result
    * where the terms of a row cancel. */
-  MALA_FLAG_FAST_GRAD = 1
+  MALA_FLAG_FAST_GRAD = 1,
+  /* bf16 backward: take the offline gate (Eq. 4) of every legal tile in a
+   * separate score pass before dK/dV, and let dK/dV stage and process only
+   * the 64-row steps that hold a kept tile, so that a skipped tile costs no
+   * dO load (App. A.1, "Fused backward execution"). Every legal score is
+   * still formed. Pays off when few tiles are kept (trained attention,
+   * larger tau); on inputs where most tiles are kept it adds one score pass
+   * (about a fifth of the backward). The decisions may differ from those of
+   * the default path only for tiles whose margin is within fp32 rounding of
+   * the threshold. Ignored for MALA_F32. */
+  MALA_FLAG_GATE_PASS = 2
 };
 
 /* One prefill/training attention problem. */

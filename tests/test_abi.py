@@ -109,6 +109,13 @@ def test_backward_workspace(lib):
     expect = -(-(4 * 100 * 4) // 256) * 256 + -(-(4 * tr * -(-tc // 32) * 4) // 256) * 256
     assert need == expect
     assert lib.mala_bwd_workspace_size(ctypes.byref(prob(head_dim=80))) == 0
+    # MALA_FLAG_GATE_PASS adds the fp32 dK, dV partials of the per-head walks
+    # (2 x B x Hq x Nk x D floats) for bf16; fp32 problems ignore the flag
+    part = -(-(2 * 4 * 100 * 128 * 4) // 256) * 256
+    assert lib.mala_bwd_workspace_size(ctypes.byref(prob(flags=M.MALA_FLAG_GATE_PASS))) == need + part
+    assert lib.mala_bwd_workspace_size(ctypes.byref(prob(flags=3))) == need + part
+    f32 = lib.mala_bwd_workspace_size(ctypes.byref(prob(dtype=M.MALA_F32)))
+    assert lib.mala_bwd_workspace_size(ctypes.byref(prob(dtype=M.MALA_F32, flags=2))) == f32
     buf = (ctypes.c_char * 1024)()
     addr = ctypes.addressof(buf)
     addr += (-addr) % 256

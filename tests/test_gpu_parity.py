@@ -30,13 +30,14 @@ def to_dev(x):
     return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
 
 
-def check_backward(x, tau, g_fwd, r_fwd, causal=True, qblocks=None, key_rows=None):
+def check_backward(x, tau, g_fwd, r_fwd, causal=True, qblocks=None, key_rows=None,
+                   gate_pass=False):
     m = lib()
     q, k, v, do = x["q"], x["k"], x["v"], x["do"]
     kind = dtype_name(q)
     _, (bq, bk, _), _ = tiling()
     g = m.mala_bwd(q, k, v, g_fwd["o"], g_fwd["lse"], do, tau, causal=causal,
-                   softmax_scale=x["scale"], want_mask=True)
+                   softmax_scale=x["scale"], want_mask=True, gate_pass=gate_pass)
     torch.cuda.synchronize()
     gmask = g["mask"].cpu().numpy()
     r = O.mala_bwd(np64(q), np64(k), np64(v), r_fwd["o"], r_fwd["lse"], np64(do), tau,
@@ -145,6 +146,57 @@ def test_structured_skipping_fwd_bwd(dtype, tau):
     bm = gb["mask"].cpu().numpy()
     assert (bm == O.SKIPPED).sum() > 0
     check_nesting(g["mask"].cpu().numpy(), bm)
+
+
+# ------------------------------------------------------------- gate pass
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("tau", [0.0, 1e-4, 1.0, 100.0])
+def test_gate_pass_shapes(shape, tau):
+    """MALA_FLAG_GATE_PASS: decisions from the separate score pass, dK/dV over
+    the steps with a kept tile only; same bar against the oracle."""
+    b, hq, hkv, nq, nk, d = shape
+    x = W.make_prefill(W.CONFIGS[2], n=nk, hq=hq, hkv=hkv, d=d, batch=b, planted=4, seed=7 + nq)
+    if nq < nk:
+        x["q"] = x["q"][:, :, nk - nq:].contiguous()
+        x["do"] = x["do"][:, :, nk - nq:].contiguous()
+    x = to_dev(x)
+    print(f"[gate pass] shape={shape} tau={tau}", flush=True)
+    g, r, _ = check_forward(x, tau, max_ties=4)
+    gb, _, _ = check_backward(x, tau, g, r, gate_pass=True)
+    check_nesting(g["mask"].cpu().numpy(), gb["mask"].cpu().numpy())
+
+
+@pytest.mark.parametrize("tau", [1e-4, 1.0])
+def test_gate_pass_structured(tau):
+    """On skipping inputs the gate pass takes the default path's decisions
+    (outside the near-tie band) and reproduces its gradients."""
+    m = lib()
+    x = to_dev(W.make_structured(1500, hq=8, hkv=2, d=128))
+    g, r, st = check_forward(x, tau, max_ties=4)
+    assert st["kept_frac"] < 0.8
+    gb, rb, _ = check_backward(x, tau, g, r, gate_pass=True)
+    ref = m.mala_bwd(x["q"], x["k"], x["v"], g["o"], g["lse"], x["do"], tau,
+                     softmax_scale=x["scale"], want_mask=True)
+    torch.cuda.synchronize()
+    a, b_ = gb["mask"].cpu().numpy(), ref["mask"].cpu().numpy()
+    clear = (a != O.NOT_VISITED) & ~(np.abs(rb["margin"]) < BAND["bf16"])
+    assert np.array_equal(a[clear], b_[clear])
+    assert (a == O.SKIPPED).sum() > 0
+    for n in ("dq", "dk", "dv"):
+        u, w = np64(gb[n]), np64(ref[n])
+        assert np.abs(u - w).max() <= 2e-2 * max(1.0, np.abs(w).max()), n
+
+
+def test_gate_pass_noncausal_and_f32():
+    """Non-causal walks through the gate pass; the flag is ignored for fp32."""
+    x = to_dev(W.make_prefill(W.CONFIGS[2], n=160, hq=2, hkv=1, d=128, planted=3))
+    for tau in (0.0, 0.5, 50.0):
+        g, r, _ = check_forward(x, tau, causal=False, max_ties=4)
+        check_backward(x, tau, g, r, causal=False, gate_pass=True)
+    x = to_dev(W.make_prefill(W.CONFIGS[1], n=150, hq=4, hkv=2, d=64, planted=4))
+    g, r, _ = check_forward(x, 1.0, max_ties=2)
+    check_backward(x, 1.0, g, r, gate_pass=True)
 
 
 # ------------------------------------------------------------- decode
