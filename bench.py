@@ -45,9 +45,9 @@ def parse():
     ap.add_argument("--fast-grad", action="store_true", help="single-bf16 dS in the backward")
     ap.add_argument("--only", default="", help="profiling: 'fwd', 'bwd' or 'decode' alone")
     ap.add_argument("--profile-structured", type=float, default=None, metavar="TAU",
-                    help="for rocprofv3: two passes of the structured 32K forward + backward "
-                         "and of the structured 128K decode (256-key splits, then one split "
-                         "per sequence) at TAU; prints no JSON")
+                    help="for rocprofv3: two passes of the structured 32K forward + backward, "
+                         "of the backward with the gate pass, and of the structured 128K decode "
+                         "(256-key splits, then one split per sequence) at TAU; prints no JSON")
     ap.add_argument("--profile", action="store_true",
                     help="for rocprofv3: one warm-up step, one step, then a 1 GiB device copy "
                          "that calibrates the byte counters; prints no JSON")
@@ -144,14 +144,18 @@ def matched_work(m, W, torch, dev, fbq, fbk, n=8192):
 
 def profile_structured(tau, m, W, torch, dev):
     """Kernel launches for a profiler on the structured inputs: two passes
-    (the first warms up) of the 32K forward + backward, then of the 128K
-    decode with 256-key splits and with one split per sequence."""
+    (the first warms up) of the 32K forward + backward, two of the backward
+    with the separate gate pass, then of the 128K decode with 256-key splits
+    and with one split per sequence."""
     x = W.make_structured(32768, hq=32, hkv=8, d=128, device=dev, dtype="bf16", with_do=False)
     q, k, v = x["q"], x["k"], x["v"]
     do = W.rademacher(q.shape, seed=20269002, device=dev, dtype="bf16")
     for _ in range(2):
         f = m.mala_fwd(q, k, v, tau, softmax_scale=x["scale"])
         m.mala_bwd(q, k, v, f["o"], f["lse"], do, tau, softmax_scale=x["scale"])
+        torch.cuda.synchronize()
+    for _ in range(2):   # the backward with the separate gate pass
+        m.mala_bwd(q, k, v, f["o"], f["lse"], do, tau, softmax_scale=x["scale"], gate_pass=True)
         torch.cuda.synchronize()
     del x, q, k, v, do, f
     torch.cuda.empty_cache()
@@ -189,6 +193,7 @@ def structured_section(args, m, W, torch, dev, tiling):
               kept=torch.empty((B, HQ, -(-N // fbq)), dtype=torch.int32, device=dev))
     bo = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
               kept=torch.empty((B, HQ, -(-N // bbq)), dtype=torch.int32, device=dev))
+    bg = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v))
     vis_f = fwd_tiles(N, N, fbq, fbk) * B * HQ
     vis_b = bwd_tiles(N, N, bbq, bbk) * B * HQ
     pre = {}
@@ -212,6 +217,25 @@ def structured_section(args, m, W, torch, dev, tiling):
         pre[tau_] = dict(fwd_ms=round(tf / args.steps, 3), bwd_ms=round(tb / args.steps, 3),
                          fwd_kept_frac=round(int(fo["kept"].sum()) / vis_f, 4),
                          bwd_kept_frac=round(int(bo["kept"].sum()) / vis_b, 4))
+        # the same backward with the separate gate pass (MALA_FLAG_GATE_PASS):
+        # dK/dV then walks only the steps with a kept tile
+        def run_gate():
+            m.mala_bwd(q, k, v, fo["o"], fo["lse"], do, tau_, softmax_scale=x["scale"], out=bg,
+                       fast_grad=args.fast_grad, gate_pass=True)
+        for _ in range(args.warmup):
+            run_gate()
+        torch.cuda.synchronize()
+        tg = 0.0
+        for _ in range(args.steps):
+            ev[0].record()
+            run_gate()
+            ev[2].record()
+            torch.cuda.synchronize()
+            tg += ev[0].elapsed_time(ev[2])
+        pre[tau_]["bwd_gate_pass_ms"] = round(tg / args.steps, 3)
+        pre[tau_]["gate_pass_vs_default"] = {   # max |difference| / max(1, max |default|)
+            n_: float((bg[n_].float() - bo[n_].float()).abs().max()
+                      / bo[n_].float().abs().max().clamp_min(1.0)) for n_ in ("dq", "dk", "dv")}
         # fidelity against tau = 0 (App. C.1/C.3 quantities): omitted normalized
         # mass per row, 1 - Z_R / Z = 1 - exp(z_tau - z_0), bounded by
         # tau / (1 + tau) (Prop. 1), and the relative L2 error of each output row
@@ -244,8 +268,12 @@ def structured_section(args, m, W, torch, dev, tiling):
             (pre[0.0]["fwd_ms"] + pre[0.0]["bwd_ms"]) / (pre[tau_]["fwd_ms"] + pre[tau_]["bwd_ms"]), 4)
         pre[tau_]["fwd_speedup"] = round(pre[0.0]["fwd_ms"] / pre[tau_]["fwd_ms"], 4)
         pre[tau_]["bwd_speedup"] = round(pre[0.0]["bwd_ms"] / pre[tau_]["bwd_ms"], 4)
+        pre[tau_]["speedup_vs_tau0_gate_pass"] = round(
+            (pre[0.0]["fwd_ms"] + pre[0.0]["bwd_ms"])
+            / (pre[tau_]["fwd_ms"] + pre[tau_]["bwd_gate_pass_ms"]), 4)
+        pre[tau_]["bwd_speedup_gate_pass"] = round(pre[0.0]["bwd_ms"] / pre[tau_]["bwd_gate_pass_ms"], 4)
     res["prefill_32k"] = {f"tau={t:g}": pre[t] for t in taus}
-    del x, q, k, v, do, fo, bo, g0
+    del x, q, k, v, do, fo, bo, bg, g0
     torch.cuda.empty_cache()
     res["matched_work_8k"] = matched_work(m, W, torch, dev, fbq, fbk)
     torch.cuda.empty_cache()
@@ -313,7 +341,7 @@ def structured_section(args, m, W, torch, dev, tiling):
 
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "mala_kernels_prefill32k_decode128k_hbm_traffic.md")
 KERNEL_ROWS = {"fwd": ("fwd_bf16_kernel<128>", "fwd_bf16.hip"),
-               "bwd_dkdv": ("bwd_dkdv_kernel<128>", "bwd_bf16.hip"),
+               "bwd_dkdv": ("bwd_dkdv_kernel<128, false>", "bwd_bf16.hip"),
                "bwd_dq": ("bwd_dq_kernel<128, true>", "bwd_bf16.hip")}
 
 
