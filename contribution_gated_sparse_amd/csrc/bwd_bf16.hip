@@ -637,6 +637,9 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
     const float L = s.causal ? (float)(q + s.offset + 1) : (float)s.nk;
     u2 = LSE[qrow0 + q] * 1.4426950408889634f + (s.log2_tau - fast_log2(L));
   }
+  // the same test on the raw scores: keep iff max S >= u2 / (scale log2 e)
+  // over a column's legal entries (a column without one has max -inf)
+  const float thr = u2 / s.scale_log2;
 
   bf16x8 kreg[KPASS];
   const int kc = tid % CPR, krr = tid / CPR;
@@ -655,7 +658,8 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
   }
 #pragma unroll
   for (int t = 0; t < KT; ++t) settle(qr[t]);
-  settle(u2);
+  float thr_s = thr;
+  settle(thr_s);
   __syncthreads();
 
   const size_t brow = (size_t)bh * tr32 + (active ? q0 / kBQ : 0);   // this wave's bit row
@@ -697,9 +701,8 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
       for (int c = 0; c < 4; ++c) {
         float x = kNegInf;
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-          x = fmaxf(x, fmaf(sacc[c >> 1][8 * (c & 1) + r], s.scale_log2, -u2));
-        const bool keep = __builtin_amdgcn_ballot_w64(x >= 0.f) != 0;
+        for (int r = 0; r < 8; ++r) x = fmaxf(x, sacc[c >> 1][8 * (c & 1) + r]);
+        const bool keep = __builtin_amdgcn_ballot_w64((x >= thr_s) & (x > kNegInf)) != 0;
         const int col = 4 * j + c;
         if (keep) word |= 1u << (col & 31);
         if (mask != nullptr && lane == 0 && col < tc16) {
