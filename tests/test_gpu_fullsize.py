@@ -11,7 +11,10 @@ checks outputs it can compute one by one:
     last 64 query rows of the group's heads reach them, so the oracle runs on
     those rows alone (bottom-right alignment keeps their positions);
   - decode: whole steps (every head, every split) of the 128K decode batch,
-    with the default 256-key splits and with the automatic split length.
+    with the default 256-key splits and with the automatic split length;
+  - the backward with the gate pass on the structured 32K workload: sampled
+    blocks against the oracle, and every decision, dK and dV against the
+    default backward.
 """
 import numpy as np
 import pytest
@@ -107,6 +110,80 @@ def test_prefill_full_size_sampled(cid):
     compare_values("dQ tail", np64(gb["dq"][:, heads, N - t:]), rbt["dq"], "bf16")
     compare_values("dK tail", np64(gb["dk"][:, kh:kh + 1, N - t:]), rbt["dk"][:, :, N - t:], "bf16")
     compare_values("dV tail", np64(gb["dv"][:, kh:kh + 1, N - t:]), rbt["dv"][:, :, N - t:], "bf16")
+
+
+def test_gate_pass_full_size_structured():
+    """MALA_FLAG_GATE_PASS at the bench's structured 32K workload (sink keys,
+    local band, retrieval keys; most tiles skipped): decisions and dQ of
+    sampled blocks against the oracle, the decision masks against the default
+    backward's, and the whole dK and dV against the default backward's."""
+    m = lib()
+    x = W.make_structured(32768, hq=32, hkv=8, d=128, device=DEV, dtype="bf16", with_do=False)
+    q, k, v, scale = x["q"], x["k"], x["v"], x["scale"]
+    do = W.rademacher(q.shape, seed=20269002, device=DEV, dtype="bf16")
+    B, HQ, N, D = q.shape
+    HKV = k.shape[1]
+    G = HQ // HKV
+    (fbq, fbk, _), (bbq, bbk, _), _ = tiling()
+    print(f"[full-size] gate pass, structured: Hq={HQ} Hkv={HKV} N={N}", flush=True)
+    g = m.mala_fwd(q, k, v, TAU, softmax_scale=scale, want_mask=True)
+    ga = m.mala_bwd(q, k, v, g["o"], g["lse"], do, TAU, softmax_scale=scale, want_mask=True)
+    gb = m.mala_bwd(q, k, v, g["o"], g["lse"], do, TAU, softmax_scale=scale, want_mask=True,
+                    gate_pass=True)
+    torch.cuda.synchronize()
+
+    ma, mb = ga["mask"].cpu().numpy(), gb["mask"].cpu().numpy()
+    assert np.array_equal(ma == O.NOT_VISITED, mb == O.NOT_VISITED)
+    assert int((mb == O.KEPT).sum()) < 0.1 * int((mb != O.NOT_VISITED).sum())
+    # the two score products round differently: decisions may differ only at
+    # near ties, which are rare
+    assert int((ma != mb).sum()) <= 16, f"{int((ma != mb).sum())} decisions differ"
+    kept_a, kept_b = ga["kept"].cpu().numpy(), gb["kept"].cpu().numpy()
+    assert np.array_equal(kept_b, (mb == O.KEPT).sum(-1))
+    assert int(np.abs(kept_a - kept_b).sum()) <= int((ma != mb).sum())
+
+    kh = 0                                   # the KV head whose key block 0 holds the sinks
+    h = kh * G
+    tr = N // fbq
+    blocks = sorted({0, 1, tr // 3, tr // 2 + 1, tr - 3, tr - 1})
+    kn, vn = np64(k[:, kh:kh + 1]), np64(v[:, kh:kh + 1])
+    qh, doh = np64(q[:, h:h + 1]), np64(do[:, h:h + 1])
+    r = O.mala_fwd(qh, kn, vn, TAU, scale, True, fbq, fbk, blocks=[(0, 0, i) for i in blocks],
+                   replay=g["mask"][:, h:h + 1].cpu().numpy(), band=BAND["bf16"])
+    rows = np.zeros((1, 1, N), bool)
+    for i in blocks:
+        rows[..., i * fbq:(i + 1) * fbq] = True
+    bmask = mb[:, h:h + 1]
+    rb = O.mala_bwd(qh, kn, vn, r["o"], r["lse"], doh, TAU, scale, True, bbq, bbk,
+                    qblocks=blocks, replay=bmask, band=BAND["bf16"], o_storage="bf16")
+    _agree(bmask, rb["mask"], rb["margin"], "backward (gate pass)")
+    # dQ on these inputs is at the conditioning limit of a bf16-stored O: in
+    # sink-dominated rows dP - D nearly cancels, and the oracle's own dQ moves
+    # by about 1% when its O is stored in bf16 (as the backward reads it)
+    # instead of kept in fp64. The bound is the stated bar or twice that
+    # movement, whichever is larger; both references are the oracle's.
+    rb64 = O.mala_bwd(qh, kn, vn, r["o"], r["lse"], doh, TAU, scale, True, bbq, bbk,
+                      qblocks=blocks, replay=bmask, band=BAND["bf16"], o_storage=None)
+    gdq = np64(gb["dq"][:, h:h + 1])[rows]
+    ref, ref64 = rb["dq"][rows], rb64["dq"][rows]
+
+    def errs(a, b_):
+        return (float(np.abs(a - b_).max() / max(1.0, np.abs(b_).max())),
+                float(np.linalg.norm(a - b_) / max(np.linalg.norm(b_), 1e-30)))
+    e_max, e_fro = errs(gdq, ref)
+    s_max, s_fro = errs(ref, ref64)
+    print(f"dQ (gate pass): {e_max:.3e} / {e_fro:.3e}; oracle bf16-O sensitivity "
+          f"{s_max:.3e} / {s_fro:.3e}", flush=True)
+    assert e_max <= max(2e-2, 2 * s_max) and e_fro <= max(1e-2, 2 * s_fro)
+    # the dQ kernel is the default path's: the same decisions give the same dQ
+    if np.array_equal(ma, mb):
+        assert torch.equal(ga["dq"], gb["dq"])
+
+    for n_ in ("dk", "dv"):
+        a, b_ = np64(gb[n_]), np64(ga[n_])
+        scaled = float(np.abs(a - b_).max() / max(1.0, np.abs(b_).max()))
+        fro = float(np.linalg.norm(a - b_) / max(np.linalg.norm(b_), 1e-30))
+        assert scaled <= 2e-2 and fro <= 1e-2, f"{n_}: {scaled:.3e} {fro:.3e}"
 
 
 @pytest.mark.parametrize("step,split_keys", [(0, 0), (63, 0), (0, -1)])
