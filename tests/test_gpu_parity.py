@@ -346,11 +346,13 @@ def test_fast_grad_flag_same_support():
 
 # ------------------------------------------------------------- autograd entry
 
-def test_autograd_chunked_prefill_matches_direct_calls():
+@pytest.mark.parametrize("gate_pass", [False, True])
+def test_autograd_chunked_prefill_matches_direct_calls(gate_pass):
     """mala_attention (torch.autograd) runs the same two C-ABI calls: its
     output and gradients equal mala_fwd / mala_bwd bit for bit, here on a
     chunked prefill (the last 100 of 356 positions query all 356 keys) whose
-    inputs come from an upstream torch op, so the gradient flows through it."""
+    inputs come from an upstream torch op, so the gradient flows through it.
+    ``gate_pass`` reaches the backward call."""
     m = lib()
     x = to_dev(W.make_prefill(W.CONFIGS[2], n=356, hq=4, hkv=2, planted=4, seed=11))
     scale = x["scale"]
@@ -359,11 +361,12 @@ def test_autograd_chunked_prefill_matches_direct_calls():
     v = x["v"].clone().requires_grad_()
     do = x["do"][:, :, -100:].contiguous()
     q = (base * 1.0).to(torch.bfloat16).contiguous()        # upstream op
-    o = m.mala_attention(q, k, v, 1e-4, softmax_scale=scale)
+    o = m.mala_attention(q, k, v, 1e-4, softmax_scale=scale, gate_pass=gate_pass)
     o.backward(do)
     qd = q.detach()
     f = m.mala_fwd(qd, k.detach(), v.detach(), 1e-4, softmax_scale=scale)
-    b = m.mala_bwd(qd, k.detach(), v.detach(), f["o"], f["lse"], do, 1e-4, softmax_scale=scale)
+    b = m.mala_bwd(qd, k.detach(), v.detach(), f["o"], f["lse"], do, 1e-4, softmax_scale=scale,
+                   gate_pass=gate_pass)
     torch.cuda.synchronize()
     assert torch.equal(o.detach(), f["o"])
     assert torch.equal(base.grad, b["dq"].float())
