@@ -188,6 +188,26 @@ def test_gate_pass_structured(tau):
         assert np.abs(u - w).max() <= 2e-2 * max(1.0, np.abs(w).max()), n
 
 
+def test_gate_pass_with_fast_grad():
+    """Both flags: the gate pass's decisions and dK/dV with the single-bf16 dS
+    of MALA_FLAG_FAST_GRAD in dQ; same decisions as the fast default path."""
+    m = lib()
+    x = to_dev(W.make_structured(900, hq=4, hkv=1, d=128))
+    f = m.mala_fwd(x["q"], x["k"], x["v"], 1e-2, softmax_scale=x["scale"])
+    a = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], 1e-2,
+                   softmax_scale=x["scale"], want_mask=True, fast_grad=True)
+    b = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], 1e-2,
+                   softmax_scale=x["scale"], want_mask=True, fast_grad=True, gate_pass=True)
+    torch.cuda.synchronize()
+    ma, mb = a["mask"].cpu().numpy(), b["mask"].cpu().numpy()
+    assert int((ma != mb).sum()) <= 2 and (mb == O.SKIPPED).sum() > 0
+    if np.array_equal(ma, mb):
+        assert torch.equal(a["dq"], b["dq"])
+    for n in ("dq", "dk", "dv"):
+        u, w = np64(b[n]), np64(a[n])
+        assert np.abs(u - w).max() <= 1e-2 * max(1.0, np.abs(w).max()), n
+
+
 def test_gate_pass_noncausal_and_f32():
     """Non-causal walks through the gate pass; the flag is ignored for fp32."""
     x = to_dev(W.make_prefill(W.CONFIGS[2], n=160, hq=2, hkv=1, d=128, planted=3))
