@@ -638,8 +638,9 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
     u2 = LSE[qrow0 + q] * 1.4426950408889634f + (s.log2_tau - fast_log2(L));
   }
   // the same test on the raw scores: keep iff max S >= u2 / (scale log2 e)
-  // over a column's legal entries (a column without one has max -inf)
-  const float thr = u2 / s.scale_log2;
+  // over a column's legal entries; the threshold is finite, so a column
+  // without a legal entry (max -inf) is never kept, even at tau = 0
+  const float thr = fmaxf(u2 / s.scale_log2, -3.402823466e38f);
 
   bf16x8 kreg[KPASS];
   const int kc = tid % CPR, krr = tid / CPR;
@@ -697,18 +698,22 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
       }
       // ---- offline gate, Eq. 4, per 16-key column c = keys 16 c .. + 15
       // of the tile: registers 8 (c % 2) .. + 7 of block c / 2
+      uint32_t keep4 = 0u;                             // bit c: column c kept
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         float x = kNegInf;
 #pragma unroll
         for (int r = 0; r < 8; ++r) x = fmaxf(x, sacc[c >> 1][8 * (c & 1) + r]);
-        const bool keep = __builtin_amdgcn_ballot_w64((x >= thr_s) & (x > kNegInf)) != 0;
-        const int col = 4 * j + c;
-        if (keep) word |= 1u << (col & 31);
-        if (mask != nullptr && lane == 0 && col < tc16) {
-          const int kc0 = 16 * col;
-          const bool legal = kc0 < s.nk && (!s.causal || kc0 <= min(q0 + 31, s.nq - 1) + s.offset);
-          if (legal) mask[brow * tc16 + col] = keep ? 1 : 0;
+        if (__builtin_amdgcn_ballot_w64(x >= thr_s) != 0) keep4 |= 1u << c;
+      }
+      word |= keep4 << ((4 * j) & 31);
+      if (mask != nullptr && lane == 0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int col = 4 * j + c, kc0 = 16 * col;
+          const bool legal = col < tc16 && kc0 < s.nk &&
+                             (!s.causal || kc0 <= min(q0 + 31, s.nq - 1) + s.offset);
+          if (legal) mask[brow * tc16 + col] = (int8_t)((keep4 >> c) & 1u);
         }
       }
       if ((j & 7) == 0) {
