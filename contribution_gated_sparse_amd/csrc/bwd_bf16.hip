@@ -1,7 +1,7 @@
 // MALA backward for bf16 inputs on gfx950 (Algorithm 2; Sec. 2.2 "Offline
 // Sparse Probability"; App. A.1 "Fused backward execution").
 //
-// Three kernels:
+// Three kernels by default:
 //   1. bwd_prep:  D_q = rowsum(O o dO) in fp32, and clears the decision bits
 //                 and the kept-tile counters.
 //   2. bwd_dkdv:  key-major. A workgroup owns 128 keys of one KV head (8 waves
@@ -20,6 +20,16 @@
 //                 dQ += dS K on chip. No atomics on dQ. It also counts the
 //                 kept tiles of each 32-row block from the bits.
 // Both kernels see the same decisions, so dQ, dK and dV use one support.
+//
+// With MALA_FLAG_GATE_PASS the decisions come first instead, for inputs on
+// which few tiles are kept:
+//   bwd_gate:     query-major; forms every legal score and writes the
+//                 decision bits (Eq. 4).
+//   bwd_dkdv (gated): one walk per (key block, query head) over the 64-row
+//                 steps that hold a kept tile of the workgroup; nothing is
+//                 staged for the others. fp32 partials per query head.
+//   bwd_dkdv_finalize: sums each KV head's group of partials into dK, dV.
+// bwd_dq is the same kernel in both modes.
 //
 // dS enters the dK and dQ products as a bf16 MFMA operand. dK takes it as one
 // bf16 operand. For dQ it is by default split into hi = bf16(dS) and
