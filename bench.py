@@ -145,7 +145,8 @@ def matched_work(m, W, torch, dev, fbq, fbk, n=8192):
 def profile_structured(tau, m, W, torch, dev):
     """Kernel launches for a profiler on the structured inputs: two passes
     (the first warms up) of the 32K forward + backward, two of the backward
-    with the separate gate pass, then of the 128K decode with 256-key splits
+    with the separate gate pass, two of the forward writing its tile mask and
+    the nested backward on it, then of the 128K decode with 256-key splits
     and with one split per sequence."""
     x = W.make_structured(32768, hq=32, hkv=8, d=128, device=dev, dtype="bf16", with_do=False)
     q, k, v = x["q"], x["k"], x["v"]
@@ -156,6 +157,11 @@ def profile_structured(tau, m, W, torch, dev):
         torch.cuda.synchronize()
     for _ in range(2):   # the backward with the separate gate pass
         m.mala_bwd(q, k, v, f["o"], f["lse"], do, tau, softmax_scale=x["scale"], gate_pass=True)
+        torch.cuda.synchronize()
+    for _ in range(2):   # the forward's tile mask and the backward on its kept tiles
+        f = m.mala_fwd(q, k, v, tau, softmax_scale=x["scale"], want_mask=True)
+        m.mala_bwd(q, k, v, f["o"], f["lse"], do, tau, softmax_scale=x["scale"],
+                   fwd_mask=f["mask"])
         torch.cuda.synchronize()
     del x, q, k, v, do, f
     torch.cuda.empty_cache()
@@ -194,6 +200,9 @@ def structured_section(args, m, W, torch, dev, tiling):
     bo = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
               kept=torch.empty((B, HQ, -(-N // bbq)), dtype=torch.int32, device=dev))
     bg = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v))
+    fn = dict(o=torch.empty_like(q), lse=torch.empty(q.shape[:3], device=dev),
+              mask=torch.empty((B, HQ, -(-N // fbq), -(-N // fbk)), dtype=torch.int8, device=dev))
+    bn = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v))
     vis_f = fwd_tiles(N, N, fbq, fbk) * B * HQ
     vis_b = bwd_tiles(N, N, bbq, bbk) * B * HQ
     pre = {}
@@ -236,6 +245,30 @@ def structured_section(args, m, W, torch, dev, tiling):
         pre[tau_]["gate_pass_vs_default"] = {   # max |difference| / max(1, max |default|)
             n_: float((bg[n_].float() - bo[n_].float()).abs().max()
                       / bo[n_].float().abs().max().clamp_min(1.0)) for n_ in ("dq", "dk", "dv")}
+        # the gate pass as a training step pairs it: the forward also writes its
+        # tile mask, and the backward scores only the tiles the forward kept
+        # (mala_bwd_nested; nested support, Sec. 2.2)
+        def run_nested():
+            m.mala_fwd(q, k, v, tau_, softmax_scale=x["scale"], out=fn, want_mask=True,
+                       want_kept=False)
+            ev[1].record()
+            m.mala_bwd(q, k, v, fn["o"], fn["lse"], do, tau_, softmax_scale=x["scale"], out=bn,
+                       fast_grad=args.fast_grad, fwd_mask=fn["mask"])
+        for _ in range(args.warmup):
+            run_nested()
+        torch.cuda.synchronize()
+        tf = tb = 0.0
+        for _ in range(args.steps):
+            ev[0].record()
+            run_nested()
+            ev[2].record()
+            torch.cuda.synchronize()
+            tf += ev[0].elapsed_time(ev[1])
+            tb += ev[1].elapsed_time(ev[2])
+        pre[tau_]["fwd_with_mask_ms"] = round(tf / args.steps, 3)
+        pre[tau_]["bwd_nested_ms"] = round(tb / args.steps, 3)
+        pre[tau_]["nested_equals_gate_pass"] = all(
+            torch.equal(bn[n_], bg[n_]) for n_ in ("dq", "dk", "dv"))
         # fidelity against tau = 0 (App. C.1/C.3 quantities): omitted normalized
         # mass per row, 1 - Z_R / Z = 1 - exp(z_tau - z_0), bounded by
         # tau / (1 + tau) (Prop. 1), and the relative L2 error of each output row
@@ -272,8 +305,12 @@ def structured_section(args, m, W, torch, dev, tiling):
             (pre[0.0]["fwd_ms"] + pre[0.0]["bwd_ms"])
             / (pre[tau_]["fwd_ms"] + pre[tau_]["bwd_gate_pass_ms"]), 4)
         pre[tau_]["bwd_speedup_gate_pass"] = round(pre[0.0]["bwd_ms"] / pre[tau_]["bwd_gate_pass_ms"], 4)
+        pre[tau_]["speedup_vs_tau0_nested"] = round(
+            (pre[0.0]["fwd_ms"] + pre[0.0]["bwd_ms"])
+            / (pre[tau_]["fwd_with_mask_ms"] + pre[tau_]["bwd_nested_ms"]), 4)
+        pre[tau_]["bwd_speedup_nested"] = round(pre[0.0]["bwd_ms"] / pre[tau_]["bwd_nested_ms"], 4)
     res["prefill_32k"] = {f"tau={t:g}": pre[t] for t in taus}
-    del x, q, k, v, do, fo, bo, bg, g0
+    del x, q, k, v, do, fo, bo, bg, fn, bn, g0
     torch.cuda.empty_cache()
     res["matched_work_8k"] = matched_work(m, W, torch, dev, fbq, fbk)
     torch.cuda.empty_cache()

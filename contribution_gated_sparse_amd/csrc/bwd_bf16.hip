@@ -24,7 +24,10 @@
 // With MALA_FLAG_GATE_PASS the decisions come first instead, for inputs on
 // which few tiles are kept:
 //   bwd_gate:     query-major; forms every legal score and writes the
-//                 decision bits (Eq. 4).
+//                 decision bits (Eq. 4). Given the forward's tile mask
+//                 (mala_bwd_nested), only the scores of the tiles the
+//                 forward kept: the others meet the skip condition
+//                 (nested support, Sec. 2.2).
 //   bwd_dkdv (gated): one walk per (key block, query head) over the 64-row
 //                 steps that hold a kept tile of the workgroup; nothing is
 //                 staged for the others. fp32 partials per query head.
@@ -598,17 +601,19 @@ struct alignas(16) GateSmem {
   bf16 k[2][64][D + 8];   // conflict-free 16-byte row reads (32x32x16 A layout)
 };
 
-template <int D>
+template <int D, bool kNested>
 __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* __restrict__ Q,
                                                           const bf16* __restrict__ K,
                                                           const float* __restrict__ LSE,
                                                           uint32_t* __restrict__ bits,
-                                                          int8_t* __restrict__ mask, int n_qb) {
+                                                          int8_t* __restrict__ mask, int n_qb,
+                                                          const int8_t* __restrict__ fmask) {
   __shared__ GateSmem<D> sm;
   constexpr int KT = D / 16;              // 16-wide k-steps of the QK contraction
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int RPP = 512 / CPR;          // K rows per load pass
   constexpr int KPASS = 64 / RPP;
+  static_assert(kFwdBq == 32 && kFwdBk == 64, "a wave's rows and a K tile are one forward tile");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -631,6 +636,57 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
   };
   const int top_b = top_tile(min(I * 256 + 255, s.nq - 1));
   const int top_w = active ? top_tile(min(q0 + 31, s.nq - 1)) : -1;
+  const size_t brow = (size_t)bh * tr32 + (active ? q0 / kBQ : 0);   // this wave's bit row
+
+  // ---- the tiles to score. By default every legal tile. Nested (Sec. 2.2):
+  // a tile the forward skipped also meets the backward skip condition, so
+  // only the forward's kept tiles are scored; the forward's decision block
+  // r of the workgroup is exactly wave r's 32 rows, and its tile j is key
+  // tile j here. The walk visits the tiles some wave's forward row kept, in
+  // descending order, through a 64-tile window of the workgroup's 8 mask
+  // rows held as ballots: bit i of `la_any` is tile la_base - i kept by some
+  // row, of `la_own` kept by this wave's row.
+  const int ftr = (s.nq + kFwdBq - 1) / kFwdBq, ftc = (s.nk + kFwdBk - 1) / kFwdBk;
+  const int8_t* frow = kNested ? fmask + ((size_t)bh * ftr + 8 * I) * ftc : nullptr;
+  const int nfr = min(8, ftr - 8 * I);     // forward rows of the workgroup (>= 1)
+  uint64_t la_any = 0u, la_own = 0u;
+  int la_base = -1;
+  auto la_fill = [&](int base) {
+    const int t = base - lane;
+    bool any = false, own = false;
+    if (t >= 0) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const bool kept = r < nfr && frow[(size_t)r * ftc + t] == 1;
+        any = any || kept;
+        own = own || (r == w && kept);
+      }
+    }
+    la_any = __builtin_amdgcn_ballot_w64(any);
+    la_own = __builtin_amdgcn_ballot_w64(own);
+    la_base = base;
+  };
+  // the highest tile <= j to visit (-1: none) and whether this wave scores it
+  auto next_tile = [&](int j, bool& own) -> int {
+    if constexpr (!kNested) {
+      own = true;
+      return j;
+    } else {
+      while (j >= 0) {
+        if (j > la_base || j < la_base - 63) la_fill(j);
+        const int sh = la_base - j;
+        const uint64_t m = la_any >> sh;
+        if (m != 0u) {
+          const int jn = j - (int)__builtin_ctzll(m);
+          own = ((la_own >> (la_base - jn)) & 1u) != 0u;
+          return jn;
+        }
+        j = la_base - 64;
+      }
+      own = false;
+      return -1;
+    }
+  };
 
   const auto qrs = make_rsrc(Q + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
   const auto krs = make_rsrc(K + krow0 * D, (uint32_t)((size_t)s.nk * D * 2));
@@ -652,6 +708,23 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
   // without a legal entry (max -inf) is never kept, even at tau = 0
   const float thr = fmaxf(u2 / s.scale_log2, -3.402823466e38f);
 
+  // a column is legal for the wave's rows iff its first key is visible to
+  // the wave's last row
+  auto legal_col = [&](int col) {
+    const int kc0 = 16 * col;
+    return col < tc16 && kc0 < s.nk &&
+           (!s.causal || kc0 <= min(q0 + 31, s.nq - 1) + s.offset);
+  };
+  if constexpr (kNested) {
+    // diagnostic mask: legal columns of the tiles this wave's forward row
+    // did not keep are skipped; the walk writes the others
+    if (mask != nullptr && active) {
+      const int8_t* orow = frow + (size_t)w * ftc;
+      for (int col = lane; col < 4 * (top_w + 1); col += 64)
+        if (legal_col(col) && orow[col >> 2] != 1) mask[brow * tc16 + col] = 0;
+    }
+  }
+
   bf16x8 kreg[KPASS];
   const int kc = tid % CPR, krr = tid / CPR;
   auto load_tile = [&](int j) {
@@ -663,9 +736,11 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
 #pragma unroll
     for (int p = 0; p < KPASS; ++p) store16(&sm.k[buf][p * RPP + krr][8 * kc], kreg[p]);
   };
-  if (top_b >= 0) {
-    load_tile(top_b);
-    store_tile(top_b & 1);
+  bool own = false;
+  int j = top_b >= 0 ? next_tile(top_b, own) : -1;
+  if (j >= 0) {
+    load_tile(j);
+    store_tile(0);
   }
 #pragma unroll
   for (int t = 0; t < KT; ++t) settle(qr[t]);
@@ -673,12 +748,13 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
   settle(thr_s);
   __syncthreads();
 
-  const size_t brow = (size_t)bh * tr32 + (active ? q0 / kBQ : 0);   // this wave's bit row
   uint32_t word = 0u;            // decisions of columns 32 (j / 8) .. + 31 of this wave's row
-  for (int j = top_b; j >= 0; --j) {
-    const int buf = j & 1;
-    if (j > 0) load_tile(j - 1);
-    if (active && j <= top_w) {
+  int buf = 0;
+  while (j >= 0) {
+    bool own_n = false;
+    const int jn = j > 0 ? next_tile(j - 1, own_n) : -1;
+    if (jn >= 0) load_tile(jn);
+    if (active && own && j <= top_w) {
       // ---- S^T[key][query], 64 keys x 32 queries: register r of block kb is
       // key 32 kb + 8 (r / 4) + 4 hf + r % 4
       f32x16 sacc[2];
@@ -719,20 +795,21 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
       word |= keep4 << ((4 * j) & 31);
       if (mask != nullptr && lane == 0) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int col = 4 * j + c, kc0 = 16 * col;
-          const bool legal = col < tc16 && kc0 < s.nk &&
-                             (!s.causal || kc0 <= min(q0 + 31, s.nq - 1) + s.offset);
-          if (legal) mask[brow * tc16 + col] = (int8_t)((keep4 >> c) & 1u);
-        }
-      }
-      if ((j & 7) == 0) {
-        if (lane == 0) bits[brow * words + (j >> 3)] = word;
-        word = 0u;
+        for (int c = 0; c < 4; ++c)
+          if (legal_col(4 * j + c)) mask[brow * tc16 + 4 * j + c] = (int8_t)((keep4 >> c) & 1u);
       }
     }
-    if (j > 0) store_tile((j - 1) & 1);
+    // the word of columns 32 (j / 8) .. is complete once the walk leaves it;
+    // the bit rows start cleared, so only words with a kept column are written
+    if (jn < 0 || (jn >> 3) != (j >> 3)) {
+      if (active && lane == 0 && word != 0u) bits[brow * words + (j >> 3)] = word;
+      word = 0u;
+    }
+    if (jn >= 0) store_tile(buf ^ 1);
     __syncthreads();
+    buf ^= 1;
+    j = jn;
+    own = own_n;
   }
 }
 
@@ -1009,8 +1086,9 @@ size_t bwd_bits_words(const Shape& s) {
 
 hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* d_o, void* dq, void* dk,
-                           void* dv, float* ws_d, uint32_t* ws_bits, float* ws_part, int8_t* mask,
-                           int32_t* kept, hipStream_t st, int stages) {
+                           void* dv, float* ws_d, uint32_t* ws_bits, float* ws_part,
+                           const int8_t* fwd_mask, int8_t* mask, int32_t* kept, hipStream_t st,
+                           int stages) {
   const int rows = s.batch * s.hq * s.nq;
   const size_t nwords = bwd_bits_words(s);
   const size_t nkept = (size_t)s.batch * s.hq * ((s.nq + kBQ - 1) / kBQ);
@@ -1033,12 +1111,16 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
   // MALA_FLAG_GATE_PASS: the gate pass writes the decisions, and dK/dV
   // visits only the steps that hold a kept tile
   const bool gated = (s.flags & MALA_FLAG_GATE_PASS) != 0;
-  auto launch = [&](auto gate, auto dkdv, auto dkdv_gated, auto dqk) {
+  auto launch = [&](auto gate, auto gate_nested, auto dkdv, auto dkdv_gated, auto dqk) {
     if (gated && (stages & kStageMain)) {
-      // decisions, then one walk per (key block, query head), then the sums
-      if (g2.x)
+      // decisions (on the forward's kept tiles only, given its mask), then
+      // one walk per (key block, query head), then the sums
+      if (g2.x && fwd_mask != nullptr)
+        hipLaunchKernelGGL(gate_nested, g2, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
+                           lse, ws_bits, mask, n_qb, fwd_mask);
+      else if (g2.x)
         hipLaunchKernelGGL(gate, g2, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k, lse,
-                           ws_bits, mask, n_qb);
+                           ws_bits, mask, n_qb, (const int8_t*)nullptr);
       const dim3 g1h((unsigned)(g1.x * s.group));
       if (g1h.x)
         hipLaunchKernelGGL(dkdv_gated, g1h, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
@@ -1065,18 +1147,18 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
   const bool split = !(s.flags & MALA_FLAG_FAST_GRAD);
   if (s.d == 128) {
     if (split)
-      launch(bwd_gate_kernel<128>, bwd_dkdv_kernel<128, false>, bwd_dkdv_kernel<128, true>,
-             bwd_dq_kernel<128, true>);
+      launch(bwd_gate_kernel<128, false>, bwd_gate_kernel<128, true>, bwd_dkdv_kernel<128, false>,
+             bwd_dkdv_kernel<128, true>, bwd_dq_kernel<128, true>);
     else
-      launch(bwd_gate_kernel<128>, bwd_dkdv_kernel<128, false>, bwd_dkdv_kernel<128, true>,
-             bwd_dq_kernel<128, false>);
+      launch(bwd_gate_kernel<128, false>, bwd_gate_kernel<128, true>, bwd_dkdv_kernel<128, false>,
+             bwd_dkdv_kernel<128, true>, bwd_dq_kernel<128, false>);
   } else {
     if (split)
-      launch(bwd_gate_kernel<64>, bwd_dkdv_kernel<64, false>, bwd_dkdv_kernel<64, true>,
-             bwd_dq_kernel<64, true>);
+      launch(bwd_gate_kernel<64, false>, bwd_gate_kernel<64, true>, bwd_dkdv_kernel<64, false>,
+             bwd_dkdv_kernel<64, true>, bwd_dq_kernel<64, true>);
     else
-      launch(bwd_gate_kernel<64>, bwd_dkdv_kernel<64, false>, bwd_dkdv_kernel<64, true>,
-             bwd_dq_kernel<64, false>);
+      launch(bwd_gate_kernel<64, false>, bwd_gate_kernel<64, true>, bwd_dkdv_kernel<64, false>,
+             bwd_dkdv_kernel<64, true>, bwd_dq_kernel<64, false>);
   }
   return hipGetLastError();
 }

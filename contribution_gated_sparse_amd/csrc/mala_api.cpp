@@ -190,13 +190,21 @@ mala_status check_decode(const mala_decode_problem* p, mala::DecodeShape* s) {
   return MALA_OK;
 }
 
+// nested: the backward on the forward's retained support (mala_bwd_nested);
+// fwd_mask is the forward's tile mask, read by the bf16 gate pass only.
 mala_status bwd_impl(int stages, const mala_problem* p, const void* q, const void* k,
                      const void* v, const void* o, const float* lse, const void* d_o, void* dq,
                      void* dk, void* dv, void* workspace, size_t ws_bytes, int8_t* tile_mask,
-                     int32_t* kept_tiles, void* stream) {
+                     int32_t* kept_tiles, void* stream, bool nested = false,
+                     const int8_t* fwd_mask = nullptr) {
   mala::Shape s;
   MALA_TRY(check_problem(p, &s));
   const bool rows = s.nq > 0;
+  if (nested) {
+    if (!(s.flags & MALA_FLAG_GATE_PASS))
+      return fail(MALA_ERR_INVALID_ARG, "mala_bwd_nested needs MALA_FLAG_GATE_PASS in p->flags");
+    if (rows && fwd_mask == nullptr) return fail(MALA_ERR_INVALID_ARG, "fwd_tile_mask is NULL");
+  }
   MALA_TRY(check_ptr(q, "q", rows));
   MALA_TRY(check_ptr(k, "k", true));
   MALA_TRY(check_ptr(v, "v", true));
@@ -220,7 +228,7 @@ mala_status bwd_impl(int stages, const mala_problem* p, const void* q, const voi
   hipError_t e;
   if (s.dtype_is_bf16())
     e = mala::launch_bwd_bf16(s, q, k, v, o, lse, d_o, dq, dk, dv, ws_d, ws_bits, ws_part,
-                              tile_mask, kept_tiles, st, stages);
+                              nested ? fwd_mask : nullptr, tile_mask, kept_tiles, st, stages);
   else
     e = mala::launch_bwd_f32(s, (const float*)q, (const float*)k, (const float*)v,
                              (const float*)o, lse, (const float*)d_o, (float*)dq, (float*)dk,
@@ -310,6 +318,15 @@ mala_status mala_bwd(const mala_problem* p, const void* q, const void* k, const 
                      int32_t* kept_tiles, void* stream) {
   return bwd_impl(mala::kStagesAll, p, q, k, v, o, lse, d_o, dq, dk, dv, workspace, ws_bytes,
                   tile_mask, kept_tiles, stream);
+}
+
+mala_status mala_bwd_nested(const mala_problem* p, const void* q, const void* k, const void* v,
+                            const void* o, const float* lse, const void* d_o,
+                            const int8_t* fwd_tile_mask, void* dq, void* dk, void* dv,
+                            void* workspace, size_t ws_bytes, int8_t* tile_mask,
+                            int32_t* kept_tiles, void* stream) {
+  return bwd_impl(mala::kStagesAll, p, q, k, v, o, lse, d_o, dq, dk, dv, workspace, ws_bytes,
+                  tile_mask, kept_tiles, stream, true, fwd_tile_mask);
 }
 
 mala_status mala_bwd_stage(int32_t stage, const mala_problem* p, const void* q, const void* k,

@@ -99,8 +99,9 @@ hipError_t launch_fwd_f32(const Shape& s, const float* q, const float* k, const 
 
 hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* d_o, void* dq, void* dk,
-                           void* dv, float* ws_d, uint32_t* ws_bits, float* ws_part, int8_t* mask,
-                           int32_t* kept, hipStream_t st, int stages);
+                           void* dv, float* ws_d, uint32_t* ws_bits, float* ws_part,
+                           const int8_t* fwd_mask, int8_t* mask, int32_t* kept, hipStream_t st,
+                           int stages);
 hipError_t launch_bwd_f32(const Shape& s, const float* q, const float* k, const float* v,
                           const float* o, const float* lse, const float* d_o, float* dq, float* dk,
                           float* dv, float* ws_d, uint32_t* ws_bits, int8_t* mask, int32_t* kept,

@@ -53,7 +53,7 @@ class DecodeProblem(ctypes.Structure):
 DECODE_SPLIT_AUTO = -1
 
 EXPORTS = ("mala_get_tiling", "mala_fwd", "mala_bwd_workspace_size", "mala_bwd",
-           "mala_bwd_stage", "mala_decode_workspace_size", "mala_decode_split_keys", "mala_decode",
+           "mala_bwd_nested", "mala_bwd_stage", "mala_decode_workspace_size", "mala_decode_split_keys", "mala_decode",
            "mala_decode_stage", "mala_last_error", "mala_version")
 BWD_PREP, BWD_DKDV, BWD_DQ = 0, 1, 2
 DECODE_SPLIT, DECODE_COMBINE = 0, 1
@@ -84,6 +84,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mala_bwd_workspace_size.restype = sz
     lib.mala_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
     lib.mala_bwd.restype = i32
+    lib.mala_bwd_nested.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    lib.mala_bwd_nested.restype = i32
     lib.mala_bwd_stage.argtypes = [i32, P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
     lib.mala_bwd_stage.restype = i32
     lib.mala_decode_stage.argtypes = [i32, DP, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
@@ -179,14 +181,30 @@ def mala_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float, caus
 def mala_bwd(q, k, v, o, lse, d_o, tau: float, causal: bool = True,
              softmax_scale: Optional[float] = None, want_mask: bool = False,
              want_kept: bool = True, out: Optional[dict] = None, fast_grad: bool = False,
-             gate_pass: bool = False, stages=None, events=None) -> dict:
+             gate_pass: bool = False, stages=None, events=None,
+             fwd_mask: Optional[torch.Tensor] = None) -> dict:
     """Backward -> dict(dq, dk, dv, mask, kept). ``gate_pass``: take the
     decisions in a separate score pass so that dK/dV visits only the steps
-    with a kept tile (MALA_FLAG_GATE_PASS). ``stages``: run only these stages
-    (BWD_PREP, BWD_DKDV, BWD_DQ) through mala_bwd_stage; ``events``: optional
-    list of torch.cuda.Event, one recorded after each stage run."""
+    with a kept tile (MALA_FLAG_GATE_PASS). ``fwd_mask``: the forward's tile
+    mask (``mala_fwd(..., want_mask=True)["mask"]``) for the same inputs; the
+    score pass then forms only the scores of the tiles the forward kept
+    (mala_bwd_nested, which runs in the gate-pass mode, so ``gate_pass`` is
+    implied). ``stages``: run only these stages (BWD_PREP, BWD_DKDV, BWD_DQ)
+    through mala_bwd_stage; ``events``: optional list of torch.cuda.Event,
+    one recorded after each stage run."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (d_o, "d_o")):
         _dev(t, n)
+    if fwd_mask is not None:
+        _dev(fwd_mask, "fwd_mask")
+        if fwd_mask.dtype != torch.int8:
+            raise TypeError("fwd_mask must be int8 (the forward's tile mask)")
+        fb, fk, _ = mala_get_tiling(OP_FWD)
+        want = (q.shape[0], q.shape[1], -(-q.shape[2] // fb), -(-k.shape[2] // fk))
+        if tuple(fwd_mask.shape) != want:
+            raise ValueError(f"fwd_mask has shape {tuple(fwd_mask.shape)}, expected {want}")
+        if stages is not None or events is not None:
+            raise ValueError("fwd_mask runs the whole backward: no stages or events")
+        gate_pass = True
     p = make_problem(q, k, tau, causal, softmax_scale,
                      (MALA_FLAG_FAST_GRAD if fast_grad else 0) | (MALA_FLAG_GATE_PASS if gate_pass else 0))
     lib = load_library()
@@ -211,7 +229,9 @@ def mala_bwd(q, k, v, o, lse, d_o, tau: float, causal: bool = True,
         kept = torch.empty((p.batch, p.n_q_heads, tr), dtype=torch.int32, device=q.device)
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(d_o), _ptr(dq),
             _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _ptr(mask), _ptr(kept), _stream())
-    if stages is None and events is None:
+    if fwd_mask is not None:
+        _check(lib.mala_bwd_nested(*args[:7], _ptr(fwd_mask), *args[7:]))
+    elif stages is None and events is None:
         _check(lib.mala_bwd(*args))
     else:
         for n, stg in enumerate(stages if stages is not None else (BWD_PREP, BWD_DKDV, BWD_DQ)):

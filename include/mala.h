@@ -173,6 +173,34 @@ mala_status mala_bwd(const mala_problem* p, const void* q, const void* k, const 
                      int8_t* tile_mask, int32_t* kept_tiles, void* stream);
 
 /*
+ * Backward on the forward's retained support (Sec. 2.2, "Offline Sparse
+ * Probability": the finalized normalizer is at least every partial one the
+ * forward tested against, so with the same tile partition a tile the forward
+ * skipped also meets the backward skip condition, and the backward support
+ * nests in the forward's). This is mala_bwd in the MALA_FLAG_GATE_PASS mode
+ * whose score pass forms only the scores of the forward's kept tiles: the
+ * cost of the decisions then follows the forward's kept fraction instead of
+ * the number of legal tiles.
+ *   fwd_tile_mask  int8 [B,Hq,Tr,Tc] (device) with the forward tiling
+ *                  (mala_get_tiling(MALA_OP_FWD)): the tile_mask mala_fwd
+ *                  wrote for the same problem, q, k and v. A tile is scored
+ *                  iff its entry is 1; its contents are not checked.
+ *   the other arguments as for mala_bwd; p->flags must include
+ *                  MALA_FLAG_GATE_PASS (else MALA_ERR_INVALID_ARG), and the
+ *                  workspace is mala_bwd_workspace_size(p).
+ * The decisions are those of mala_bwd with the same flags except for a tile
+ * that the gate pass would keep while the forward skipped it, which exact
+ * arithmetic rules out: both margins then lie within fp32 rounding of the
+ * threshold. For MALA_F32 the forward mask is not read and the call is
+ * mala_bwd.
+ */
+mala_status mala_bwd_nested(const mala_problem* p, const void* q, const void* k, const void* v,
+                            const void* o, const float* lse, const void* d_o,
+                            const int8_t* fwd_tile_mask, void* dq, void* dk, void* dv,
+                            void* workspace, size_t ws_bytes, int8_t* tile_mask,
+                            int32_t* kept_tiles, void* stream);
+
+/*
  * The backward as three stages, for callers that schedule or time them
  * separately. Calling MALA_BWD_PREP, MALA_BWD_DKDV, MALA_BWD_DQ in this order
  * on one stream with the same arguments and workspace is mala_bwd.

@@ -39,6 +39,10 @@ int main(void) {
   CHECK(mala_fwd(&p, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == MALA_ERR_INVALID_ARG);
   CHECK(strstr(mala_last_error(), "tau") != NULL);
   CHECK(mala_fwd(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == MALA_ERR_INVALID_ARG);
+  p.tau = 1e-4f;                                   /* the nested backward needs the flag */
+  CHECK(mala_bwd_nested(&p, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0,
+                        NULL, NULL, NULL) == MALA_ERR_INVALID_ARG);
+  CHECK(strstr(mala_last_error(), "MALA_FLAG_GATE_PASS") != NULL);
 
   mala_decode_problem d;
   memset(&d, 0, sizeof d);

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
     assert set(names) == set(M.EXPORTS)
@@ -125,6 +125,32 @@ def test_backward_workspace(lib):
     st = lib.mala_bwd(ctypes.byref(p), g, g, g, g, g, g, g, g, g, ctypes.c_void_p(addr + 16),
                       need, None, None, None)
     assert st == M.MALA_ERR_INVALID_ARG and "256-byte" in lib.mala_last_error().decode()
+
+
+def test_nested_backward_arguments(lib):
+    """mala_bwd_nested runs in the gate-pass mode and needs the forward's
+    mask; both are checked before anything is enqueued, and its workspace is
+    the gate-pass one."""
+    buf = (ctypes.c_char * 1024)()
+    addr = ctypes.addressof(buf)
+    addr += (-addr) % 256
+    g = ctypes.c_void_p(addr)
+    fm = ctypes.c_void_p(addr + 1)          # a byte mask needs no alignment
+    p = prob()
+    need = lib.mala_bwd_workspace_size(ctypes.byref(p))
+    st = lib.mala_bwd_nested(ctypes.byref(p), g, g, g, g, g, g, fm, g, g, g, g, need, None, None,
+                             None)
+    assert st == M.MALA_ERR_INVALID_ARG and "MALA_FLAG_GATE_PASS" in lib.mala_last_error().decode()
+    p = prob(flags=M.MALA_FLAG_GATE_PASS)
+    need_gp = lib.mala_bwd_workspace_size(ctypes.byref(p))
+    st = lib.mala_bwd_nested(ctypes.byref(p), g, g, g, g, g, g, None, g, g, g, g, need_gp, None,
+                             None, None)
+    assert st == M.MALA_ERR_INVALID_ARG and "fwd_tile_mask" in lib.mala_last_error().decode()
+    st = lib.mala_bwd_nested(ctypes.byref(p), g, g, g, g, g, g, fm, g, g, g, g, need_gp - 1, None,
+                             None, None)
+    assert st == M.MALA_ERR_WORKSPACE
+    assert lib.mala_bwd_nested(None, g, g, g, g, g, g, fm, g, g, g, g, need_gp, None, None,
+                               None) == M.MALA_ERR_INVALID_ARG
 
 
 def dprob(**kw):

@@ -116,7 +116,8 @@ def test_gate_pass_full_size_structured():
     """MALA_FLAG_GATE_PASS at the bench's structured 32K workload (sink keys,
     local band, retrieval keys; most tiles skipped): decisions and dQ of
     sampled blocks against the oracle, the decision masks against the default
-    backward's, and the whole dK and dV against the default backward's."""
+    backward's, and the whole dK and dV against the default backward's; the
+    nested call (the forward's kept tiles only) against the gate pass."""
     m = lib()
     x = W.make_structured(32768, hq=32, hkv=8, d=128, device=DEV, dtype="bf16", with_do=False)
     q, k, v, scale = x["q"], x["k"], x["v"], x["scale"]
@@ -184,6 +185,22 @@ def test_gate_pass_full_size_structured():
         scaled = float(np.abs(a - b_).max() / max(1.0, np.abs(b_).max()))
         fro = float(np.linalg.norm(a - b_) / max(np.linalg.norm(b_), 1e-30))
         assert scaled <= 2e-2 and fro <= 1e-2, f"{n_}: {scaled:.3e} {fro:.3e}"
+
+    # on the forward's kept tiles only (mala_bwd_nested): the gate pass's
+    # decisions restricted to those tiles, which exact arithmetic makes the
+    # same decisions, and then the same gradients bit for bit
+    gc = m.mala_bwd(q, k, v, g["o"], g["lse"], do, TAU, softmax_scale=scale, want_mask=True,
+                    fwd_mask=g["mask"])
+    torch.cuda.synchronize()
+    mc = gc["mask"].cpu().numpy()
+    up = np.repeat(np.repeat(g["mask"].cpu().numpy(), fbq // bbq, axis=2), fbk // bbk,
+                   axis=3)[:, :, :mb.shape[2], :mb.shape[3]]
+    assert np.array_equal(mc, np.where((mb == O.KEPT) & (up != O.KEPT), O.SKIPPED, mb))
+    assert int((mc != mb).sum()) <= 16, f"{int((mc != mb).sum())} decisions differ"
+    assert np.array_equal(gc["kept"].cpu().numpy(), (mc == O.KEPT).sum(-1))
+    if np.array_equal(mb, mc):
+        for n_ in ("dq", "dk", "dv"):
+            assert torch.equal(gb[n_], gc[n_]), n_
 
 
 @pytest.mark.parametrize("step,split_keys", [(0, 0), (63, 0), (0, -1)])

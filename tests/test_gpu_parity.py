@@ -31,13 +31,14 @@ def to_dev(x):
 
 
 def check_backward(x, tau, g_fwd, r_fwd, causal=True, qblocks=None, key_rows=None,
-                   gate_pass=False):
+                   gate_pass=False, fwd_mask=None):
     m = lib()
     q, k, v, do = x["q"], x["k"], x["v"], x["do"]
     kind = dtype_name(q)
     _, (bq, bk, _), _ = tiling()
     g = m.mala_bwd(q, k, v, g_fwd["o"], g_fwd["lse"], do, tau, causal=causal,
-                   softmax_scale=x["scale"], want_mask=True, gate_pass=gate_pass)
+                   softmax_scale=x["scale"], want_mask=True, gate_pass=gate_pass,
+                   fwd_mask=fwd_mask)
     torch.cuda.synchronize()
     gmask = g["mask"].cpu().numpy()
     r = O.mala_bwd(np64(q), np64(k), np64(v), r_fwd["o"], r_fwd["lse"], np64(do), tau,
@@ -186,6 +187,12 @@ def test_gate_pass_structured(tau):
     for n in ("dq", "dk", "dv"):
         u, w = np64(gb[n]), np64(ref[n])
         assert np.abs(u - w).max() <= 2e-2 * max(1.0, np.abs(w).max()), n
+    # on the forward's kept tiles only: the same decisions and gradients
+    _, a2, b2, want = nested_vs_gate_pass(x, tau, g["mask"])
+    if np.array_equal(a2["mask"].cpu().numpy(), want):
+        for n in ("dq", "dk", "dv"):
+            assert torch.equal(a2[n], b2[n]), n
+    assert int((a2["mask"].cpu().numpy() != want).sum()) <= 2
 
 
 def test_gate_pass_with_fast_grad():
@@ -217,6 +224,112 @@ def test_gate_pass_noncausal_and_f32():
     x = to_dev(W.make_prefill(W.CONFIGS[1], n=150, hq=4, hkv=2, d=64, planted=4))
     g, r, _ = check_forward(x, 1.0, max_ties=2)
     check_backward(x, 1.0, g, r, gate_pass=True)
+
+
+def expand_fwd(fmask, shape):
+    """The forward tile mask on the backward partition (each backward tile
+    lies in one forward tile)."""
+    (fbq, fbk, _), (bbq, bbk, _), _ = tiling()
+    up = np.repeat(np.repeat(fmask, fbq // bbq, axis=2), fbk // bbk, axis=3)
+    return up[:, :, :shape[2], :shape[3]]
+
+
+def nested_vs_gate_pass(x, tau, fwd_mask, causal=True):
+    """mala_bwd_nested with ``fwd_mask`` against the gate pass on the same
+    inputs: its decisions are the gate pass's restricted to the forward's
+    kept tiles, bit for bit; returns both results and the expected mask."""
+    m = lib()
+    f = m.mala_fwd(x["q"], x["k"], x["v"], tau, causal=causal, softmax_scale=x["scale"])
+    a = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], tau, causal=causal,
+                   softmax_scale=x["scale"], want_mask=True, gate_pass=True)
+    b = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], tau, causal=causal,
+                   softmax_scale=x["scale"], want_mask=True, fwd_mask=fwd_mask)
+    torch.cuda.synchronize()
+    ma, mb = a["mask"].cpu().numpy(), b["mask"].cpu().numpy()
+    up = expand_fwd(fwd_mask.cpu().numpy(), ma.shape)
+    want = np.where((ma == O.KEPT) & (up != O.KEPT), O.SKIPPED, ma)
+    assert np.array_equal(mb, want), f"{int((mb != want).sum())} decisions differ"
+    assert np.array_equal(b["kept"].cpu().numpy(), (mb == O.KEPT).sum(-1))
+    return f, a, b, want
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("tau", [0.0, 1e-4, 1.0, 100.0])
+def test_nested_shapes(shape, tau):
+    """mala_bwd_nested on the forward's own mask: the oracle's bar, support
+    nested in the forward's, and the gate pass's decisions and gradients
+    wherever the two agree (exact arithmetic makes them agree everywhere)."""
+    b, hq, hkv, nq, nk, d = shape
+    x = W.make_prefill(W.CONFIGS[2], n=nk, hq=hq, hkv=hkv, d=d, batch=b, planted=4, seed=7 + nq)
+    if nq < nk:
+        x["q"] = x["q"][:, :, nk - nq:].contiguous()
+        x["do"] = x["do"][:, :, nk - nq:].contiguous()
+    x = to_dev(x)
+    print(f"[nested] shape={shape} tau={tau}", flush=True)
+    g, r, _ = check_forward(x, tau, max_ties=4)
+    gb, _, _ = check_backward(x, tau, g, r, fwd_mask=g["mask"])
+    check_nesting(g["mask"].cpu().numpy(), gb["mask"].cpu().numpy())
+    _, a, b_, want = nested_vs_gate_pass(x, tau, g["mask"])
+    if np.array_equal(a["mask"].cpu().numpy(), want):
+        for n in ("dq", "dk", "dv"):
+            assert torch.equal(a[n], b_[n]), n
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("density", [0.0, 0.03, 0.5, 1.0])
+def test_nested_arbitrary_forward_masks(causal, density):
+    """The walk over the forward's kept tiles with masks the forward would not
+    write (sparse, dense, empty; more than 64 key tiles, so the look-ahead
+    window moves): decisions are exactly the gate pass's on the given tiles,
+    and the gradients are the oracle's on that support."""
+    nq, nk = 300, 4700
+    x = W.make_prefill(W.CONFIGS[2], n=nk, hq=2, hkv=1, d=128, planted=4, seed=11)
+    x["q"] = x["q"][:, :, nk - nq:].contiguous()
+    x["do"] = x["do"][:, :, nk - nq:].contiguous()
+    x = to_dev(x)
+    tau = 1e-4
+    print(f"[nested mask] causal={causal} density={density}", flush=True)
+    fm = lib().mala_fwd(x["q"], x["k"], x["v"], tau, causal=causal, softmax_scale=x["scale"],
+                        want_mask=True)["mask"].cpu().numpy()
+    rng = np.random.default_rng(int(1000 * density) + causal)
+    rand = np.where(rng.random(fm.shape) < density, O.KEPT, O.SKIPPED).astype(np.int8)
+    fm = np.where(fm == O.NOT_VISITED, fm, rand)
+    f, a, b, want = nested_vs_gate_pass(x, tau, torch.from_numpy(fm).to(DEV), causal=causal)
+    if density == 0.0:
+        assert not (want == O.KEPT).any()
+        for n in ("dq", "dk", "dv"):
+            assert not b[n].any(), n
+    _, (bq, bk, _), _ = tiling()
+    r = O.mala_bwd(np64(x["q"]), np64(x["k"]), np64(x["v"]), np64(f["o"]), np64(f["lse"]),
+                   np64(x["do"]), tau, x["scale"], causal, bq, bk, replay=want, band=np.inf,
+                   o_storage="bf16")
+    assert np.array_equal(r["mask"], want)
+    for n in ("dq", "dk", "dv"):
+        compare_values(n, np64(b[n]), r[n], "bf16")
+
+
+def test_nested_noncausal_fast_grad_and_f32():
+    """The nested call with MALA_FLAG_FAST_GRAD, non-causal, and for fp32
+    (where the forward mask is not read and the call is the backward)."""
+    m = lib()
+    x = to_dev(W.make_structured(900, hq=4, hkv=1, d=128))
+    f = m.mala_fwd(x["q"], x["k"], x["v"], 1e-2, softmax_scale=x["scale"], want_mask=True)
+    a = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], 1e-2,
+                   softmax_scale=x["scale"], want_mask=True, fast_grad=True, gate_pass=True)
+    b = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], 1e-2,
+                   softmax_scale=x["scale"], want_mask=True, fast_grad=True, fwd_mask=f["mask"])
+    torch.cuda.synchronize()
+    if torch.equal(a["mask"], b["mask"]):
+        for n in ("dq", "dk", "dv"):
+            assert torch.equal(a[n], b[n]), n
+    assert int((a["mask"] != b["mask"]).sum()) <= 2
+    x = to_dev(W.make_prefill(W.CONFIGS[2], n=160, hq=2, hkv=1, d=128, planted=3))
+    for tau in (0.0, 0.5, 50.0):
+        g, r, _ = check_forward(x, tau, causal=False, max_ties=4)
+        check_backward(x, tau, g, r, causal=False, fwd_mask=g["mask"])
+    x = to_dev(W.make_prefill(W.CONFIGS[1], n=150, hq=4, hkv=2, d=64, planted=4))
+    g, r, _ = check_forward(x, 1.0, max_ties=2)
+    check_backward(x, 1.0, g, r, fwd_mask=g["mask"])
 
 
 # ------------------------------------------------------------- decode
@@ -372,7 +485,8 @@ def test_autograd_chunked_prefill_matches_direct_calls(gate_pass):
     output and gradients equal mala_fwd / mala_bwd bit for bit, here on a
     chunked prefill (the last 100 of 356 positions query all 356 keys) whose
     inputs come from an upstream torch op, so the gradient flows through it.
-    ``gate_pass`` reaches the backward call."""
+    With ``gate_pass`` the forward also writes its tile mask and the backward
+    is mala_bwd_nested on it."""
     m = lib()
     x = to_dev(W.make_prefill(W.CONFIGS[2], n=356, hq=4, hkv=2, planted=4, seed=11))
     scale = x["scale"]
@@ -384,9 +498,9 @@ def test_autograd_chunked_prefill_matches_direct_calls(gate_pass):
     o = m.mala_attention(q, k, v, 1e-4, softmax_scale=scale, gate_pass=gate_pass)
     o.backward(do)
     qd = q.detach()
-    f = m.mala_fwd(qd, k.detach(), v.detach(), 1e-4, softmax_scale=scale)
+    f = m.mala_fwd(qd, k.detach(), v.detach(), 1e-4, softmax_scale=scale, want_mask=gate_pass)
     b = m.mala_bwd(qd, k.detach(), v.detach(), f["o"], f["lse"], do, 1e-4, softmax_scale=scale,
-                   gate_pass=gate_pass)
+                   fwd_mask=f["mask"])
     torch.cuda.synchronize()
     assert torch.equal(o.detach(), f["o"])
     assert torch.equal(base.grad, b["dq"].float())
