@@ -65,16 +65,22 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int rows, int d, const bf
     for (size_t i = gtid; i < nkept; i += nthr) kept[i] = 0;
   if (mask != nullptr)
     for (size_t i = gtid; i < nmask; i += nthr) mask[i] = -1;   // not a legal tile
-  // one wave per row: 64 lanes x (d/64) elements
+  // 16-byte chunks: d / 8 consecutive lanes per row (a power of two that
+  // divides 64, so a row never straddles two waves' ranges)
   const int lane = threadIdx.x & 63;
+  const int cpr = d >> 3;
+  const size_t nchunks = (size_t)rows * cpr;
   const size_t wave = gtid >> 6, nwave = nthr >> 6;
-  for (size_t r = wave; r < (size_t)rows; r += nwave) {
+  for (size_t base = wave * 64; base < nchunks; base += nwave * 64) {
+    const size_t c = base + lane;
     float acc = 0.f;
-    for (int e = lane; e < d; e += 64)
-      acc += (float)O[r * d + e] * (float)dO[r * d + e];
+    if (c < nchunks) {
+      const bf16x8 o = load16(O + 8 * c), g = load16(dO + 8 * c);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (lane == 0) Dq[r] = acc;
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)g[e], acc);
+    }
+    for (int off = cpr >> 1; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (c < nchunks && (lane & (cpr - 1)) == 0) Dq[c / cpr] = acc;
   }
 }
 
@@ -103,12 +109,83 @@ struct alignas(16) DkdvSmem {
   uint32_t keep[2];             // [buf] bit w / 8 + w: wave w kept its first / second half
 };
 
+// Gated walks (MALA_FLAG_GATE_PASS): a key block whose KV head's group of
+// query heads keeps at most kGroupWalkPairs (head, 64-row step) pairs is
+// walked by one workgroup over all the group's heads, which writes dK and dV
+// directly; a block with more is walked per head in parallel, into fp32
+// partials that the finalize kernel sums. Both kernels take the choice from
+// the same count of the decision bits.
+constexpr int kGroupWalkPairs = 32;
+
+// Kept (query head, 64-row step) pairs of KV head (b, hk)'s group for key
+// block J (128 keys): a pair is kept when either 32-row half of the step
+// holds a kept tile of the block, i.e. byte J of bit row 2 i or 2 i + 1 is
+// nonzero. The workgroup's waves add their counts through red (one int per
+// wave); every thread returns the total.
+__device__ int group_kept_pairs(const Shape& s, const uint8_t* bit_bytes, int b, int hk, int J,
+                                int i_start, int* red) {
+  const int tr32 = (s.nq + kBQ - 1) / kBQ, tr64 = (s.nq + 63) / 64;
+  const uint32_t rstride = (uint32_t)(((s.nk + kBK - 1) / kBK + 31) / 32) * 4u;
+  const int nsteps = tr64 - i_start;
+  const int pairs = s.group * nsteps;
+  const auto rs = make_rsrc(bit_bytes + ((size_t)b * s.hq + (size_t)hk * s.group) * tr32 * rstride + J,
+                            (uint32_t)(s.group * tr32) * rstride - (uint32_t)J);
+  // four pairs per thread and pass, their loads issued together; a pair
+  // past the group reads row 0 and is not counted
+  int c = 0;
+  const int bd = (int)blockDim.x;
+  for (int t0 = (int)threadIdx.x; t0 < pairs; t0 += 4 * bd) {
+    uint32_t lo[4], hi[4];
+    bool in[4], two[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + u * bd;
+      in[u] = t < pairs;
+      const int tt = in[u] ? t : 0;
+      const int hs = tt / nsteps, i = i_start + tt % nsteps;
+      const uint32_t r = (uint32_t)(hs * tr32 + 2 * i);
+      lo[u] = __builtin_amdgcn_raw_buffer_load_b8(rs, r * rstride, 0, 0);
+      hi[u] = __builtin_amdgcn_raw_buffer_load_b8(rs, (r + 1) * rstride, 0, 0);
+      two[u] = 2 * i + 1 < tr32;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) c += in[u] && (lo[u] | (two[u] ? hi[u] : 0u)) != 0u ? 1 : 0;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+  __syncthreads();
+  int total = 0;
+  for (int k = 0; k < (int)(blockDim.x >> 6); ++k) total += red[k];
+  __syncthreads();
+  return total;
+}
+
+// First 64-row step with a legal entry for the first key of 128-key block J.
+__device__ __forceinline__ int block_first_step(const Shape& s, int J) {
+  if (!s.causal) return 0;
+  const int need = J * 128 - s.offset;
+  return need <= 0 ? 0 : need / 64;
+}
+
+// The gated walks' plan: kept pairs of every (batch, KV head, 128-key block),
+// one workgroup (one wave) each; plan[(b * Hkv + hk) * n_kb + J].
+__global__ __launch_bounds__(64) void bwd_plan_kernel(Shape s, const uint32_t* __restrict__ bits,
+                                                      int32_t* __restrict__ plan) {
+  __shared__ int red[1];
+  const int n_kb = (s.nk + 127) / 128;
+  const int J = (int)(blockIdx.x % n_kb), bkv = (int)(blockIdx.x / n_kb);
+  const int c = group_kept_pairs(s, reinterpret_cast<const uint8_t*>(bits), bkv / s.hkv,
+                                 bkv % s.hkv, J, block_first_step(s, J), red);
+  if (threadIdx.x == 0) plan[blockIdx.x] = c;
+}
+
 template <int D, bool kGated>
 __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
     Shape s, const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dq,
     bf16* __restrict__ dK, bf16* __restrict__ dV, uint32_t* __restrict__ bits,
-    int8_t* __restrict__ mask, float* __restrict__ part) {
+    int8_t* __restrict__ mask, float* __restrict__ part, const int32_t* __restrict__ plan) {
   __shared__ DkdvSmem<D> sm;
   constexpr int ST = DkdvSmem<D>::kStride;
   constexpr int KS = D / 32;      // 32-wide k-steps over d (16x16x32 MFMA)
@@ -127,6 +204,16 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int rem = (int)(blockIdx.x % (bk_count * nsub));
   const int bkv = rem / nsub, hsub = rem % nsub;
   const int b = bkv / s.hkv, hk = bkv % s.hkv;
+  // gated: a block walked per head (into partials) or by one workgroup over
+  // the group; which workgroup takes a group walk rotates with the block, so
+  // that the walking ones spread over the XCDs (the dispatcher deals
+  // consecutive workgroups to consecutive XCDs)
+  bool gsplit = false;
+  if constexpr (kGated) {
+    const int n_kb = (s.nk + 127) / 128;
+    gsplit = plan[bkv * n_kb + J] > kGroupWalkPairs;
+    if (!gsplit && hsub != (J + bkv) % s.group) return;
+  }
   const int kw0 = J * 128 + w * kBK;                   // this wave's first key
   const size_t krow0 = ((size_t)b * s.hkv + hk) * (size_t)s.nk;
   const int tr32 = (s.nq + kBQ - 1) / kBQ;
@@ -154,13 +241,8 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
     for (int r = 0; r < 4; ++r) { dk[db][r] = 0.f; dv[db][r] = 0.f; }
 
-  // first 64-row step with a legal entry for the block's first key
-  int i_start = 0;
-  if (s.causal) {
-    const int need = J * 128 - s.offset;
-    i_start = need <= 0 ? 0 : need / 64;
-  }
-  const int total = (kGated ? 1 : s.group) * (tr64 - i_start);   // (head, 64-row step) pairs
+  const int i_start = block_first_step(s, J);   // first 64-row step with a legal entry
+  const int total = s.group * (tr64 - i_start);   // (head, 64-row step) pairs of the default walk
 
   // staging: 64 rows x CPR chunks of Q and of dO, NPASS chunks each per thread.
   // The buffer resources span one query head (rows past N_q read as zeros)
@@ -405,132 +487,191 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   } else {
     // ---- decisions from the gate pass: only steps that hold a kept tile of
     // this workgroup are staged; a wave forms scores only for its kept tiles.
-    // Step t of the walk is head hk * group + t / nsteps, row step
-    // i_start + t % nsteps.
+    // A light block is one walk over the group's heads, a heavy one a walk
+    // per head (kGroupWalkPairs). Step t of a walk over nh heads from h0 is
+    // head h0 + t / nsteps, row step i_start + t % nsteps.
     const int nsteps = tr64 - i_start;
-    auto step_hi = [&](int t, int& hh, int& ii) {
-      hh = hk * s.group + hsub + t / nsteps;
-      ii = i_start + t % nsteps;
-    };
-    // look-ahead over 64 steps at a time: lane k holds the two decision
-    // bytes of step la_base + k, and bit k of la says whether any is set
-    uint64_t la = 0u;
-    int la_base = -64;
-    uint32_t la_val = 0u;
+    const int h0 = hk * s.group + (gsplit ? hsub : 0);
+    const int nh = gsplit ? 1 : s.group;
+    const int tot = nh * nsteps;
+    // decision bytes J of the walk's bit rows; bytes past the last row read 0
+    const uint32_t rstride = (uint32_t)words * 4u;
+    const auto drs = make_rsrc(bit_bytes + ((size_t)b * s.hq + h0) * tr32 * rstride + J,
+                               (uint32_t)(nh * tr32) * rstride - (uint32_t)J);
+    // look-ahead: the bytes of 512 steps are fetched at once; lane k of
+    // window x holds the two bytes (rows 2 i, 2 i + 1) of step
+    // la_base + 64 x + k, so a walk waits on the bit rows once per 512 steps
+    uint32_t la_val[8];
+    int la_base = -512;
     auto la_fill = [&](int t0) {
-      const int t = t0 + lane;
-      uint32_t v = 0u;
-      if (t < total) {
-        int hh, ii;
-        step_hi(t, hh, ii);
-        const size_t row = ((size_t)b * s.hq + hh) * tr32 + 2 * ii;
-        v = bit_bytes[row * (size_t)words * 4 + J];
-        if (2 * ii + 1 < tr32) v |= (uint32_t)bit_bytes[(row + 1) * (size_t)words * 4 + J] << 8;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int t = t0 + 64 * x + lane;
+        const int hs = t / nsteps, i = i_start + t % nsteps;
+        const uint32_t r = (uint32_t)(hs * tr32 + 2 * i);
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b8(drs, r * rstride, 0, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b8(drs, (r + 1) * rstride, 0, 0);
+        la_val[x] = lo | (2 * i + 1 < tr32 ? hi << 8 : 0u);
       }
-      la_val = v;
-      la = __builtin_amdgcn_ballot_w64(v != 0u);
       la_base = t0;
     };
-    // the first step at or after t with a kept tile (total if none) and its bytes
+    // the first step at or after t with a kept tile (tot if none) and its bytes
     auto next_kept = [&](int t, uint32_t& v) {
-      while (t < total) {
-        if (t >= la_base + 64) la_fill(t);
-        const uint64_t m = la >> (t - la_base);
+      while (t < tot) {
+        if (t >= la_base + 512) la_fill(t);
+        const int off = t - la_base, x = off >> 6, bit = off & 63;
+        uint32_t sel = la_val[0];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) sel = x == k ? la_val[k] : sel;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(sel != 0u) >> bit;
         if (m != 0u) {
-          t += (int)__builtin_ctzll(m);
-          v = __builtin_amdgcn_readlane(la_val, t - la_base);
-          return t;
+          const int adv = (int)__builtin_ctzll(m);
+          v = __builtin_amdgcn_readlane(sel, bit + adv);
+          return t + adv < tot ? t + adv : tot;
         }
-        t = la_base + 64;
+        t = la_base + 64 * (x + 1);
       }
       v = 0u;
-      return total;
+      return tot;
     };
 
-    uint32_t v;
+    // a step's Q and dO rows, z and D, in registers: two sets, so that the
+    // loads of the step after next are in flight while a step is processed
+    // (a sparse step is short against the memory latency); z and D through
+    // bounded loads that every wave issues, so no load sits in a branch
+    struct StepRegs {
+      bf16x8 q[NPASS], o[NPASS];
+      float z, d;
+    };
+    // step t of the walk -> (head, row step)
+    auto pair_of = [&](int t, int& hh, int& i) {
+      const int hs = t / nsteps;
+      hh = h0 + hs;
+      i = i_start + t - hs * nsteps;
+    };
+    auto gload = [&](StepRegs& R, int hh, int i) {
+      const auto lq = make_rsrc(Q + head_row0(hh) * D, head_bytes);
+      const auto lo = make_rsrc(dO + head_row0(hh) * D, head_bytes);
+      const auto lz = make_rsrc(LSE + head_row0(hh), (uint32_t)s.nq * 4u);
+      const auto ld = make_rsrc(Dq + head_row0(hh), (uint32_t)s.nq * 4u);
+      const uint32_t off0 = toff + (uint32_t)(i * 64) * (uint32_t)(D * 2);
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p) {
+        const uint32_t off = off0 + (uint32_t)(p * RPP * D * 2);
+        R.q[p] = buf_load16(lq, off);
+        R.o[p] = buf_load16(lo, off);
+      }
+      const uint32_t roff = (uint32_t)(i * 64 + lane) * 4u;
+      R.z = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lz, roff, 0, 0));
+      R.d = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ld, roff, 0, 0));
+    };
+    auto gstore = [&](const StepRegs& R, int bf) {
+#pragma unroll
+      for (int p = 0; p < NPASS; ++p) {
+        store16(&sm.q[bf][p * RPP + srow][8 * sc], R.q[p]);
+        store16(&sm.dout[bf][p * RPP + srow][8 * sc], R.o[p]);
+      }
+      if (tid < 64) {
+        sm.z2[bf][tid] = R.z * 1.4426950408889634f;
+        sm.dd[bf][tid] = R.d;
+      }
+    };
+    // this wave's kept halves of step i (decision bytes v), staged in bf
+    auto step_tiles = [&](int bf, int i, uint32_t v) {
+      const uint32_t mine = ((v >> w) & 1u) | (((v >> (8 + w)) & 1u) << 1);
+      if (mine == 0u) return;
+      bool bnd[2] = {false, false};
+      if (!(keys_in && i >= i_lo && i < i_hi)) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int r0 = i * 64 + 32 * half;
+          bnd[half] = (r0 + 32 > s.nq) || (kw0 + kBK > s.nk) || (s.causal && kw0 + kBK - 1 > r0 + s.offset);
+        }
+      }
+      f32x4 sacc[4];
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sacc[qb][r] = 0.f;
+      {
+        bf16x8 qrow[KS][4];
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+#pragma unroll
+          for (int qb = 0; qb < 4; ++qb) qrow[k][qb] = load16(&sm.q[bf][16 * qb + l16][32 * k + 8 * g]);
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+#pragma unroll
+          for (int qb = 0; qb < 4; ++qb) sacc[qb] = mfma16(qrow[k][qb], kr[k], sacc[qb]);
+      }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if (!bnd[half]) continue;
+        const int r0 = i * 64 + 32 * half;
+#pragma unroll
+        for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int q = r0 + 16 * qh + 4 * g + r;
+            const bool ok = (q < s.nq) & (key < s.nk) & ((key <= q + s.offset) | (s.causal == 0));
+            sacc[2 * half + qh][r] = ok ? sacc[2 * half + qh][r] : kNegInf;   // P = 0 there
+          }
+      }
+      if (mine & 1u) kept_tile(bf, 0, sacc[0], sacc[1]);
+      if (mine & 2u) kept_tile(bf, 1, sacc[2], sacc[3]);
+    };
+
+    // t: the step in LDS buffer buf; tn: the next kept step, in flight in
+    // one register set; tnn: the one after, loaded into the other set while
+    // t is processed. Past the last kept step the loads repeat a staged step.
+    StepRegs ra, rb;
+    uint32_t v = 0u, vn = 0u, vnn = 0u;
     int t = next_kept(0, v);
-    int h = hk * s.group + hsub, i = i_start;
-    if (t < total) step_hi(t, h, i);
-    int hl = h;
-    auto lq = make_rsrc(Q + head_row0(h) * D, head_bytes);
-    auto lo = make_rsrc(dO + head_row0(h) * D, head_bytes);
-    load_step(lq, lo, h, i);
-    store_step(0, i);
+    int h = h0, i = i_start;
+    if (t < tot) pair_of(t, h, i);
+    gload(ra, h, i);
+    gstore(ra, 0);
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
       settle(kr[k]);
       settle(vr[k]);
     }
+    int tn = t < tot ? next_kept(t + 1, vn) : tot;
+    int hn = h, in = i;
+    if (tn < tot) pair_of(tn, hn, in);
+    gload(ra, hn, in);
     __syncthreads();
     int buf = 0;
-    while (t < total) {
-      uint32_t vn;
-      const int tn = next_kept(t + 1, vn);
-      int hn = h, in = i;                              // after the last: the current step again
-      if (tn < total) step_hi(tn, hn, in);
-      if (hn != hl) {
-        hl = hn;
-        lq = make_rsrc(Q + head_row0(hn) * D, head_bytes);
-        lo = make_rsrc(dO + head_row0(hn) * D, head_bytes);
-      }
-      load_step(lq, lo, hn, in);
-      // this wave's kept halves of step t
-      const uint32_t mine = ((v >> w) & 1u) | (((v >> (8 + w)) & 1u) << 1);
-      if (mine != 0u) {
-        bool bnd[2] = {false, false};
-        if (!(keys_in && i >= i_lo && i < i_hi)) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int r0 = i * 64 + 32 * half;
-            bnd[half] = (r0 + 32 > s.nq) || (kw0 + kBK > s.nk) || (s.causal && kw0 + kBK - 1 > r0 + s.offset);
-          }
-        }
-        f32x4 sacc[4];
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sacc[qb][r] = 0.f;
-        {
-          bf16x8 qrow[KS][4];
-#pragma unroll
-          for (int k = 0; k < KS; ++k)
-#pragma unroll
-            for (int qb = 0; qb < 4; ++qb) qrow[k][qb] = load16(&sm.q[buf][16 * qb + l16][32 * k + 8 * g]);
-#pragma unroll
-          for (int k = 0; k < KS; ++k)
-#pragma unroll
-            for (int qb = 0; qb < 4; ++qb) sacc[qb] = mfma16(qrow[k][qb], kr[k], sacc[qb]);
-        }
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          if (!bnd[half]) continue;
-          const int r0 = i * 64 + 32 * half;
-#pragma unroll
-          for (int qh = 0; qh < 2; ++qh)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int q = r0 + 16 * qh + 4 * g + r;
-              const bool ok = (q < s.nq) & (key < s.nk) & ((key <= q + s.offset) | (s.causal == 0));
-              sacc[2 * half + qh][r] = ok ? sacc[2 * half + qh][r] : kNegInf;   // P = 0 there
-            }
-        }
-        if (mine & 1u) kept_tile(buf, 0, sacc[0], sacc[1]);
-        if (mine & 2u) kept_tile(buf, 1, sacc[2], sacc[3]);
-      }
-      store_step(buf ^ 1, in);
-      t = tn;
-      v = vn;
-      h = hn;
-      i = in;
-      buf ^= 1;
+    while (t < tot) {
+      int tnn = tn < tot ? next_kept(tn + 1, vnn) : tot;
+      int hnn = hn, inn = in;
+      if (tnn < tot) pair_of(tnn, hnn, inn);
+      gload(rb, hnn, inn);
+      step_tiles(buf, i, v);
+      gstore(ra, buf ^ 1);
       __syncthreads();
+      buf ^= 1;
+      t = tn; i = in; v = vn;
+      tn = tnn; hn = hnn; in = inn; vn = vnn;
+      if (t >= tot) break;
+      tnn = tn < tot ? next_kept(tn + 1, vnn) : tot;
+      hnn = hn;
+      inn = in;
+      if (tnn < tot) pair_of(tnn, hnn, inn);
+      gload(ra, hnn, inn);
+      step_tiles(buf, i, v);
+      gstore(rb, buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+      t = tn; i = in; v = vn;
+      tn = tnn; hn = hnn; in = inn; vn = vnn;
     }
   }
 
   // ---- store dK = scale * sum dS^T Q and dV (summed over the group's heads):
   // lane (key l16, group g) holds d = 16 db + 4 g + r
   if (key >= s.nk) return;
-  if constexpr (kGated) {
+  if (kGated && gsplit) {
     // this walk's head only: fp32 partials [2][B][Hq][N_k][D] (dK unscaled)
     const size_t prow = ((size_t)b * s.hq + hk * s.group + hsub) * (size_t)s.nk + key;
     float* pk = part + prow * D;
@@ -555,32 +696,38 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   }
 }
 
-// The gated walks' partials summed over each KV head's group of query heads
-// (in head order, so the result does not depend on scheduling): dK = scale *
-// sum, dV = sum, in bf16.
+// The gated walks' partials of the key blocks walked per head, summed over
+// each KV head's group of query heads (in head order, so the result does not
+// depend on scheduling): dK = scale * sum, dV = sum, in bf16. A workgroup per
+// (batch, KV head, 128-key block); blocks walked as one group are already
+// written.
 __global__ __launch_bounds__(256) void bwd_dkdv_finalize_kernel(Shape s, const float* __restrict__ part,
+                                                                const int32_t* __restrict__ plan,
                                                                 bf16* __restrict__ dK,
                                                                 bf16* __restrict__ dV) {
+  const int n_kb = (s.nk + 127) / 128;
+  const int J = (int)(blockIdx.x % n_kb);
+  const int bkv = (int)(blockIdx.x / n_kb);
+  const int b = bkv / s.hkv, hk = bkv % s.hkv;
+  if (plan[blockIdx.x] <= kGroupWalkPairs) return;
+  const int k0 = J * 128, nkeys = min(128, s.nk - k0);
   const size_t per_head = (size_t)s.nk * s.d;                 // floats of one head's partial
-  const size_t n4 = (size_t)s.batch * s.hkv * per_head / 4;   // 4-element chunks of dK
   const size_t dv_off = (size_t)s.batch * s.hq * per_head;
+  const size_t p0 = ((size_t)b * s.hq + (size_t)hk * s.group) * per_head + (size_t)k0 * s.d;
+  const size_t o0 = ((size_t)b * s.hkv + hk) * per_head + (size_t)k0 * s.d;
   const float sc_nat = s.scale_log2 * 0.69314718055994531f;
-  const size_t nthr = (size_t)gridDim.x * blockDim.x;
-  for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < n4; c += nthr) {
-    const size_t e = 4 * c;                                   // element of [B][Hkv][N_k][D]
-    const size_t bk = e / per_head, within = e % per_head;
-    const size_t b = bk / s.hkv, hk = bk % s.hkv;
-    const size_t p0 = ((b * s.hq + hk * s.group) * per_head) + within;
+  for (int c = (int)threadIdx.x; c < nkeys * s.d / 4; c += (int)blockDim.x) {
+    const size_t e = 4 * (size_t)c;
     f32x4 a = {0.f, 0.f, 0.f, 0.f}, v = {0.f, 0.f, 0.f, 0.f};
     for (int hs = 0; hs < s.group; ++hs) {
-      a += *reinterpret_cast<const f32x4*>(part + p0 + hs * per_head);
-      v += *reinterpret_cast<const f32x4*>(part + dv_off + p0 + hs * per_head);
+      a += *reinterpret_cast<const f32x4*>(part + p0 + hs * per_head + e);
+      v += *reinterpret_cast<const f32x4*>(part + dv_off + p0 + hs * per_head + e);
     }
     const bf16x4 ka = {(bf16)(a[0] * sc_nat), (bf16)(a[1] * sc_nat), (bf16)(a[2] * sc_nat),
                        (bf16)(a[3] * sc_nat)};
     const bf16x4 va = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-    *reinterpret_cast<bf16x4*>(dK + e) = ka;
-    *reinterpret_cast<bf16x4*>(dV + e) = va;
+    *reinterpret_cast<bf16x4*>(dK + o0 + e) = ka;
+    *reinterpret_cast<bf16x4*>(dV + o0 + e) = va;
   }
 }
 
@@ -1079,6 +1226,11 @@ size_t bwd_part_floats(const Shape& s) {
   return 2 * (size_t)s.batch * s.hq * s.nk * s.d;
 }
 
+size_t bwd_plan_ints(const Shape& s) {
+  if (!s.dtype_is_bf16() || !(s.flags & MALA_FLAG_GATE_PASS)) return 0;
+  return (size_t)s.batch * s.hkv * ((s.nk + 127) / 128);
+}
+
 size_t bwd_bits_words(const Shape& s) {
   const size_t tr = (s.nq + kBQ - 1) / kBQ, tc = (s.nk + kBK - 1) / kBK;
   return (size_t)s.batch * s.hq * tr * ((tc + 31) / 32);
@@ -1087,15 +1239,15 @@ size_t bwd_bits_words(const Shape& s) {
 hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* d_o, void* dq, void* dk,
                            void* dv, float* ws_d, uint32_t* ws_bits, float* ws_part,
-                           const int8_t* fwd_mask, int8_t* mask, int32_t* kept, hipStream_t st,
-                           int stages) {
+                           int32_t* ws_plan, const int8_t* fwd_mask, int8_t* mask, int32_t* kept,
+                           hipStream_t st, int stages) {
   const int rows = s.batch * s.hq * s.nq;
   const size_t nwords = bwd_bits_words(s);
   const size_t nkept = (size_t)s.batch * s.hq * ((s.nq + kBQ - 1) / kBQ);
   if (stages & kStagePrep) {
     const size_t nmask =
         mask ? (size_t)s.batch * s.hq * ((s.nq + kBQ - 1) / kBQ) * ((s.nk + kBK - 1) / kBK) : 0;
-    size_t work = (size_t)rows;
+    size_t work = (size_t)rows * (s.d / 8) / 64;   // waves: 64 16-byte chunks of O, dO each
     if (nwords / 64 > work) work = nwords / 64;
     if (nmask / 64 > work) work = nmask / 64;
     size_t blocks = (work + 3) / 4 + 1;
@@ -1121,21 +1273,22 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
       else if (g2.x)
         hipLaunchKernelGGL(gate, g2, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k, lse,
                            ws_bits, mask, n_qb, (const int8_t*)nullptr);
+      // the kept pairs of each key block choose its walks
+      if (g1.x)
+        hipLaunchKernelGGL(bwd_plan_kernel, g1, dim3(64), 0, st, s, (const uint32_t*)ws_bits,
+                           ws_plan);
       const dim3 g1h((unsigned)(g1.x * s.group));
       if (g1h.x)
         hipLaunchKernelGGL(dkdv_gated, g1h, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
                            (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dk, (bf16*)dv,
-                           ws_bits, mask, ws_part);
-      const size_t n4 = (size_t)s.batch * s.hkv * s.nk * s.d / 4;
-      size_t blocks = (n4 + 255) / 256;
-      if (blocks > 65536) blocks = 65536;
-      if (n4)
-        hipLaunchKernelGGL(bwd_dkdv_finalize_kernel, dim3((unsigned)blocks), dim3(256), 0, st, s,
-                           (const float*)ws_part, (bf16*)dk, (bf16*)dv);
+                           ws_bits, mask, ws_part, (const int32_t*)ws_plan);
+      if (g1.x)
+        hipLaunchKernelGGL(bwd_dkdv_finalize_kernel, g1, dim3(256), 0, st, s,
+                           (const float*)ws_part, (const int32_t*)ws_plan, (bf16*)dk, (bf16*)dv);
     } else if (g1.x && (stages & kStageMain)) {
       hipLaunchKernelGGL(dkdv, g1, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
                          (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dk, (bf16*)dv,
-                         ws_bits, mask, (float*)nullptr);
+                         ws_bits, mask, (float*)nullptr, (const int32_t*)nullptr);
     }
     // dynamic LDS: the needed-tile bitmap, one bit per 64-key tile
     const size_t need_bytes = (size_t)((s.nk + 64 * 32 - 1) / (64 * 32)) * 4;

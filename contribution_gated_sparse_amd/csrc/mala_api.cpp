@@ -109,7 +109,8 @@ mala_status check_ptr(const void* ptr, const char* name, bool needed) {
 size_t bwd_ws_bytes(const mala::Shape& s) {
   return round_up(mala::bwd_ws_d_floats(s) * sizeof(float)) +
          round_up(mala::bwd_bits_words(s) * sizeof(uint32_t)) +
-         round_up(mala::bwd_part_floats(s) * sizeof(float));
+         round_up(mala::bwd_part_floats(s) * sizeof(float)) +
+         round_up(mala::bwd_plan_ints(s) * sizeof(int32_t));
 }
 
 // Keys per split for a checked decode problem (the rule mala_decode_split_keys
@@ -225,9 +226,10 @@ mala_status bwd_impl(int stages, const mala_problem* p, const void* q, const voi
   uint32_t* ws_bits =
       (uint32_t*)((char*)workspace + round_up(mala::bwd_ws_d_floats(s) * sizeof(float)));
   float* ws_part = (float*)((char*)ws_bits + round_up(mala::bwd_bits_words(s) * sizeof(uint32_t)));
+  int32_t* ws_plan = (int32_t*)((char*)ws_part + round_up(mala::bwd_part_floats(s) * sizeof(float)));
   hipError_t e;
   if (s.dtype_is_bf16())
-    e = mala::launch_bwd_bf16(s, q, k, v, o, lse, d_o, dq, dk, dv, ws_d, ws_bits, ws_part,
+    e = mala::launch_bwd_bf16(s, q, k, v, o, lse, d_o, dq, dk, dv, ws_d, ws_bits, ws_part, ws_plan,
                               nested ? fwd_mask : nullptr, tile_mask, kept_tiles, st, stages);
   else
     e = mala::launch_bwd_f32(s, (const float*)q, (const float*)k, (const float*)v,

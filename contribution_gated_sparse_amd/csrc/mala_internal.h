@@ -100,7 +100,7 @@ hipError_t launch_fwd_f32(const Shape& s, const float* q, const float* k, const 
 hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* d_o, void* dq, void* dk,
                            void* dv, float* ws_d, uint32_t* ws_bits, float* ws_part,
-                           const int8_t* fwd_mask, int8_t* mask, int32_t* kept, hipStream_t st,
+                           int32_t* ws_plan, const int8_t* fwd_mask, int8_t* mask, int32_t* kept, hipStream_t st,
                            int stages);
 hipError_t launch_bwd_f32(const Shape& s, const float* q, const float* k, const float* v,
                           const float* o, const float* lse, const float* d_o, float* dq, float* dk,
@@ -126,6 +126,7 @@ hipError_t launch_decode_combine_f32(const DecodeShape& s, const float* ws, floa
 size_t bwd_ws_d_floats(const Shape& s);    // D = rowsum(O o dO), fp32 [B, Hq, Nq]
 size_t bwd_bits_words(const Shape& s);     // backward decisions, one bit per tile
 size_t bwd_part_floats(const Shape& s);    // gate pass: fp32 dK, dV partials [2, B, Hq, N_k, D]
+size_t bwd_plan_ints(const Shape& s);      // gate pass: kept pairs per [B, Hkv, 128-key block]
 size_t decode_ws_floats(const DecodeShape& s);
 
 }  // namespace mala

@@ -110,10 +110,13 @@ def test_backward_workspace(lib):
     assert need == expect
     assert lib.mala_bwd_workspace_size(ctypes.byref(prob(head_dim=80))) == 0
     # MALA_FLAG_GATE_PASS adds the fp32 dK, dV partials of the per-head walks
-    # (2 x B x Hq x Nk x D floats) for bf16; fp32 problems ignore the flag
+    # (2 x B x Hq x Nk x D floats) and the walks' plan (one int per batch, KV
+    # head and 128-key block) for bf16; fp32 problems ignore the flag
     part = -(-(2 * 4 * 100 * 128 * 4) // 256) * 256
-    assert lib.mala_bwd_workspace_size(ctypes.byref(prob(flags=M.MALA_FLAG_GATE_PASS))) == need + part
-    assert lib.mala_bwd_workspace_size(ctypes.byref(prob(flags=3))) == need + part
+    plan = -(-(1 * 2 * 1 * 4) // 256) * 256
+    assert lib.mala_bwd_workspace_size(ctypes.byref(prob(flags=M.MALA_FLAG_GATE_PASS))) == \
+        need + part + plan
+    assert lib.mala_bwd_workspace_size(ctypes.byref(prob(flags=3))) == need + part + plan
     f32 = lib.mala_bwd_workspace_size(ctypes.byref(prob(dtype=M.MALA_F32)))
     assert lib.mala_bwd_workspace_size(ctypes.byref(prob(dtype=M.MALA_F32, flags=2))) == f32
     buf = (ctypes.c_char * 1024)()
