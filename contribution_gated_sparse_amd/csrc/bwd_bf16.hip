@@ -28,10 +28,13 @@
 //                 (mala_bwd_nested), only the scores of the tiles the
 //                 forward kept: the others meet the skip condition
 //                 (nested support, Sec. 2.2).
-//   bwd_dkdv (gated): one walk per (key block, query head) over the 64-row
-//                 steps that hold a kept tile of the workgroup; nothing is
-//                 staged for the others. fp32 partials per query head.
-//   bwd_dkdv_finalize: sums each KV head's group of partials into dK, dV.
+//   bwd_plan:     counts each key block's kept (query head, 64-row step)
+//                 pairs over its KV head's group.
+//   bwd_dkdv (gated): walks over the steps that hold a kept tile of the
+//                 workgroup; nothing is staged for the others. A light key
+//                 block is one walk over the group's heads, writing dK, dV;
+//                 a heavy one a walk per query head, into fp32 partials.
+//   bwd_dkdv_finalize: sums the heavy blocks' partials into dK, dV.
 // bwd_dq is the same kernel in both modes.
 //
 // dS enters the dK and dQ products as a bf16 MFMA operand. dK takes it as one
