@@ -152,8 +152,8 @@ mala_status mala_fwd(const mala_problem* p, const void* q, const void* k, const 
 /* Bytes of device workspace mala_bwd needs for problem p (the per-row
  * D = rowsum(O o dO) in fp32 and one decision bit per backward tile; with
  * MALA_FLAG_GATE_PASS on a bf16 problem also fp32 dK, dV partials per query
- * head, 8 * B * Hq * Nk * d bytes); 0 if p is invalid. The size depends on
- * p->flags. */
+ * head, 8 * B * Hq * Nk * d bytes, and 4 bytes per batch, KV head and
+ * 128-key block); 0 if p is invalid. The size depends on p->flags. */
 size_t mala_bwd_workspace_size(const mala_problem* p);
 
 /*
