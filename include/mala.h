@@ -71,11 +71,13 @@ enum {
    * separate score pass before dK/dV, and let dK/dV stage and process only
    * the 64-row steps that hold a kept tile, so that a skipped tile costs no
    * dO load (App. A.1, "Fused backward execution"). Every legal score is
-   * still formed. Pays off when few tiles are kept (trained attention,
-   * larger tau); on inputs where most tiles are kept it adds one score pass
-   * (about a fifth of the backward). The decisions may differ from those of
-   * the default path only for tiles whose margin is within fp32 rounding of
-   * the threshold. Ignored for MALA_F32. */
+   * still formed, unless mala_bwd_nested passes the forward's tile mask:
+   * then only the forward's kept tiles are scored. Pays off when few tiles
+   * are kept (trained attention, larger tau); on inputs where every tile is
+   * kept the score pass costs about a tenth of the backward and the walks
+   * gain part of it back (+4% in all at 32K). The decisions may differ from
+   * those of the default path only for tiles whose margin is within fp32
+   * rounding of the threshold. Ignored for MALA_F32. */
   MALA_FLAG_GATE_PASS = 2
 };
 
