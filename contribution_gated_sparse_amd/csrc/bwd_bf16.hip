@@ -131,8 +131,9 @@ __device__ int group_kept_pairs(const Shape& s, const uint8_t* bit_bytes, int b,
   const uint32_t rstride = (uint32_t)(((s.nk + kBK - 1) / kBK + 31) / 32) * 4u;
   const int nsteps = tr64 - i_start;
   const int pairs = s.group * nsteps;
+  const uint32_t span = (uint32_t)(s.group * tr32) * rstride;   // 0 without query rows
   const auto rs = make_rsrc(bit_bytes + ((size_t)b * s.hq + (size_t)hk * s.group) * tr32 * rstride + J,
-                            (uint32_t)(s.group * tr32) * rstride - (uint32_t)J);
+                            span > (uint32_t)J ? span - (uint32_t)J : 0u);
   // four pairs per thread and pass, their loads issued together; a pair
   // past the group reads row 0 and is not counted
   int c = 0;
@@ -499,8 +500,9 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     const int tot = nh * nsteps;
     // decision bytes J of the walk's bit rows; bytes past the last row read 0
     const uint32_t rstride = (uint32_t)words * 4u;
+    const uint32_t span = (uint32_t)(nh * tr32) * rstride;        // 0 without query rows
     const auto drs = make_rsrc(bit_bytes + ((size_t)b * s.hq + h0) * tr32 * rstride + J,
-                               (uint32_t)(nh * tr32) * rstride - (uint32_t)J);
+                               span > (uint32_t)J ? span - (uint32_t)J : 0u);
     // look-ahead: the bytes of 512 steps are fetched at once; lane k of
     // window x holds the two bytes (rows 2 i, 2 i + 1) of step
     // la_base + 64 x + k, so a walk waits on the bit rows once per 512 steps

@@ -450,6 +450,13 @@ def test_empty_query_rows():
     b = m.mala_bwd(q, k, k, out["o"], out["lse"], q, 1e-4)
     torch.cuda.synchronize()
     assert torch.count_nonzero(b["dk"]) == 0 and torch.count_nonzero(b["dv"]) == 0
+    # the gate-pass walks and the nested call write the zero dK, dV themselves
+    f = m.mala_fwd(q, k, k, 1e-4, want_mask=True)
+    for kw in (dict(gate_pass=True), dict(fwd_mask=f["mask"])):
+        dk = torch.full_like(k, 7.0)
+        g = m.mala_bwd(q, k, k, f["o"], f["lse"], q, 1e-4, out=dict(dk=dk), **kw)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(g["dk"]) == 0 and torch.count_nonzero(g["dv"]) == 0, kw
 
 
 def test_fast_grad_flag_same_support():
