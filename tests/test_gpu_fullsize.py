@@ -48,8 +48,10 @@ def _agree(gm, om, margin, what):
     return int((seen & ~clear).sum())
 
 
-@pytest.mark.parametrize("cid", [2, 3, 4])
-def test_prefill_full_size_sampled(cid):
+# C3 runs at every tolerance of its sweep (tau = 0 is dense attention)
+@pytest.mark.parametrize("cid,tau", [(2, 1e-4), (3, 0.0), (3, 1e-5), (3, 1e-4), (3, 1e-3),
+                                     (4, 1e-4)])
+def test_prefill_full_size_sampled(cid, tau):
     m = lib()
     cfg = W.CONFIGS[cid]
     x = W.make_prefill(cfg, device=DEV)
@@ -60,10 +62,10 @@ def test_prefill_full_size_sampled(cid):
     G = HQ // HKV
     (fbq, fbk, _), (bbq, bbk, _), _ = tiling()
     assert N % 64 == 0 and fbq == bbq
-    print(f"[full-size] config {cid}: B={B} Hq={HQ} Hkv={HKV} N={N} d={D}", flush=True)
+    print(f"[full-size] config {cid} tau={tau}: B={B} Hq={HQ} Hkv={HKV} N={N} d={D}", flush=True)
 
-    g = m.mala_fwd(q, k, v, TAU, softmax_scale=scale, want_mask=True)
-    gb = m.mala_bwd(q, k, v, g["o"], g["lse"], do, TAU, softmax_scale=scale, want_mask=True)
+    g = m.mala_fwd(q, k, v, tau, softmax_scale=scale, want_mask=True)
+    gb = m.mala_bwd(q, k, v, g["o"], g["lse"], do, tau, softmax_scale=scale, want_mask=True)
     torch.cuda.synchronize()
 
     kh = HKV - 1
@@ -76,7 +78,7 @@ def test_prefill_full_size_sampled(cid):
     kn, vn = np64(k[:, kh:kh + 1]), np64(v[:, kh:kh + 1])
     qh, doh = np64(q[:, h:h + 1]), np64(do[:, h:h + 1])
     fmask = g["mask"][:, h:h + 1].cpu().numpy()
-    r = O.mala_fwd(qh, kn, vn, TAU, scale, True, fbq, fbk,
+    r = O.mala_fwd(qh, kn, vn, tau, scale, True, fbq, fbk,
                    blocks=[(0, 0, i) for i in blocks], replay=fmask, band=BAND["bf16"])
     _agree(fmask, r["mask"], r["margin"], "forward")
     kept = g["kept"][:, h:h + 1].cpu().numpy()
@@ -90,7 +92,7 @@ def test_prefill_full_size_sampled(cid):
     assert dl <= 2e-3, f"LSE error {dl:.3e}"
 
     bmask = gb["mask"][:, h:h + 1].cpu().numpy()
-    rb = O.mala_bwd(qh, kn, vn, r["o"], r["lse"], doh, TAU, scale, True, bbq, bbk,
+    rb = O.mala_bwd(qh, kn, vn, r["o"], r["lse"], doh, tau, scale, True, bbq, bbk,
                     qblocks=blocks, replay=bmask, band=BAND["bf16"], o_storage="bf16")
     _agree(bmask, rb["mask"], rb["margin"], "backward")
     compare_values("dQ", np64(gb["dq"][:, h:h + 1]), rb["dq"], "bf16", rows)
@@ -100,11 +102,11 @@ def test_prefill_full_size_sampled(cid):
     t = 64
     qt, dot = np64(q[:, heads, N - t:]), np64(do[:, heads, N - t:])
     ft = g["mask"][:, heads, -(t // fbq):].cpu().numpy()
-    rt = O.mala_fwd(qt, kn, vn, TAU, scale, True, fbq, fbk, replay=ft, band=BAND["bf16"])
+    rt = O.mala_fwd(qt, kn, vn, tau, scale, True, fbq, fbk, replay=ft, band=BAND["bf16"])
     _agree(ft, rt["mask"], rt["margin"], "forward (tail)")
     compare_values("O tail", np64(g["o"][:, heads, N - t:]), rt["o"], "bf16")
     bt = gb["mask"][:, heads, -(t // bbq):].cpu().numpy()
-    rbt = O.mala_bwd(qt, kn, vn, rt["o"], rt["lse"], dot, TAU, scale, True, bbq, bbk,
+    rbt = O.mala_bwd(qt, kn, vn, rt["o"], rt["lse"], dot, tau, scale, True, bbq, bbk,
                      replay=bt, band=BAND["bf16"], o_storage="bf16")
     _agree(bt, rbt["mask"], rbt["margin"], "backward (tail)")
     compare_values("dQ tail", np64(gb["dq"][:, heads, N - t:]), rbt["dq"], "bf16")
