@@ -308,6 +308,21 @@ def test_nested_arbitrary_forward_masks(causal, density):
         compare_values(n, np64(b[n]), r[n], "bf16")
 
 
+def test_backward_modes_are_deterministic():
+    """Every backward mode gives the same bits on a second run: the default
+    path, the gate pass (whose heavy key blocks sum per-head partials in head
+    order) and the nested call."""
+    m = lib()
+    x = to_dev(W.make_structured(2000, hq=8, hkv=2, d=128))
+    f = m.mala_fwd(x["q"], x["k"], x["v"], 1e-4, softmax_scale=x["scale"], want_mask=True)
+    for kw in (dict(), dict(gate_pass=True), dict(fwd_mask=f["mask"])):
+        runs = [m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], 1e-4,
+                           softmax_scale=x["scale"], **kw) for _ in range(2)]
+        torch.cuda.synchronize()
+        for n in ("dq", "dk", "dv", "kept"):
+            assert torch.equal(runs[0][n], runs[1][n]), (n, list(kw))
+
+
 def test_nested_noncausal_fast_grad_and_f32():
     """The nested call with MALA_FLAG_FAST_GRAD, non-causal, and for fp32
     (where the forward mask is not read and the call is the backward)."""
