@@ -201,8 +201,10 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const int bk_count = s.batch * s.hkv;
-  // walks per key block: one over the whole group, or (gated) one per query
-  // head, whose fp32 partials the finalize kernel sums
+  // workgroups per key block: one, walking the whole group; or (gated) one
+  // per query head, each walking its head into fp32 partials that the
+  // finalize kernel sums (heavy blocks), or one of them walking the group
+  // (light blocks)
   const int nsub = kGated ? s.group : 1;
   const int J = (int)(blockIdx.x / (bk_count * nsub));  // key block (0 = longest)
   const int rem = (int)(blockIdx.x % (bk_count * nsub));
