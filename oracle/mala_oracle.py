@@ -31,7 +31,9 @@ tolerance rules in the design notes of this repository):
 
 Every function is pinned by tests against something other than itself: the
 tau = 0 limit against torch's fp64 scaled-dot-product attention and autograd,
-per-key brute force of Eq. 2/3 in ratio form, Proposition 1 and Eqs. 9-10,
+per-key brute force of Eq. 2/3 in ratio form (for the forward and for the
+split decode, whose splits gate against their own partial normalizers with
+L = N_k), Proposition 1, the per-key bound of its proof and Eqs. 9-10,
 support nesting, and a closed form for constant scores.
 """
 from __future__ import annotations

@@ -391,14 +391,93 @@ def test_decode_split_bound_and_first_tiles(tau):
             tiles = -(-(min(n, 256 * ci + 256) - 256 * ci) // 64)
             assert (r["mask"][bb, :, ci, tiles - 1] == O.KEPT).all()
         # each chunk tests against its own partial normalizer, which is no
-        # larger than the unsplit one, so the split support contains every
-        # key whose ratio to the final normalizer clears tau / L, and the
-        # omitted mass obeys the forward bound of Prop. 1
+        # larger than the merged one, so every omitted key's ratio to the
+        # merged normalizer is below tau / N_k (the step of Prop. 1's proof,
+        # with L = N_k for the decode row), and the omitted mass obeys the
+        # forward bound of Prop. 1
         for h in range(hq):
             s = 0.5 * kc[bb, 0, :n] @ q[bb, h]
             zd = np.log(np.exp(s - s.max()).sum()) + s.max()
             eps = 1 - np.exp(r["lse"][bb, h] - zd)
             assert eps <= tau / (1 + tau) + 1e-12
+            omitted = ~decode_kept_keys(r["mask"][bb, h], n, 256, 64)
+            assert omitted.any() or tau < 10.0
+            assert (np.exp(s[omitted] - r["lse"][bb, h]) < tau / n).all()
+
+
+def decode_kept_keys(mask_bh, n, chunk, bk):
+    """Boolean [n]: key lies in a tile that its split kept."""
+    kept = np.zeros(n, bool)
+    for ci in range(mask_bh.shape[0]):
+        for t in range(mask_bh.shape[1]):
+            if mask_bh[ci, t] == O.KEPT:
+                kept[ci * chunk + t * bk: min(n, ci * chunk + (t + 1) * bk)] = True
+    return kept
+
+
+def brute_decode(q, kc, vc, lens, tau, scale, chunk, bk):
+    """Scalar loops over the split rule (Sec. 2.4, App. A.1 "Fused decoding
+    execution") in ratio form. Every split of ``chunk`` keys starts with an
+    empty normalizer Z = 0 and tests its tiles newest first; a tile is skipped
+    iff Z > 0 and exp(max s) / Z < tau / N_k, where N_k counts the query's
+    whole causal context (the decode row's L_0), not the split's keys; a kept
+    tile adds exp(s) of its keys to the split's Z. The output is the softmax
+    over the union of the splits' kept keys."""
+    b_, hq, d = q.shape
+    g = hq // kc.shape[1]
+    nch = -(-max(lens) // chunk)
+    mask = np.full((b_, hq, nch, chunk // bk), -1, dtype=np.int8)
+    o = np.zeros((b_, hq, vc.shape[3]))
+    lse = np.zeros((b_, hq))
+    for b in range(b_):
+        n = lens[b]
+        for h in range(hq):
+            kh = h // g
+            s = [scale * sum(q[b, h, e] * kc[b, kh, kk, e] for e in range(d)) for kk in range(n)]
+            kept = []
+            for ci in range(-(-n // chunk)):
+                c0, c1 = ci * chunk, min(ci * chunk + chunk, n)
+                Z = 0.0
+                for t in reversed(range(-(-(c1 - c0) // bk))):
+                    keys = list(range(c0 + t * bk, min(c0 + (t + 1) * bk, c1)))
+                    skip = Z > 0.0 and math.exp(max(s[kk] for kk in keys)) / Z < tau / n
+                    mask[b, h, ci, t] = 0 if skip else 1
+                    if not skip:
+                        for kk in keys:
+                            Z += math.exp(s[kk])
+                            kept.append(kk)
+            tot = sum(math.exp(s[kk]) for kk in kept)
+            for kk in kept:
+                o[b, h] += math.exp(s[kk]) / tot * vc[b, kh, kk]
+            lse[b, h] = math.log(tot)
+    return mask, o, lse
+
+
+DECODE_TAUS = [0.0, 1e-3, 0.05, 0.5, 2.0, 20.0, 1e3]
+
+
+def _decode_pin_problem():
+    rng = np.random.default_rng(73)
+    b, hq, hkv, cap, d = 2, 4, 2, 300, 6
+    q = rng.standard_normal((b, hq, d)) * 2.5
+    kc = rng.standard_normal((b, hkv, cap, d))
+    vc = rng.standard_normal((b, hkv, cap, d))
+    return q, kc, vc, [300, 161]
+
+
+@pytest.mark.parametrize("tau", DECODE_TAUS)
+def test_decode_multi_split_matches_bruteforce(tau):
+    """Several splits per sequence (64-key splits, 16-key tiles): the
+    oracle's decisions, output and log-normalizer equal the per-key scalar
+    loops of the split rule with L = N_k."""
+    q, kc, vc, lens = _decode_pin_problem()
+    r = O.mala_decode(q, kc, vc, lens, tau, 0.6, 64, 16)
+    m, o, lse = brute_decode(q, kc, vc, lens, tau, 0.6, 64, 16)
+    np.testing.assert_array_equal(r["mask"], m)
+    np.testing.assert_allclose(r["o"], o, atol=1e-12)
+    np.testing.assert_allclose(r["lse"], lse, atol=1e-12)
+    if tau >= 0.5:
+        assert (m == O.SKIPPED).any()      # the sweep exercises the skip branch
 
 
 # ------------------------------------------------ mutation checks of the pins
@@ -447,6 +526,55 @@ def test_pins_catch_planted_forward_mistakes(kind, monkeypatch):
         if not np.array_equal(r["mask"], m):
             caught = True
     assert caught
+
+
+def _split_local_length_mutant(tau):
+    """fwd_block as the decode would call it if L counted only the keys of
+    the split being gated instead of the query's whole context."""
+    orig = O.fwd_block
+
+    def mutant(s, c, bk, valid_rows, replay=None, band=0.0):
+        c_local = np.full(c.shape, math.log(tau) - math.log(s.shape[1]))
+        return orig(s, c_local, bk, valid_rows, replay, band)
+    return mutant
+
+
+def test_pins_catch_split_local_length(monkeypatch):
+    """A decode that uses the split's own length in tau / L fails both the
+    brute-force pin of the split rule and the per-key bound exp(s_k) / Z_R <
+    tau / N_k on omitted keys."""
+    q, kc, vc, lens = _decode_pin_problem()
+    refs = {tau: brute_decode(q, kc, vc, lens, tau, 0.6, 64, 16) for tau in DECODE_TAUS[1:]}
+    mismatched = 0
+    for tau, (m, _, _) in refs.items():
+        monkeypatch.setattr(O, "fwd_block", _split_local_length_mutant(tau))
+        r = O.mala_decode(q, kc, vc, lens, tau, 0.6, 64, 16)
+        mismatched += int((r["mask"] != m).sum())
+    # the per-key bound sees the mutant where one split holds most of the
+    # mass (its partial normalizer is then close to the merged one): here
+    # the newest of four 64-key splits, whose keys are twice as long
+    rng = np.random.default_rng(74)
+    q = rng.standard_normal((1, 4, 6)) * 2.5
+    kc = rng.standard_normal((1, 1, 256, 6))
+    vc = rng.standard_normal((1, 1, 256, 6))
+    kc[:, :, 192:] *= 2.0
+    bound_broken = 0
+    for tau in (0.05, 0.2, 0.5, 5.0):
+        monkeypatch.setattr(O, "fwd_block", _split_local_length_mutant(tau))
+        r = O.mala_decode(q, kc, vc, [256], tau, 0.6, 64, 16)
+        monkeypatch.undo()
+        ok = O.mala_decode(q, kc, vc, [256], tau, 0.6, 64, 16)
+        for h in range(4):
+            s = 0.6 * kc[0, 0] @ q[0, h]
+            for res, tally in ((r, True), (ok, False)):
+                omitted = ~decode_kept_keys(res["mask"][0, h], 256, 64, 16)
+                broken = int((np.exp(s[omitted] - res["lse"][0, h]) >= tau / 256).sum())
+                if tally:
+                    bound_broken += broken
+                else:
+                    assert broken == 0       # the oracle itself keeps the bound
+    monkeypatch.undo()
+    assert mismatched > 0 and bound_broken > 0
 
 
 def test_pins_catch_forced_backward_diagonal(monkeypatch):
