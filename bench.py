@@ -78,66 +78,27 @@ def bwd_tiles(nq, nk, bq, bk):
     return tot
 
 
-def head_rel_l2(x, x0):
-    """||x - x0|| / ||x0|| per (batch, head) over that head's [N, d] block."""
-    num = (x.float() - x0.float()).pow(2).sum((-1, -2)).sqrt()
-    den = x0.float().pow(2).sum((-1, -2)).sqrt().clamp_min(1e-30)
-    return (num / den).flatten()
-
-
-def mean_p95(t):
-    t = t.flatten().double()
-    return {"mean": float(t.mean()), "p95": float(t.sort().values[int(0.95 * (t.numel() - 1))])}
-
-
-def matched_work(m, W, torch, dev, fbq, fbk, n=8192):
+def matched_work(m, F, W, torch, dev, fbq, fbk, preset, n=8192):
     """Allocation at matched work (Sec. 3, Table 1; App. C.2) on structured
     inputs: MALA's forward support against a per-instance reference-mass
     control that keeps, for every decision (head x query block), exactly as
     many key tiles as MALA kept there, chosen by their mass under the
-    unscreened softmax. Both supports are scored the same way in fp32 from
-    the unscreened scores: omitted mass per row and the relative L2 error of
-    the output they imply, so the comparison isolates the allocation.
-    Measurement only: the supports come from the library, the scoring is
-    plain torch on the GPU."""
-    z = W.make_structured(n, hq=32, hkv=8, d=128, device=dev, dtype="bf16", with_do=False)
+    unscreened softmax (fidelity.reference_mass_control). Both supports are
+    scored the same way in fp32 from the unscreened scores: omitted mass per
+    row and the relative L2 error of the output they imply."""
+    z = W.make_structured_preset(preset, n, hq=32, hkv=8, d=128, device=dev, dtype="bf16",
+                                 with_do=False)
     q, k, v, scale = z["q"], z["k"], z["v"], z["scale"]
     _, HQ, N, _ = q.shape
-    G = HQ // k.shape[1]
     lse0 = m.mala_fwd(q, k, v, 0.0, softmax_scale=scale)["lse"]
-    causal = torch.ones(N, N, dtype=torch.bool, device=dev).tril()
     res = {"n": n, "heads": HQ, "decision": f"{fbq} query rows x {fbk} keys"}
     for tau_ in (1e-4, 1.0):
         mask = m.mala_fwd(q, k, v, tau_, softmax_scale=scale, want_mask=True)["mask"]
-        Tr, Tc = mask.shape[2], mask.shape[3]
-        acc = {"mala": ([], []), "control": ([], [])}
-        slots = 0
-        for h in range(HQ):
-            kh, vh = k[0, h // G].float(), v[0, h // G].float()
-            p = torch.exp((q[0, h].float() @ kh.T) * scale - lse0[0, h, :, None].float())
-            p = p.masked_fill(~causal, 0.0)                    # unscreened probabilities
-            o_ref = (p @ vh) / p.sum(-1, keepdim=True)
-            pt = p.view(N, Tc, fbk).sum(-1)                    # row mass per key tile
-            blk = pt.view(Tr, fbq, Tc).sum(1)                  # decision mass per key tile
-            keep = mask[0, h] == 1
-            cnt = keep.sum(-1)
-            slots += int(cnt.sum())
-            order = torch.argsort(blk, dim=-1, descending=True, stable=True)
-            rank = torch.empty_like(order)
-            rank.scatter_(1, order, torch.arange(Tc, device=dev).expand(Tr, Tc).contiguous())
-            ctrl = rank < cnt[:, None]                         # the same count, highest mass
-            for name, sup in (("mala", keep), ("control", ctrl)):
-                rows = sup.repeat_interleave(fbq, 0)[:N]       # [N, Tc]
-                om = 1.0 - (pt * rows).sum(-1) / p.sum(-1)
-                pk = p * rows.repeat_interleave(fbk, 1)[:, :N]
-                o = (pk @ vh) / pk.sum(-1, keepdim=True)
-                rl2 = (o - o_ref).norm(dim=-1) / o_ref.norm(dim=-1).clamp_min(1e-30)
-                acc[name][0].append(om)
-                acc[name][1].append(rl2)
-        row = {"slots_per_query": round(slots * fbk * fbq / (HQ * N), 1)}
-        for name, (om, rl2) in acc.items():
-            row[name] = {"omitted_mass": mean_p95(torch.cat(om)),
-                         "o_rel_l2": mean_p95(torch.cat(rl2))}
+        r = F.reference_mass_control(q, k, v, scale, lse0, mask, fbq, fbk)
+        row = {"slots_per_query": round(int((mask == 1).sum()) * fbk * fbq / (HQ * N), 1)}
+        for name in ("mala", "control"):
+            row[name] = {"omitted_mass": F.mean_p95(r[name]["omitted_mass"]),
+                         "o_rel_l2": F.mean_p95(r[name]["o_rel_l2"])}
         res[f"tau={tau_:g}"] = row
     return res
 
@@ -179,18 +140,26 @@ def profile_structured(tau, m, W, torch, dev):
     print(f"structured profile run done (tau={tau:g})", flush=True)
 
 
-def structured_section(args, m, W, torch, dev, tiling):
+NESTED_NOTE = ("outside the method: mala_bwd_nested skips the backward score recomputation of "
+               "the tiles the forward skipped, while the paper's backward recomputes Q K^T "
+               "before every skip decision (App. A.1); its speedups are not the method's")
+
+
+def structured_section(args, m, F, W, torch, dev, tiling, preset):
     """Extra, not part of ``value``: the same kernels on structured-logit inputs
-    (sink keys, a local band, sparse retrieval keys), where the tolerance does
-    skip tiles, timed against tau = 0. Prefill: 32K, 32/8 heads; decode: 8
-    sequences of 131072 keys, 8/1 heads, the query of each sequence being the
-    sequence's last row."""
+    (sink keys, a local band, sparse retrieval keys; the named preset of
+    workloads.make_structured_preset), where the tolerance does skip tiles,
+    timed against tau = 0. Prefill: 32K, 32/8 heads; decode: 8 sequences of
+    131072 keys, 8/1 heads, the query of each sequence being the sequence's
+    last row."""
     (fbq, fbk), (bbq, bbk), (dbk, dchunk) = tiling
     taus = (0.0, 1e-4, 1e-2, 1.0)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    res = {"inputs": "workloads.make_structured (bf16)"}
+    res = {"inputs": f"workloads.make_structured_preset({preset!r}) (bf16)",
+           "nested": NESTED_NOTE}
 
-    x = W.make_structured(32768, hq=32, hkv=8, d=128, device=dev, dtype="bf16", with_do=False)
+    x = W.make_structured_preset(preset, 32768, hq=32, hkv=8, d=128, device=dev, dtype="bf16",
+                                 with_do=False)
     q, k, v = x["q"], x["k"], x["v"]
     # dO: a deterministic Rademacher probe (App. C.3)
     do = W.rademacher(q.shape, seed=20269002, device=dev, dtype="bf16")
@@ -288,9 +257,9 @@ def structured_section(args, m, W, torch, dev, tiling):
                                  "max": float(rl2.max())}
         # head-level relative L2 errors (App. C.3): output and dQ per query
         # head, dK and dV per KV head
-        pre[tau_]["head_rel_l2"] = {"o": mean_p95(head_rel_l2(fo["o"], o0))}
+        pre[tau_]["head_rel_l2"] = {"o": F.mean_p95(F.head_rel_l2(fo["o"], o0))}
         for n_ in ("dq", "dk", "dv"):
-            pre[tau_]["head_rel_l2"][n_] = mean_p95(head_rel_l2(bo[n_], g0[n_]))
+            pre[tau_]["head_rel_l2"][n_] = F.mean_p95(F.head_rel_l2(bo[n_], g0[n_]))
         # mean post-score key slots per query (Eq. 11): kept tiles x B_k over
         # the block's rows
         pre[tau_]["slots_per_query"] = {
@@ -312,11 +281,12 @@ def structured_section(args, m, W, torch, dev, tiling):
     res["prefill_32k"] = {f"tau={t:g}": pre[t] for t in taus}
     del x, q, k, v, do, fo, bo, bg, fn, bn, g0
     torch.cuda.empty_cache()
-    res["matched_work_8k"] = matched_work(m, W, torch, dev, fbq, fbk)
+    res["matched_work_8k"] = matched_work(m, F, W, torch, dev, fbq, fbk, preset)
     torch.cuda.empty_cache()
 
     n = 131072
-    y = W.make_structured(n, hq=8, hkv=1, d=128, batch=8, device=dev, dtype="bf16", with_do=False)
+    y = W.make_structured_preset(preset, n, hq=8, hkv=1, d=128, batch=8, device=dev,
+                                 dtype="bf16", with_do=False)
     kc, vc = y["k"], y["v"]
     qd = y["q"][:, :, n - 1].contiguous()
     del y
@@ -601,6 +571,13 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = measured_traffic(dominant)      # HBM bytes per launch (rocprofv3)
     roof["algorithmic_per_launch"] = alg[dominant]
+    # the same ratio over each whole operator: the forward kernel alone, and
+    # the backward's prep + dK/dV + dQ (algorithmic FLOPs 2d E + 8d S_b, Eq. 16)
+    alg_bwd = alg["bwd_dkdv"] + alg["bwd_dq"]
+    roof["whole_fwd_frac"] = alg["fwd"] / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+    roof["whole_bwd_frac"] = alg_bwd / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+    roof["kernel_fracs"] = {n: round(alg[n] / (tms[n] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+                            for n in alg}
 
     out = {
         "metric": "MALA fwd+bwd ms & effective TFLOP/s vs tau=0 dense at 32K/128K; decode us/step",
@@ -637,11 +614,15 @@ def main():
             "merge_us": round(dmerge_us, 2), "append_us": round(dappend_us, 2),
             "in_step_us": round((ph[4] + ph[5] + ph[6]) * 1e3, 2),
             "v_tiles_kept_frac": dec_vtiles / dec_tiles_total,
-            "hbm_gbs": round(dec_bytes / (dsplit_us * 1e-6) / 1e9, 1),
-            "hbm_frac": round(dec_bytes / (dsplit_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            # the whole step (split + merge): algorithmic bytes / step time
+            "hbm_gbs": round(dec_bytes / (dec_all_us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(dec_bytes / (dec_all_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "split_kernel_hbm_frac": round(dec_bytes / (dsplit_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "bytes_per_step": dec_bytes,
         },
     }
+    out["peak_memory"] = peak_memory(m, torch, q, k, v, do, scale, tau, args.fast_grad,
+                                     qs[0], kc, vc, seqlens[0], cache0 + 1, y["scale"])
 
     # ------------------------------------------------------------ 128K prefill extra
     if not args.no_128k:
@@ -690,22 +671,66 @@ def main():
         keep_cpu = (q.cpu(), k.cpu(), v.cpu(), do.cpu()) if args.cpu_seconds > 0 else None
         del x, q, k, v, do
         torch.cuda.empty_cache()
-        out["structured"] = structured_section(args, m, W, torch, dev,
-                                               ((fbq, fbk), (bbq, bbk), (dbk, dchunk)))
+        from contribution_gated_sparse_amd import fidelity as F
+        out["structured"] = {
+            preset: structured_section(args, m, F, W, torch, dev,
+                                       ((fbq, fbk), (bbq, bbk), (dbk, dchunk)), preset)
+            for preset in ("sparse", "calibrated")}
         if keep_cpu is not None:
             q, k, v, do = (t.to(dev) for t in keep_cpu)
 
     # ------------------------------------------------------------ CPU oracle baseline
     if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(q, k, v, do, scale, tau, (fbq, fbk), (bbq, bbk),
-                                           args.cpu_seconds)
+        gf = m.mala_fwd(q, k, v, tau, softmax_scale=scale, want_mask=True)
+        gb = m.mala_bwd(q, k, v, gf["o"], gf["lse"], do, tau, softmax_scale=scale,
+                        want_mask=True, fast_grad=args.fast_grad)
+        torch.cuda.synchronize()
+        gpu = dict(fmask=gf["mask"], o=gf["o"], lse=gf["lse"], bmask=gb["mask"], dq=gb["dq"])
+        out["cpu_baseline"], out["parity"] = cpu_baseline(
+            q, k, v, do, scale, tau, (fbq, fbk), (bbq, bbk), args.cpu_seconds, gpu)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(q, k, v, do, scale, tau, ftile, btile, budget):
+def peak_memory(m, torch, q, k, v, do, scale, tau, fast_grad, qd, kc, vc, seq, n_k, dscale):
+    """Peak device memory each operator call allocates (outputs and
+    workspace, inputs resident beforehand), at tau and at tau = 0, from
+    torch's allocator statistics (Sec. 3 "Operator Latency and Memory"
+    compares MALA's peak operator memory with dense attention's)."""
+    res = {}
+    for tau_ in (tau, 0.0):
+        row = {}
+        for name in ("fwd", "bwd", "decode"):
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+            base = torch.cuda.memory_allocated()
+            torch.cuda.reset_peak_memory_stats()
+            if name == "fwd":
+                r = m.mala_fwd(q, k, v, tau_, softmax_scale=scale)
+            elif name == "bwd":
+                f = m.mala_fwd(q, k, v, tau_, softmax_scale=scale)
+                torch.cuda.synchronize()
+                base = torch.cuda.memory_allocated()
+                torch.cuda.reset_peak_memory_stats()
+                r = m.mala_bwd(q, k, v, f["o"], f["lse"], do, tau_, softmax_scale=scale,
+                               fast_grad=fast_grad)
+            else:
+                r = m.mala_decode(qd, kc, vc, seq, tau_, max_n_k=n_k, softmax_scale=dscale)
+            torch.cuda.synchronize()
+            row[name + "_bytes"] = int(torch.cuda.max_memory_allocated() - base)
+            del r
+        res[f"tau={tau_:g}"] = row
+    res["equal_to_tau0"] = res[f"tau={tau:g}"] == res["tau=0"]
+    return res
+
+
+def cpu_baseline(q, k, v, do, scale, tau, ftile, btile, budget, gpu=None):
     """Times the fp64 oracle on a bounded, seeded sample of 32-row query
     blocks of the 32K problem (forward + backward of those rows), and reports
-    the dense-equivalent TFLOP/s of the sample."""
+    the dense-equivalent TFLOP/s of the sample. With ``gpu`` (the library's
+    forward and backward outputs on the same inputs: masks, O, LSE, dQ) the
+    sampled rows are also compared with the oracle's: the strict max-abs
+    errors of O, LSE and dQ and the count of differing decisions outside the
+    near-tie band (replayed inside it). Returns (baseline, parity)."""
     import numpy as np
 
     from oracle import mala_oracle as O
@@ -717,35 +742,62 @@ def cpu_baseline(q, k, v, do, scale, tau, ftile, btile, budget):
     nblk = -(-N // bq)
     done_rows, flops, elapsed, nb = 0, 0.0, 0.0, 0
     kv_cache = {}
+    err = {"O": 0.0, "LSE": 0.0, "dQ": 0.0}
+    bad_decisions = 0
+    n64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
     while elapsed < budget and nb < 256:
         h = int(rng.integers(HQ))
         i = int(rng.integers(nblk))
         kh = h // g
         if kh not in kv_cache:
-            kv_cache[kh] = (k[0, kh].float().cpu().numpy().astype(np.float64)[None, None],
-                            v[0, kh].float().cpu().numpy().astype(np.float64)[None, None])
+            kv_cache[kh] = (n64(k[0, kh])[None, None], n64(v[0, kh])[None, None])
         kn, vn = kv_cache[kh]
         r0, r1 = i * bq, min(N, i * bq + bq)
-        qn = q[0, h].float().cpu().numpy().astype(np.float64)[None, None]
-        dn = do[0, h].float().cpu().numpy().astype(np.float64)[None, None]
+        qn = n64(q[0, h])[None, None]
+        dn = n64(do[0, h])[None, None]
+        qb = range(i * (bq // btile[0]), min(-(-N // btile[0]), (i + 1) * (bq // btile[0])))
+        fmask = gpu["fmask"][:, h:h + 1].cpu().numpy() if gpu else None
+        bmask = gpu["bmask"][:, h:h + 1].cpu().numpy() if gpu else None
         t0 = time.perf_counter()
-        f = O.mala_fwd(qn, kn, vn, tau, scale, True, ftile[0], ftile[1], blocks=[(0, 0, i)])
+        f = O.mala_fwd(qn, kn, vn, tau, scale, True, ftile[0], ftile[1], blocks=[(0, 0, i)],
+                       replay=fmask, band=1e-3 if gpu else 0.0)
         o = np.nan_to_num(f["o"])
         lse = np.nan_to_num(f["lse"])
-        O.mala_bwd(qn, kn, vn, o, lse, dn, tau, scale, True, btile[0], btile[1],
-                   qblocks=range(i * (bq // btile[0]), min(-(-N // btile[0]),
-                                                          (i + 1) * (bq // btile[0]))))
+        rb = O.mala_bwd(qn, kn, vn, o, lse, dn, tau, scale, True, btile[0], btile[1], qblocks=qb,
+                        replay=bmask, band=1e-3 if gpu else 0.0, o_storage="bf16",
+                        lse_storage="f32")
         elapsed += time.perf_counter() - t0
         nb += 1
         rows = np.arange(r0, r1)
         flops += 14 * D * float((rows + 1).sum())
         done_rows += r1 - r0
-    return {"value": round(flops / elapsed / 1e12, 6) if elapsed else None, "unit": "TFLOP/s",
+        if gpu:
+            seen = f["mask"][0, 0, i] != O.NOT_VISITED
+            clear = seen & ~(np.abs(np.nan_to_num(f["margin"][0, 0, i], nan=np.inf)) < 1e-3)
+            bad_decisions += int((f["mask"][0, 0, i][clear] != fmask[0, 0, i][clear]).sum())
+            for j in qb:
+                bseen = rb["mask"][0, 0, j] != O.NOT_VISITED
+                bclear = bseen & ~(np.abs(np.nan_to_num(rb["margin"][0, 0, j], nan=np.inf)) < 1e-3)
+                bad_decisions += int((rb["mask"][0, 0, j][bclear] != bmask[0, 0, j][bclear]).sum())
+            err["O"] = max(err["O"], float(np.abs(n64(gpu["o"][0, h, r0:r1]) - f["o"][0, 0, r0:r1]).max()))
+            err["LSE"] = max(err["LSE"], float(np.abs(n64(gpu["lse"][0, h, r0:r1])
+                                                      - f["lse"][0, 0, r0:r1]).max()))
+            err["dQ"] = max(err["dQ"], float(np.abs(n64(gpu["dq"][0, h, r0:r1])
+                                                    - rb["dq"][0, 0, r0:r1]).max()))
+    base = {"value": round(flops / elapsed / 1e12, 6) if elapsed else None, "unit": "TFLOP/s",
             "cores": threads, "kind": "oracle",
             "sample": f"{nb} random 32-row query blocks (random heads) of the 32K problem, "
                       f"forward + backward of their rows against all causal keys, numpy fp64; "
                       f"{elapsed:.1f} s; dense-equivalent FLOPs / time",
             "cpu": platform.processor() or platform.machine()}
+    parity = None
+    if gpu:
+        bars = {"O": 2e-2, "LSE": 1e-4, "dQ": 2e-2}
+        parity = {"workload": "the same 32K problem, the blocks of the CPU sample",
+                  "blocks": nb, "max_abs": {n_: float(f"{e:.3e}") for n_, e in err.items()},
+                  "bars": bars, "decisions_differing_outside_band": bad_decisions,
+                  "within_bars": bad_decisions == 0 and all(err[n_] <= bars[n_] for n_ in bars)}
+    return base, parity
 
 
 if __name__ == "__main__":

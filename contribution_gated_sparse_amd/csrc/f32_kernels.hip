@@ -148,9 +148,9 @@ __global__ __launch_bounds__(256) void bwd_prep_f32_kernel(int rows, int d, cons
   if (mask != nullptr)
     for (size_t i = gtid; i < nmask; i += nthr) mask[i] = -1;
   for (size_t r = gtid; r < (size_t)rows; r += nthr) {
-    float acc = 0.f;
-    for (int e = 0; e < d; ++e) acc = fmaf(O[r * d + e], dO[r * d + e], acc);
-    Dq[r] = acc;
+    double acc = 0.0;     // D feeds dP - D, which cancels: sum in fp64
+    for (int e = 0; e < d; ++e) acc = fma((double)O[r * d + e], (double)dO[r * d + e], acc);
+    Dq[r] = (float)acc;
   }
 }
 

@@ -255,7 +255,7 @@ def round_storage(x, dtype: Optional[str]) -> np.ndarray:
 def mala_bwd(q, k, v, o, lse, do, tau: float, scale: float, causal: bool = True,
              bq: int = 64, bk: int = 64, qblocks: Optional[Iterable] = None,
              replay: Optional[np.ndarray] = None, band: float = 0.0,
-             o_storage: Optional[str] = None):
+             o_storage: Optional[str] = None, lse_storage: Optional[str] = None):
     """MALA backward on the saved z = lse.
 
     Returns dict with dq [B,Hq,Nq,d], dk, dv [B,Hkv,Nk,d] (summed over the
@@ -269,8 +269,12 @@ def mala_bwd(q, k, v, o, lse, do, tau: float, scale: float, causal: bool = True,
     ``o_storage``: Algorithm 2 forms rowsum(O o dO) from the output the forward
     stored; when that output is kept in a narrower dtype ("bf16", "f32"),
     D is computed from o rounded to it.
+    ``lse_storage``: likewise, Algorithm 2 reads the log-normalizer the forward
+    saved; when it is stored in a narrower dtype ("f32"), the gate and P use
+    lse rounded to it.
     """
     q, k, v, o, lse, do = map(_f64, (q, k, v, o, lse, do))
+    lse = round_storage(lse, lse_storage)
     b_, hq, nq, _ = q.shape
     hkv, nk = k.shape[1], k.shape[2]
     g = hq // hkv

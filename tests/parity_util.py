@@ -2,6 +2,8 @@
 the exact same (rounded) inputs, and compare decisions and values."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -10,17 +12,65 @@ from oracle import mala_oracle as O
 # Near-tie band of a decision margin (nats): decisions this close to the
 # threshold may go either way between an fp64 and an fp32 evaluation.
 BAND = {"f32": 1e-4, "bf16": 1e-3}
-# Value tolerances, stated for unit-scale tensors: fp32 inputs max error 1e-5
-# against the oracle; bf16 inputs max error 2e-2 and relative Frobenius error
-# 1e-2. The max error is taken relative to the tensor's scale,
-# max|got - ref| <= tol * max(1, max|ref|): a gradient entry is a sum of
-# terms of the tensor's magnitude, and bf16 (fp32) operands round each term by
-# up to 2^-9 (2^-24) of it, so an entry of size 1 inside a tensor of size 14
-# cannot be within 2e-2 absolute in any bf16-operand implementation. The
-# strict element-wise absolute error is reported next to it.
+# The stated value bars against the oracle, as absolute element-wise errors:
+# fp32 inputs max |got - ref| <= 1e-5; bf16 inputs max |got - ref| <= 2e-2
+# and relative Frobenius error <= 1e-2. Every comparison records the strict
+# absolute error, the tensor's largest magnitude, the error scaled by
+# max(1, max|ref|) and the relative Frobenius error (STATS), and asserts the
+# strict bar unless the caller names the comparison a known deviation
+# (``strict=False``, each listed with its measured size and cause in the
+# design notes); those still assert the scaled bar.
 TOL_F32 = 1e-5
 TOL_BF16_ABS = 2e-2
 TOL_BF16_FRO = 1e-2
+# Log-normalizer (LSE, natural log) bars. fp32 inputs: the fp32 kernels
+# compute in fp64 and round z once to fp32 (|z| < 64 here: 2^-19 absolute),
+# so 1e-5 leaves a wide margin. bf16 inputs: scores are exact fp32 products of
+# bf16 values; the error is the fp32 running sum of up to N_k/64 tile sums
+# (relative error below N_k/64 * 2^-24, 5e-5 at 128K) plus the hardware
+# exp2/log2 approximations (a few ulp), so 1e-4 nats.
+TOL_LSE = {"f32": 1e-5, "bf16": 1e-4}
+# Known deviations from the strict absolute bar: (test function, tensor) ->
+# the absolute bound asserted instead (about twice the largest error measured
+# over the test's cases). The bf16 entries are gradients of problems whose
+# entries reach 3-100: P enters dV^T = dO^T P and dS enters dK^T = Q^T dS as
+# bf16 MFMA operands (relative rounding up to 2^-9 per term), so the error of
+# an entry grows with the magnitude of the terms summed into it. The fp32
+# entry (F32_KNOWN_DEVIATIONS) is dK of the structured inputs, whose entries
+# reach 74: 1.6e-5 there is two fp32 ulps. The graded workloads (8K, 32K over
+# its tolerance sweep, 128K, the 128K decode, and the tiny fp32 problem) meet
+# the strict bar.
+F32_KNOWN_DEVIATIONS = {
+    ("test_structured_skipping_fwd_bwd", "dK"): 3e-5,
+}
+KNOWN_DEVIATIONS = {
+    ("test_bf16_shapes_fwd_bwd", "dK"): 0.25,
+    ("test_bf16_shapes_fwd_bwd", "dQ"): 0.05,
+    ("test_bf16_shapes_fwd_bwd", "dV"): 0.1,
+    ("test_gate_pass_shapes", "dK"): 0.25,
+    ("test_gate_pass_shapes", "dQ"): 0.05,
+    ("test_gate_pass_shapes", "dV"): 0.1,
+    ("test_nested_shapes", "dK"): 0.25,
+    ("test_nested_shapes", "dQ"): 0.05,
+    ("test_nested_shapes", "dV"): 0.1,
+    ("test_noncausal", "dK"): 0.12,
+    ("test_gate_pass_noncausal_and_f32", "dK"): 0.12,
+    ("test_nested_noncausal_fast_grad_and_f32", "dK"): 0.12,
+    ("test_fast_grad_flag_same_support", "dk fast"): 0.07,
+    ("test_fast_grad_flag_same_support", "dk split"): 0.07,
+    ("test_nested_arbitrary_forward_masks", "dk"): 0.07,
+    ("test_gate_pass_structured", "dK"): 1.25,
+    ("test_gate_pass_structured", "dQ"): 0.13,
+    ("test_gate_pass_structured", "dV"): 0.16,
+    ("test_structured_skipping_fwd_bwd", "dK"): 0.6,
+    ("test_structured_skipping_fwd_bwd", "dQ"): 0.12,
+    ("test_structured_skipping_fwd_bwd", "dV"): 0.1,
+    ("test_structured_calibrated_fwd_bwd", "dK"): 3.0,
+    ("test_structured_calibrated_fwd_bwd", "dV"): 0.5,
+}
+# With MALA_PARITY_COLLECT=1 a failed strict bar is recorded instead of
+# raised (the scaled bar is still asserted), to survey a whole run at once.
+COLLECT = os.environ.get("MALA_PARITY_COLLECT", "") == "1"
 
 
 def np64(t: torch.Tensor) -> np.ndarray:
@@ -39,8 +89,20 @@ def tiling():
 STATS = []
 
 
-def compare_values(name, got, ref, kind, rows=None):
-    """Return (max_abs, rel_fro) and assert the tolerance of ``kind``."""
+def _current_test():
+    return os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+
+
+def record(name, **kw):
+    STATS.append(dict(test=_current_test(), name=name, **kw))
+
+
+def compare_values(name, got, ref, kind, rows=None, strict=True):
+    """Compare ``got`` with the oracle's ``ref``; return (max_abs, rel_fro).
+
+    Asserts the stated bar of ``kind`` on the strict absolute error, or only
+    the error scaled by max(1, max|ref|) for a known deviation
+    (``strict=False``)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     if rows is not None:
@@ -52,16 +114,44 @@ def compare_values(name, got, ref, kind, rows=None):
     den = float(np.linalg.norm(ref.ravel()))
     fro = float(np.linalg.norm((got - ref).ravel()) / den) if den > 0 else mx
     scaled = mx / max(1.0, rmax)
-    msg = (f"{name}: max abs {mx:.3e}, max|ref| {rmax:.3e}, max abs / max(1, max|ref|) "
-           f"{scaled:.3e}, rel fro {fro:.3e}")
-    STATS.append(msg)
-    print(msg)
-    if kind == "f32":
-        assert scaled <= TOL_F32, msg
+    bar = TOL_F32 if kind == "f32" else TOL_BF16_ABS
+    fn = _current_test().split("::")[-1].split("[")[0]
+    table = KNOWN_DEVIATIONS if kind == "bf16" else F32_KNOWN_DEVIATIONS
+    if strict and (fn, name) in table:
+        strict = False
+        dev_bar = table[(fn, name)]
     else:
-        assert scaled <= TOL_BF16_ABS, msg
+        dev_bar = None
+    strict_ok = mx <= bar
+    msg = (f"{name}: max abs {mx:.3e} (bar {bar:g}), max|ref| {rmax:.3e}, "
+           f"max abs / max(1, max|ref|) {scaled:.3e}, rel fro {fro:.3e}"
+           + ("" if strict_ok else (" [known deviation]" if not strict else " [STRICT BAR FAILED]")))
+    record(name, kind=kind, max_abs=mx, max_ref=rmax, scaled=scaled, rel_fro=fro, bar=bar,
+           strict=strict, strict_ok=strict_ok, deviation_bar=dev_bar)
+    print(msg)
+    assert scaled <= bar, msg
+    if kind == "bf16":
         assert fro <= TOL_BF16_FRO, msg
+    if dev_bar is not None:
+        assert mx <= dev_bar, msg + f" (known-deviation bound {dev_bar:g})"
+    if strict and not COLLECT:
+        assert strict_ok, msg
     return mx, fro
+
+
+def check_lse(name, got, ref, kind):
+    """Largest LSE error against the oracle, asserted against TOL_LSE."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(got)), f"{name}: -inf rows differ"
+    d = float(np.abs(got[fin] - ref[fin]).max()) if fin.any() else 0.0
+    record(name, kind=kind, max_abs=d, bar=TOL_LSE[kind], strict=True,
+           strict_ok=d <= TOL_LSE[kind])
+    print(f"{name}: max abs {d:.3e} nats (bar {TOL_LSE[kind]:g})")
+    if not COLLECT:
+        assert d <= TOL_LSE[kind], f"{name} error {d:.3e}"
+    return d
 
 
 def check_forward(x, tau, causal=True, blocks=None, max_ties=None):
@@ -91,14 +181,117 @@ def check_forward(x, tau, causal=True, blocks=None, max_ties=None):
     rows = np.repeat(done, bq, axis=-1)[..., : q.shape[2]]
     go, gl = np64(g["o"]), np64(g["lse"])
     e_o = compare_values("O", go, r["o"], kind, rows)
-    d_l = float(np.abs(gl[rows] - r["lse"][rows]).max()) if rows.any() else 0.0
-    assert d_l <= (1e-5 if kind == "f32" else 2e-3), f"LSE error {d_l:.3e}"
+    d_l = check_lse("LSE", gl[rows], r["lse"][rows], kind)
+    record("forward near ties", kind=kind, count=int(r["near_ties"]), bar=max_ties)
     if max_ties is not None:
         assert r["near_ties"] <= max_ties, f"{r['near_ties']} near-tie decisions"
     visited = om != O.NOT_VISITED
     stats = dict(o_max_abs=e_o[0], o_rel_fro=e_o[1], lse_max_abs=d_l, near_ties=r["near_ties"],
                  kept_frac=float((om == O.KEPT).sum() / max(1, visited.sum())))
     return g, r, stats
+
+
+def check_ties(name, count, bar, kind="bf16"):
+    """Bound a count of near-tie decisions (margins inside BAND)."""
+    record(name, kind=kind, count=int(count), bar=bar)
+    print(f"{name}: {int(count)} (bar {bar})")
+    if bar is not None and not COLLECT:
+        assert count <= bar, f"{name}: {int(count)} near-tie decisions (bar {bar})"
+
+
+def assert_bitwise_where_agree(ma, mb, a, b, group, dkdv=True):
+    """Two backward runs that differ only in how they reach their decisions
+    (``ma``, ``mb``: backward tile masks) give the same bits wherever they
+    decided alike: dQ on every 32-row block whose decision row agrees (the
+    dQ kernel is the same in every mode), and with ``dkdv`` dK and dV on
+    every 128-key block (one dK/dV workgroup) whose decisions agree over all
+    rows of the KV head's query heads. Returns the number of row blocks and
+    key blocks compared; only decisions that differ may take one out."""
+    (_, _, _), (bq, bk, _), _ = tiling()
+    agree_rows = (ma == mb).all(-1)                          # [B, Hq, Tr]
+    dq_a, dq_b = a["dq"].cpu(), b["dq"].cpu()
+    n_rows = 0
+    for (bb, h, i) in zip(*np.nonzero(agree_rows)):
+        sl = slice(i * bq, (i + 1) * bq)
+        assert torch.equal(dq_a[bb, h, sl], dq_b[bb, h, sl]), ("dq", bb, h, i)
+        n_rows += 1
+    ndiff = int((ma != mb).sum())
+    assert n_rows >= agree_rows.size - ndiff
+    if not dkdv:
+        return n_rows, 0
+    B, HQ, TR, TC = ma.shape
+    per = 128 // bk
+    nkb = -(-TC // per)
+    same = np.ones((B, HQ // group, nkb * per), bool)
+    same[:, :, :TC] = (ma == mb).reshape(B, HQ // group, group * TR, TC).all(2)
+    agree_kb = same.reshape(B, HQ // group, nkb, per).all(-1)          # [B, Hkv, n_kb]
+    n_kb = 0
+    for n in ("dk", "dv"):
+        ta, tb = a[n].cpu(), b[n].cpu()
+        for (bb, hk, j) in zip(*np.nonzero(agree_kb)):
+            sl = slice(j * 128, (j + 1) * 128)
+            assert torch.equal(ta[bb, hk, sl], tb[bb, hk, sl]), (n, bb, hk, j)
+            n_kb += n == "dk"
+    assert n_kb >= agree_kb.size - ndiff
+    return n_rows, n_kb
+
+
+def o_rounding_dq_term(q, k, v, do, scale, causal, fwd, bwd, rows=None):
+    """Per-element bound on how far dQ can move between two correct
+    backwards that each read their own bf16-stored O (Algorithm 2 forms
+    D_q = rowsum(O o dO) from the stored output).
+
+    Both sides round O to bf16 (unit roundoff u = 2^-8): the oracle its fp64
+    O once; the library an fp32 O whose P V products took P in bf16 (at most
+    2u of sum_k P_qk |v_kd| more). The two D_q then differ by at most
+    dD_q = 4u sum_d |dO_qd| A_qd, A_qd = sum_k P_qk |v_kd| (P: the forward's
+    retained probabilities), and dQ_q = scale sum_k P^b_qk (dP_qk - D_q) k_k
+    moves by at most scale dD_q |(P^b K)_qd| (P^b: the backward's kept
+    probabilities against the stored fp32 z). ``fwd``, ``bwd``: the oracle's
+    forward and backward results (their masks and z); q, k, v, do: fp64
+    arrays [B,H,N,d]. Returns an array shaped like dQ (or dQ[rows])."""
+    b_, hq, nq, d = q.shape
+    hkv, nk = k.shape[1], k.shape[2]
+    g = hq // hkv
+    (fbq, fbk, _), (bbq, bbk, _), _ = tiling()
+    out = np.zeros(q.shape)
+    keys = np.arange(nk)
+    for b in range(b_):
+        for h in range(hq):
+            kh = h // g
+            ridx = np.arange(nq) if rows is None else np.nonzero(rows[b, h])[0]
+            if ridx.size == 0:
+                continue
+            s = scale * (q[b, h, ridx] @ k[b, kh].T)
+            legal = (keys[None, :] <= ridx[:, None] + (nk - nq)) if causal else np.ones(s.shape, bool)
+            fk = fwd["mask"][b, h][ridx // fbq][:, keys // fbk] == O.KEPT
+            z = fwd["lse"][b, h, ridx]
+            p_f = np.where(legal & fk, np.exp(s - z[:, None]), 0.0)
+            a_f = p_f @ np.abs(v[b, kh])
+            z32 = z.astype(np.float32).astype(np.float64)
+            bk_ = bwd["mask"][b, h][ridx // bbq][:, keys // bbk] == O.KEPT
+            p_b = np.where(legal & bk_, np.exp(s - z32[:, None]), 0.0)
+            d_d = 4 * 2.0 ** -8 * (np.abs(do[b, h, ridx]) * a_f).sum(-1)
+            out[b, h, ridx] = scale * d_d[:, None] * np.abs(p_b @ k[b, kh])
+    return out if rows is None else out[rows]
+
+
+def check_dq_o_rounding(name, got, ref, term):
+    """dQ within the stated bar plus the bf16-O rounding term, element by
+    element and in Frobenius norm (o_rounding_dq_term)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    ratio = float((err / (TOL_BF16_ABS + term)).max())
+    fro = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    fro_bar = TOL_BF16_FRO + float(np.linalg.norm(term) / np.linalg.norm(ref))
+    record(name, kind="bf16", max_abs=float(err.max()), max_ref=float(np.abs(ref).max()),
+           bound_ratio=ratio, rel_fro=fro, fro_bar=fro_bar, largest_term=float(term.max()))
+    msg = (f"{name}: max abs {err.max():.3e}, max|ref| {np.abs(ref).max():.3e}, error / (2e-2 + "
+           f"O-rounding term) {ratio:.3f} (largest term {term.max():.3e}), rel fro {fro:.3e} "
+           f"(bar {fro_bar:.3e})")
+    print(msg, flush=True)
+    assert ratio <= 1.0 and fro <= fro_bar, msg
 
 
 def check_nesting(fmask, bmask):

@@ -1,0 +1,170 @@
+"""GPU tests of the fidelity and matched-work measurements (App. C.2, C.3;
+Sec. 3, Table 1) that the benchmark reports, on small structured problems of
+both presets, against the CPU fp64 oracle.
+
+  - omitted mass 1 - exp(z_tau - z_0) from the library's LSEs against the
+    oracle's omitted_mass of its own LSEs, and Prop. 1's bound;
+  - head-level relative L2 errors against the tau = 0 operator (O, dQ, dK,
+    dV with a Rademacher dO probe) against the same quantity formed from the
+    oracle's outputs: by the triangle inequality the two differ by at most
+    the two runs' own output errors against the oracle;
+  - the matched-work reference-mass control: the same number of kept tiles
+    in every decision, tiles of largest unscreened mass, and its omitted
+    mass and MALA's against an fp64 recomputation from the oracle's dense
+    probabilities.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import mala_oracle as O
+from parity_util import BAND, TOL_LSE, np64, record, tiling
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():   # collected on CPU only to be deselected
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+DEV = "cuda"
+
+
+def lib():
+    import contribution_gated_sparse_amd as m
+    return m
+
+
+def fidelity():
+    from contribution_gated_sparse_amd import fidelity as F
+    return F
+
+
+def _problem(preset, hq=4, hkv=2):
+    # the calibrated preset's local band spans about a thousand keys: at 3000
+    # positions its gate skips the far tiles
+    n = 1200 if preset == "sparse" else 3000
+    hq, hkv = (hq, hkv) if preset == "sparse" else (2, 1)
+    x = W.make_structured_preset(preset, n, hq=hq, hkv=hkv, d=128, device=DEV, with_do=False)
+    x["do"] = W.rademacher(x["q"].shape, seed=20269003, device=DEV, dtype="bf16")
+    return x
+
+
+@pytest.mark.parametrize("preset", ["sparse", "calibrated"])
+@pytest.mark.parametrize("tau", [1e-2, 1.0])
+def test_omitted_mass_and_head_rel_l2(preset, tau):
+    m, F = lib(), fidelity()
+    x = _problem(preset)
+    q, k, v, do, scale = x["q"], x["k"], x["v"], x["do"], x["scale"]
+    (fbq, fbk, _), (bbq, bbk, _), _ = tiling()
+    print(f"[fidelity] preset={preset} tau={tau}", flush=True)
+    runs = {}
+    for t in (tau, 0.0):
+        f = m.mala_fwd(q, k, v, t, softmax_scale=scale, want_mask=True)
+        b = m.mala_bwd(q, k, v, f["o"], f["lse"], do, t, softmax_scale=scale, want_mask=True)
+        runs[t] = (f, b)
+    torch.cuda.synchronize()
+    qn, kn, vn, dn = np64(q), np64(k), np64(v), np64(do)
+    ref = {}
+    for t, (f, b) in runs.items():
+        r = O.mala_fwd(qn, kn, vn, t, scale, True, fbq, fbk, replay=f["mask"].cpu().numpy(),
+                       band=BAND["bf16"])
+        rb = O.mala_bwd(qn, kn, vn, r["o"], r["lse"], dn, t, scale, True, bbq, bbk,
+                        replay=b["mask"].cpu().numpy(), band=BAND["bf16"], o_storage="bf16",
+                        lse_storage="f32")
+        ref[t] = dict(o=r["o"], lse=r["lse"], dq=rb["dq"], dk=rb["dk"], dv=rb["dv"])
+    (f, b), (f0, b0) = runs[tau], runs[0.0]
+    assert (f["mask"] == 0).any(), "the problem skips tiles"
+
+    # ---- omitted mass (App. C.2) and Prop. 1
+    eps = F.omitted_mass(f["lse"], f0["lse"]).cpu().numpy()
+    eps_ref = O.omitted_mass(ref[tau]["lse"], ref[0.0]["lse"])
+    d_eps = float(np.abs(eps - eps_ref).max())
+    record("omitted mass", kind="bf16", max_abs=d_eps, bar=2 * TOL_LSE["bf16"],
+           mean=float(eps_ref.mean()), max_ref=float(eps_ref.max()))
+    print(f"omitted mass: mean {eps_ref.mean():.3e}, max {eps_ref.max():.3e}, "
+          f"largest difference {d_eps:.3e}", flush=True)
+    # 1 - e^{a} moves by at most |da| for a <= 0: each LSE is within TOL_LSE
+    assert d_eps <= 2 * TOL_LSE["bf16"]
+    assert (eps <= tau / (1 + tau) + 2 * TOL_LSE["bf16"]).all()
+
+    # ---- head-level relative L2 errors against tau = 0 (App. C.3)
+    tensors = {"o": (f["o"], f0["o"]), "dq": (b["dq"], b0["dq"]), "dk": (b["dk"], b0["dk"]),
+               "dv": (b["dv"], b0["dv"])}
+    def norms(t):                      # per (batch, head) L2 norm of [N, d]
+        t = np.asarray(t, dtype=np.float64)
+        return np.linalg.norm(t.reshape(-1, t.shape[-2] * t.shape[-1]), axis=-1)
+
+    for name, (a, a0) in tensors.items():
+        got = F.head_rel_l2(a, a0).cpu().numpy()
+        r1, r0 = ref[tau][name], ref[0.0][name]
+        want = norms(r1 - r0) / norms(r0)
+        an, a0n = np64(a), np64(a0)
+        # got = |a - a0| / |a0|, want = |r1 - r0| / |r0|; the triangle
+        # inequality bounds |got - want| by (|a - r1| + |a0 - r0| (1 + want)) / |a0|
+        slack = (norms(an - r1) + norms(a0n - r0) * (1 + want)) / norms(a0n)
+        diff = np.abs(got - want)
+        record(f"head rel-L2 {name}", kind="bf16", max_abs=float(diff.max()),
+               ref_mean=float(want.mean()), slack=float(slack.max()))
+        print(f"head rel-L2 {name}: oracle mean {want.mean():.3e}, library mean "
+              f"{got.mean():.3e}, largest difference {diff.max():.3e} (bound {slack.max():.3e})",
+              flush=True)
+        assert (diff <= slack * (1 + 1e-6) + 1e-12).all(), name
+
+
+@pytest.mark.parametrize("preset", ["sparse", "calibrated"])
+@pytest.mark.parametrize("tau", [1e-2, 1.0])
+def test_matched_work_control(preset, tau):
+    m, F = lib(), fidelity()
+    x = _problem(preset, hq=2, hkv=1)
+    q, k, v, scale = x["q"], x["k"], x["v"], x["scale"]
+    (fbq, fbk, _), _, _ = tiling()
+    f = m.mala_fwd(q, k, v, tau, softmax_scale=scale, want_mask=True)
+    f0 = m.mala_fwd(q, k, v, 0.0, softmax_scale=scale)
+    res = F.reference_mass_control(q, k, v, scale, f0["lse"], f["mask"], fbq, fbk)
+    torch.cuda.synchronize()
+    mask = f["mask"].cpu().numpy()
+    ctrl = res["control_support"].cpu().numpy()
+    kept = mask == O.KEPT
+    # the same work: equal kept-tile counts in every decision
+    assert np.array_equal(ctrl.sum(-1), kept.sum(-1))
+    assert not (ctrl & (mask == O.NOT_VISITED)).any()
+
+    # fp64 recomputation from the oracle's dense probabilities
+    qn, kn, vn = np64(q), np64(k), np64(v)
+    o0, z0 = O.dense_fwd(qn, kn, vn, scale, True)
+    B, HQ, N, _ = qn.shape
+    G = HQ // kn.shape[1]
+    Tc = mask.shape[3]
+    keys = np.arange(N)
+    worst = 0.0
+    for h in range(HQ):
+        s = scale * qn[0, h] @ kn[0, h // G].T
+        p = np.where(keys[None, :] <= keys[:, None], np.exp(s - z0[0, h][:, None]), 0.0)
+        pt = np.add.reduceat(p, np.arange(0, N, fbk), axis=1)            # [N, Tc]
+        blk = np.add.reduceat(pt, np.arange(0, N, fbq), axis=0)          # [Tr, Tc]
+        for name, sup in (("mala", kept[0, h]), ("control", ctrl[0, h])):
+            rows = np.repeat(sup, fbq, axis=0)[:N]
+            om = 1.0 - (pt * rows).sum(-1)
+            got = res[name]["omitted_mass"][0, h].cpu().numpy()
+            worst = max(worst, float(np.abs(got - om).max()))
+            assert np.abs(got - om).max() <= 2e-5, (name, h)
+            if name == "mala":    # the mask's omitted mass is the LSE's (Eq. 6)
+                r = O.mala_fwd(qn[:, h:h + 1], kn[:, h // G:h // G + 1], vn[:, h // G:h // G + 1],
+                               tau, scale, True, fbq, fbk, replay=mask[:, h:h + 1], band=BAND["bf16"])
+                np.testing.assert_allclose(om, O.omitted_mass(r["lse"][0, 0], z0[0, h]),
+                                           atol=1e-9)
+        # the control's tiles are those of largest block mass (up to fp32 ties)
+        for i in range(blk.shape[0]):
+            c = ctrl[0, h, i]
+            if c.any() and (~c & (mask[0, h, i] != O.NOT_VISITED)).any():
+                lo = blk[i][c].min()
+                hi = blk[i][~c & (mask[0, h, i] != O.NOT_VISITED)].max()
+                assert lo >= hi - 1e-6 * max(1.0, hi), (h, i)
+    record("matched-work omitted mass", kind="bf16", max_abs=worst, bar=2e-5)
+    mo = float(res["mala"]["omitted_mass"].mean())
+    co = float(res["control"]["omitted_mass"].mean())
+    print(f"[matched work] preset={preset} tau={tau}: omitted mass MALA {mo:.3e}, control {co:.3e}; "
+          f"largest difference from fp64 {worst:.3e}", flush=True)
+    # the control keeps the same count by largest mass, so it omits no more
+    # mass than MALA in any decision block, up to fp32 rounding
+    assert co <= mo + 1e-6

@@ -22,7 +22,8 @@ import torch
 
 import workloads as W
 from oracle import mala_oracle as O
-from parity_util import BAND, compare_values, np64, tiling
+from parity_util import (BAND, assert_bitwise_where_agree, check_dq_o_rounding, check_lse,
+                         check_ties, compare_values, np64, o_rounding_dq_term, tiling)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,14 +39,16 @@ def lib():
     return m
 
 
-def _agree(gm, om, margin, what):
+def _agree(gm, om, margin, what, max_ties=8):
     """Decisions agree wherever the oracle visited and the margin is clear of
-    the near-tie band."""
+    the near-tie band; the near ties themselves are counted and bounded."""
     seen = om != O.NOT_VISITED
     clear = seen & ~(np.abs(np.nan_to_num(margin, nan=np.inf)) < BAND["bf16"])
     bad = int((gm[clear] != om[clear]).sum())
     assert bad == 0, f"{what}: {bad} decisions differ outside the near-tie band"
-    return int((seen & ~clear).sum())
+    ties = int((seen & ~clear).sum())
+    check_ties(f"{what} near ties (of {int(seen.sum())})", ties, max_ties)
+    return ties
 
 
 # C3 runs at every tolerance of its sweep (tau = 0 is dense attention)
@@ -88,12 +91,12 @@ def test_prefill_full_size_sampled(cid, tau):
     for i in blocks:
         rows[..., i * fbq:(i + 1) * fbq] = True
     compare_values("O", np64(g["o"][:, h:h + 1]), r["o"], "bf16", rows)
-    dl = float(np.abs(np64(g["lse"][:, h:h + 1])[rows] - r["lse"][rows]).max())
-    assert dl <= 2e-3, f"LSE error {dl:.3e}"
+    check_lse("LSE", np64(g["lse"][:, h:h + 1])[rows], r["lse"][rows], "bf16")
 
     bmask = gb["mask"][:, h:h + 1].cpu().numpy()
     rb = O.mala_bwd(qh, kn, vn, r["o"], r["lse"], doh, tau, scale, True, bbq, bbk,
-                    qblocks=blocks, replay=bmask, band=BAND["bf16"], o_storage="bf16")
+                    qblocks=blocks, replay=bmask, band=BAND["bf16"], o_storage="bf16",
+                    lse_storage="f32")
     _agree(bmask, rb["mask"], rb["margin"], "backward")
     compare_values("dQ", np64(gb["dq"][:, h:h + 1]), rb["dq"], "bf16", rows)
 
@@ -107,7 +110,8 @@ def test_prefill_full_size_sampled(cid, tau):
     compare_values("O tail", np64(g["o"][:, heads, N - t:]), rt["o"], "bf16")
     bt = gb["mask"][:, heads, -(t // bbq):].cpu().numpy()
     rbt = O.mala_bwd(qt, kn, vn, rt["o"], rt["lse"], dot, tau, scale, True, bbq, bbk,
-                     replay=bt, band=BAND["bf16"], o_storage="bf16")
+                     replay=bt, band=BAND["bf16"], o_storage="bf16",
+                    lse_storage="f32")
     _agree(bt, rbt["mask"], rbt["margin"], "backward (tail)")
     compare_values("dQ tail", np64(gb["dq"][:, heads, N - t:]), rbt["dq"], "bf16")
     compare_values("dK tail", np64(gb["dk"][:, kh:kh + 1, N - t:]), rbt["dk"][:, :, N - t:], "bf16")
@@ -158,29 +162,17 @@ def test_gate_pass_full_size_structured():
         rows[..., i * fbq:(i + 1) * fbq] = True
     bmask = mb[:, h:h + 1]
     rb = O.mala_bwd(qh, kn, vn, r["o"], r["lse"], doh, TAU, scale, True, bbq, bbk,
-                    qblocks=blocks, replay=bmask, band=BAND["bf16"], o_storage="bf16")
+                    qblocks=blocks, replay=bmask, band=BAND["bf16"], o_storage="bf16",
+                    lse_storage="f32")
     _agree(bmask, rb["mask"], rb["margin"], "backward (gate pass)")
-    # dQ on these inputs is at the conditioning limit of a bf16-stored O: in
-    # sink-dominated rows dP - D nearly cancels, and the oracle's own dQ moves
-    # by about 1% when its O is stored in bf16 (as the backward reads it)
-    # instead of kept in fp64. The bound is the stated bar or twice that
-    # movement, whichever is larger; both references are the oracle's.
-    rb64 = O.mala_bwd(qh, kn, vn, r["o"], r["lse"], doh, TAU, scale, True, bbq, bbk,
-                      qblocks=blocks, replay=bmask, band=BAND["bf16"], o_storage=None)
-    gdq = np64(gb["dq"][:, h:h + 1])[rows]
-    ref, ref64 = rb["dq"][rows], rb64["dq"][rows]
-
-    def errs(a, b_):
-        return (float(np.abs(a - b_).max() / max(1.0, np.abs(b_).max())),
-                float(np.linalg.norm(a - b_) / max(np.linalg.norm(b_), 1e-30)))
-    e_max, e_fro = errs(gdq, ref)
-    s_max, s_fro = errs(ref, ref64)
-    print(f"dQ (gate pass): {e_max:.3e} / {e_fro:.3e}; oracle bf16-O sensitivity "
-          f"{s_max:.3e} / {s_fro:.3e}", flush=True)
-    assert e_max <= max(2e-2, 2 * s_max) and e_fro <= max(1e-2, 2 * s_fro)
+    # dQ on these inputs is at the conditioning limit of a bf16-stored O (in
+    # sink-led rows dP - D nearly cancels): the stated bar plus the bf16-O
+    # rounding term of o_rounding_dq_term, element by element and in norm
+    term = o_rounding_dq_term(qh, kn, vn, doh, scale, True, r, rb, rows)
+    check_dq_o_rounding("dQ (gate pass, structured)", np64(gb["dq"][:, h:h + 1])[rows],
+                        rb["dq"][rows], term)
     # the dQ kernel is the default path's: the same decisions give the same dQ
-    if np.array_equal(ma, mb):
-        assert torch.equal(ga["dq"], gb["dq"])
+    assert_bitwise_where_agree(ma, mb, ga, gb, G, dkdv=False)
 
     for n_ in ("dk", "dv"):
         a, b_ = np64(gb[n_]), np64(ga[n_])
@@ -200,9 +192,7 @@ def test_gate_pass_full_size_structured():
     assert np.array_equal(mc, np.where((mb == O.KEPT) & (up != O.KEPT), O.SKIPPED, mb))
     assert int((mc != mb).sum()) <= 16, f"{int((mc != mb).sum())} decisions differ"
     assert np.array_equal(gc["kept"].cpu().numpy(), (mc == O.KEPT).sum(-1))
-    if np.array_equal(mb, mc):
-        for n_ in ("dq", "dk", "dv"):
-            assert torch.equal(gb[n_], gc[n_]), n_
+    assert_bitwise_where_agree(mb, mc, gb, gc, G)
 
 
 @pytest.mark.parametrize("step,split_keys", [(0, 0), (63, 0), (0, -1)])
@@ -231,5 +221,4 @@ def test_decode_full_size(step, split_keys):
     assert np.array_equal(kept[:, :HQ], (r["mask"] == O.KEPT).sum((-1, -2)))
     assert np.array_equal(kept[:, HQ:], r["v_tiles"].sum((-1, -2)))
     compare_values("decode O", np64(g["o"]), r["o"], "bf16")
-    dl = float(np.abs(np64(g["lse"]) - r["lse"]).max())
-    assert dl <= 2e-3, f"LSE error {dl:.3e}"
+    check_lse("decode LSE", np64(g["lse"]), r["lse"], "bf16")
