@@ -12,7 +12,9 @@
 //     is consumed, so one barrier per tile suffices;
 //   - V^T, the A operand of O^T += V^T P^T, comes from the row-major V tile
 //     through transposing LDS reads (ds_read_b64_tr_b16), so V is written to
-//     LDS with plain 16-byte stores;
+//     LDS with plain 16-byte stores; at d = 128 the V tile is unpadded, its
+//     16-byte chunks XOR-swizzled by row (chunk c of row r at c ^ 4 (r % 4)),
+//     which keeps the transposing reads conflict-free in 16 KB per tile;
 //   - scores are formed transposed, S^T = K Q^T, with the 32x32x16 bf16 MFMA,
 //     so each lane owns one query column: the row max and row sum are in-lane
 //     reductions plus one permlane32 swap;
@@ -42,8 +44,14 @@ struct FwdSmem {
   // conflict-free at D + 8; transposing reads of V (the same layout, taken
   // down the columns) are conflict-free at D + 32
   bf16 k[2][kBK][D + 8];
-  bf16 v[2][kBK][D + 32];
+  alignas(16) bf16 v[2][kBK][D == 128 ? D : D + 32];
 };
+
+// d = 128: element offset of V tile row r, 8-element chunk c, in the swizzled
+// layout. A transposing read of the P V product covers, per 32 lanes, rows
+// r0 .. r0 + 3 (r0 a multiple of 4) and the four chunks 4 db .. 4 db + 3,
+// which the swizzle spreads over all 64 banks.
+__device__ __forceinline__ int v_swz(int r, int c) { return r * 128 + ((c ^ (4 * (r & 3))) << 3); }
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
@@ -100,7 +108,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
 
-  constexpr int SV = D + 32;
+  constexpr int SV = D == 128 ? D : D + 32;
   const int i16 = lane & 15, gg = lane >> 4;
   bf16x8 kreg[KPASS], vreg[KPASS];
   const int kc = tid % CPR, kr = tid / CPR;
@@ -116,10 +124,21 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 #pragma unroll
     for (int p = 0; p < KPASS; ++p) {
       store16(&sm.k[buf][p * RPP + kr][8 * kc], kreg[p]);
-      store16(&sm.v[buf][p * RPP + kr][8 * kc], vreg[p]);
+      if constexpr (D == 128) store16(&sm.v[buf][0][0] + v_swz(p * RPP + kr, kc), vreg[p]);
+      else store16(&sm.v[buf][p * RPP + kr][8 * kc], vreg[p]);
     }
   };
 
+  // (d = 128) this lane's transposing-read offsets into the V tile, one per
+  // 32-column block db: lane i16 of a 16-lane group reads row
+  // 16 t + 4 hf + i16 / 4 (+ 8), columns 32 db + 16 (gg % 2) + 4 (i16 % 4)
+  // .. + 3, i.e. chunk 4 db + 2 (gg % 2) + (i16 % 4) / 2, half i16 % 2; the
+  // swizzle depends on the row only through i16 / 4, so the steps t and the
+  // +8 rows are fixed offsets from these
+  int voff[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+    voff[db] = v_swz(4 * hf + (i16 >> 2), 4 * db + 2 * (gg & 1) + ((i16 & 3) >> 1)) + 4 * (i16 & 1);
   int nkept = 0;
   if (top_b >= 0) {
     load_tile(top_b);
@@ -212,9 +231,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
         for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const int r0 = 16 * t + 4 * hf, c0 = 32 * db + 16 * (gg & 1);
-            const bf16x8 va = cat8(lds_read_tr(&sm.v[buf][0][0], SV, r0, c0, i16),
-                                   lds_read_tr(&sm.v[buf][0][0], SV, r0 + 8, c0, i16));
+            bf16x8 va;
+            if constexpr (D == 128) {
+              const bf16* vt = &sm.v[buf][0][0];
+              va = cat8(lds_read_tr_at(vt + voff[db] + 16 * t * D),
+                        lds_read_tr_at(vt + voff[db] + (16 * t + 8) * D));
+            } else {
+              const int r0 = 16 * t + 4 * hf, c0 = 32 * db + 16 * (gg & 1);
+              va = cat8(lds_read_tr(&sm.v[buf][0][0], SV, r0, c0, i16),
+                        lds_read_tr(&sm.v[buf][0][0], SV, r0 + 8, c0, i16));
+            }
             oacc[db] = mfma32(va, pb[t], oacc[db]);
           }
         ++nkept;
