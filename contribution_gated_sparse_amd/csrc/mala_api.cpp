@@ -1,6 +1,7 @@
 // C ABI of libmala: argument validation, workspace carving and launches.
 // Every entry point either enqueues all of its work on the caller's stream
 // and returns MALA_OK, or enqueues nothing and returns an error status.
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -268,6 +269,37 @@ mala_status decode_impl(int stages, const mala_decode_problem* p, const void* q,
   return finish(e, st, "mala_decode launch");
 }
 
+// Device scratch of mala_decode_noalloc: one copy in each GPU the library
+// runs on, held until the process ends. In host code `scratch` names a
+// host-side stand-in, not the device array: host code uses only the device
+// address looked up below.
+static __device__ __align__(256) unsigned char scratch[MALA_DECODE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch`, looked up on the first call on
+// that device (every lookup yields the same address, so racing first calls
+// are harmless).
+mala_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MALA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MALA_ERR_UNSUPPORTED, "device %d is past the %d devices the scratch covers", dev,
+                kMaxDevices);
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(MALA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return MALA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -370,6 +402,24 @@ mala_status mala_decode_stage(int32_t stage, const mala_decode_problem* p, const
   return decode_impl(stage == MALA_DECODE_SPLIT ? mala::kStageMain : mala::kStageCombine, p, q,
                      k_cache, v_cache, seqlens_k, o, lse, workspace, ws_bytes, tile_mask,
                      kept_tiles, stream);
+}
+
+mala_status mala_decode_noalloc(const mala_decode_problem* p, const void* q,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* seqlens_k, void* o, float* lse,
+                                int8_t* tile_mask, int32_t* kept_tiles, void* stream) {
+  mala::DecodeShape s;
+  MALA_TRY(check_decode(p, &s));
+  const size_t need = round_up(mala::decode_ws_floats(s) * sizeof(float));
+  if (need > MALA_DECODE_NOALLOC_SCRATCH_BYTES)
+    return fail(MALA_ERR_UNSUPPORTED,
+                "this decode problem needs %zu bytes of scratch; mala_decode_noalloc holds %zu "
+                "(use mala_decode with a workspace)",
+                need, (size_t)MALA_DECODE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  MALA_TRY(scratch_of_current_device(&ws));
+  return decode_impl(mala::kStageMain | mala::kStageCombine, p, q, k_cache, v_cache, seqlens_k, o,
+                     lse, ws, MALA_DECODE_NOALLOC_SCRATCH_BYTES, tile_mask, kept_tiles, stream);
 }
 
 const char* mala_last_error(void) { return g_err; }

@@ -54,7 +54,7 @@ DECODE_SPLIT_AUTO = -1
 
 EXPORTS = ("mala_get_tiling", "mala_fwd", "mala_bwd_workspace_size", "mala_bwd",
            "mala_bwd_nested", "mala_bwd_stage", "mala_decode_workspace_size", "mala_decode_split_keys", "mala_decode",
-           "mala_decode_stage", "mala_last_error", "mala_version")
+           "mala_decode_stage", "mala_decode_noalloc", "mala_last_error", "mala_version")
 BWD_PREP, BWD_DKDV, BWD_DQ = 0, 1, 2
 DECODE_SPLIT, DECODE_COMBINE = 0, 1
 
@@ -96,6 +96,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mala_decode_split_keys.restype = i32
     lib.mala_decode.argtypes = [DP, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
     lib.mala_decode.restype = i32
+    lib.mala_decode_noalloc.argtypes = [DP, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.mala_decode_noalloc.restype = i32
     lib.mala_last_error.argtypes = []
     lib.mala_last_error.restype = ctypes.c_char_p
     lib.mala_version.argtypes = []
@@ -265,11 +267,14 @@ def mala_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                 seqlens_k: torch.Tensor, tau: float, max_n_k: Optional[int] = None,
                 softmax_scale: Optional[float] = None, want_mask: bool = False,
                 want_kept: bool = True, out: Optional[dict] = None, events=None,
-                split_keys: int = 0) -> dict:
+                split_keys: int = 0, noalloc: bool = False) -> dict:
     """One split-KV decode step. q [B,Hq,d]; caches [B,Hkv,cap,d]; seqlens_k
     int32 [B] on the device (N_k including the current token). ``split_keys``:
     0 for the default split, DECODE_SPLIT_AUTO, or a multiple of 64; the
-    returned ``split`` is the length used (the mask is [B,Hq,n_chunks,split/64])."""
+    returned ``split`` is the length used (the mask is [B,Hq,n_chunks,split/64]).
+    ``noalloc``: call mala_decode_noalloc, which takes no workspace (the
+    library's fixed device scratch; outputs are still allocated here unless
+    given in ``out``)."""
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (seqlens_k, "seqlens_k")):
         _dev(t, n)
     if seqlens_k.dtype != torch.int32:
@@ -286,10 +291,12 @@ def mala_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     o = torch.empty_like(q) if o is None else o
     lse = out.get("lse")
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device) if lse is None else lse
-    nws = lib.mala_decode_workspace_size(ctypes.byref(p))
-    ws = out.get("ws")
-    if ws is None or ws.numel() < nws:
-        ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=q.device)
+    ws = None
+    if not noalloc:
+        nws = lib.mala_decode_workspace_size(ctypes.byref(p))
+        ws = out.get("ws")
+        if ws is None or ws.numel() < nws:
+            ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=q.device)
     mask = out.get("mask") if want_mask else None
     if want_mask and mask is None:
         mask = torch.empty((p.batch, p.n_q_heads, nch, chunk // bk), dtype=torch.int8,
@@ -298,6 +305,13 @@ def mala_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if want_kept and kept is None:
         kept = torch.empty((p.batch, p.n_q_heads + p.n_kv_heads), dtype=torch.int32,
                            device=q.device)
+    if noalloc:
+        if events is not None:
+            raise ValueError("noalloc runs the whole decode step: no events")
+        _check(lib.mala_decode_noalloc(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(seqlens_k), _ptr(o), _ptr(lse), _ptr(mask),
+                                       _ptr(kept), _stream()))
+        return dict(o=o, lse=lse, mask=mask, kept=kept, ws=None, split=chunk)
     args = (ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k), _ptr(o),
             _ptr(lse), _ptr(ws), ws.numel(), _ptr(mask), _ptr(kept), _stream())
     if events is None:

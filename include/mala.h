@@ -28,8 +28,9 @@
  *     dense softmax attention (Sec. 2.3).
  *   - All pointers except `p` and the tiling outputs are device pointers.
  *     The caller owns every buffer; the library allocates nothing, keeps no
- *     state between calls and never synchronizes: work is enqueued on
- *     `stream` (a hipStream_t; NULL = the default stream) and the call returns.
+ *     state between calls (mala_decode_noalloc's fixed device scratch aside)
+ *     and never synchronizes: work is enqueued on `stream` (a hipStream_t;
+ *     NULL = the default stream) and the call returns.
  *   - Errors: a non-MALA_OK status means nothing was enqueued and no output
  *     was written; mala_last_error() describes it (thread-local). A fault
  *     inside a kernel surfaces at the caller's next synchronization.
@@ -277,6 +278,30 @@ mala_status mala_decode_stage(int32_t stage, const mala_decode_problem* p, const
                               const void* k_cache, const void* v_cache, const int32_t* seqlens_k,
                               void* o, float* lse, void* workspace, size_t ws_bytes,
                               int8_t* tile_mask, int32_t* kept_tiles, void* stream);
+
+/*
+ * Split-KV decode that allocates nothing, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation. It is mala_decode without the workspace
+ * argument (same problem, inputs, outputs, diagnostics and results): the
+ * partial states and decision bits go to a scratch array of
+ * MALA_DECODE_NOALLOC_SCRATCH_BYTES of device memory that the library holds
+ * in each GPU it runs on, until the process ends.
+ *   - A problem whose mala_decode_workspace_size exceeds that size is
+ *     rejected with MALA_ERR_UNSUPPORTED (the 128K decode batch of 8
+ *     sequences x 8 query heads with 256-key splits needs about 17 MB).
+ *   - All calls on one GPU share that GPU's scratch. Calls that overlap on
+ *     one GPU (several streams, several threads) race on it: the caller
+ *     serializes them. The kernels write every scratch word they read, so
+ *     nothing needs clearing between calls.
+ *   - `stream` must belong to the calling thread's current device; the first
+ *     call on a device looks up that device's scratch address.
+ */
+#define MALA_DECODE_NOALLOC_SCRATCH_BYTES (32u << 20)
+mala_status mala_decode_noalloc(const mala_decode_problem* p, const void* q,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* seqlens_k, void* o, float* lse,
+                                int8_t* tile_mask, int32_t* kept_tiles, void* stream);
 
 /* Description of the last error on the calling thread ("" if none). */
 const char* mala_last_error(void);

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
     assert set(names) == set(M.EXPORTS)
@@ -185,6 +185,21 @@ def test_decode_validation_and_workspace(lib):
         assert st != 0 and word in lib.mala_last_error().decode()
     # fp32 decode supports head_dim 64
     assert lib.mala_decode_workspace_size(ctypes.byref(dprob(head_dim=64, dtype=M.MALA_F32))) > 0
+
+
+def test_decode_noalloc_rejects_problems_past_its_scratch(lib):
+    """mala_decode_noalloc refuses a problem whose workspace exceeds the fixed
+    scratch, before touching a device; the 128K decode batch fits."""
+    big = dprob(batch=64, n_q_heads=16, n_kv_heads=1, cache_capacity=131136, max_n_k=131136)
+    assert lib.mala_decode_workspace_size(ctypes.byref(big)) > (32 << 20)
+    g = ctypes.c_void_p(1 << 20)
+    st = lib.mala_decode_noalloc(ctypes.byref(big), g, g, g, g, g, g, None, None, None)
+    assert st == M.MALA_ERR_UNSUPPORTED and "scratch" in lib.mala_last_error().decode()
+    c5 = dprob(batch=8, n_q_heads=8, n_kv_heads=1, cache_capacity=131136, max_n_k=131136)
+    assert lib.mala_decode_workspace_size(ctypes.byref(c5)) <= (32 << 20)
+    bad = dprob(tau=-1.0)
+    st = lib.mala_decode_noalloc(ctypes.byref(bad), g, g, g, g, g, g, None, None, None)
+    assert st == M.MALA_ERR_INVALID_ARG
 
 
 def test_decode_split_keys_rule(lib):
