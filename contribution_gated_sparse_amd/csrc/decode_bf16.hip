@@ -660,22 +660,33 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeShape s,
   const bool dok = d0 < s.d;                            // d is a multiple of 32
   const float* po = ws + dec_o_at(s, bh, 0) + (dok ? d0 : 0);
   // kept-tile counters from the splits' decision bits, counted by every
-  // thread of the first column block and issued ahead of the merge loads:
+  // thread of the first column block, their loads issued ahead of the merge
+  // loads:
   // [b][h] for the head, [b][Hq + g] (by the group's first head) for the V
   // tiles of KV head g
   const bool count = kept != nullptr && blockIdx.y == 0;
   const int cb_ = bh / s.hq, ch_ = bh % s.hq, chk_ = ch_ / s.group;
   const bool vhead = ch_ % s.group == 0;
   int nh = 0, nv = 0;
-  if (count) {
-    const uint32_t* wbits = reinterpret_cast<const uint32_t*>(ws);
-    // a head's (and a KV head's) words of all splits are contiguous
-    const uint32_t* hb = wbits + dec_kbits_at(s, bh, 0);
-    const uint32_t* vbw = wbits + dec_vbits_at(s, (size_t)cb_ * s.hkv + chk_, 0);
-    for (int x = tid; x < s.n_chunks * s.wps; x += 256) {
-      nh += __popc(hb[x]);
-      if (vhead) nv += __popc(vbw[x]);
-    }
+  // a head's (and a KV head's) words of all splits are contiguous; the first
+  // kCw words per thread are loaded here, together, so that their round trip
+  // overlaps the merge loads' (the counts are taken after the fold), and any
+  // further words in a loop at the end
+  constexpr int kCw = 4;
+  const int nwords = count ? s.n_chunks * s.wps : 0;
+  const uint32_t* wbits = reinterpret_cast<const uint32_t*>(ws);
+  const uint32_t* hb = wbits + dec_kbits_at(s, bh, 0);
+  const uint32_t* vbw = wbits + dec_vbits_at(s, (size_t)cb_ * s.hkv + chk_, 0);
+  // bounded buffer loads: words past the range read as zero, with no branch
+  // (a guarded plain load would wait for each word in turn)
+  const auto hrs = make_rsrc(hb, (uint32_t)nwords * 4u);
+  const auto vrs = make_rsrc(vbw, vhead ? (uint32_t)nwords * 4u : 0u);
+  uint32_t hw[kCw], vw[kCw];
+#pragma unroll
+  for (int u = 0; u < kCw; ++u) {
+    const uint32_t off = (uint32_t)(tid + 256 * u) * 4u;
+    hw[u] = __builtin_amdgcn_raw_buffer_load_b32(hrs, off, 0, 0);
+    vw[u] = __builtin_amdgcn_raw_buffer_load_b32(vrs, off, 0, 0);
   }
   float mrun = kNegInf, zrun = 0.f;
   f32x4 orun = {0.f, 0.f, 0.f, 0.f};
@@ -714,6 +725,15 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeShape s,
   if (dq == 0) { sm_m[cl] = mrun; sm_z[cl] = zrun; }
   sm_o[cl][dq] = orun;
   if (count) {
+#pragma unroll
+    for (int u = 0; u < kCw; ++u) {
+      nh += __popc(hw[u]);
+      nv += __popc(vw[u]);
+    }
+    for (int x = tid + 256 * kCw; x < nwords; x += 256) {
+      nh += __popc(hb[x]);
+      if (vhead) nv += __popc(vbw[x]);
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       nh += __shfl_xor(nh, off, 64);
