@@ -707,28 +707,41 @@ def peak_memory(m, torch, q, k, v, do, scale, tau, fast_grad, qd, kc, vc, seq, n
     """Peak device memory each operator call allocates (outputs and
     workspace, inputs resident beforehand), at tau and at tau = 0, from
     torch's allocator statistics (Sec. 3 "Operator Latency and Memory"
-    compares MALA's peak operator memory with dense attention's)."""
+    compares MALA's peak operator memory with dense attention's). The bytes
+    are those requested: the allocator's block sizes can exceed them by an
+    unsplit remainder of a reused cached block, which depends on what was
+    freed before, not on the call."""
+    def cur():
+        return torch.cuda.memory_stats().get("requested_bytes.all.current",
+                                             torch.cuda.memory_allocated())
+
+    def peak():
+        return torch.cuda.memory_stats().get("requested_bytes.all.peak",
+                                             torch.cuda.max_memory_allocated())
     res = {}
-    for tau_ in (tau, 0.0):
+    # a first pass over both tolerances takes any one-time allocation (the
+    # binding's cached buffers, the allocator's first blocks of a size) out
+    # of the measured one
+    for tau_ in (tau, 0.0, tau, 0.0):
         row = {}
         for name in ("fwd", "bwd", "decode"):
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
-            base = torch.cuda.memory_allocated()
+            base = cur()
             torch.cuda.reset_peak_memory_stats()
             if name == "fwd":
                 r = m.mala_fwd(q, k, v, tau_, softmax_scale=scale)
             elif name == "bwd":
                 f = m.mala_fwd(q, k, v, tau_, softmax_scale=scale)
                 torch.cuda.synchronize()
-                base = torch.cuda.memory_allocated()
+                base = cur()
                 torch.cuda.reset_peak_memory_stats()
                 r = m.mala_bwd(q, k, v, f["o"], f["lse"], do, tau_, softmax_scale=scale,
                                fast_grad=fast_grad)
             else:
                 r = m.mala_decode(qd, kc, vc, seq, tau_, max_n_k=n_k, softmax_scale=dscale)
             torch.cuda.synchronize()
-            row[name + "_bytes"] = int(torch.cuda.max_memory_allocated() - base)
+            row[name + "_bytes"] = int(peak() - base)
             del r
         res[f"tau={tau_:g}"] = row
     res["equal_to_tau0"] = res[f"tau={tau:g}"] == res["tau=0"]
