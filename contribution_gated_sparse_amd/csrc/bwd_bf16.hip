@@ -108,7 +108,7 @@ struct alignas(16) DkdvSmem {
   bf16 dout[2][64][kStride];
   alignas(16) float z2[2][64];  // z_q * log2 e
   float u2[2][64];              // z_q * log2 e + log2(tau / L_q): skip iff s2 < u2 everywhere
-  float dd[2][64];              // D_q
+  float dd[2][64];              // -D_q (the dP accumulators start from it)
   uint32_t keep[2];             // [buf] bit w / 8 + w: wave w kept its first / second half
 };
 
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       const float z2 = zreg * 1.4426950408889634f;
       sm.z2[buf][tid] = z2;
       sm.u2[buf][tid] = z2 + (s.log2_tau - fast_log2(L));
-      sm.dd[buf][tid] = dreg;
+      sm.dd[buf][tid] = -dreg;
     }
   };
   // the previous step's decision word (byte 0: first half, byte 1: second
@@ -336,12 +336,11 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
         pb[4 * qb + r] = (bf16)pv[qb][r];
       }
     }
-    // ---- dP = dO V^T and dV^T += dO^T P, independent products
+    // ---- dP - D = dO V^T - D (the accumulators start at -D) and
+    // dV^T += dO^T P, independent products
     f32x4 dp[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dp[qb][r] = 0.f;
+    for (int qb = 0; qb < 2; ++qb) dp[qb] = *reinterpret_cast<const f32x4*>(&sm.dd[bf][lr + 16 * qb + 4 * g]);
 #pragma unroll
     for (int t = 0; t < KS; ++t)
 #pragma unroll
@@ -350,11 +349,9 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     for (int db = 0; db < DB; ++db) dv[db] = mfma16(ocol[db], pb, dv[db]);
     // ---- dS = P o (dP - D), then dK^T += Q^T dS
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const f32x4 ddv = *reinterpret_cast<const f32x4*>(&sm.dd[bf][lr + 16 * qb + 4 * g]);
+    for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dsb[4 * qb + r] = (bf16)(pv[qb][r] * (dp[qb][r] - ddv[r]));
-    }
+      for (int r = 0; r < 4; ++r) dsb[4 * qb + r] = (bf16)(pv[qb][r] * dp[qb][r]);
 #pragma unroll
     for (int db = 0; db < DB; ++db) dk[db] = mfma16(qcol[db], dsb, dk[db]);
   };
@@ -476,11 +473,8 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
           if (legal[half])
             mask[(bh * tr32 + 2 * i + half) * tc16 + kw0 / kBK] = (int8_t)((kept_halves >> half) & 1u);
       }
-#pragma unroll 1
-      for (int half = 0; half < 2; ++half) {
-        if (!(kept_halves & (1u << half))) continue;
-        kept_tile(buf, half, half ? sacc[2] : sacc[0], half ? sacc[3] : sacc[1]);
-      }
+      if (kept_halves & 1u) kept_tile(buf, 0, sacc[0], sacc[1]);
+      if (kept_halves & 2u) kept_tile(buf, 1, sacc[2], sacc[3]);
     }
     prev_h = h;
     prev_i = i;
@@ -580,7 +574,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
       }
       if (tid < 64) {
         sm.z2[bf][tid] = R.z * 1.4426950408889634f;
-        sm.dd[bf][tid] = R.d;
+        sm.dd[bf][tid] = -R.d;
       }
     };
     // this wave's kept halves of step i (decision bytes v), staged in bf
