@@ -10,9 +10,10 @@ import torch
 
 import workloads as W
 from oracle import mala_oracle as O
-from parity_util import (BAND, assert_bitwise_where_agree, check_dq_o_rounding, check_forward,
-                         check_lse, check_nesting, check_ties, compare_values, dtype_name, np64,
-                         o_rounding_dq_term, tiling)
+from parity_util import (BAND, add_output_rounding, assert_bitwise_where_agree, check_dq_o_rounding,
+                         check_forward, check_lse, check_nesting, check_ties, compare_values,
+                         dtype_name, grad_rounding_bounds, is_bounded, np64, o_rounding_dq_term,
+                         tiling)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,18 +62,28 @@ def check_backward(x, tau, g_fwd, r_fwd, causal=True, qblocks=None, key_rows=Non
         for i in qblocks:
             rows[:, :, i * bq:min(nq, (i + 1) * bq)] = True
     st = {}
+    # the derived rounding bounds, for the comparisons that take them
+    bd = {"dq": None, "dk": None, "dv": None}
+    if any(is_bounded(nm, kind) for nm in ("dQ", "dK", "dV")):
+        bd = grad_rounding_bounds(np64(q), np64(k), np64(v), np64(do), x["scale"], causal, r_fwd,
+                                  r["mask"], kind, lse_gpu=g_fwd["lse"].cpu().numpy(),
+                                  o_gpu=np64(g_fwd["o"]))
+        bd = add_output_rounding(bd, r, kind)
     if dq_o_rounding:     # inputs whose dQ is conditioned by the bf16 rounding of the stored O
         term = o_rounding_dq_term(np64(q), np64(k), np64(v), np64(do), x["scale"], causal,
                                   r_fwd, r, rows)
         check_dq_o_rounding("dQ", np64(g["dq"])[rows], r["dq"][rows], term)
     else:
-        st["dq"] = compare_values("dQ", np64(g["dq"]), r["dq"], kind, rows, strict=strict)
+        st["dq"] = compare_values("dQ", np64(g["dq"]), r["dq"], kind, rows, strict=strict,
+                                  bound=bd["dq"])
     if key_rows is not None or qblocks is None:
         kr = slice(None) if key_rows is None else key_rows
         st["dk"] = compare_values("dK", np64(g["dk"])[:, :, kr], r["dk"][:, :, kr], kind,
-                                  strict=strict)
+                                  strict=strict,
+                                  bound=None if bd["dk"] is None else bd["dk"][:, :, kr])
         st["dv"] = compare_values("dV", np64(g["dv"])[:, :, kr], r["dv"][:, :, kr], kind,
-                                  strict=strict)
+                                  strict=strict,
+                                  bound=None if bd["dv"] is None else bd["dv"][:, :, kr])
     st["ties"] = int((checked & ~clear).sum())
     check_ties("backward near ties", st["ties"], max_ties, kind)
     return g, r, st
@@ -348,8 +359,12 @@ def test_nested_arbitrary_forward_masks(causal, density):
     # or a replayed near tie)
     rr = O.mala_bwd(qn, kn, vn, rf["o"], rf["lse"], don, tau, x["scale"], causal, bq, bk,
                     replay=want, band=np.inf, o_storage="bf16", lse_storage="f32")
+    bd = add_output_rounding(grad_rounding_bounds(qn, kn, vn, don, x["scale"], causal, rf, want,
+                                                  "bf16", lse_gpu=f["lse"].cpu().numpy(),
+                                                  o_gpu=np64(f["o"])),
+                             rr, "bf16")
     for n in ("dq", "dk", "dv"):
-        compare_values(n, np64(b[n]), rr[n], "bf16")
+        compare_values(n, np64(b[n]), rr[n], "bf16", bound=bd[n])
 
 
 def test_backward_modes_are_deterministic():
@@ -547,9 +562,15 @@ def test_fast_grad_flag_same_support():
                    softmax_scale=x["scale"], want_mask=True)["mask"].cpu().numpy(), band=1e-3)
     rb = O.mala_bwd(np64(x["q"]), np64(x["k"]), np64(x["v"]), r["o"], r["lse"], np64(x["do"]),
                     1e-4, x["scale"], True, *tiling()[1][:2], o_storage="bf16", lse_storage="f32")
+    bd = {}
+    for split in (False, True):
+        bd[split] = add_output_rounding(
+            grad_rounding_bounds(np64(x["q"]), np64(x["k"]), np64(x["v"]), np64(x["do"]), x["scale"],
+                                 True, r, rb["mask"], "bf16", split_dq=split,
+                                 lse_gpu=f["lse"].cpu().numpy(), o_gpu=np64(f["o"])), rb, "bf16")
     for name in ("dq", "dk"):
-        compare_values(name + " fast", np64(b[name]), rb[name], "bf16")
-        compare_values(name + " split", np64(a[name]), rb[name], "bf16")
+        compare_values(name + " fast", np64(b[name]), rb[name], "bf16", bound=bd[False][name])
+        compare_values(name + " split", np64(a[name]), rb[name], "bf16", bound=bd[True][name])
 
 
 # ------------------------------------------------------------- autograd entry
