@@ -17,9 +17,9 @@ BAND = {"f32": 1e-4, "bf16": 1e-3}
 # and relative Frobenius error <= 1e-2. Every comparison records the strict
 # absolute error, the tensor's largest magnitude, the error scaled by
 # max(1, max|ref|) and the relative Frobenius error (STATS), and asserts the
-# strict bar unless the caller names the comparison a known deviation
-# (``strict=False``, each listed with its measured size and cause in the
-# design notes); those still assert the scaled bar.
+# strict bar, except the comparisons listed in BOUNDED, which assert the bar
+# plus a rounding bound derived from the arithmetic (grad_rounding_bounds),
+# and the scaled and Frobenius bars.
 TOL_F32 = 1e-5
 TOL_BF16_ABS = 2e-2
 TOL_BF16_FRO = 1e-2
