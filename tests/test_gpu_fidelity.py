@@ -168,3 +168,53 @@ def test_matched_work_control(preset, tau):
     # the control keeps the same count by largest mass, so it omits no more
     # mass than MALA in any decision block, up to fp32 rounding
     assert co <= mo + 1e-6
+
+
+def test_peak_operator_memory_equals_dense():
+    """Peak operator memory against tau = 0 (Sec. 3 compares it with dense
+    attention's): the bytes each call requests from the allocator (outputs,
+    workspace, counters) do not depend on tau, on inputs where tiles are
+    skipped. Measured as requested bytes after a warm pass, so the
+    allocator's block sizes (an unsplit remainder of a reused cached block)
+    do not enter."""
+    m = lib()
+    x = W.make_structured_preset("sparse", 2000, hq=4, hkv=2, d=128, device=DEV)
+    q, k, v, do, scale = x["q"], x["k"], x["v"], x["do"], x["scale"]
+    y = W.make_decode(W.CONFIGS[5], cache=3000, steps=1, batch=2, hq=4, hkv=2, planted=4)
+    qd = y["q_steps"][0].to(DEV).contiguous()
+    kc, vc = y["k_cache"].to(DEV), y["v_cache"].to(DEV)
+    seq = torch.tensor([3001, 1700], dtype=torch.int32, device=DEV)
+
+    def stats(key):
+        st = torch.cuda.memory_stats()
+        return st.get(f"requested_bytes.all.{key}")
+
+    if stats("current") is None:
+        pytest.skip("torch's allocator does not report requested bytes")
+
+    def peak(fn):
+        torch.cuda.synchronize()
+        base = stats("current")
+        torch.cuda.reset_peak_memory_stats()
+        r = fn()
+        torch.cuda.synchronize()
+        got = stats("peak") - base
+        del r
+        return got
+
+    res = {}
+    for tau in (1e-2, 0.0, 1e-2, 0.0):          # the first pass warms up
+        f = m.mala_fwd(q, k, v, tau, softmax_scale=scale)
+        res[tau] = dict(
+            fwd=peak(lambda: m.mala_fwd(q, k, v, tau, softmax_scale=scale)),
+            bwd=peak(lambda: m.mala_bwd(q, k, v, f["o"], f["lse"], do, tau, softmax_scale=scale)),
+            gate_pass=peak(lambda: m.mala_bwd(q, k, v, f["o"], f["lse"], do, tau,
+                                              softmax_scale=scale, gate_pass=True)),
+            decode=peak(lambda: m.mala_decode(qd, kc, vc, seq, tau, max_n_k=3001,
+                                              softmax_scale=y["scale"])))
+        del f
+    print(f"[peak memory] {res}", flush=True)
+    assert res[1e-2] == res[0.0]
+    # and the forward's are its outputs: O, z and the kept-tile counters
+    b_, hq, n, d = q.shape
+    assert res[0.0]["fwd"] == b_ * hq * n * d * 2 + b_ * hq * n * 4 + b_ * hq * (-(-n // 32)) * 4
