@@ -279,21 +279,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 // 64 banks, and V chunk c of row r at c ^ 4 (r % 4) (v_swz).
 constexpr int kD128 = 128;
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// one 16-byte LDS-DMA load per lane: lane l writes bytes [16 l, 16 l + 16) of
-// the 1 KB block at lds (wave-uniform) with the 16 bytes at voff of rs (zeros
-// past the end of the buffer)
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, bf16* lds, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, 0, 0, 0);
-}
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0f70); }        // vmcnt(0)
-__device__ __forceinline__ void wait_dma_but4() { __builtin_amdgcn_s_waitcnt(0x0f74); }   // vmcnt(4)
-// barrier for LDS traffic only: waits for this wave's LDS reads and writes,
-// not for its DMAs in flight
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_d128_kernel(
     Shape s, const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
@@ -476,7 +461,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_d128_kernel(
     }
     // tile j - 1's DMAs (issued one step back) have landed once at most
     // this step's four remain
-    wait_dma_but4();
+    wait_vm<4>();
     lds_barrier();
   };
 
@@ -496,14 +481,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_d128_kernel(
     dma_tile(k1, v1, j0 - 1);
 #pragma unroll
     for (int t = 0; t < KT; ++t) settle(qr[t]);
-    wait_dma();
+    wait_vm<0>();
     __syncthreads();
     for (int j = j0; j >= 2; j -= 3) {
       step(std::integral_constant<int, 2>(), j);
       step(std::integral_constant<int, 1>(), j - 1);
       step(std::integral_constant<int, 0>(), j - 2);
     }
-    wait_dma();
+    wait_vm<0>();
   }
 
   if (!active) return;

@@ -100,4 +100,25 @@ __device__ __forceinline__ bf16x8 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t 
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// LDS-DMA: one 16-byte buffer load per lane straight into LDS. Lane l writes
+// bytes [16 l, 16 l + 16) of the 1 KB block at lds (wave-uniform) with the 16
+// bytes at voff of rs (zeros past the end of the buffer). The loads count in
+// the vector-memory counter like any other load and complete in order with
+// them; the LDS block is written when the count says so.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, bf16* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | N);
+}
+// barrier for LDS traffic only: waits for this wave's LDS reads and writes,
+// not for its loads in flight (the DMAs stay outstanding across it)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 }  // namespace mala
