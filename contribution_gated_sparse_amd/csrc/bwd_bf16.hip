@@ -963,9 +963,11 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
 
 // ---------------------------------------------------------------- dQ
 // A workgroup owns 256 query rows (8 waves x 32) of one (batch, query head).
-// Key tiles of 64 rows (K and V, row-major, double-buffered) stream through
-// LDS, only those that some wave of the block keeps; K^T, the A operand of
-// dQ^T = K^T dS^T, comes from the K tile through transposing reads.
+// Key tiles of 64 rows (K and V, row-major) stream through LDS, only those
+// that some wave of the block keeps; K^T, the A operand of dQ^T = K^T dS^T,
+// comes from the K tile through transposing reads. This kernel stages the
+// tiles through registers into double-buffered LDS and serves d = 64; the
+// d = 128 kernel below stages them by LDS-DMA loads two tiles ahead.
 //
 // The K tile is read both as rows (16-byte reads, S^T = K Q^T) and through
 // transposing reads (K^T). No single row stride serves both without bank
@@ -1218,6 +1220,281 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
     }
 }
 
+
+// d = 128: the same walk with the K and V tiles staged by LDS-DMA buffer
+// loads (global memory straight into LDS: no registers, no LDS stores) two
+// needed tiles ahead, in three buffers. Step n reads buffer n % 3, issues the
+// DMA of the needed tile two ahead into the buffer that held the previous
+// one, and before an LDS-only barrier waits only for the next tile's loads,
+// issued one step earlier. The buffers are six separate LDS arrays and the
+// walk runs its steps in the fixed order 0, 1, 2, so each read names its
+// array at compile time and the compiler's DMA wait covers only reads of the
+// array a DMA fills.
+//
+// Both tiles are unpadded (256-byte rows) with 16-byte chunk c of row r at
+// c ^ f(r % 16), f(r) = r ^ 4 (r % 4): among the row permutations timed on
+// this LDS for these two access patterns, it runs the K row reads and the
+// K^T transposing reads at the conflict-free rate (f(r) = r halves the
+// transposing reads' rate); V, read as rows only, shares it.
+__device__ __forceinline__ int dq_swz(int r) { return r ^ ((r & 3) << 2); }
+
+template <bool kSplit>
+__global__ __launch_bounds__(512, 1) void bwd_dq_d128_kernel(
+    Shape s, const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dq,
+    bf16* __restrict__ dQ, const uint32_t* __restrict__ bits, int32_t* __restrict__ kept,
+    int n_qb) {
+  constexpr int D = 128;
+  constexpr int KT = D / 16, DB = D / 32;
+  constexpr int TILE = 64 * D;
+  constexpr uint32_t TILE_BYTES = TILE * 2;
+  __shared__ __attribute__((aligned(16))) bf16 k0[TILE], k1[TILE], k2[TILE], v0[TILE], v1[TILE], v2[TILE];
+  extern __shared__ uint32_t need[];   // ceil(tiles / 32) words, sized at launch
+
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int gg = lane >> 4, i16 = lane & 15;
+  const int bh_count = s.batch * s.hq;
+  const int I = n_qb - 1 - (int)(blockIdx.x / bh_count);
+  const int bh = (int)(blockIdx.x % bh_count);
+  const int b = bh / s.hq, h = bh % s.hq, hk = h / s.group;
+  const size_t qrow0 = (size_t)bh * (size_t)s.nq;
+  const size_t krow0 = ((size_t)b * s.hkv + hk) * (size_t)s.nk;
+  const int tr32 = (s.nq + kBQ - 1) / kBQ;
+  const int tc16 = (s.nk + kBK - 1) / kBK;
+  const int words = (tc16 + 31) / 32;
+  const int q0 = I * 256 + w * 32;
+  const bool active = q0 < s.nq;
+  const int q = q0 + l32;
+
+  const auto qrs = make_rsrc(Q + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
+  const auto ors = make_rsrc(dO + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
+  const auto krs = make_rsrc(K + krow0 * D, (uint32_t)((size_t)s.nk * D * 2));
+  const auto vrs = make_rsrc(V + krow0 * D, (uint32_t)((size_t)s.nk * D * 2));
+  // zero-sized: the loads of a step past the walk return zeros and touch nothing
+  const auto krs0 = make_rsrc(K + krow0 * D, 0u);
+  const auto vrs0 = make_rsrc(V + krow0 * D, 0u);
+
+  bf16x8 qr[KT], orr[KT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    qr[t] = buf_load16(qrs, (uint32_t)(q * D + 16 * t + 8 * hf) * 2);
+    orr[t] = buf_load16(ors, (uint32_t)(q * D + 16 * t + 8 * hf) * 2);
+  }
+  const float z2 = q < s.nq ? LSE[qrow0 + q] * 1.4426950408889634f : 0.f;
+  const float dd = q < s.nq ? Dq[qrow0 + q] : 0.f;
+  f32x16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[db][r] = 0.f;
+
+  const int last_row = min(I * 256 + 255, s.nq - 1);
+  const int lastkey = s.causal ? min(last_row + s.offset, s.nk - 1) : s.nk - 1;
+  const int ntiles = lastkey < 0 ? 0 : lastkey / 64 + 1;
+  const uint32_t* mybits = bits + ((size_t)bh * tr32 + (active ? q0 / kBQ : 0)) * words;
+
+  if (kept != nullptr && active) {
+    int cnt = 0;
+    for (int x = lane; x < words; x += 64) cnt += __popc(mybits[x]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
+    if (lane == 0) kept[(size_t)bh * tr32 + q0 / kBQ] = cnt;
+  }
+
+  auto tile_bits = [&](const uint32_t* row_bits, int j) -> uint32_t {
+    return (row_bits[(4 * j) >> 5] >> ((4 * j) & 31)) & 15u;
+  };
+  const int nrb = min(8, (s.nq - I * 256 + 31) / 32);
+  const uint32_t* blockbits = bits + ((size_t)bh * tr32 + I * 8) * words;
+  const int nneed = (ntiles + 31) / 32;
+  for (int x = tid; x < nneed; x += 512) need[x] = 0u;
+  __syncthreads();
+  for (int t = tid; t < ntiles; t += 512) {
+    uint32_t any = 0;
+#pragma unroll
+    for (int ww = 0; ww < 8; ++ww)
+      if (ww < nrb) any |= tile_bits(blockbits + (size_t)ww * words, t);
+    if (any) atomicOr(&need[t >> 5], 1u << (t & 31));
+  }
+  __syncthreads();
+  auto next_needed = [&](int j) -> int {
+    while (j >= 0) {
+      const uint32_t wv = __builtin_amdgcn_readfirstlane(need[j >> 5]) &
+                          (0xffffffffu >> (31 - (j & 31)));
+      if (wv != 0u) return (j & ~31) + 31 - __clz(wv);
+      j = (j & ~31) - 1;
+    }
+    return -1;
+  };
+
+  // ---- DMA: wave w fills rows 8 w .. 8 w + 7 of a tile, four per
+  // instruction; lane l fills slot l % 16 of row 8 w + 4 p + l / 16 with
+  // global chunk (l % 16) ^ f(row % 16)
+  uint32_t dvo[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int row = 8 * w + 4 * p + (lane >> 4);
+    dvo[p] = (uint32_t)(row * D + 8 * ((lane & 15) ^ dq_swz(row & 15))) * 2;
+  }
+  auto dma_tile = [&](bf16* kd, bf16* vd, int j) {
+    const bool live = j >= 0;
+    const auto kr_ = live ? krs : krs0;
+    const auto vr_ = live ? vrs : vrs0;
+    const uint32_t off = (uint32_t)(live ? j : 0) * TILE_BYTES;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) dma16(kr_, kd + (8 * w + 4 * p) * D, dvo[p] + off);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) dma16(vr_, vd + (8 * w + 4 * p) * D, dvo[p] + off);
+  };
+
+  // ---- LDS addressing (bytes). Row reads: row 32 half + l32, chunk 2t + hf,
+  // at slot 2 t ^ Y. Transposing reads: row 32 half + 16 t + 4 hf + i16 / 4
+  // (+ 8), chunk 4 db + cc, half i16 % 2, at slot 4 db ^ Z (^ 8 for the + 8
+  // rows, f(r + 8) = f(r) ^ 8).
+  const int Y = hf ^ dq_swz(l32 & 15);
+  const int cc = 2 * (gg & 1) + ((i16 & 3) >> 1);
+  const int rt = 4 * hf + (i16 >> 2);
+  const int Z = cc ^ dq_swz(rt);
+  int ra[KT], ta[DB];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) ra[t] = l32 * 256 + ((16 * Y) ^ (32 * t));
+#pragma unroll
+  for (int db = 0; db < DB; ++db) ta[db] = rt * 256 + ((16 * Z) ^ (64 * db)) + 8 * (i16 & 1);
+  auto rowrd = [&](const bf16* tile, int R, int t) {
+    return load16(reinterpret_cast<const char*>(tile) + R * 256 + ra[t]);
+  };
+  auto trrd = [&](const bf16* tile, int R, int db) {
+    return lds_read_tr_at(reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(tile) + R * 256 + ta[db]));
+  };
+  // the same eight rows further down: slot bit 3 flips (byte bit 7)
+  auto trrd8 = [&](const bf16* tile, int R, int db) {
+    return lds_read_tr_at(
+        reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(tile) + R * 256 + 2048 + (ta[db] ^ 128)));
+  };
+
+  // one step at needed tile j (buffer B); jnn: the needed tile two ahead
+  auto step = [&](auto bc, int j, int jnn, uint32_t wd) {
+    constexpr int B = decltype(bc)::value;
+    constexpr int B2 = (B + 2) % 3;
+    const bf16* const kt = B == 0 ? k0 : B == 1 ? k1 : k2;
+    const bf16* const vt = B == 0 ? v0 : B == 1 ? v1 : v2;
+    dma_tile(B2 == 0 ? k0 : B2 == 1 ? k1 : k2, B2 == 0 ? v0 : B2 == 1 ? v1 : v2, jnn);
+    if (active && j >= 0) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const uint32_t cols = (wd >> (2 * half)) & 3u;
+        if (cols == 0) continue;
+        const int key0 = j * 64 + 32 * half;
+        f32x16 sacc, dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; dp[r] = 0.f; }
+        bf16x8 ka_[KT], va_[KT];
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+          ka_[t] = rowrd(kt, 32 * half, t);
+          va_[t] = rowrd(vt, 32 * half, t);
+        }
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+          sacc = mfma32(ka_[t], qr[t], sacc);
+          dp = mfma32(va_[t], orr[t], dp);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int u = 0; u < 2 * KT - 4; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        const bool boundary = (key0 + 32 > s.nk) || (q0 + 32 > s.nq) ||
+                              (s.causal && key0 + 31 > q0 + s.offset);
+        if (boundary) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = key0 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const bool ok = (kk < s.nk) & (q < s.nq) & ((kk <= q + s.offset) | (s.causal == 0));
+            sacc[r] = ok ? sacc[r] : kNegInf;
+          }
+        }
+        if (cols != 3u) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sacc[r] = ((cols >> (r >> 3)) & 1u) ? sacc[r] : kNegInf;
+        }
+        bf16x8 dsb[2], dsl[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(sacc[r], s.scale_log2, -z2));
+          const float ds = p * (dp[r] - dd);
+          const bf16 hi = (bf16)ds;
+          dsb[r >> 3][r & 7] = hi;
+          if constexpr (kSplit) dsl[r >> 3][r & 7] = (bf16)(ds - (float)hi);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int R = 32 * half + 16 * t;
+            const bf16x8 ka = cat8(trrd(kt, R, db), trrd8(kt, R, db));
+            dq[db] = mfma32(ka, dsb[t], dq[db]);
+            if constexpr (kSplit) dq[db] = mfma32(ka, dsl[t], dq[db]);
+          }
+      }
+    }
+    wait_vm<4>();
+    lds_barrier();
+  };
+
+  // walk the needed tiles from the top; (j, jn, jnn) the current one and the
+  // next two
+  int j = next_needed(ntiles - 1);
+  if (j >= 0) {
+    int jn = next_needed(j - 1);
+    dma_tile(k0, v0, j);
+    dma_tile(k1, v1, jn);
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      settle(qr[t]);
+      settle(orr[t]);
+    }
+    wait_vm<0>();
+    __syncthreads();
+    int jnn = jn < 1 ? -1 : next_needed(jn - 1);
+    uint32_t wd = active ? tile_bits(mybits, j) : 0u;
+    auto advance = [&]() {
+      j = jn;
+      jn = jnn;
+      jnn = jn < 1 ? -1 : next_needed(jn - 1);
+      wd = j >= 0 && active ? tile_bits(mybits, j) : 0u;
+    };
+    while (true) {
+      step(std::integral_constant<int, 0>(), j, jnn, wd);
+      advance();
+      if (j < 0) break;
+      step(std::integral_constant<int, 1>(), j, jnn, wd);
+      advance();
+      if (j < 0) break;
+      step(std::integral_constant<int, 2>(), j, jnn, wd);
+      advance();
+      if (j < 0) break;
+    }
+    wait_vm<0>();
+  }
+
+  if (!active || q >= s.nq) return;
+  const float sc_nat = s.scale_log2 * 0.69314718055994531f;
+  bf16* row = dQ + (qrow0 + q) * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 y = {(bf16)(dq[db][4 * g] * sc_nat), (bf16)(dq[db][4 * g + 1] * sc_nat),
+                  (bf16)(dq[db][4 * g + 2] * sc_nat), (bf16)(dq[db][4 * g + 3] * sc_nat)};
+      *reinterpret_cast<bf16x4*>(row + 32 * db + 8 * g + 4 * hf) = y;
+    }
+}
+
 }  // namespace
 
 size_t bwd_ws_d_floats(const Shape& s) { return (size_t)s.batch * s.hq * s.nq; }
@@ -1302,10 +1579,10 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
   if (s.d == 128) {
     if (split)
       launch(bwd_gate_kernel<128, false>, bwd_gate_kernel<128, true>, bwd_dkdv_kernel<128, false>,
-             bwd_dkdv_kernel<128, true>, bwd_dq_kernel<128, true>);
+             bwd_dkdv_kernel<128, true>, bwd_dq_d128_kernel<true>);
     else
       launch(bwd_gate_kernel<128, false>, bwd_gate_kernel<128, true>, bwd_dkdv_kernel<128, false>,
-             bwd_dkdv_kernel<128, true>, bwd_dq_kernel<128, false>);
+             bwd_dkdv_kernel<128, true>, bwd_dq_d128_kernel<false>);
   } else {
     if (split)
       launch(bwd_gate_kernel<64, false>, bwd_gate_kernel<64, true>, bwd_dkdv_kernel<64, false>,
