@@ -347,9 +347,9 @@ def structured_section(args, m, F, W, torch, dev, tiling, preset):
 
 
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "mala_kernels_prefill32k_decode128k_hbm_traffic.md")
-KERNEL_ROWS = {"fwd": ("fwd_bf16_kernel<128>", "fwd_bf16.hip"),
+KERNEL_ROWS = {"fwd": ("fwd_bf16_d128_kernel", "fwd_bf16.hip"),
                "bwd_dkdv": ("bwd_dkdv_kernel<128, false>", "bwd_bf16.hip"),
-               "bwd_dq": ("bwd_dq_kernel<128, true>", "bwd_bf16.hip")}
+               "bwd_dq": ("bwd_dq_d128_kernel<true>", "bwd_bf16.hip")}
 
 
 def measured_traffic(kernel: str):
