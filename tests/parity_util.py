@@ -43,6 +43,8 @@ BOUNDED = {
     "bf16": {
         ("test_bf16_shapes_fwd_bwd", "dK"), ("test_bf16_shapes_fwd_bwd", "dQ"),
         ("test_bf16_shapes_fwd_bwd", "dV"),
+        ("test_bf16_tile_counts_fwd_bwd", "dK"), ("test_bf16_tile_counts_fwd_bwd", "dQ"),
+        ("test_bf16_tile_counts_fwd_bwd", "dV"),
         ("test_gate_pass_shapes", "dK"), ("test_gate_pass_shapes", "dQ"),
         ("test_gate_pass_shapes", "dV"),
         ("test_nested_shapes", "dK"), ("test_nested_shapes", "dQ"), ("test_nested_shapes", "dV"),

@@ -131,6 +131,21 @@ def test_bf16_shapes_fwd_bwd(shape, tau):
     check_nesting(g["mask"].cpu().numpy(), gb["mask"].cpu().numpy())
 
 
+# The d = 128 forward and dQ kernels stage K and V three tiles deep and run
+# their steps unrolled by three: the forward's walk starts at a tile with
+# index 2 mod 3 (up to two steps past the top tile), and dQ's walk leaves after
+# whichever of its three steps meets the last needed tile. Problems of 1 to 7
+# key tiles (and a ragged length) take every start and exit position.
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("n", [64, 128, 192, 256, 320, 384, 448, 470])
+def test_bf16_tile_counts_fwd_bwd(n, causal):
+    x = to_dev(W.make_prefill(W.CONFIGS[2], n=n, hq=2, hkv=1, d=128, batch=1, planted=4, seed=11 + n))
+    for tau in (0.0, 1.0):
+        g, r, st = check_forward(x, tau, causal=causal, max_ties=4)
+        gb, rb, stb = check_backward(x, tau, g, r, causal=causal)
+        check_nesting(g["mask"].cpu().numpy(), gb["mask"].cpu().numpy())
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_noncausal(dtype):
     cfg = W.CONFIGS[2] if dtype == torch.bfloat16 else W.CONFIGS[1]
