@@ -1129,9 +1129,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
         const int key0 = j * 64 + 32 * half;
         // ---- S^T = K Q^T and dP^T = V dO^T: lane (query l32, half hf), regs = keys
         const int krow = 32 * half + l32;
+        // dP^T accumulates from -D_q: dS = P o (dP - D) takes no subtraction
         f32x16 sacc, dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; dp[r] = 0.f; }
+        for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; dp[r] = -dd; }
         // K and V row operands, read four ahead of their products: the
         // schedule is pinned to four LDS reads, then alternating product and
         // read, so the two product chains (S^T, dP^T) hide the read latency
@@ -1174,7 +1175,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(fmaf(sacc[r], s.scale_log2, -z2));
-          const float ds = p * (dp[r] - dd);
+          const float ds = p * dp[r];
           const bf16 hi = (bf16)ds;
           dsb[r >> 3][r & 7] = hi;
           if constexpr (kSplit) dsl[r >> 3][r & 7] = (bf16)(ds - (float)hi);
@@ -1386,9 +1387,10 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d128_kernel(
         const uint32_t cols = (wd >> (2 * half)) & 3u;
         if (cols == 0) continue;
         const int key0 = j * 64 + 32 * half;
+        // dP^T accumulates from -D_q: dS = P o (dP - D) takes no subtraction
         f32x16 sacc, dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; dp[r] = 0.f; }
+        for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; dp[r] = -dd; }
         bf16x8 ka_[KT], va_[KT];
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
@@ -1426,7 +1428,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d128_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(fmaf(sacc[r], s.scale_log2, -z2));
-          const float ds = p * (dp[r] - dd);
+          const float ds = p * dp[r];
           const bf16 hi = (bf16)ds;
           dsb[r >> 3][r & 7] = hi;
           if constexpr (kSplit) dsl[r >> 3][r & 7] = (bf16)(ds - (float)hi);
