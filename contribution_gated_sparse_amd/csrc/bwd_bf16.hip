@@ -46,6 +46,8 @@
 // of the terms rather than of the result. A column of dS has no such
 // identity, and dK keeps its error well inside the same bound with one
 // rounding. MALA_FLAG_FAST_GRAD skips the lo half in dQ as well.
+#include <type_traits>
+
 #include "mala_device.h"
 #include "mala_internal.h"
 
@@ -961,6 +963,162 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
   }
 }
 
+// d = 128, every legal tile (the gate pass): the walk above with the K tiles
+// staged by LDS-DMA loads two tiles ahead in three buffers, as in the forward
+// (fwd_bf16.hip): step j reads buffer j % 3, fills the buffer that held tile
+// j + 1 with tile j - 2, waits only for tile j - 1's loads and meets the other
+// waves at an LDS-only barrier. The walk starts at a tile with j % 3 == 2 (at
+// most two past the top, which no wave scores) so that the steps run in the
+// fixed buffer order 2, 1, 0. K chunk c of row r sits at c ^ (r % 16), which
+// keeps the 16-byte row reads conflict-free.
+__global__ __launch_bounds__(512, 1) void bwd_gate_d128_kernel(Shape s, const bf16* __restrict__ Q,
+                                                               const bf16* __restrict__ K,
+                                                               const float* __restrict__ LSE,
+                                                               uint32_t* __restrict__ bits,
+                                                               int8_t* __restrict__ mask, int n_qb,
+                                                               const int8_t* __restrict__ /*fmask*/) {
+  constexpr int D = 128;
+  constexpr int KT = D / 16;
+  constexpr int TILE = 64 * D;
+  constexpr uint32_t TILE_BYTES = TILE * 2;
+  __shared__ __attribute__((aligned(16))) bf16 k0[TILE], k1[TILE], k2[TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int bh_count = s.batch * s.hq;
+  const int I = n_qb - 1 - (int)(blockIdx.x / bh_count);     // longest blocks first
+  const int bh = (int)(blockIdx.x % bh_count);
+  const int b = bh / s.hq, h = bh % s.hq, hk = h / s.group;
+  const size_t qrow0 = (size_t)bh * (size_t)s.nq;
+  const size_t krow0 = ((size_t)b * s.hkv + hk) * (size_t)s.nk;
+  const int tr32 = (s.nq + kBQ - 1) / kBQ;
+  const int tc16 = (s.nk + kBK - 1) / kBK;
+  const int words = (tc16 + 31) / 32;
+
+  const int q0 = I * 256 + 32 * w;
+  const bool active = q0 < s.nq;
+  auto top_tile = [&](int last_row) {
+    const int lastkey = s.causal ? min(last_row + s.offset, s.nk - 1) : s.nk - 1;
+    return lastkey / 64;
+  };
+  const int top_b = top_tile(min(I * 256 + 255, s.nq - 1));
+  const int top_w = active ? top_tile(min(q0 + 31, s.nq - 1)) : -1;
+  const size_t brow = (size_t)bh * tr32 + (active ? q0 / kBQ : 0);   // this wave's bit row
+
+  const auto qrs = make_rsrc(Q + qrow0 * D, (uint32_t)((size_t)s.nq * D * 2));
+  const auto krs = make_rsrc(K + krow0 * D, (uint32_t)((size_t)s.nk * D * 2));
+  const int q = q0 + l32;
+  const bool rvalid = q < s.nq;
+  bf16x8 qr[KT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) qr[t] = buf_load16(qrs, (uint32_t)(q * D + 16 * t + 8 * hf) * 2);
+  float u2 = __builtin_inff();
+  if (rvalid) {
+    const float L = s.causal ? (float)(q + s.offset + 1) : (float)s.nk;
+    u2 = LSE[qrow0 + q] * 1.4426950408889634f + (s.log2_tau - fast_log2(L));
+  }
+  const float thr = fmaxf(u2 / s.scale_log2, -3.402823466e38f);
+  auto legal_col = [&](int col) {
+    const int kc0 = 16 * col;
+    return col < tc16 && kc0 < s.nk &&
+           (!s.causal || kc0 <= min(q0 + 31, s.nq - 1) + s.offset);
+  };
+
+  // DMA: wave w stages rows 8 w .. 8 w + 7 of a tile, four per instruction;
+  // lane l fills slot l % 16 of row 8 w + 4 p + l / 16 with global chunk
+  // (l % 16) ^ (row % 16)
+  uint32_t kvo[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int row = 8 * w + 4 * p + (lane >> 4);
+    kvo[p] = (uint32_t)(row * D + 8 * ((lane & 15) ^ (row & 15))) * 2;
+  }
+  auto dma_k = [&](bf16* dst, int j) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) dma16(krs, dst + (8 * w + 4 * p) * D, kvo[p] + (uint32_t)j * TILE_BYTES);
+  };
+  const int ky = hf ^ (l32 & 15);   // row 32 kb + l32, chunk 2t + hf at slot 2t ^ ky
+
+  uint32_t word = 0u;            // decisions of columns 32 (j / 8) .. + 31 of this wave's row
+  float thr_s = thr;
+  auto step = [&](auto which, int j) {
+    constexpr int P = decltype(which)::value;   // j % 3
+    constexpr int PN = (P + 1) % 3;              // (j - 2) % 3
+    const bf16* const kt = P == 0 ? k0 : P == 1 ? k1 : k2;
+    dma_k(PN == 0 ? k0 : PN == 1 ? k1 : k2, max(j - 2, 0));
+    if (active && j <= top_w) {
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+      bf16x8 ka[KT][2];
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) ka[t][kb] = load16(kt + (32 * kb + l32) * D + 8 * ((2 * t) ^ ky));
+#pragma unroll
+      for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sacc[kb] = mfma32(ka[t][kb], qr[t], sacc[kb]);
+      const int key0 = j * 64;
+      if ((key0 + 64 > s.nk) || (q0 + 32 > s.nq) || (s.causal && key0 + 63 > q0 + s.offset)) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const bool ok = rvalid && key < s.nk && (!s.causal || key <= q + s.offset);
+            sacc[kb][r] = ok ? sacc[kb][r] : kNegInf;
+          }
+      }
+      // ---- offline gate, Eq. 4, per 16-key column c = keys 16 c .. + 15
+      uint32_t keep4 = 0u;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float x = kNegInf;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) x = fmaxf(x, sacc[c >> 1][8 * (c & 1) + r]);
+        if (__builtin_amdgcn_ballot_w64(x >= thr_s) != 0) keep4 |= 1u << c;
+      }
+      word |= keep4 << ((4 * j) & 31);
+      if (mask != nullptr && lane == 0) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (legal_col(4 * j + c)) mask[brow * tc16 + 4 * j + c] = (int8_t)((keep4 >> c) & 1u);
+      }
+    }
+    // the word of columns 32 (j / 8) .. is complete once the walk leaves it;
+    // the bit rows start cleared, so only words with a kept column are written
+    if ((j & 7) == 0) {
+      if (active && lane == 0 && word != 0u) bits[brow * words + (j >> 3)] = word;
+      word = 0u;
+    }
+    // tile j - 1's loads (issued one step back) have landed once at most this
+    // step's two remain
+    wait_vm<2>();
+    lds_barrier();
+  };
+
+  if (top_b >= 0) {
+    const int j0 = top_b + (2 - top_b % 3);
+    dma_k(k2, j0);
+    dma_k(k1, j0 - 1);
+#pragma unroll
+    for (int t = 0; t < KT; ++t) settle(qr[t]);
+    settle(thr_s);
+    wait_vm<0>();
+    __syncthreads();
+    for (int j = j0; j >= 2; j -= 3) {
+      step(std::integral_constant<int, 2>(), j);
+      step(std::integral_constant<int, 1>(), j - 1);
+      step(std::integral_constant<int, 0>(), j - 2);
+    }
+    wait_vm<0>();
+  }
+}
+
 // ---------------------------------------------------------------- dQ
 // A workgroup owns 256 query rows (8 waves x 32) of one (batch, query head).
 // Key tiles of 64 rows (K and V, row-major) stream through LDS, only those
@@ -1580,10 +1738,10 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
   const bool split = !(s.flags & MALA_FLAG_FAST_GRAD);
   if (s.d == 128) {
     if (split)
-      launch(bwd_gate_kernel<128, false>, bwd_gate_kernel<128, true>, bwd_dkdv_kernel<128, false>,
+      launch(bwd_gate_d128_kernel, bwd_gate_kernel<128, true>, bwd_dkdv_kernel<128, false>,
              bwd_dkdv_kernel<128, true>, bwd_dq_d128_kernel<true>);
     else
-      launch(bwd_gate_kernel<128, false>, bwd_gate_kernel<128, true>, bwd_dkdv_kernel<128, false>,
+      launch(bwd_gate_d128_kernel, bwd_gate_kernel<128, true>, bwd_dkdv_kernel<128, false>,
              bwd_dkdv_kernel<128, true>, bwd_dq_d128_kernel<false>);
   } else {
     if (split)
