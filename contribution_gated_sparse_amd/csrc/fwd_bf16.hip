@@ -335,7 +335,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_d128_kernel(
 
   // DMA: wave w stages rows 8w .. 8w + 7 of a tile, four per instruction;
   // lane l fills LDS chunk l % 16 of row 8w + 4p + l / 16 with global chunk
-  // (l % 16) ^ swizzle(row)
+  // (l % 16) ^ swizzle(row). Every row of a visited tile is written, rows past
+  // the end of the sequence as zeros (they meet P = 0).
   const int dpos = lane & 15;
   uint32_t kvo[2], vvo[2];
 #pragma unroll
@@ -466,13 +467,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_d128_kernel(
   };
 
   if (top_b >= 0) {
-    // V rows past the end of the sequence meet P = 0: keep them finite
-#pragma unroll
-    for (int x = tid; x < TILE / 8; x += kThreads) {
-      store16(&v0[8 * x], zero8());
-      store16(&v1[8 * x], zero8());
-    }
-    __syncthreads();
     // the walk starts at the first tile at or above the top with j % 3 == 2
     // (at most two tiles past the top, which no wave reaches), so that the
     // steps run in the fixed buffer order 2, 1, 0
