@@ -169,6 +169,7 @@ def structured_section(args, m, F, W, torch, dev, tiling, preset):
     bo = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
               kept=torch.empty((B, HQ, -(-N // bbq)), dtype=torch.int32, device=dev))
     bg = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v))
+    ba = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v))
     fn = dict(o=torch.empty_like(q), lse=torch.empty(q.shape[:3], device=dev),
               mask=torch.empty((B, HQ, -(-N // fbq), -(-N // fbk)), dtype=torch.int8, device=dev))
     bn = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v))
@@ -214,6 +215,26 @@ def structured_section(args, m, F, W, torch, dev, tiling, preset):
         pre[tau_]["gate_pass_vs_default"] = {   # max |difference| / max(1, max |default|)
             n_: float((bg[n_].float() - bo[n_].float()).abs().max()
                       / bo[n_].float().abs().max().clamp_min(1.0)) for n_ in ("dq", "dk", "dv")}
+        # the walk chosen on the device from the forward's kept counters
+        # (mala_bwd_auto): the gate-pass walks below half of the legal tiles
+        def run_auto():
+            m.mala_bwd(q, k, v, fo["o"], fo["lse"], do, tau_, softmax_scale=x["scale"], out=ba,
+                       fast_grad=args.fast_grad, fwd_kept=fo["kept"])
+        for _ in range(args.warmup):
+            run_auto()
+        torch.cuda.synchronize()
+        ta = 0.0
+        for _ in range(args.steps):
+            ev[0].record()
+            run_auto()
+            ev[2].record()
+            torch.cuda.synchronize()
+            ta += ev[0].elapsed_time(ev[2])
+        pre[tau_]["bwd_auto_ms"] = round(ta / args.steps, 3)
+        # which walk ran: its result equals that walk's own call bit for bit
+        same = lambda r: all(torch.equal(ba[n_], r[n_]) for n_ in ("dq", "dk", "dv"))
+        pre[tau_]["bwd_auto_walk"] = ("gate_pass" if same(bg) else
+                                      "default" if same(bo) else "neither")
         # the gate pass as a training step pairs it: the forward also writes its
         # tile mask, and the backward scores only the tiles the forward kept
         # (mala_bwd_nested; nested support, Sec. 2.2)

@@ -167,6 +167,48 @@ __device__ int group_kept_pairs(const Shape& s, const uint8_t* bit_bytes, int b,
   return total;
 }
 
+// Automatic walk choice (mala_bwd_auto): both walks' kernels are launched
+// and a workgroup of the walk not taken returns at once. take: the flag the
+// choice kernel wrote (1: the gate-pass walks, 0: the default walk), or
+// nullptr outside that mode.
+__device__ __forceinline__ bool walk_not_taken(const int32_t* take, int mine) {
+  return take != nullptr && __builtin_amdgcn_readfirstlane(*take) != mine;
+}
+
+// The choice: the gate-pass walks when the forward kept fewer than half of
+// its legal tiles. fwd_kept: the forward's kept tiles per (b, h, 32-row
+// block); a block's legal tiles are the 64-key tiles up to the one that
+// holds its last row's last visible key. One workgroup.
+__global__ __launch_bounds__(256) void bwd_choose_kernel(Shape s, const int32_t* __restrict__ fwd_kept,
+                                                         int32_t* __restrict__ take) {
+  __shared__ long long red[2][4];
+  const int ftr = (s.nq + kFwdBq - 1) / kFwdBq;
+  long long kept = 0, legal = 0;
+  const long long n = (long long)s.batch * s.hq * ftr;
+  for (long long x = threadIdx.x; x < n; x += 256) {
+    const int i = (int)(x % ftr);
+    const int last = min(i * kFwdBq + kFwdBq - 1, s.nq - 1);
+    const int lastkey = s.causal ? min(last + s.offset, s.nk - 1) : s.nk - 1;
+    kept += fwd_kept[x];
+    legal += lastkey < 0 ? 0 : lastkey / kFwdBk + 1;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    kept += __shfl_xor(kept, off, 64);
+    legal += __shfl_xor(legal, off, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = kept;
+    red[1][threadIdx.x >> 6] = legal;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const long long k = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    const long long l = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    *take = 2 * k < l ? 1 : 0;
+  }
+}
+
 // First 64-row step with a legal entry for the first key of 128-key block J.
 __device__ __forceinline__ int block_first_step(const Shape& s, int J) {
   if (!s.causal) return 0;
@@ -177,7 +219,9 @@ __device__ __forceinline__ int block_first_step(const Shape& s, int J) {
 // The gated walks' plan: kept pairs of every (batch, KV head, 128-key block),
 // one workgroup (one wave) each; plan[(b * Hkv + hk) * n_kb + J].
 __global__ __launch_bounds__(64) void bwd_plan_kernel(Shape s, const uint32_t* __restrict__ bits,
-                                                      int32_t* __restrict__ plan) {
+                                                      int32_t* __restrict__ plan,
+                                                      const int32_t* __restrict__ take) {
+  if (walk_not_taken(take, 1)) return;
   __shared__ int red[1];
   const int n_kb = (s.nk + 127) / 128;
   const int J = (int)(blockIdx.x % n_kb), bkv = (int)(blockIdx.x / n_kb);
@@ -191,7 +235,9 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     Shape s, const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dq,
     bf16* __restrict__ dK, bf16* __restrict__ dV, uint32_t* __restrict__ bits,
-    int8_t* __restrict__ mask, float* __restrict__ part, const int32_t* __restrict__ plan) {
+    int8_t* __restrict__ mask, float* __restrict__ part, const int32_t* __restrict__ plan,
+    const int32_t* __restrict__ take) {
+  if (walk_not_taken(take, kGated ? 1 : 0)) return;
   __shared__ DkdvSmem<D> sm;
   constexpr int ST = DkdvSmem<D>::kStride;
   constexpr int KS = D / 32;      // 32-wide k-steps over d (16x16x32 MFMA)
@@ -707,7 +753,9 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 __global__ __launch_bounds__(256) void bwd_dkdv_finalize_kernel(Shape s, const float* __restrict__ part,
                                                                 const int32_t* __restrict__ plan,
                                                                 bf16* __restrict__ dK,
-                                                                bf16* __restrict__ dV) {
+                                                                bf16* __restrict__ dV,
+                                                                const int32_t* __restrict__ take) {
+  if (walk_not_taken(take, 1)) return;
   const int n_kb = (s.nk + 127) / 128;
   const int J = (int)(blockIdx.x % n_kb);
   const int bkv = (int)(blockIdx.x / n_kb);
@@ -757,7 +805,9 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
                                                           const float* __restrict__ LSE,
                                                           uint32_t* __restrict__ bits,
                                                           int8_t* __restrict__ mask, int n_qb,
-                                                          const int8_t* __restrict__ fmask) {
+                                                          const int8_t* __restrict__ fmask,
+                                                          const int32_t* __restrict__ take) {
+  if (walk_not_taken(take, 1)) return;
   __shared__ GateSmem<D> sm;
   constexpr int KT = D / 16;              // 16-wide k-steps of the QK contraction
   constexpr int CPR = D / 8;              // 16-byte chunks per row
@@ -976,7 +1026,9 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_d128_kernel(Shape s, const bf
                                                                const float* __restrict__ LSE,
                                                                uint32_t* __restrict__ bits,
                                                                int8_t* __restrict__ mask, int n_qb,
-                                                               const int8_t* __restrict__ /*fmask*/) {
+                                                               const int8_t* __restrict__ /*fmask*/,
+                                                               const int32_t* __restrict__ take) {
+  if (walk_not_taken(take, 1)) return;
   constexpr int D = 128;
   constexpr int KT = D / 16;
   constexpr int TILE = 64 * D;
@@ -1666,7 +1718,7 @@ size_t bwd_part_floats(const Shape& s) {
 
 size_t bwd_plan_ints(const Shape& s) {
   if (!s.dtype_is_bf16() || !(s.flags & MALA_FLAG_GATE_PASS)) return 0;
-  return (size_t)s.batch * s.hkv * ((s.nk + 127) / 128);
+  return (size_t)s.batch * s.hkv * ((s.nk + 127) / 128) + 1;   // + the walk choice
 }
 
 size_t bwd_bits_words(const Shape& s) {
@@ -1678,7 +1730,7 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
                            const void* o, const float* lse, const void* d_o, void* dq, void* dk,
                            void* dv, float* ws_d, uint32_t* ws_bits, float* ws_part,
                            int32_t* ws_plan, const int8_t* fwd_mask, int8_t* mask, int32_t* kept,
-                           hipStream_t st, int stages) {
+                           hipStream_t st, int stages, const int32_t* fwd_kept) {
   const int rows = s.batch * s.hq * s.nq;
   const size_t nwords = bwd_bits_words(s);
   const size_t nkept = (size_t)s.batch * s.hq * ((s.nq + kBQ - 1) / kBQ);
@@ -1699,34 +1751,51 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
   const int n_qb = (s.nq + 255) / 256;
   const dim3 g2((unsigned)(n_qb * s.batch * s.hq));
   // MALA_FLAG_GATE_PASS: the gate pass writes the decisions, and dK/dV
-  // visits only the steps that hold a kept tile
+  // visits only the steps that hold a kept tile. fwd_kept (mala_bwd_auto):
+  // both walks are launched, and the choice kernel's flag (after the plan
+  // entries) lets the workgroups of one of them run
   const bool gated = (s.flags & MALA_FLAG_GATE_PASS) != 0;
+  const bool choose = fwd_kept != nullptr && gated;
+  const int32_t* take = nullptr;
+  if (choose && (stages & kStageMain)) {
+    int32_t* flag = ws_plan + (bwd_plan_ints(s) - 1);
+    hipLaunchKernelGGL(bwd_choose_kernel, dim3(1), dim3(256), 0, st, s, fwd_kept, flag);
+    take = flag;
+  }
   auto launch = [&](auto gate, auto gate_nested, auto dkdv, auto dkdv_gated, auto dqk) {
+    if (choose && g1.x && (stages & kStageMain)) {
+      // the default walk; its workgroups return unless the flag is 0
+      hipLaunchKernelGGL(dkdv, g1, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
+                         (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dk, (bf16*)dv,
+                         ws_bits, mask, (float*)nullptr, (const int32_t*)nullptr, take);
+    }
     if (gated && (stages & kStageMain)) {
       // decisions (on the forward's kept tiles only, given its mask), then
       // one walk per (key block, query head), then the sums
       if (g2.x && fwd_mask != nullptr)
         hipLaunchKernelGGL(gate_nested, g2, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
-                           lse, ws_bits, mask, n_qb, fwd_mask);
+                           lse, ws_bits, mask, n_qb, fwd_mask, take);
       else if (g2.x)
         hipLaunchKernelGGL(gate, g2, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k, lse,
-                           ws_bits, mask, n_qb, (const int8_t*)nullptr);
+                           ws_bits, mask, n_qb, (const int8_t*)nullptr, take);
       // the kept pairs of each key block choose its walks
       if (g1.x)
         hipLaunchKernelGGL(bwd_plan_kernel, g1, dim3(64), 0, st, s, (const uint32_t*)ws_bits,
-                           ws_plan);
+                           ws_plan, take);
       const dim3 g1h((unsigned)(g1.x * s.group));
       if (g1h.x)
         hipLaunchKernelGGL(dkdv_gated, g1h, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
                            (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dk, (bf16*)dv,
-                           ws_bits, mask, ws_part, (const int32_t*)ws_plan);
+                           ws_bits, mask, ws_part, (const int32_t*)ws_plan, take);
       if (g1.x)
         hipLaunchKernelGGL(bwd_dkdv_finalize_kernel, g1, dim3(256), 0, st, s,
-                           (const float*)ws_part, (const int32_t*)ws_plan, (bf16*)dk, (bf16*)dv);
+                           (const float*)ws_part, (const int32_t*)ws_plan, (bf16*)dk, (bf16*)dv,
+                           take);
     } else if (g1.x && (stages & kStageMain)) {
       hipLaunchKernelGGL(dkdv, g1, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
                          (const bf16*)v, (const bf16*)d_o, lse, ws_d, (bf16*)dk, (bf16*)dv,
-                         ws_bits, mask, (float*)nullptr, (const int32_t*)nullptr);
+                         ws_bits, mask, (float*)nullptr, (const int32_t*)nullptr,
+                         (const int32_t*)nullptr);
     }
     // dynamic LDS: the needed-tile bitmap, one bit per 64-key tile
     const size_t need_bytes = (size_t)((s.nk + 64 * 32 - 1) / (64 * 32)) * 4;

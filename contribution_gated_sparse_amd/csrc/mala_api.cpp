@@ -194,14 +194,23 @@ mala_status check_decode(const mala_decode_problem* p, mala::DecodeShape* s) {
 
 // nested: the backward on the forward's retained support (mala_bwd_nested);
 // fwd_mask is the forward's tile mask, read by the bf16 gate pass only.
+// fwd_kept (mala_bwd_auto): the forward's kept-tile counters, from which the
+// bf16 backward chooses its walk on the device; the problem then takes the
+// gate-pass workspace.
 mala_status bwd_impl(int stages, const mala_problem* p, const void* q, const void* k,
                      const void* v, const void* o, const float* lse, const void* d_o, void* dq,
                      void* dk, void* dv, void* workspace, size_t ws_bytes, int8_t* tile_mask,
                      int32_t* kept_tiles, void* stream, bool nested = false,
-                     const int8_t* fwd_mask = nullptr) {
+                     const int8_t* fwd_mask = nullptr, const int32_t* fwd_kept = nullptr) {
   mala::Shape s;
   MALA_TRY(check_problem(p, &s));
   const bool rows = s.nq > 0;
+  const bool autosel = fwd_kept != nullptr;
+  if (autosel) {
+    if (s.flags & MALA_FLAG_GATE_PASS)
+      return fail(MALA_ERR_INVALID_ARG, "mala_bwd_auto chooses the walk: MALA_FLAG_GATE_PASS must not be set");
+    if (s.dtype_is_bf16()) s.flags |= MALA_FLAG_GATE_PASS;
+  }
   if (nested) {
     if (!(s.flags & MALA_FLAG_GATE_PASS))
       return fail(MALA_ERR_INVALID_ARG, "mala_bwd_nested needs MALA_FLAG_GATE_PASS in p->flags");
@@ -231,7 +240,8 @@ mala_status bwd_impl(int stages, const mala_problem* p, const void* q, const voi
   hipError_t e;
   if (s.dtype_is_bf16())
     e = mala::launch_bwd_bf16(s, q, k, v, o, lse, d_o, dq, dk, dv, ws_d, ws_bits, ws_part, ws_plan,
-                              nested ? fwd_mask : nullptr, tile_mask, kept_tiles, st, stages);
+                              nested ? fwd_mask : nullptr, tile_mask, kept_tiles, st, stages,
+                              rows ? fwd_kept : nullptr);
   else
     e = mala::launch_bwd_f32(s, (const float*)q, (const float*)k, (const float*)v,
                              (const float*)o, lse, (const float*)d_o, (float*)dq, (float*)dk,
@@ -361,6 +371,20 @@ mala_status mala_bwd_nested(const mala_problem* p, const void* q, const void* k,
                             int32_t* kept_tiles, void* stream) {
   return bwd_impl(mala::kStagesAll, p, q, k, v, o, lse, d_o, dq, dk, dv, workspace, ws_bytes,
                   tile_mask, kept_tiles, stream, true, fwd_tile_mask);
+}
+
+mala_status mala_bwd_auto(const mala_problem* p, const void* q, const void* k, const void* v,
+                          const void* o, const float* lse, const void* d_o,
+                          const int32_t* fwd_kept_tiles, void* dq, void* dk, void* dv,
+                          void* workspace, size_t ws_bytes, int8_t* tile_mask, int32_t* kept_tiles,
+                          void* stream) {
+  if (p != nullptr && p->n_q > 0 && fwd_kept_tiles == nullptr)
+    return fail(MALA_ERR_INVALID_ARG, "fwd_kept_tiles is NULL");
+  // the pointer marks the mode even when there are no query rows
+  static const int32_t kNoRows = 0;
+  return bwd_impl(mala::kStagesAll, p, q, k, v, o, lse, d_o, dq, dk, dv, workspace, ws_bytes,
+                  tile_mask, kept_tiles, stream, false, nullptr,
+                  fwd_kept_tiles != nullptr ? fwd_kept_tiles : &kNoRows);
 }
 
 mala_status mala_bwd_stage(int32_t stage, const mala_problem* p, const void* q, const void* k,

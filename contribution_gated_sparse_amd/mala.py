@@ -53,8 +53,9 @@ class DecodeProblem(ctypes.Structure):
 DECODE_SPLIT_AUTO = -1
 
 EXPORTS = ("mala_get_tiling", "mala_fwd", "mala_bwd_workspace_size", "mala_bwd",
-           "mala_bwd_nested", "mala_bwd_stage", "mala_decode_workspace_size", "mala_decode_split_keys", "mala_decode",
-           "mala_decode_stage", "mala_decode_noalloc", "mala_last_error", "mala_version")
+           "mala_bwd_nested", "mala_bwd_auto", "mala_bwd_stage", "mala_decode_workspace_size",
+           "mala_decode_split_keys", "mala_decode", "mala_decode_stage", "mala_decode_noalloc",
+           "mala_last_error", "mala_version")
 BWD_PREP, BWD_DKDV, BWD_DQ = 0, 1, 2
 DECODE_SPLIT, DECODE_COMBINE = 0, 1
 
@@ -86,6 +87,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.mala_bwd.restype = i32
     lib.mala_bwd_nested.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
     lib.mala_bwd_nested.restype = i32
+    lib.mala_bwd_auto.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    lib.mala_bwd_auto.restype = i32
     lib.mala_bwd_stage.argtypes = [i32, P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
     lib.mala_bwd_stage.restype = i32
     lib.mala_decode_stage.argtypes = [i32, DP, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
@@ -184,16 +187,21 @@ def mala_bwd(q, k, v, o, lse, d_o, tau: float, causal: bool = True,
              softmax_scale: Optional[float] = None, want_mask: bool = False,
              want_kept: bool = True, out: Optional[dict] = None, fast_grad: bool = False,
              gate_pass: bool = False, stages=None, events=None,
-             fwd_mask: Optional[torch.Tensor] = None) -> dict:
+             fwd_mask: Optional[torch.Tensor] = None,
+             fwd_kept: Optional[torch.Tensor] = None) -> dict:
     """Backward -> dict(dq, dk, dv, mask, kept). ``gate_pass``: take the
     decisions in a separate score pass so that dK/dV visits only the steps
     with a kept tile (MALA_FLAG_GATE_PASS). ``fwd_mask``: the forward's tile
     mask (``mala_fwd(..., want_mask=True)["mask"]``) for the same inputs; the
     score pass then forms only the scores of the tiles the forward kept
     (mala_bwd_nested, which runs in the gate-pass mode, so ``gate_pass`` is
-    implied). ``stages``: run only these stages (BWD_PREP, BWD_DKDV, BWD_DQ)
-    through mala_bwd_stage; ``events``: optional list of torch.cuda.Event,
-    one recorded after each stage run."""
+    implied). ``fwd_kept``: the forward's kept-tile counters
+    (``mala_fwd(...)["kept"]``) for the same inputs; the backward then takes
+    the gate-pass walks when the forward kept fewer than half of its legal
+    tiles and the default walk otherwise, chosen on the device
+    (mala_bwd_auto; ``gate_pass`` must be False). ``stages``: run only these
+    stages (BWD_PREP, BWD_DKDV, BWD_DQ) through mala_bwd_stage; ``events``:
+    optional list of torch.cuda.Event, one recorded after each stage run."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (d_o, "d_o")):
         _dev(t, n)
     if fwd_mask is not None:
@@ -207,6 +215,16 @@ def mala_bwd(q, k, v, o, lse, d_o, tau: float, causal: bool = True,
         if stages is not None or events is not None:
             raise ValueError("fwd_mask runs the whole backward: no stages or events")
         gate_pass = True
+    if fwd_kept is not None:
+        _dev(fwd_kept, "fwd_kept")
+        if fwd_kept.dtype != torch.int32:
+            raise TypeError("fwd_kept must be int32 (the forward's kept-tile counters)")
+        fb, _, _ = mala_get_tiling(OP_FWD)
+        want = (q.shape[0], q.shape[1], -(-q.shape[2] // fb))
+        if tuple(fwd_kept.shape) != want:
+            raise ValueError(f"fwd_kept has shape {tuple(fwd_kept.shape)}, expected {want}")
+        if gate_pass or fwd_mask is not None or stages is not None or events is not None:
+            raise ValueError("fwd_kept chooses the walk itself: no gate_pass, fwd_mask, stages or events")
     p = make_problem(q, k, tau, causal, softmax_scale,
                      (MALA_FLAG_FAST_GRAD if fast_grad else 0) | (MALA_FLAG_GATE_PASS if gate_pass else 0))
     lib = load_library()
@@ -219,7 +237,11 @@ def mala_bwd(q, k, v, o, lse, d_o, tau: float, causal: bool = True,
     dk = torch.empty_like(k) if dk is None else dk
     dv = out.get("dv")
     dv = torch.empty_like(v) if dv is None else dv
-    nws = lib.mala_bwd_workspace_size(ctypes.byref(p))
+    if fwd_kept is not None:    # the gate-pass workspace, whichever walk runs
+        pg = make_problem(q, k, tau, causal, softmax_scale, p.flags | MALA_FLAG_GATE_PASS)
+        nws = lib.mala_bwd_workspace_size(ctypes.byref(pg))
+    else:
+        nws = lib.mala_bwd_workspace_size(ctypes.byref(p))
     ws = out.get("ws")
     if ws is None or ws.numel() < nws:
         ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=q.device)
@@ -233,6 +255,8 @@ def mala_bwd(q, k, v, o, lse, d_o, tau: float, causal: bool = True,
             _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _ptr(mask), _ptr(kept), _stream())
     if fwd_mask is not None:
         _check(lib.mala_bwd_nested(*args[:7], _ptr(fwd_mask), *args[7:]))
+    elif fwd_kept is not None:
+        _check(lib.mala_bwd_auto(*args[:7], _ptr(fwd_kept), *args[7:]))
     elif stages is None and events is None:
         _check(lib.mala_bwd(*args))
     else:

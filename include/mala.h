@@ -204,6 +204,34 @@ mala_status mala_bwd_nested(const mala_problem* p, const void* q, const void* k,
                             int32_t* kept_tiles, void* stream);
 
 /*
+ * The backward with its dK/dV walk chosen on the device from the forward's
+ * kept fraction: the gate-pass walks (MALA_FLAG_GATE_PASS: the Eq. 4
+ * decisions of every legal tile in a separate score pass, then only the
+ * steps that hold a kept tile) when the forward kept fewer than half of its
+ * legal tiles, else the default walk. Both recompute every legal score
+ * before its decision (Sec. 2.2 "Offline Sparse Probability"; App. A.1
+ * "Fused backward execution"); the result is, bit for bit, that of mala_bwd
+ * with MALA_FLAG_GATE_PASS when the gate-pass walks are taken and that of
+ * mala_bwd without it otherwise. The choice needs no host round trip: a
+ * one-workgroup kernel reduces the counters, both walks' kernels are
+ * launched, and the workgroups of the walk not taken return at once.
+ *   fwd_kept_tiles int32 [B,Hq,Tr] (device), Tr = ceil(Nq/bq) with the
+ *                  forward tiling: the kept_tiles mala_fwd wrote for the same
+ *                  problem, q, k and v. Required when n_q > 0.
+ *   the other arguments as for mala_bwd; p->flags must not include
+ *                  MALA_FLAG_GATE_PASS (MALA_ERR_INVALID_ARG), and the
+ *                  workspace is mala_bwd_workspace_size of p with
+ *                  MALA_FLAG_GATE_PASS added to p->flags (MALA_ERR_WORKSPACE
+ *                  if smaller).
+ * For MALA_F32 the counters are not read and the call is mala_bwd.
+ */
+mala_status mala_bwd_auto(const mala_problem* p, const void* q, const void* k, const void* v,
+                          const void* o, const float* lse, const void* d_o,
+                          const int32_t* fwd_kept_tiles, void* dq, void* dk, void* dv,
+                          void* workspace, size_t ws_bytes, int8_t* tile_mask,
+                          int32_t* kept_tiles, void* stream);
+
+/*
  * The backward as three stages, for callers that schedule or time them
  * separately. Calling MALA_BWD_PREP, MALA_BWD_DKDV, MALA_BWD_DQ in this order
  * on one stream with the same arguments and workspace is mala_bwd.

@@ -43,6 +43,9 @@ int main(void) {
   CHECK(mala_bwd_nested(&p, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0,
                         NULL, NULL, NULL) == MALA_ERR_INVALID_ARG);
   CHECK(strstr(mala_last_error(), "MALA_FLAG_GATE_PASS") != NULL);
+  CHECK(mala_bwd_auto(&p, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0,
+                      NULL, NULL, NULL) == MALA_ERR_INVALID_ARG);  /* no forward counters */
+  CHECK(strstr(mala_last_error(), "fwd_kept_tiles") != NULL);
 
   mala_decode_problem d;
   memset(&d, 0, sizeof d);

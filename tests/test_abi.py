@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
     assert set(names) == set(M.EXPORTS)
@@ -154,6 +154,34 @@ def test_nested_backward_arguments(lib):
     assert st == M.MALA_ERR_WORKSPACE
     assert lib.mala_bwd_nested(None, g, g, g, g, g, g, fm, g, g, g, g, need_gp, None, None,
                                None) == M.MALA_ERR_INVALID_ARG
+
+
+def test_auto_backward_arguments(lib):
+    """mala_bwd_auto needs the forward's kept-tile counters, chooses the walk
+    itself (MALA_FLAG_GATE_PASS set by the caller is an error) and takes the
+    gate-pass workspace; all checked before anything is enqueued."""
+    buf = (ctypes.c_char * 1024)()
+    addr = ctypes.addressof(buf)
+    addr += (-addr) % 256
+    g = ctypes.c_void_p(addr)
+    fk = ctypes.c_void_p(addr + 4)
+    p = prob()
+    need = lib.mala_bwd_workspace_size(ctypes.byref(p))
+    need_gp = lib.mala_bwd_workspace_size(ctypes.byref(prob(flags=M.MALA_FLAG_GATE_PASS)))
+    assert need_gp > need
+    st = lib.mala_bwd_auto(ctypes.byref(p), g, g, g, g, g, g, None, g, g, g, g, need_gp, None,
+                           None, None)
+    assert st == M.MALA_ERR_INVALID_ARG and "fwd_kept_tiles" in lib.mala_last_error().decode()
+    gp = prob(flags=M.MALA_FLAG_GATE_PASS)
+    st = lib.mala_bwd_auto(ctypes.byref(gp), g, g, g, g, g, g, fk, g, g, g, g, need_gp, None,
+                           None, None)
+    assert st == M.MALA_ERR_INVALID_ARG and "MALA_FLAG_GATE_PASS" in lib.mala_last_error().decode()
+    # the default backward's workspace is too small: the gate pass's is needed
+    st = lib.mala_bwd_auto(ctypes.byref(p), g, g, g, g, g, g, fk, g, g, g, g, need, None, None,
+                           None)
+    assert st == M.MALA_ERR_WORKSPACE
+    assert lib.mala_bwd_auto(None, g, g, g, g, g, g, fk, g, g, g, g, need_gp, None, None,
+                             None) == M.MALA_ERR_INVALID_ARG
 
 
 def dprob(**kw):

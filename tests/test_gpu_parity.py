@@ -280,6 +280,68 @@ def test_gate_pass_noncausal_and_f32():
     check_backward(x, 1.0, g, r, gate_pass=True)
 
 
+def auto_takes_gate_pass(fwd_kept, nq, nk, causal):
+    """The walk mala_bwd_auto documents: the gate-pass walks when the forward
+    kept fewer than half of its legal tiles (each 32-row block's tiles up to
+    the one holding its last row's last visible key)."""
+    (fbq, fbk, _), _, _ = tiling()
+    legal = 0
+    for i in range(-(-nq // fbq)):
+        last = min(i * fbq + fbq - 1, nq - 1)
+        lastkey = min(last + nk - nq, nk - 1) if causal else nk - 1
+        legal += lastkey // fbk + 1 if lastkey >= 0 else 0
+    kt = fwd_kept.cpu().numpy()
+    return 2 * int(kt.sum()) < legal * kt.shape[0] * kt.shape[1]
+
+
+def assert_auto_is_chosen_walk(x, tau, causal=True, want_gate=None):
+    """mala_bwd_auto against the explicit call of the walk its rule picks:
+    gradients, tile mask and kept counters equal bit for bit."""
+    m = lib()
+    nq, nk = x["q"].shape[2], x["k"].shape[2]
+    f = m.mala_fwd(x["q"], x["k"], x["v"], tau, causal=causal, softmax_scale=x["scale"])
+    gate = auto_takes_gate_pass(f["kept"], nq, nk, causal)
+    if want_gate is not None:
+        assert gate == want_gate
+    a = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], tau, causal=causal,
+                   softmax_scale=x["scale"], want_mask=True, fwd_kept=f["kept"])
+    b = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], tau, causal=causal,
+                   softmax_scale=x["scale"], want_mask=True, gate_pass=gate)
+    torch.cuda.synchronize()
+    for n in ("dq", "dk", "dv", "mask", "kept"):
+        assert torch.equal(a[n], b[n]), (n, gate)
+    return gate
+
+
+@pytest.mark.parametrize("preset,tau,want_gate", [("sparse", 1.0, True), ("sparse", 1e-4, True),
+                                                  ("calibrated", 1.0, False),
+                                                  ("sparse", 0.0, False)])
+def test_auto_walk_choice_structured(preset, tau, want_gate):
+    """mala_bwd_auto on structured inputs: the sparse preset keeps about a
+    quarter of the legal tiles at 1,500 keys (the gate-pass walks), the
+    calibrated one most of them and tau = 0 all of them (the default walk).
+    Both walks are held to the oracle by the tests above, on these inputs."""
+    x = to_dev(W.make_structured_preset(preset, 1500, hq=8, hkv=2, d=128))
+    print(f"[auto] preset={preset} tau={tau}", flush=True)
+    assert assert_auto_is_chosen_walk(x, tau, want_gate=want_gate) == want_gate
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_auto_walk_choice_shapes(shape):
+    """Ragged shapes, both head sizes, causal and not: whichever walk the
+    rule picks, the result is that walk's."""
+    b, hq, hkv, nq, nk, d = shape
+    x = W.make_prefill(W.CONFIGS[2], n=nk, hq=hq, hkv=hkv, d=d, batch=b, planted=4, seed=5 + nq)
+    if nq < nk:
+        x["q"] = x["q"][:, :, nk - nq:].contiguous()
+        x["do"] = x["do"][:, :, nk - nq:].contiguous()
+    x = to_dev(x)
+    print(f"[auto] shape={shape}", flush=True)
+    for causal in (True, False):
+        for tau in (1e-4, 100.0):
+            assert_auto_is_chosen_walk(x, tau, causal=causal)
+
+
 def expand_fwd(fmask, shape):
     """The forward tile mask on the backward partition (each backward tile
     lies in one forward tile)."""
@@ -590,7 +652,7 @@ def test_fast_grad_flag_same_support():
 
 # ------------------------------------------------------------- autograd entry
 
-@pytest.mark.parametrize("mode", ["default", "gate_pass", "nested"])
+@pytest.mark.parametrize("mode", ["default", "gate_pass", "nested", "auto"])
 def test_autograd_chunked_prefill_matches_direct_calls(mode):
     """mala_attention (torch.autograd) runs the same two C-ABI calls: its
     output and gradients equal mala_fwd / mala_bwd bit for bit, here on a
@@ -606,14 +668,17 @@ def test_autograd_chunked_prefill_matches_direct_calls(mode):
     v = x["v"].clone().requires_grad_()
     do = x["do"][:, :, -100:].contiguous()
     q = (base * 1.0).to(torch.bfloat16).contiguous()        # upstream op
-    o = m.mala_attention(q, k, v, 1e-4, softmax_scale=scale, gate_pass=mode == "gate_pass",
+    gp = "auto" if mode == "auto" else mode == "gate_pass"
+    o = m.mala_attention(q, k, v, 1e-4, softmax_scale=scale, gate_pass=gp,
                          nested=mode == "nested")
     o.backward(do)
     qd = q.detach()
     f = m.mala_fwd(qd, k.detach(), v.detach(), 1e-4, softmax_scale=scale,
                    want_mask=mode == "nested")
+    if mode == "auto":      # the walk the forward's kept fraction chooses
+        gp = auto_takes_gate_pass(f["kept"], 100, 356, True)
     b = m.mala_bwd(qd, k.detach(), v.detach(), f["o"], f["lse"], do, 1e-4, softmax_scale=scale,
-                   gate_pass=mode == "gate_pass", fwd_mask=f["mask"])
+                   gate_pass=gp, fwd_mask=f["mask"])
     torch.cuda.synchronize()
     assert torch.equal(o.detach(), f["o"])
     assert torch.equal(base.grad, b["dq"].float())
