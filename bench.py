@@ -106,7 +106,8 @@ def matched_work(m, F, W, torch, dev, fbq, fbk, preset, n=8192):
 def profile_structured(tau, m, W, torch, dev):
     """Kernel launches for a profiler on the structured inputs: two passes
     (the first warms up) of the 32K forward + backward, two of the backward
-    with the separate gate pass, two of the forward writing its tile mask and
+    with the separate gate pass, two with the walk chosen on the device
+    (mala_bwd_auto), two of the forward writing its tile mask and
     the nested backward on it, then of the 128K decode with 256-key splits
     and with one split per sequence."""
     x = W.make_structured(32768, hq=32, hkv=8, d=128, device=dev, dtype="bf16", with_do=False)
@@ -118,6 +119,9 @@ def profile_structured(tau, m, W, torch, dev):
         torch.cuda.synchronize()
     for _ in range(2):   # the backward with the separate gate pass
         m.mala_bwd(q, k, v, f["o"], f["lse"], do, tau, softmax_scale=x["scale"], gate_pass=True)
+        torch.cuda.synchronize()
+    for _ in range(2):   # the walk chosen on the device from the forward's kept counters
+        m.mala_bwd(q, k, v, f["o"], f["lse"], do, tau, softmax_scale=x["scale"], fwd_kept=f["kept"])
         torch.cuda.synchronize()
     for _ in range(2):   # the forward's tile mask and the backward on its kept tiles
         f = m.mala_fwd(q, k, v, tau, softmax_scale=x["scale"], want_mask=True)

@@ -53,7 +53,7 @@ def mala_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float
     score pass over all legal tiles (MALA_FLAG_GATE_PASS), then skips the
     steps without a kept tile (for inputs where few tiles are kept). "auto":
     the forward also returns its kept-tile counters, and the backward takes
-    that mode when the forward kept fewer than half of its legal tiles, the
+    that mode when the forward kept fewer than 70% of its legal tiles, the
     default walk otherwise, chosen on the device (mala_bwd_auto).
     ``nested``: the backward scores only the tiles the forward kept
     (mala_bwd_nested, which runs in the gate-pass mode): the forward also

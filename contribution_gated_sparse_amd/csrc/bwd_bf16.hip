@@ -46,6 +46,7 @@
 // of the terms rather than of the result. A column of dS has no such
 // identity, and dK keeps its error well inside the same bound with one
 // rounding. MALA_FLAG_FAST_GRAD skips the lo half in dQ as well.
+#include <algorithm>
 #include <type_traits>
 
 #include "mala_device.h"
@@ -175,37 +176,35 @@ __device__ __forceinline__ bool walk_not_taken(const int32_t* take, int mine) {
   return take != nullptr && __builtin_amdgcn_readfirstlane(*take) != mine;
 }
 
-// The choice: the gate-pass walks when the forward kept fewer than half of
+// The choice: the gate-pass walks when the forward kept fewer than 70% of
 // its legal tiles. fwd_kept: the forward's kept tiles per (b, h, 32-row
-// block); a block's legal tiles are the 64-key tiles up to the one that
-// holds its last row's last visible key. One workgroup.
-__global__ __launch_bounds__(256) void bwd_choose_kernel(Shape s, const int32_t* __restrict__ fwd_kept,
-                                                         int32_t* __restrict__ take) {
-  __shared__ long long red[2][4];
-  const int ftr = (s.nq + kFwdBq - 1) / kFwdBq;
-  long long kept = 0, legal = 0;
-  const long long n = (long long)s.batch * s.hq * ftr;
-  for (long long x = threadIdx.x; x < n; x += 256) {
-    const int i = (int)(x % ftr);
-    const int last = min(i * kFwdBq + kFwdBq - 1, s.nq - 1);
-    const int lastkey = s.causal ? min(last + s.offset, s.nk - 1) : s.nk - 1;
-    kept += fwd_kept[x];
-    legal += lastkey < 0 ? 0 : lastkey / kFwdBk + 1;
+// block), n entries; legal: the forward's legal tiles over all of them (a
+// function of the shape, counted on the host). One workgroup of 1024
+// threads; each thread issues its 8 loads of a round before it adds.
+__global__ __launch_bounds__(1024) void bwd_choose_kernel(const int32_t* __restrict__ fwd_kept,
+                                                          long long n, long long legal,
+                                                          int32_t* __restrict__ take) {
+  __shared__ long long red[16];
+  long long kept = 0;
+  for (long long x0 = 0; x0 < n; x0 += 8 * 1024) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const long long x = x0 + u * 1024 + threadIdx.x;
+      v[u] = x < n ? fwd_kept[x] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) kept += v[u];
   }
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    kept += __shfl_xor(kept, off, 64);
-    legal += __shfl_xor(legal, off, 64);
-  }
-  if ((threadIdx.x & 63) == 0) {
-    red[0][threadIdx.x >> 6] = kept;
-    red[1][threadIdx.x >> 6] = legal;
-  }
+  for (int off = 32; off >= 1; off >>= 1) kept += __shfl_xor(kept, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = kept;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const long long k = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-    const long long l = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-    *take = 2 * k < l ? 1 : 0;
+    long long k = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) k += red[u];
+    *take = 10 * k < 7 * legal ? 1 : 0;
   }
 }
 
@@ -1758,8 +1757,19 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
   const bool choose = fwd_kept != nullptr && gated;
   const int32_t* take = nullptr;
   if (choose && (stages & kStageMain)) {
+    // the forward's legal tiles: per 32-row block, the 64-key tiles up to
+    // the one that holds its last row's last visible key
+    const int ftr = (s.nq + kFwdBq - 1) / kFwdBq;
+    long long legal = 0;
+    for (int i = 0; i < ftr; ++i) {
+      const int last = std::min(i * kFwdBq + kFwdBq - 1, s.nq - 1);
+      const int lastkey = s.causal ? std::min(last + s.offset, s.nk - 1) : s.nk - 1;
+      legal += lastkey < 0 ? 0 : lastkey / kFwdBk + 1;
+    }
+    legal *= (long long)s.batch * s.hq;
     int32_t* flag = ws_plan + (bwd_plan_ints(s) - 1);
-    hipLaunchKernelGGL(bwd_choose_kernel, dim3(1), dim3(256), 0, st, s, fwd_kept, flag);
+    hipLaunchKernelGGL(bwd_choose_kernel, dim3(1), dim3(1024), 0, st, fwd_kept,
+                       (long long)s.batch * s.hq * ftr, legal, flag);
     take = flag;
   }
   auto launch = [&](auto gate, auto gate_nested, auto dkdv, auto dkdv_gated, auto dqk) {

@@ -197,7 +197,7 @@ def mala_bwd(q, k, v, o, lse, d_o, tau: float, causal: bool = True,
     (mala_bwd_nested, which runs in the gate-pass mode, so ``gate_pass`` is
     implied). ``fwd_kept``: the forward's kept-tile counters
     (``mala_fwd(...)["kept"]``) for the same inputs; the backward then takes
-    the gate-pass walks when the forward kept fewer than half of its legal
+    the gate-pass walks when the forward kept fewer than 70% of its legal
     tiles and the default walk otherwise, chosen on the device
     (mala_bwd_auto; ``gate_pass`` must be False). ``stages``: run only these
     stages (BWD_PREP, BWD_DKDV, BWD_DQ) through mala_bwd_stage; ``events``:

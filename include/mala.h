@@ -207,7 +207,7 @@ mala_status mala_bwd_nested(const mala_problem* p, const void* q, const void* k,
  * The backward with its dK/dV walk chosen on the device from the forward's
  * kept fraction: the gate-pass walks (MALA_FLAG_GATE_PASS: the Eq. 4
  * decisions of every legal tile in a separate score pass, then only the
- * steps that hold a kept tile) when the forward kept fewer than half of its
+ * steps that hold a kept tile) when the forward kept fewer than 70% of its
  * legal tiles, else the default walk. Both recompute every legal score
  * before its decision (Sec. 2.2 "Offline Sparse Probability"; App. A.1
  * "Fused backward execution"); the result is, bit for bit, that of mala_bwd
