@@ -52,9 +52,9 @@ def mala_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tau: float
     ``gate_pass``: True: the backward takes every decision in a separate
     score pass over all legal tiles (MALA_FLAG_GATE_PASS), then skips the
     steps without a kept tile (for inputs where few tiles are kept). "auto":
-    the forward also returns its kept-tile counters, and the backward takes
-    that mode when the forward kept fewer than 70% of its legal tiles, the
-    default walk otherwise, chosen on the device (mala_bwd_auto).
+    the forward also returns its kept-tile counters, and the backward
+    chooses between that mode and the default walk on the device, from its
+    own decisions on a sample of the key tiles (mala_bwd_auto).
     ``nested``: the backward scores only the tiles the forward kept
     (mala_bwd_nested, which runs in the gate-pass mode): the forward also
     stores its tile mask, int8 [B,Hq,ceil(Nq/32),ceil(Nk/64)], until the

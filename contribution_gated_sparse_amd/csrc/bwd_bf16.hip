@@ -176,16 +176,23 @@ __device__ __forceinline__ bool walk_not_taken(const int32_t* take, int mine) {
   return take != nullptr && __builtin_amdgcn_readfirstlane(*take) != mine;
 }
 
-// The choice: the gate-pass walks when the forward kept fewer than 70% of
-// its legal tiles. fwd_kept: the forward's kept tiles per (b, h, 32-row
-// block), n entries; legal: the forward's legal tiles over all of them (a
-// function of the shape, counted on the host). One workgroup of 1024
-// threads; each thread issues its 8 loads of a round before it adds.
+// The choice. counts: the sampled gate's kept and legal 16-key columns per
+// workgroup (n_slots pairs); from a sample of at least kMinSampleCols legal
+// columns, the gate-pass walks are taken when fewer than 60% were kept.
+// Otherwise the forward's counters decide: the gate-pass walks when the
+// forward kept fewer than 70% of its legal tiles (fwd_kept: kept tiles per
+// (b, h, 32-row block), n entries; legal: the forward's legal tiles, a
+// function of the shape counted on the host). One workgroup of 1024
+// threads; each thread issues its loads of a round before it adds.
+constexpr long long kMinSampleCols = 256;
+
 __global__ __launch_bounds__(1024) void bwd_choose_kernel(const int32_t* __restrict__ fwd_kept,
                                                           long long n, long long legal,
+                                                          const uint32_t* __restrict__ counts,
+                                                          long long n_slots,
                                                           int32_t* __restrict__ take) {
-  __shared__ long long red[16];
-  long long kept = 0;
+  __shared__ long long red[3][16];
+  long long kept = 0, sk = 0, sl = 0;
   for (long long x0 = 0; x0 < n; x0 += 8 * 1024) {
     int v[8];
 #pragma unroll
@@ -196,15 +203,41 @@ __global__ __launch_bounds__(1024) void bwd_choose_kernel(const int32_t* __restr
 #pragma unroll
     for (int u = 0; u < 8; ++u) kept += v[u];
   }
+  for (long long x0 = 0; x0 < n_slots; x0 += 4 * 1024) {
+    uint32_t a[4], c[4];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) kept += __shfl_xor(kept, off, 64);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = kept;
+    for (int u = 0; u < 4; ++u) {
+      const long long x = x0 + u * 1024 + threadIdx.x;
+      a[u] = x < n_slots ? counts[2 * x] : 0u;
+      c[u] = x < n_slots ? counts[2 * x + 1] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sk += a[u];
+      sl += c[u];
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    kept += __shfl_xor(kept, off, 64);
+    sk += __shfl_xor(sk, off, 64);
+    sl += __shfl_xor(sl, off, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = kept;
+    red[1][threadIdx.x >> 6] = sk;
+    red[2][threadIdx.x >> 6] = sl;
+  }
   __syncthreads();
   if (threadIdx.x == 0) {
-    long long k = 0;
+    long long k = 0, a = 0, c = 0;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) k += red[u];
-    *take = 10 * k < 7 * legal ? 1 : 0;
+    for (int u = 0; u < 16; ++u) {
+      k += red[0][u];
+      a += red[1][u];
+      c += red[2][u];
+    }
+    *take = c >= kMinSampleCols ? (10 * a < 6 * c ? 1 : 0) : (10 * k < 7 * legal ? 1 : 0);
   }
 }
 
@@ -798,14 +831,20 @@ struct alignas(16) GateSmem {
   bf16 k[2][64][D + 8];   // conflict-free 16-byte row reads (32x32x16 A layout)
 };
 
-template <int D, bool kNested>
+// kSample (mala_bwd_auto): the same scores and votes on the tiles j with
+// j = phase (mod stride) only, where the phase varies with the workgroup;
+// nothing is written but the workgroup's counts of kept and legal 16-key
+// columns, to counts[2 blockIdx.x] and counts[2 blockIdx.x + 1].
+template <int D, bool kNested, bool kSample = false>
 __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* __restrict__ Q,
                                                           const bf16* __restrict__ K,
                                                           const float* __restrict__ LSE,
                                                           uint32_t* __restrict__ bits,
                                                           int8_t* __restrict__ mask, int n_qb,
                                                           const int8_t* __restrict__ fmask,
-                                                          const int32_t* __restrict__ take) {
+                                                          const int32_t* __restrict__ take,
+                                                          uint32_t* __restrict__ counts,
+                                                          int stride) {
   if (walk_not_taken(take, 1)) return;
   __shared__ GateSmem<D> sm;
   constexpr int KT = D / 16;              // 16-wide k-steps of the QK contraction
@@ -865,9 +904,15 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
     la_own = __builtin_amdgcn_ballot_w64(own);
     la_base = base;
   };
+  const int phase = (int)((7u * (uint32_t)I + 3u * (uint32_t)bh) % (uint32_t)stride);
   // the highest tile <= j to visit (-1: none) and whether this wave scores it
   auto next_tile = [&](int j, bool& own) -> int {
-    if constexpr (!kNested) {
+    if constexpr (kSample) {
+      own = true;
+      if (j < 0) return -1;
+      const int jj = j - ((j - phase) % stride + stride) % stride;
+      return jj >= 0 ? jj : -1;
+    } else if constexpr (!kNested) {
       own = true;
       return j;
     } else {
@@ -948,6 +993,7 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
   __syncthreads();
 
   uint32_t word = 0u;            // decisions of columns 32 (j / 8) .. + 31 of this wave's row
+  uint32_t n_kept = 0u, n_legal = 0u;   // kSample: this wave's column counts
   int buf = 0;
   while (j >= 0) {
     bool own_n = false;
@@ -991,8 +1037,14 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
         for (int r = 0; r < 8; ++r) x = fmaxf(x, sacc[c >> 1][8 * (c & 1) + r]);
         if (__builtin_amdgcn_ballot_w64(x >= thr_s) != 0) keep4 |= 1u << c;
       }
+      if constexpr (kSample) {
+        // a column without a legal entry is never kept (its scores are -inf)
+        n_kept += (uint32_t)__builtin_popcount(keep4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) n_legal += legal_col(4 * j + c) ? 1u : 0u;
+      }
       word |= keep4 << ((4 * j) & 31);
-      if (mask != nullptr && lane == 0) {
+      if (!kSample && mask != nullptr && lane == 0) {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
           if (legal_col(4 * j + c)) mask[brow * tc16 + 4 * j + c] = (int8_t)((keep4 >> c) & 1u);
@@ -1001,7 +1053,7 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
     // the word of columns 32 (j / 8) .. is complete once the walk leaves it;
     // the bit rows start cleared, so only words with a kept column are written
     if (jn < 0 || (jn >> 3) != (j >> 3)) {
-      if (active && lane == 0 && word != 0u) bits[brow * words + (j >> 3)] = word;
+      if (!kSample && active && lane == 0 && word != 0u) bits[brow * words + (j >> 3)] = word;
       word = 0u;
     }
     if (jn >= 0) store_tile(buf ^ 1);
@@ -1009,6 +1061,20 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
     buf ^= 1;
     j = jn;
     own = own_n;
+  }
+  if constexpr (kSample) {
+    __shared__ uint32_t cnt[2][8];
+    if (lane == 0) {
+      cnt[0][w] = n_kept;
+      cnt[1][w] = n_legal;
+    }
+    __syncthreads();
+    if (tid < 2) {
+      uint32_t t = 0u;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) t += cnt[tid][x];
+      counts[2 * (size_t)blockIdx.x + tid] = t;
+    }
   }
 }
 
@@ -1026,7 +1092,9 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_d128_kernel(Shape s, const bf
                                                                uint32_t* __restrict__ bits,
                                                                int8_t* __restrict__ mask, int n_qb,
                                                                const int8_t* __restrict__ /*fmask*/,
-                                                               const int32_t* __restrict__ take) {
+                                                               const int32_t* __restrict__ take,
+                                                               uint32_t* __restrict__ /*counts*/,
+                                                               int /*stride*/) {
   if (walk_not_taken(take, 1)) return;
   constexpr int D = 128;
   constexpr int KT = D / 16;
@@ -1715,9 +1783,15 @@ size_t bwd_part_floats(const Shape& s) {
   return 2 * (size_t)s.batch * s.hq * s.nk * s.d;
 }
 
+size_t bwd_plan_entries(const Shape& s) { return (size_t)s.batch * s.hkv * ((s.nk + 127) / 128); }
+
+// workgroups of the query-major gate kernels: 256 rows of one head each
+size_t bwd_gate_groups(const Shape& s) { return (size_t)((s.nq + 255) / 256) * s.batch * s.hq; }
+
 size_t bwd_plan_ints(const Shape& s) {
   if (!s.dtype_is_bf16() || !(s.flags & MALA_FLAG_GATE_PASS)) return 0;
-  return (size_t)s.batch * s.hkv * ((s.nk + 127) / 128) + 1;   // + the walk choice
+  // the plan, the walk choice, and the sampled gate's two counts per workgroup
+  return bwd_plan_entries(s) + 1 + 2 * bwd_gate_groups(s);
 }
 
 size_t bwd_bits_words(const Shape& s) {
@@ -1767,9 +1841,27 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
       legal += lastkey < 0 ? 0 : lastkey / kFwdBk + 1;
     }
     legal *= (long long)s.batch * s.hq;
-    int32_t* flag = ws_plan + (bwd_plan_ints(s) - 1);
+    int32_t* flag = ws_plan + bwd_plan_entries(s);
+    uint32_t* slots = reinterpret_cast<uint32_t*>(flag + 1);
+    // the backward's own decisions on a sample of the key tiles: about 16
+    // tiles per 256-row block, at most one in 32
+    const int tc64 = (s.nk + 63) / 64;
+    const int stride = std::max(1, std::min(32, tc64 / 16));
+    if (g2.x) {
+      if (s.d == 128)
+        hipLaunchKernelGGL((bwd_gate_kernel<128, false, true>), g2, dim3(512), 0, st, s,
+                           (const bf16*)q, (const bf16*)k, lse, (uint32_t*)nullptr,
+                           (int8_t*)nullptr, n_qb, (const int8_t*)nullptr,
+                           (const int32_t*)nullptr, slots, stride);
+      else
+        hipLaunchKernelGGL((bwd_gate_kernel<64, false, true>), g2, dim3(512), 0, st, s,
+                           (const bf16*)q, (const bf16*)k, lse, (uint32_t*)nullptr,
+                           (int8_t*)nullptr, n_qb, (const int8_t*)nullptr,
+                           (const int32_t*)nullptr, slots, stride);
+    }
     hipLaunchKernelGGL(bwd_choose_kernel, dim3(1), dim3(1024), 0, st, fwd_kept,
-                       (long long)s.batch * s.hq * ftr, legal, flag);
+                       (long long)s.batch * s.hq * ftr, legal, (const uint32_t*)slots,
+                       (long long)g2.x, flag);
     take = flag;
   }
   auto launch = [&](auto gate, auto gate_nested, auto dkdv, auto dkdv_gated, auto dqk) {
@@ -1784,10 +1876,10 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
       // one walk per (key block, query head), then the sums
       if (g2.x && fwd_mask != nullptr)
         hipLaunchKernelGGL(gate_nested, g2, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
-                           lse, ws_bits, mask, n_qb, fwd_mask, take);
+                           lse, ws_bits, mask, n_qb, fwd_mask, take, (uint32_t*)nullptr, 1);
       else if (g2.x)
         hipLaunchKernelGGL(gate, g2, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k, lse,
-                           ws_bits, mask, n_qb, (const int8_t*)nullptr, take);
+                           ws_bits, mask, n_qb, (const int8_t*)nullptr, take, (uint32_t*)nullptr, 1);
       // the kept pairs of each key block choose its walks
       if (g1.x)
         hipLaunchKernelGGL(bwd_plan_kernel, g1, dim3(64), 0, st, s, (const uint32_t*)ws_bits,

@@ -196,10 +196,11 @@ def mala_bwd(q, k, v, o, lse, d_o, tau: float, causal: bool = True,
     score pass then forms only the scores of the tiles the forward kept
     (mala_bwd_nested, which runs in the gate-pass mode, so ``gate_pass`` is
     implied). ``fwd_kept``: the forward's kept-tile counters
-    (``mala_fwd(...)["kept"]``) for the same inputs; the backward then takes
-    the gate-pass walks when the forward kept fewer than 70% of its legal
-    tiles and the default walk otherwise, chosen on the device
-    (mala_bwd_auto; ``gate_pass`` must be False). ``stages``: run only these
+    (``mala_fwd(...)["kept"]``) for the same inputs; the backward then
+    chooses on the device between the gate-pass walks and the default walk,
+    from its own decisions on a sample of the key tiles, or from the
+    forward's counters when the sample is small (mala_bwd_auto; ``gate_pass``
+    must be False). ``stages``: run only these
     stages (BWD_PREP, BWD_DKDV, BWD_DQ) through mala_bwd_stage; ``events``:
     optional list of torch.cuda.Event, one recorded after each stage run."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (d_o, "d_o")):

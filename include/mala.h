@@ -204,17 +204,22 @@ mala_status mala_bwd_nested(const mala_problem* p, const void* q, const void* k,
                             int32_t* kept_tiles, void* stream);
 
 /*
- * The backward with its dK/dV walk chosen on the device from the forward's
- * kept fraction: the gate-pass walks (MALA_FLAG_GATE_PASS: the Eq. 4
- * decisions of every legal tile in a separate score pass, then only the
- * steps that hold a kept tile) when the forward kept fewer than 70% of its
- * legal tiles, else the default walk. Both recompute every legal score
- * before its decision (Sec. 2.2 "Offline Sparse Probability"; App. A.1
- * "Fused backward execution"); the result is, bit for bit, that of mala_bwd
- * with MALA_FLAG_GATE_PASS when the gate-pass walks are taken and that of
- * mala_bwd without it otherwise. The choice needs no host round trip: a
- * one-workgroup kernel reduces the counters, both walks' kernels are
- * launched, and the workgroups of the walk not taken return at once.
+ * The backward with its dK/dV walk chosen on the device: the gate-pass walks
+ * (MALA_FLAG_GATE_PASS: the Eq. 4 decisions of every legal tile in a
+ * separate score pass, then only the steps that hold a kept tile) or the
+ * default walk, whichever the step's sparsity favours. Both recompute every
+ * legal score before its decision (Sec. 2.2 "Offline Sparse Probability";
+ * App. A.1 "Fused backward execution"); the result is, bit for bit, that of
+ * mala_bwd with MALA_FLAG_GATE_PASS when the gate-pass walks are taken and
+ * that of mala_bwd without it otherwise.
+ * The rule: the Eq. 4 decisions are first taken on a sample of the key tiles
+ * (every tile below 2,048 keys; about 16 tiles per 256 query rows, at most one
+ * in 32, above). If the sample holds at least 256 legal 16-key columns, the
+ * gate-pass walks run when fewer than 60% of them are kept. Otherwise the
+ * forward's counters decide: the gate-pass walks when the forward kept fewer
+ * than 70% of its legal tiles. The choice needs no host round trip: a
+ * one-workgroup kernel reduces the counts, both walks' kernels are launched,
+ * and the workgroups of the walk not taken return at once.
  *   fwd_kept_tiles int32 [B,Hq,Tr] (device), Tr = ceil(Nq/bq) with the
  *                  forward tiling: the kept_tiles mala_fwd wrote for the same
  *                  problem, q, k and v. Required when n_q > 0.
@@ -223,7 +228,8 @@ mala_status mala_bwd_nested(const mala_problem* p, const void* q, const void* k,
  *                  workspace is mala_bwd_workspace_size of p with
  *                  MALA_FLAG_GATE_PASS added to p->flags (MALA_ERR_WORKSPACE
  *                  if smaller).
- * For MALA_F32 the counters are not read and the call is mala_bwd.
+ * For MALA_F32 nothing is sampled, the counters are not read and the call
+ * is mala_bwd.
  */
 mala_status mala_bwd_auto(const mala_problem* p, const void* q, const void* k, const void* v,
                           const void* o, const float* lse, const void* d_o,

@@ -280,50 +280,78 @@ def test_gate_pass_noncausal_and_f32():
     check_backward(x, 1.0, g, r, gate_pass=True)
 
 
-def auto_takes_gate_pass(fwd_kept, nq, nk, causal):
-    """The walk mala_bwd_auto documents: the gate-pass walks when the forward
-    kept fewer than 70% of its legal tiles (each 32-row block's tiles up to
-    the one holding its last row's last visible key)."""
+def fwd_legal_tiles(nq, nk, causal):
+    """The forward's legal tiles of one head: each 32-row block's tiles up to
+    the one holding its last row's last visible key."""
     (fbq, fbk, _), _, _ = tiling()
     legal = 0
     for i in range(-(-nq // fbq)):
         last = min(i * fbq + fbq - 1, nq - 1)
         lastkey = min(last + nk - nq, nk - 1) if causal else nk - 1
         legal += lastkey // fbk + 1 if lastkey >= 0 else 0
+    return legal
+
+
+def auto_takes_gate_pass(fwd_kept, gate_mask, nq, nk, causal):
+    """The walk mala_bwd_auto documents. Below 2,048 keys its sample is every
+    key tile, so it sees the backward's own decisions (``gate_mask``: the gate
+    pass's tile mask): with at least 256 legal 16-key columns the gate-pass
+    walks are taken when fewer than 60% of them are kept; with fewer, the
+    forward's counters decide (fewer than 70% of its legal tiles kept)."""
+    assert nk < 2048
+    gm = gate_mask.cpu().numpy()
+    legal_s, kept_s = int((gm != O.NOT_VISITED).sum()), int((gm == O.KEPT).sum())
+    if legal_s >= 256:
+        return 10 * kept_s < 6 * legal_s
     kt = fwd_kept.cpu().numpy()
-    return 10 * int(kt.sum()) < 7 * legal * kt.shape[0] * kt.shape[1]
+    return 10 * int(kt.sum()) < 7 * fwd_legal_tiles(nq, nk, causal) * kt.shape[0] * kt.shape[1]
 
 
 def assert_auto_is_chosen_walk(x, tau, causal=True, want_gate=None):
     """mala_bwd_auto against the explicit call of the walk its rule picks:
-    gradients, tile mask and kept counters equal bit for bit."""
+    gradients, tile mask and kept counters equal bit for bit. Returns the
+    walk and the forward's kept fraction."""
     m = lib()
     nq, nk = x["q"].shape[2], x["k"].shape[2]
     f = m.mala_fwd(x["q"], x["k"], x["v"], tau, causal=causal, softmax_scale=x["scale"])
-    gate = auto_takes_gate_pass(f["kept"], nq, nk, causal)
+    kw = dict(causal=causal, softmax_scale=x["scale"], want_mask=True)
+    g = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], tau, gate_pass=True, **kw)
+    d = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], tau, **kw)
+    a = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], tau, fwd_kept=f["kept"], **kw)
+    torch.cuda.synchronize()
+    gate = auto_takes_gate_pass(f["kept"], g["mask"], nq, nk, causal)
     if want_gate is not None:
         assert gate == want_gate
-    a = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], tau, causal=causal,
-                   softmax_scale=x["scale"], want_mask=True, fwd_kept=f["kept"])
-    b = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], tau, causal=causal,
-                   softmax_scale=x["scale"], want_mask=True, gate_pass=gate)
-    torch.cuda.synchronize()
+    b = g if gate else d
     for n in ("dq", "dk", "dv", "mask", "kept"):
         assert torch.equal(a[n], b[n]), (n, gate)
-    return gate
+    kt = f["kept"].cpu().numpy()
+    frac = int(kt.sum()) / (fwd_legal_tiles(nq, nk, causal) * kt.shape[0] * kt.shape[1])
+    return gate, frac
 
 
 @pytest.mark.parametrize("preset,tau,want_gate", [("sparse", 1.0, True), ("sparse", 1e-4, True),
-                                                  ("calibrated", 1.0, False),
+                                                  ("calibrated", 1.0, None),
                                                   ("sparse", 0.0, False)])
 def test_auto_walk_choice_structured(preset, tau, want_gate):
     """mala_bwd_auto on structured inputs: the sparse preset keeps about a
-    quarter of the legal tiles at 1,500 keys (the gate-pass walks), the
-    calibrated one most of them and tau = 0 all of them (the default walk).
-    Both walks are held to the oracle by the tests above, on these inputs."""
+    quarter of the legal tiles at 1,500 keys (the gate-pass walks), tau = 0
+    all of them (the default walk). Both walks are held to the oracle by the
+    tests above, on these inputs."""
     x = to_dev(W.make_structured_preset(preset, 1500, hq=8, hkv=2, d=128))
     print(f"[auto] preset={preset} tau={tau}", flush=True)
-    assert assert_auto_is_chosen_walk(x, tau, want_gate=want_gate) == want_gate
+    assert_auto_is_chosen_walk(x, tau, want_gate=want_gate)
+
+
+def test_auto_walk_choice_sinks():
+    """Mass on the sink keys and the rest of the logits flat: the forward,
+    which meets the sinks last, keeps nearly every tile, while the backward
+    keeps few. The choice follows the backward's own sampled decisions and
+    takes the gate-pass walks."""
+    x = to_dev(W.make_structured(1500, hq=8, hkv=2, d=128, window=65536))
+    print("[auto] sinks", flush=True)
+    gate, frac = assert_auto_is_chosen_walk(x, 1.0, want_gate=True)
+    assert frac > 0.7
 
 
 @pytest.mark.parametrize("shape", SHAPES)
@@ -340,6 +368,23 @@ def test_auto_walk_choice_shapes(shape):
     for causal in (True, False):
         for tau in (1e-4, 100.0):
             assert_auto_is_chosen_walk(x, tau, causal=causal)
+
+
+def test_auto_walk_f32_is_plain_backward():
+    """fp32 has one backward walk: mala_bwd_auto reads no counters and equals
+    mala_bwd bit for bit, at a tolerance that keeps few tiles and one that
+    keeps most."""
+    m = lib()
+    x = to_dev(W.make_prefill(W.CONFIGS[1], n=150, hq=4, hkv=2, d=64, planted=4))
+    for tau in (1e-4, 100.0):
+        f = m.mala_fwd(x["q"], x["k"], x["v"], tau, softmax_scale=x["scale"])
+        a = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], tau,
+                       softmax_scale=x["scale"], want_mask=True, fwd_kept=f["kept"])
+        b = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], tau,
+                       softmax_scale=x["scale"], want_mask=True)
+        torch.cuda.synchronize()
+        for n in ("dq", "dk", "dv", "mask", "kept"):
+            assert torch.equal(a[n], b[n]), (n, tau)
 
 
 def expand_fwd(fmask, shape):
@@ -675,8 +720,10 @@ def test_autograd_chunked_prefill_matches_direct_calls(mode):
     qd = q.detach()
     f = m.mala_fwd(qd, k.detach(), v.detach(), 1e-4, softmax_scale=scale,
                    want_mask=mode == "nested")
-    if mode == "auto":      # the walk the forward's kept fraction chooses
-        gp = auto_takes_gate_pass(f["kept"], 100, 356, True)
+    if mode == "auto":      # the walk the sampled backward decisions choose
+        gm = m.mala_bwd(qd, k.detach(), v.detach(), f["o"], f["lse"], do, 1e-4,
+                        softmax_scale=scale, gate_pass=True, want_mask=True)["mask"]
+        gp = auto_takes_gate_pass(f["kept"], gm, 100, 356, True)
     b = m.mala_bwd(qd, k.detach(), v.detach(), f["o"], f["lse"], do, 1e-4, softmax_scale=scale,
                    gate_pass=gp, fwd_mask=f["mask"])
     torch.cuda.synchronize()
