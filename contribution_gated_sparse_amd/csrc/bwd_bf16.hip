@@ -182,27 +182,30 @@ __device__ __forceinline__ bool walk_not_taken(const int32_t* take, int mine) {
 // Otherwise the forward's counters decide: the gate-pass walks when the
 // forward kept fewer than 70% of its legal tiles (fwd_kept: kept tiles per
 // (b, h, 32-row block), n entries; legal: the forward's legal tiles, a
-// function of the shape counted on the host). One workgroup of 1024
-// threads; each thread issues its loads of a round before it adds.
+// function of the shape counted on the host); they are read only then. One
+// workgroup of 1024 threads; each thread issues its loads of a round before
+// it adds.
 constexpr long long kMinSampleCols = 256;
+
+__device__ __forceinline__ long long block_sum_1024(long long x, long long* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  long long t = 0;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) t += red[u];
+  return t;
+}
 
 __global__ __launch_bounds__(1024) void bwd_choose_kernel(const int32_t* __restrict__ fwd_kept,
                                                           long long n, long long legal,
                                                           const uint32_t* __restrict__ counts,
                                                           long long n_slots,
                                                           int32_t* __restrict__ take) {
-  __shared__ long long red[3][16];
-  long long kept = 0, sk = 0, sl = 0;
-  for (long long x0 = 0; x0 < n; x0 += 8 * 1024) {
-    int v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const long long x = x0 + u * 1024 + threadIdx.x;
-      v[u] = x < n ? fwd_kept[x] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) kept += v[u];
-  }
+  __shared__ long long red[16];
+  long long sk = 0, sl = 0;
   for (long long x0 = 0; x0 < n_slots; x0 += 4 * 1024) {
     uint32_t a[4], c[4];
 #pragma unroll
@@ -217,28 +220,25 @@ __global__ __launch_bounds__(1024) void bwd_choose_kernel(const int32_t* __restr
       sl += c[u];
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    kept += __shfl_xor(kept, off, 64);
-    sk += __shfl_xor(sk, off, 64);
-    sl += __shfl_xor(sl, off, 64);
+  sk = block_sum_1024(sk, red);
+  sl = block_sum_1024(sl, red);
+  if (sl >= kMinSampleCols) {
+    if (threadIdx.x == 0) *take = 10 * sk < 6 * sl ? 1 : 0;
+    return;
   }
-  if ((threadIdx.x & 63) == 0) {
-    red[0][threadIdx.x >> 6] = kept;
-    red[1][threadIdx.x >> 6] = sk;
-    red[2][threadIdx.x >> 6] = sl;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    long long k = 0, a = 0, c = 0;
+  long long kept = 0;
+  for (long long x0 = 0; x0 < n; x0 += 8 * 1024) {
+    int v[8];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      k += red[0][u];
-      a += red[1][u];
-      c += red[2][u];
+    for (int u = 0; u < 8; ++u) {
+      const long long x = x0 + u * 1024 + threadIdx.x;
+      v[u] = x < n ? fwd_kept[x] : 0;
     }
-    *take = c >= kMinSampleCols ? (10 * a < 6 * c ? 1 : 0) : (10 * k < 7 * legal ? 1 : 0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) kept += v[u];
   }
+  kept = block_sum_1024(kept, red);
+  if (threadIdx.x == 0) *take = 10 * kept < 7 * legal ? 1 : 0;
 }
 
 // First 64-row step with a legal entry for the first key of 128-key block J.
@@ -831,10 +831,11 @@ struct alignas(16) GateSmem {
   bf16 k[2][64][D + 8];   // conflict-free 16-byte row reads (32x32x16 A layout)
 };
 
-// kSample (mala_bwd_auto): the same scores and votes on the tiles j with
-// j = phase (mod stride) only, where the phase varies with the workgroup;
-// nothing is written but the workgroup's counts of kept and legal 16-key
-// columns, to counts[2 blockIdx.x] and counts[2 blockIdx.x + 1].
+// kSample (mala_bwd_auto): the same scores and votes on every rowstride-th
+// 256-row block (the grid has a workgroup for each of those only) and there
+// on the tiles j with j = phase (mod stride), where the phase varies with the
+// workgroup; nothing is written but the workgroup's counts of kept and legal
+// 16-key columns, to counts[2 blockIdx.x] and counts[2 blockIdx.x + 1].
 template <int D, bool kNested, bool kSample = false>
 __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* __restrict__ Q,
                                                           const bf16* __restrict__ K,
@@ -844,7 +845,7 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
                                                           const int8_t* __restrict__ fmask,
                                                           const int32_t* __restrict__ take,
                                                           uint32_t* __restrict__ counts,
-                                                          int stride) {
+                                                          int stride, int rowstride) {
   if (walk_not_taken(take, 1)) return;
   __shared__ GateSmem<D> sm;
   constexpr int KT = D / 16;              // 16-wide k-steps of the QK contraction
@@ -857,7 +858,8 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
   const int bh_count = s.batch * s.hq;
-  const int I = n_qb - 1 - (int)(blockIdx.x / bh_count);     // longest blocks first
+  // longest blocks first
+  const int I = n_qb - 1 - (kSample ? rowstride : 1) * (int)(blockIdx.x / bh_count);
   const int bh = (int)(blockIdx.x % bh_count);
   const int b = bh / s.hq, h = bh % s.hq, hk = h / s.group;
   const size_t qrow0 = (size_t)bh * (size_t)s.nq;
@@ -1094,7 +1096,7 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_d128_kernel(Shape s, const bf
                                                                const int8_t* __restrict__ /*fmask*/,
                                                                const int32_t* __restrict__ take,
                                                                uint32_t* __restrict__ /*counts*/,
-                                                               int /*stride*/) {
+                                                               int /*stride*/, int /*rowstride*/) {
   if (walk_not_taken(take, 1)) return;
   constexpr int D = 128;
   constexpr int KT = D / 16;
@@ -1785,6 +1787,16 @@ size_t bwd_part_floats(const Shape& s) {
 
 size_t bwd_plan_entries(const Shape& s) { return (size_t)s.batch * s.hkv * ((s.nk + 127) / 128); }
 
+// the sampled gate of mala_bwd_auto: every rowstride-th 256-row block of
+// every head (about 256 workgroups, one round of the chip), one key tile in
+// `stride` of each walk (about 8 tiles); both 1 for small problems, where
+// the sample is the whole gate
+void sample_strides(const Shape& s, int* rowstride, int* stride) {
+  const long long groups = (long long)((s.nq + 255) / 256) * s.batch * s.hq;
+  *rowstride = (int)std::max(1LL, groups / 256);
+  *stride = std::max(1, ((s.nk + 63) / 64) / 16);
+}
+
 // workgroups of the query-major gate kernels: 256 rows of one head each
 size_t bwd_gate_groups(const Shape& s) { return (size_t)((s.nq + 255) / 256) * s.batch * s.hq; }
 
@@ -1843,25 +1855,27 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
     legal *= (long long)s.batch * s.hq;
     int32_t* flag = ws_plan + bwd_plan_entries(s);
     uint32_t* slots = reinterpret_cast<uint32_t*>(flag + 1);
-    // the backward's own decisions on a sample of the key tiles: about 16
-    // tiles per 256-row block, at most one in 32
-    const int tc64 = (s.nk + 63) / 64;
-    const int stride = std::max(1, std::min(32, tc64 / 16));
-    if (g2.x) {
+    // the backward's own decisions on a sample: about 256 workgroups of the
+    // gate kernel (every rowstride-th 256-row block of every head), each on
+    // about 8 key tiles of its walk (one in `stride`)
+    int rowstride, stride;
+    sample_strides(s, &rowstride, &stride);
+    const dim3 gs((unsigned)(((n_qb + rowstride - 1) / rowstride) * s.batch * s.hq));
+    if (gs.x) {
       if (s.d == 128)
-        hipLaunchKernelGGL((bwd_gate_kernel<128, false, true>), g2, dim3(512), 0, st, s,
+        hipLaunchKernelGGL((bwd_gate_kernel<128, false, true>), gs, dim3(512), 0, st, s,
                            (const bf16*)q, (const bf16*)k, lse, (uint32_t*)nullptr,
                            (int8_t*)nullptr, n_qb, (const int8_t*)nullptr,
-                           (const int32_t*)nullptr, slots, stride);
+                           (const int32_t*)nullptr, slots, stride, rowstride);
       else
-        hipLaunchKernelGGL((bwd_gate_kernel<64, false, true>), g2, dim3(512), 0, st, s,
+        hipLaunchKernelGGL((bwd_gate_kernel<64, false, true>), gs, dim3(512), 0, st, s,
                            (const bf16*)q, (const bf16*)k, lse, (uint32_t*)nullptr,
                            (int8_t*)nullptr, n_qb, (const int8_t*)nullptr,
-                           (const int32_t*)nullptr, slots, stride);
+                           (const int32_t*)nullptr, slots, stride, rowstride);
     }
     hipLaunchKernelGGL(bwd_choose_kernel, dim3(1), dim3(1024), 0, st, fwd_kept,
                        (long long)s.batch * s.hq * ftr, legal, (const uint32_t*)slots,
-                       (long long)g2.x, flag);
+                       (long long)gs.x, flag);
     take = flag;
   }
   auto launch = [&](auto gate, auto gate_nested, auto dkdv, auto dkdv_gated, auto dqk) {
@@ -1876,10 +1890,11 @@ hipError_t launch_bwd_bf16(const Shape& s, const void* q, const void* k, const v
       // one walk per (key block, query head), then the sums
       if (g2.x && fwd_mask != nullptr)
         hipLaunchKernelGGL(gate_nested, g2, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k,
-                           lse, ws_bits, mask, n_qb, fwd_mask, take, (uint32_t*)nullptr, 1);
+                           lse, ws_bits, mask, n_qb, fwd_mask, take, (uint32_t*)nullptr, 1, 1);
       else if (g2.x)
         hipLaunchKernelGGL(gate, g2, dim3(512), 0, st, s, (const bf16*)q, (const bf16*)k, lse,
-                           ws_bits, mask, n_qb, (const int8_t*)nullptr, take, (uint32_t*)nullptr, 1);
+                           ws_bits, mask, n_qb, (const int8_t*)nullptr, take, (uint32_t*)nullptr, 1,
+                           1);
       // the kept pairs of each key block choose its walks
       if (g1.x)
         hipLaunchKernelGGL(bwd_plan_kernel, g1, dim3(64), 0, st, s, (const uint32_t*)ws_bits,

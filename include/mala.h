@@ -212,9 +212,11 @@ mala_status mala_bwd_nested(const mala_problem* p, const void* q, const void* k,
  * App. A.1 "Fused backward execution"); the result is, bit for bit, that of
  * mala_bwd with MALA_FLAG_GATE_PASS when the gate-pass walks are taken and
  * that of mala_bwd without it otherwise.
- * The rule: the Eq. 4 decisions are first taken on a sample of the key tiles
- * (every tile below 2,048 keys; about 16 tiles per 256 query rows, at most one
- * in 32, above). If the sample holds at least 256 legal 16-key columns, the
+ * The rule: the Eq. 4 decisions are first taken on a sample: about 256 of
+ * the blocks of 256 query rows over all heads, and about 8 key tiles of each
+ * block's walk (the whole backward gate when there are fewer than 512 such
+ * blocks and fewer than 2,048 keys). If it holds at least 256 legal 16-key
+ * columns, the
  * gate-pass walks run when fewer than 60% of them are kept. Otherwise the
  * forward's counters decide: the gate-pass walks when the forward kept fewer
  * than 70% of its legal tiles. The choice needs no host round trip: a
