@@ -215,7 +215,7 @@ mala_status mala_bwd_nested(const mala_problem* p, const void* q, const void* k,
  * The rule: the Eq. 4 decisions are first taken on a sample: about 256 of
  * the blocks of 256 query rows over all heads, and about 8 key tiles of each
  * block's walk (the whole backward gate when there are fewer than 512 such
- * blocks and fewer than 2,048 keys). If it holds at least 256 legal 16-key
+ * blocks and at most 1,984 keys, fewer than 32 tiles of 64). If it holds at least 256 legal 16-key
  * columns, the
  * gate-pass walks run when fewer than 60% of them are kept. Otherwise the
  * forward's counters decide: the gate-pass walks when the forward kept fewer

@@ -293,13 +293,14 @@ def fwd_legal_tiles(nq, nk, causal):
 
 
 def auto_takes_gate_pass(fwd_kept, gate_mask, nq, nk, causal):
-    """The walk mala_bwd_auto documents. Below 2,048 keys its sample is every
-    key tile, so it sees the backward's own decisions (``gate_mask``: the gate
+    """The walk mala_bwd_auto documents. At these sizes (at most 1,984 keys,
+    fewer than 512 blocks of 256 rows) its sample is the whole backward gate,
+    so it sees the backward's own decisions (``gate_mask``: the gate
     pass's tile mask): with at least 256 legal 16-key columns the gate-pass
     walks are taken when fewer than 60% of them are kept; with fewer, the
     forward's counters decide (fewer than 70% of its legal tiles kept)."""
-    assert nk < 2048
     gm = gate_mask.cpu().numpy()
+    assert nk <= 1984 and gm.shape[0] * gm.shape[1] * -(-nq // 256) < 512
     legal_s, kept_s = int((gm != O.NOT_VISITED).sum()), int((gm == O.KEPT).sum())
     if legal_s >= 256:
         return 10 * kept_s < 6 * legal_s
@@ -655,9 +656,11 @@ def test_empty_query_rows():
     b = m.mala_bwd(q, k, k, out["o"], out["lse"], q, 1e-4)
     torch.cuda.synchronize()
     assert torch.count_nonzero(b["dk"]) == 0 and torch.count_nonzero(b["dv"]) == 0
-    # the gate-pass walks and the nested call write the zero dK, dV themselves
+    # the gate-pass walks, the nested call and the automatic choice (which
+    # takes the gate-pass walks without rows to sample) write the zero dK, dV
+    # themselves
     f = m.mala_fwd(q, k, k, 1e-4, want_mask=True)
-    for kw in (dict(gate_pass=True), dict(fwd_mask=f["mask"])):
+    for kw in (dict(gate_pass=True), dict(fwd_mask=f["mask"]), dict(fwd_kept=f["kept"])):
         dk = torch.full_like(k, 7.0)
         g = m.mala_bwd(q, k, k, f["o"], f["lse"], q, 1e-4, out=dict(dk=dk), **kw)
         torch.cuda.synchronize()
