@@ -149,6 +149,56 @@ NESTED_NOTE = ("outside the method: mala_bwd_nested skips the backward score rec
                "before every skip decision (App. A.1); its speedups are not the method's")
 
 
+def prefill_128k_structured(args, m, W, torch, dev, fb, bb, preset):
+    """One GPU's share of the 128K layer (B=1, 8 query / 1 KV head, d=128)
+    on the structured preset at tau = 0 and tau = 1: the forward, the default
+    backward and the backward with the walk chosen on the device
+    (mala_bwd_auto). The pages quote their 128K operator ratios at tau = 1 on
+    other hardware (context only)."""
+    (fbq, fbk), (bbq, bbk) = fb, bb
+    x = W.make_structured_preset(preset, 131072, hq=8, hkv=1, d=128, device=dev, dtype="bf16",
+                                 with_do=False)
+    q, k, v = x["q"], x["k"], x["v"]
+    do = W.rademacher(q.shape, seed=20269002, device=dev, dtype="bf16")
+    B, HQ, N, _ = q.shape
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn):
+        for _ in range(max(1, args.warmup)):
+            fn()
+        torch.cuda.synchronize()
+        t = 0.0
+        for _ in range(args.steps):
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            t += ev[0].elapsed_time(ev[1])
+        return round(t / args.steps, 3)
+
+    out = {}
+    for tau_ in (0.0, 1.0):
+        fo, bo = {}, {}
+        tf = timed(lambda: fo.update(m.mala_fwd(q, k, v, tau_, softmax_scale=x["scale"])))
+        tb = timed(lambda: bo.update(m.mala_bwd(q, k, v, fo["o"], fo["lse"], do, tau_,
+                                                softmax_scale=x["scale"])))
+        ta = timed(lambda: m.mala_bwd(q, k, v, fo["o"], fo["lse"], do, tau_,
+                                      softmax_scale=x["scale"], fwd_kept=fo["kept"]))
+        out[tau_] = dict(fwd_ms=tf, bwd_ms=tb, bwd_auto_ms=ta, slots_per_query={
+            "fwd": round(float(fo["kept"].double().sum()) * fbk * fbq / (B * HQ * N), 1),
+            "bwd": round(float(bo["kept"].double().sum()) * bbk * bbq / (B * HQ * N), 1)})
+        del fo, bo
+    z, r = out[0.0], out[1.0]
+    r["fwd_speedup"] = round(z["fwd_ms"] / r["fwd_ms"], 4)
+    r["bwd_speedup"] = round(z["bwd_ms"] / r["bwd_ms"], 4)
+    r["bwd_speedup_auto"] = round(z["bwd_ms"] / r["bwd_auto_ms"], 4)
+    r["speedup_vs_tau0"] = round((z["fwd_ms"] + z["bwd_ms"]) / (r["fwd_ms"] + r["bwd_ms"]), 4)
+    r["speedup_vs_tau0_auto"] = round((z["fwd_ms"] + z["bwd_ms"]) / (r["fwd_ms"] + r["bwd_auto_ms"]),
+                                      4)
+    del x, q, k, v, do
+    return {"shape": "B=1, 8 query / 1 KV head, d=128, L=131072", **{f"tau={t:g}": out[t] for t in out}}
+
+
 def structured_section(args, m, F, W, torch, dev, tiling, preset):
     """Extra, not part of ``value``: the same kernels on structured-logit inputs
     (sink keys, a local band, sparse retrieval keys; the named preset of
@@ -299,6 +349,10 @@ def structured_section(args, m, F, W, torch, dev, tiling, preset):
             (pre[0.0]["fwd_ms"] + pre[0.0]["bwd_ms"])
             / (pre[tau_]["fwd_ms"] + pre[tau_]["bwd_gate_pass_ms"]), 4)
         pre[tau_]["bwd_speedup_gate_pass"] = round(pre[0.0]["bwd_ms"] / pre[tau_]["bwd_gate_pass_ms"], 4)
+        pre[tau_]["speedup_vs_tau0_auto"] = round(
+            (pre[0.0]["fwd_ms"] + pre[0.0]["bwd_ms"])
+            / (pre[tau_]["fwd_ms"] + pre[tau_]["bwd_auto_ms"]), 4)
+        pre[tau_]["bwd_speedup_auto"] = round(pre[0.0]["bwd_ms"] / pre[tau_]["bwd_auto_ms"], 4)
         pre[tau_]["speedup_vs_tau0_nested"] = round(
             (pre[0.0]["fwd_ms"] + pre[0.0]["bwd_ms"])
             / (pre[tau_]["fwd_with_mask_ms"] + pre[tau_]["bwd_nested_ms"]), 4)
@@ -307,6 +361,9 @@ def structured_section(args, m, F, W, torch, dev, tiling, preset):
     del x, q, k, v, do, fo, bo, bg, fn, bn, g0
     torch.cuda.empty_cache()
     res["matched_work_8k"] = matched_work(m, F, W, torch, dev, fbq, fbk, preset)
+    torch.cuda.empty_cache()
+    res["prefill_128k"] = prefill_128k_structured(args, m, W, torch, dev, (fbq, fbk), (bbq, bbk),
+                                                  preset)
     torch.cuda.empty_cache()
 
     n = 131072
