@@ -161,7 +161,10 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
     const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dq,
     float* __restrict__ dK, float* __restrict__ dV, uint32_t* __restrict__ bits,
     int8_t* __restrict__ mask, int32_t* __restrict__ kept) {
-  using Acc = typename std::conditional<D == 64, double, float>::type;
+  // dK and dV accumulate in fp64, 64 columns per pass over the rows (two
+  // passes at d = 128, which recompute S and dP; the decisions are written
+  // in the first)
+  constexpr int DA = 64, NPASS = D / DA;
   __shared__ float kv[2][64][D + 1];
   __shared__ float qs[32][D];
   __shared__ float os[32][D];
@@ -178,15 +181,17 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
     kv[0][t][e] = key < s.nk ? K[(krow0 + key) * D + e] : 0.f;
     kv[1][t][e] = key < s.nk ? V[(krow0 + key) * D + e] : 0.f;
   }
-  Acc dk[D], dv[D];
-#pragma unroll
-  for (int e = 0; e < D; ++e) { dk[e] = 0; dv[e] = 0; }
   const int kc0 = J * 64 + 16 * qtr;           // first key of this lane's column
   int i_start = 0;
   if (s.causal) {
     const int need = J * 64 - s.offset;
     i_start = need <= 0 ? 0 : need / 32;
   }
+  for (int pass = 0; pass < NPASS; ++pass) {
+  const int ca = pass * DA;                    // first accumulated column
+  double dk[DA], dv[DA];
+#pragma unroll
+  for (int e = 0; e < DA; ++e) { dk[e] = 0.0; dv[e] = 0.0; }
   for (int hh = 0; hh < s.group; ++hh) {
     const int h = hk * s.group + hh;
     const size_t bh = (size_t)b * s.hq + h, qrow0 = bh * s.nq;
@@ -221,7 +226,7 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
         if (ok) x = fmax(x, sc[qq] - uu[qq]);
       }
       const bool keep = legal_tile && quarter_any(x >= 0.0);
-      if (legal_tile && (t & 15) == 0) {
+      if (pass == 0 && legal_tile && (t & 15) == 0) {
         const int j16 = kc0 / 16;
         if (keep) atomicOr(&bits[(bh * tr + i) * words + (j16 >> 5)], 1u << (j16 & 31));
         if (mask != nullptr) mask[(bh * tr + i) * tc + j16] = keep ? 1 : 0;
@@ -234,21 +239,22 @@ __global__ __launch_bounds__(64) void bwd_dkdv_f32_kernel(
 #pragma unroll 16
           for (int e = 0; e < D; ++e) dp = fma((double)kv[1][t][e], (double)os[qq][e], dp);
           const double ds = p * (dp - dd[qq]);
-          const Acc pa = (Acc)p, da = (Acc)ds;
 #pragma unroll
-          for (int e = 0; e < D; ++e) {
-            dv[e] += pa * (Acc)os[qq][e];
-            dk[e] += da * (Acc)qs[qq][e];
+          for (int e = 0; e < DA; ++e) {
+            dv[e] += p * (double)os[qq][ca + e];
+            dk[e] += ds * (double)qs[qq][ca + e];
           }
         }
       }
     }
   }
-  if (key >= s.nk) return;
+  if (key < s.nk) {
 #pragma unroll
-  for (int e = 0; e < D; ++e) {
-    dK[(krow0 + key) * D + e] = (float)(dk[e] * (Acc)s.scale);
-    dV[(krow0 + key) * D + e] = (float)dv[e];
+    for (int e = 0; e < DA; ++e) {
+      dK[(krow0 + key) * D + ca + e] = (float)(dk[e] * s.scale);
+      dV[(krow0 + key) * D + ca + e] = (float)dv[e];
+    }
+  }
   }
 }
 
@@ -258,7 +264,9 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
     Shape s, const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dq,
     float* __restrict__ dQ, const uint32_t* __restrict__ bits) {
-  using Acc = typename std::conditional<D == 64, double, float>::type;
+  // dQ accumulates in fp64, 64 columns per pass over the keys (two passes
+  // at d = 128, which recompute S and dP)
+  constexpr int DA = 64, NPASS = D / DA;
   __shared__ float dorow[64][D + 1];
   __shared__ float ks[16][D];
   __shared__ float vs[16][D];
@@ -272,17 +280,20 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
   const bool valid = q < s.nq;
   const int tr = (s.nq + 31) / 32, tc = (s.nk + 15) / 16, words = (tc + 31) / 32;
   float qr[D];
-  Acc dq[D];
 #pragma unroll
   for (int e = 0; e < D; ++e) {
     qr[e] = valid ? Q[(qrow0 + q) * D + e] : 0.f;
     dorow[t][e] = valid ? dO[(qrow0 + q) * D + e] : 0.f;
-    dq[e] = 0;
   }
   const double z = valid ? (double)LSE[qrow0 + q] : 0.0;
   const double dd = valid ? (double)Dq[qrow0 + q] : 0.0;
   const int i32 = min(blk * 2 + half, tr - 1);
   const uint32_t* mybits = bits + ((size_t)bh * tr + i32) * words;
+  for (int pass = 0; pass < NPASS; ++pass) {
+  const int ca = pass * DA;                    // first accumulated column
+  double dq[DA];
+#pragma unroll
+  for (int e = 0; e < DA; ++e) dq[e] = 0.0;
   for (int j = 0; j < tc; ++j) {
     __syncthreads();
     const int r = t & 15, c0 = (t >> 4) * (D / 4);
@@ -304,14 +315,16 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(
         dp = fma((double)dorow[t][e], (double)vs[k][e], dp);
       }
       const double p = exp(acc * s.scale - z);
-      const Acc ds = (Acc)(p * (dp - dd));
+      const double ds = p * (dp - dd);
 #pragma unroll
-      for (int e = 0; e < D; ++e) dq[e] += ds * (Acc)ks[k][e];
+      for (int e = 0; e < DA; ++e) dq[e] += ds * (double)ks[k][ca + e];
     }
   }
-  if (!valid) return;
+  if (valid) {
 #pragma unroll
-  for (int e = 0; e < D; ++e) dQ[(qrow0 + q) * D + e] = (float)(dq[e] * (Acc)s.scale);
+    for (int e = 0; e < DA; ++e) dQ[(qrow0 + q) * D + ca + e] = (float)(dq[e] * s.scale);
+  }
+  }
 }
 
 // ---------------------------------------------------------------- decode

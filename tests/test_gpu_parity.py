@@ -388,6 +388,42 @@ def test_auto_walk_f32_is_plain_backward():
             assert torch.equal(a[n], b[n]), (n, tau)
 
 
+def random_case(case):
+    """Seeded shape and options of one randomized parity case."""
+    rng = np.random.default_rng(20260000 + case)
+    hkv = int(rng.choice([1, 2]))
+    c = dict(d=int(rng.choice([64, 128])), hkv=hkv, hq=hkv * int(rng.choice([1, 2, 4])),
+             b=int(rng.choice([1, 2])), nk=int(rng.integers(1, 420)),
+             causal=bool(rng.random() < 0.7), tau=float(rng.choice([0.0, 1e-4, 1e-2, 1.0, 100.0])),
+             fp32=bool(rng.random() < 0.25), planted=int(rng.integers(0, 7)))
+    c["nq"] = c["nk"] if rng.random() < 0.5 else int(rng.integers(1, c["nk"] + 1))
+    return c
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_shapes(case):
+    """Seeded random problems (batch, GQA group, ragged and chunked lengths,
+    both head sizes, causal or not, the tolerance from 0 to 100, bf16 or
+    fp32): the forward, and the default, gate-pass and automatic backward,
+    each against the oracle at the same bars (the automatic one also against
+    the walk it picks, bit for bit)."""
+    c = random_case(case)
+    print(f"[random] case={case} {c}", flush=True)
+    cfg = W.CONFIGS[1] if c["fp32"] else W.CONFIGS[2]
+    x = W.make_prefill(cfg, n=c["nk"], hq=c["hq"], hkv=c["hkv"], d=c["d"], batch=c["b"],
+                       planted=c["planted"], seed=31 + case)
+    if c["nq"] < c["nk"]:
+        x["q"] = x["q"][:, :, c["nk"] - c["nq"]:].contiguous()
+        x["do"] = x["do"][:, :, c["nk"] - c["nq"]:].contiguous()
+    x = to_dev(x)
+    tau, causal = c["tau"], c["causal"]
+    g, r, _ = check_forward(x, tau, causal=causal, max_ties=4)
+    gb, _, _ = check_backward(x, tau, g, r, causal=causal)
+    check_nesting(g["mask"].cpu().numpy(), gb["mask"].cpu().numpy())
+    check_backward(x, tau, g, r, causal=causal, gate_pass=True)
+    assert_auto_is_chosen_walk(x, tau, causal=causal)
+
+
 def expand_fwd(fmask, shape):
     """The forward tile mask on the backward partition (each backward tile
     lies in one forward tile)."""
