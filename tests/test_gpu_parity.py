@@ -400,7 +400,7 @@ def random_case(case):
     return c
 
 
-@pytest.mark.parametrize("case", range(24))
+@pytest.mark.parametrize("case", range(48))
 def test_random_shapes(case):
     """Seeded random problems (batch, GQA group, ragged and chunked lengths,
     both head sizes, causal or not, the tolerance from 0 to 100, bf16 or
@@ -576,8 +576,8 @@ def check_decode(x, lens, tau, steps_q, max_ties=4, split_keys=0):
     g = m.mala_decode(q, kc, vc, seq, tau, max_n_k=max(lens), softmax_scale=x["scale"],
                       want_mask=True, split_keys=split_keys)
     torch.cuda.synchronize()
-    if split_keys == 0:
-        assert g["split"] == chunk
+    if split_keys == 0:   # 256 keys, capped at max_n_k rounded up to 64 (one split)
+        assert g["split"] == min(chunk, -(-max(lens) // 64) * 64)
     chunk = g["split"]
     gmask = g["mask"].cpu().numpy()
     r = O.mala_decode(np64(q), np64(kc), np64(vc), lens, tau, x["scale"], chunk, dbk,
@@ -655,6 +655,38 @@ def test_decode_f32_split_lengths(split_keys):
     x = {k: (v.float() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
     x = to_dev(x)
     check_decode(x, [2201, 130], 1e-4, x["q_steps"][0].contiguous(), split_keys=split_keys)
+
+
+def random_decode_case(case):
+    """Seeded shape and options of one randomized decode case."""
+    rng = np.random.default_rng(20261000 + case)
+    hkv = int(rng.choice([1, 2]))
+    cache = int(rng.integers(1, 3000))
+    c = dict(batch=int(rng.integers(1, 7)), hkv=hkv, hq=hkv * int(rng.choice([1, 2, 4, 8])),
+             cache=cache, tau=float(rng.choice([0.0, 1e-4, 1.0, 50.0])),
+             fp32=bool(rng.random() < 0.25), planted=int(rng.integers(0, 9)),
+             split=str(rng.choice(["default", "auto", "multiple", "unsplit"])),
+             mult=64 * int(rng.integers(1, 40)))
+    c["lens"] = [int(x) for x in rng.integers(1, cache + 2, size=c["batch"])]
+    return c
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_decode(case):
+    """Seeded random decode batches (ragged lengths from 1 key up, GQA groups
+    up to 8, the default, automatic, any-multiple-of-64 and one-per-sequence
+    split lengths, the tolerance from 0 to 50, bf16 or fp32) against the
+    oracle: decisions, counters, O and LSE."""
+    c = random_decode_case(case)
+    print(f"[random decode] case={case} {c}", flush=True)
+    x = W.make_decode(W.CONFIGS[5], cache=c["cache"], steps=1, batch=c["batch"], hq=c["hq"],
+                      hkv=c["hkv"], planted=c["planted"], seed=77 + case)
+    if c["fp32"]:
+        x = {k: (v.float() if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    x = to_dev(x)
+    sk = {"default": 0, "auto": lib().DECODE_SPLIT_AUTO, "multiple": c["mult"],
+          "unsplit": -(-max(c["lens"]) // 64) * 64}[c["split"]]
+    check_decode(x, c["lens"], c["tau"], x["q_steps"][0].contiguous(), split_keys=sk)
 
 
 def test_decode_clamps_out_of_range_lengths():
