@@ -59,6 +59,8 @@ BOUNDED = {
         ("test_structured_skipping_fwd_bwd", "dV"),
         ("test_structured_calibrated_fwd_bwd", "dK"), ("test_structured_calibrated_fwd_bwd", "dV"),
         ("test_random_shapes", "dK"), ("test_random_shapes", "dQ"), ("test_random_shapes", "dV"),
+        ("test_random_long_shapes", "dK"), ("test_random_long_shapes", "dQ"),
+        ("test_random_long_shapes", "dV"),
     },
     "f32": {("test_structured_skipping_fwd_bwd", "dK"), ("test_random_shapes", "dK")},
 }

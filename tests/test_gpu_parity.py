@@ -424,6 +424,44 @@ def test_random_shapes(case):
     assert_auto_is_chosen_walk(x, tau, causal=causal)
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_random_long_shapes(case):
+    """Seeded random bf16 problems of 1,000-3,000 keys (many phases of the
+    forward's and dQ's three-buffer staging, several 128-key dK/dV blocks per
+    head): the forward, the default and gate-pass backward, the nested call
+    and the single-bf16 dS of MALA_FLAG_FAST_GRAD, each against the oracle."""
+    rng = np.random.default_rng(20262000 + case)
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    nk = int(rng.integers(1000, 3000))
+    nq = nk if rng.random() < 0.6 else int(rng.integers(1, nk + 1))
+    d = int(rng.choice([64, 128]))
+    tau = float(rng.choice([1e-4, 1e-2, 1.0]))
+    print(f"[random long] case={case} hq={hq} hkv={hkv} nq={nq} nk={nk} d={d} tau={tau}",
+          flush=True)
+    x = W.make_prefill(W.CONFIGS[2], n=nk, hq=hq, hkv=hkv, d=d, batch=1,
+                       planted=int(rng.integers(0, 32)), seed=131 + case)
+    if nq < nk:
+        x["q"] = x["q"][:, :, nk - nq:].contiguous()
+        x["do"] = x["do"][:, :, nk - nq:].contiguous()
+    x = to_dev(x)
+    g, r, _ = check_forward(x, tau, max_ties=4)
+    check_backward(x, tau, g, r)
+    check_backward(x, tau, g, r, gate_pass=True)
+    check_backward(x, tau, g, r, fwd_mask=g["mask"])
+    m = lib()
+    a = m.mala_bwd(x["q"], x["k"], x["v"], g["o"], g["lse"], x["do"], tau,
+                   softmax_scale=x["scale"], want_mask=True)
+    b = m.mala_bwd(x["q"], x["k"], x["v"], g["o"], g["lse"], x["do"], tau,
+                   softmax_scale=x["scale"], want_mask=True, fast_grad=True)
+    torch.cuda.synchronize()
+    # the flag changes only dQ's dS precision: same decisions, dK and dV
+    assert torch.equal(a["mask"], b["mask"]) and torch.equal(a["dk"], b["dk"])
+    assert torch.equal(a["dv"], b["dv"])
+    u, w = np64(b["dq"]), np64(a["dq"])
+    assert np.abs(u - w).max() <= 2e-2 * max(1.0, np.abs(w).max())
+
+
 def expand_fwd(fmask, shape):
     """The forward tile mask on the backward partition (each backward tile
     lies in one forward tile)."""
