@@ -861,6 +861,15 @@ def test_staged_entry_points_match_single_calls(dtype):
     torch.cuda.synchronize()
     for name in ("dq", "dk", "dv", "mask", "kept"):
         assert torch.equal(a[name], b[name]), name
+    # the same with the gate pass, whose main stage is the gate, plan, walks
+    # and finalize
+    a = m.mala_bwd(q, k, v, f["o"], f["lse"], do, 1e-2, softmax_scale=x["scale"], want_mask=True,
+                   gate_pass=True)
+    b = m.mala_bwd(q, k, v, f["o"], f["lse"], do, 1e-2, softmax_scale=x["scale"], want_mask=True,
+                   gate_pass=True, stages=(m.mala.BWD_PREP, m.mala.BWD_DKDV, m.mala.BWD_DQ))
+    torch.cuda.synchronize()
+    for name in ("dq", "dk", "dv", "mask", "kept"):
+        assert torch.equal(a[name], b[name]), ("gate pass", name)
 
     y = W.make_decode(W.CONFIGS[5], cache=700, steps=1, batch=2, planted=4)
     y = to_dev({k: (v.to(dtype) if isinstance(v, torch.Tensor) and v.is_floating_point() else v)
