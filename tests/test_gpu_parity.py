@@ -841,6 +841,62 @@ def test_autograd_chunked_prefill_matches_direct_calls(mode):
     assert torch.equal(k.grad, b["dk"]) and torch.equal(v.grad, b["dv"])
 
 
+# ------------------------------------------------------------- graph capture
+
+def test_graph_capture_replays_match_eager():
+    """The forward, the default and the automatic backward and a decode step
+    captured in one HIP graph (torch.cuda.CUDAGraph): a call only launches
+    kernels (no allocation, memset or synchronization inside it), so every
+    replay gives the eager results bit for bit. Before each replay every
+    output and workspace is overwritten with garbage and unrelated eager
+    work runs, with synchronizations in between."""
+    m = lib()
+    x = to_dev(W.make_structured_preset("sparse", 1500, hq=8, hkv=2, d=128))
+    q, k, v, do, sc = x["q"], x["k"], x["v"], x["do"], x["scale"]
+    y = to_dev(W.make_decode(W.CONFIGS[5], cache=700, steps=1, batch=2, planted=4))
+    qd = y["q_steps"][0].contiguous()
+    seq = torch.tensor([701, 300], dtype=torch.int32, device=DEV)
+    tau = 1e-2
+
+    def step(bufs):
+        f = m.mala_fwd(q, k, v, tau, softmax_scale=sc, out=bufs["f"])
+        b = m.mala_bwd(q, k, v, f["o"], f["lse"], do, tau, softmax_scale=sc, want_mask=True,
+                       out=bufs["b"])
+        a = m.mala_bwd(q, k, v, f["o"], f["lse"], do, tau, softmax_scale=sc, want_mask=True,
+                       fwd_kept=f["kept"], out=bufs["a"])
+        d = m.mala_decode(qd, y["k_cache"], y["v_cache"], seq, tau, max_n_k=701,
+                          softmax_scale=y["scale"], want_mask=True, out=bufs["d"])
+        return dict(f=f, b=b, a=a, d=d)
+
+    eager = step({"f": {}, "b": {}, "a": {}, "d": {}})
+    torch.cuda.synchronize()
+    ref = {s_: {n: t.clone() for n, t in r.items() if isinstance(t, torch.Tensor) and n != "ws"}
+           for s_, r in eager.items()}
+    bufs = {s_: dict(r) for s_, r in eager.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(bufs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = step(bufs)
+    other = to_dev(W.make_prefill(W.CONFIGS[2], n=300, hq=2, hkv=2, planted=2, seed=5))
+    for rep in range(3):
+        for r in outs.values():
+            for n, t in r.items():
+                if isinstance(t, torch.Tensor):
+                    t.fill_(7 if t.is_floating_point() else -3)
+        m.mala_fwd(other["q"], other["k"], other["v"], 1e-4, softmax_scale=other["scale"])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for s_, r in ref.items():
+            for n, t in r.items():
+                assert torch.equal(outs[s_][n], t), (rep, s_, n)
+
+
 # ------------------------------------------------------------- staged entry points
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
