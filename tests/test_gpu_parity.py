@@ -12,8 +12,8 @@ import workloads as W
 from oracle import mala_oracle as O
 from parity_util import (BAND, add_output_rounding, assert_bitwise_where_agree, check_dq_o_rounding,
                          check_forward, check_lse, check_nesting, check_ties, compare_values,
-                         dtype_name, grad_rounding_bounds, is_bounded, np64, o_rounding_dq_term,
-                         tiling)
+                         dtype_name, grad_rounding_bounds, is_bounded, np64, o_rounding_dk_term,
+                         o_rounding_dq_term, tiling)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +33,8 @@ def to_dev(x):
 
 
 def check_backward(x, tau, g_fwd, r_fwd, causal=True, qblocks=None, key_rows=None,
-                   gate_pass=False, fwd_mask=None, max_ties=4, strict=True, dq_o_rounding=False):
+                   gate_pass=False, fwd_mask=None, max_ties=4, strict=True, dq_o_rounding=False,
+                   fro_o_rounding=False):
     m = lib()
     q, k, v, do = x["q"], x["k"], x["v"], x["do"]
     kind = dtype_name(q)
@@ -74,13 +75,26 @@ def check_backward(x, tau, g_fwd, r_fwd, causal=True, qblocks=None, key_rows=Non
                                   r_fwd, r, rows)
         check_dq_o_rounding("dQ", np64(g["dq"])[rows], r["dq"][rows], term)
     else:
+        # fro_o_rounding (bf16): the Frobenius bars of dQ and dK widened by the
+        # bf16-O rounding terms, for inputs whose gradients can be near zero
+        # (their relative error is then that rounding's); the element-wise
+        # bars stay as they are
+        ft = None
+        if fro_o_rounding and kind == "bf16":
+            ft = o_rounding_dq_term(np64(q), np64(k), np64(v), np64(do), x["scale"], causal,
+                                    r_fwd, r)
         st["dq"] = compare_values("dQ", np64(g["dq"]), r["dq"], kind, rows, strict=strict,
-                                  bound=bd["dq"])
+                                  bound=bd["dq"], fro_term=ft)
     if key_rows is not None or qblocks is None:
         kr = slice(None) if key_rows is None else key_rows
+        fk = None
+        if fro_o_rounding and kind == "bf16":
+            fk = o_rounding_dk_term(np64(q), np64(k), np64(v), np64(do), x["scale"], causal,
+                                    r_fwd, r)[:, :, kr]
         st["dk"] = compare_values("dK", np64(g["dk"])[:, :, kr], r["dk"][:, :, kr], kind,
                                   strict=strict,
-                                  bound=None if bd["dk"] is None else bd["dk"][:, :, kr])
+                                  bound=None if bd["dk"] is None else bd["dk"][:, :, kr],
+                                  fro_term=fk)
         st["dv"] = compare_values("dV", np64(g["dv"])[:, :, kr], r["dv"][:, :, kr], kind,
                                   strict=strict,
                                   bound=None if bd["dv"] is None else bd["dv"][:, :, kr])
@@ -400,7 +414,8 @@ def random_case(case):
     return c
 
 
-@pytest.mark.parametrize("case", range(48))
+# case 161: one query row, non-causal, tau = 100: dQ and dK near zero
+@pytest.mark.parametrize("case", list(range(48)) + [161])
 def test_random_shapes(case):
     """Seeded random problems (batch, GQA group, ragged and chunked lengths,
     both head sizes, causal or not, the tolerance from 0 to 100, bf16 or
@@ -418,9 +433,11 @@ def test_random_shapes(case):
     x = to_dev(x)
     tau, causal = c["tau"], c["causal"]
     g, r, _ = check_forward(x, tau, causal=causal, max_ties=4)
-    gb, _, _ = check_backward(x, tau, g, r, causal=causal)
+    # a random problem can leave dQ and dK near zero (one query row, tau =
+    # 100), where their relative Frobenius error is the bf16-O rounding of D
+    gb, _, _ = check_backward(x, tau, g, r, causal=causal, fro_o_rounding=True)
     check_nesting(g["mask"].cpu().numpy(), gb["mask"].cpu().numpy())
-    check_backward(x, tau, g, r, causal=causal, gate_pass=True)
+    check_backward(x, tau, g, r, causal=causal, gate_pass=True, fro_o_rounding=True)
     assert_auto_is_chosen_walk(x, tau, causal=causal)
 
 
