@@ -441,6 +441,37 @@ def test_random_shapes(case):
     assert_auto_is_chosen_walk(x, tau, causal=causal)
 
 
+@pytest.mark.parametrize("case", range(24))
+def test_random_structured(case):
+    """Seeded random structured-logit problems (sink logits up to 30, band
+    widths 16 to 65,536, retrieval keys up to 64 at logits up to 40, peaks up
+    to 60, tolerances 1e-4 to 100): the forward, and the default, gate-pass
+    and automatic backward, each against the oracle. dQ takes the bf16-O
+    rounding term, as on the other structured inputs: where the sink keys
+    dominate, dP - D cancels and the stored O's rounding is amplified."""
+    rng = np.random.default_rng(20263000 + case)
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4]))
+    n = int(rng.integers(100, 1600))
+    window = int(rng.choice([16, 64, 128, 512, 2048, 65536]))
+    kw = dict(hq=hq, hkv=hkv, d=128, window=window, seed=900 + case,
+              sink_logit=float(rng.choice([0.0, 8.0, 18.0, 30.0])),
+              retrieval=int(rng.choice([0, 4, 16, 64])),
+              retrieval_logit=float(rng.choice([10.0, 22.0, 40.0])),
+              peak=float(rng.choice([5.0, 25.0, 60.0])))
+    tau = float(rng.choice([1e-4, 1e-2, 1.0, 100.0]))
+    causal = bool(rng.random() < 0.8)
+    print(f"[random structured] case={case} n={n} tau={tau} causal={causal} {kw}", flush=True)
+    x = to_dev(W.make_structured(n, **kw))
+    g, r, _ = check_forward(x, tau, causal=causal, max_ties=12)
+    gb, _, _ = check_backward(x, tau, g, r, causal=causal, dq_o_rounding=True,
+                              fro_o_rounding=True, max_ties=12)
+    check_nesting(g["mask"].cpu().numpy(), gb["mask"].cpu().numpy())
+    check_backward(x, tau, g, r, causal=causal, gate_pass=True, dq_o_rounding=True,
+                   fro_o_rounding=True, max_ties=12)
+    assert_auto_is_chosen_walk(x, tau, causal=causal)
+
+
 @pytest.mark.parametrize("case", range(8))
 def test_random_long_shapes(case):
     """Seeded random bf16 problems of 1,000-3,000 keys (many phases of the
