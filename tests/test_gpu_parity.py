@@ -775,6 +775,33 @@ def test_random_decode(case):
     check_decode(x, c["lens"], c["tau"], x["q_steps"][0].contiguous(), split_keys=sk)
 
 
+@pytest.mark.parametrize("case", range(16))
+def test_random_structured_decode(case):
+    """Seeded random decode batches over structured-logit caches (sinks up to
+    logit 30, band widths 16 to 65,536, retrieval keys), each sequence's query
+    its last visible row, every split-length mode: decisions, counters, O and
+    LSE against the oracle."""
+    rng = np.random.default_rng(20264000 + case)
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    n = int(rng.integers(64, 3000))
+    b = int(rng.integers(1, 5))
+    kw = dict(hq=hq, hkv=hkv, d=128, batch=b, seed=700 + case, with_do=False,
+              window=int(rng.choice([16, 128, 1024, 65536])),
+              sink_logit=float(rng.choice([0.0, 8.0, 18.0, 30.0])),
+              retrieval=int(rng.choice([0, 16, 64])))
+    tau = float(rng.choice([1e-4, 1e-2, 1.0, 50.0]))
+    split = str(rng.choice(["default", "auto", "multiple", "unsplit"]))
+    lens = [int(v) for v in rng.integers(1, n + 1, size=b)]
+    print(f"[random structured decode] case={case} n={n} tau={tau} split={split}", flush=True)
+    x = W.make_structured(n, **kw)
+    q = torch.stack([x["q"][i, :, lens[i] - 1] for i in range(b)]).to(DEV).contiguous()
+    y = to_dev({"k_cache": x["k"], "v_cache": x["v"], "scale": x["scale"]})
+    sk = {"default": 0, "auto": lib().DECODE_SPLIT_AUTO, "multiple": 64 * int(rng.integers(1, 30)),
+          "unsplit": -(-max(lens) // 64) * 64}[split]
+    check_decode(y, lens, tau, q, split_keys=sk, max_ties=8)
+
+
 def test_decode_clamps_out_of_range_lengths():
     """seqlens_k outside [1, max_n_k] is clamped on the device (the header's
     contract): lengths 0 and 5000 with max_n_k = 701 give exactly the results
