@@ -281,6 +281,11 @@ def test_gate_pass_with_fast_grad():
     for n in ("dq", "dk", "dv"):
         u, w = np64(b[n]), np64(a[n])
         assert np.abs(u - w).max() <= 1e-2 * max(1.0, np.abs(w).max()), n
+    # the automatic choice keeps the flag: its result is one of the two fast walks
+    c = m.mala_bwd(x["q"], x["k"], x["v"], f["o"], f["lse"], x["do"], 1e-2,
+                   softmax_scale=x["scale"], want_mask=True, fast_grad=True, fwd_kept=f["kept"])
+    torch.cuda.synchronize()
+    assert any(all(torch.equal(c[n], r[n]) for n in ("dq", "dk", "dv", "mask")) for r in (a, b))
 
 
 def test_gate_pass_noncausal_and_f32():
