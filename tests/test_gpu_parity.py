@@ -482,7 +482,8 @@ def test_random_long_shapes(case):
     """Seeded random bf16 problems of 1,000-3,000 keys (many phases of the
     forward's and dQ's three-buffer staging, several 128-key dK/dV blocks per
     head): the forward, the default and gate-pass backward, the nested call
-    and the single-bf16 dS of MALA_FLAG_FAST_GRAD, each against the oracle."""
+    and the single-bf16 dS of MALA_FLAG_FAST_GRAD, each against the oracle,
+    and the automatic choice against the walk it returns."""
     rng = np.random.default_rng(20262000 + case)
     hkv = int(rng.choice([1, 2]))
     hq = hkv * int(rng.choice([1, 2, 4]))
@@ -513,6 +514,15 @@ def test_random_long_shapes(case):
     assert torch.equal(a["dv"], b["dv"])
     u, w = np64(b["dq"]), np64(a["dq"])
     assert np.abs(u - w).max() <= 2e-2 * max(1.0, np.abs(w).max())
+    # the automatic choice (a sampled gate above 1,984 keys): one of the two
+    # walks, bit for bit
+    c = m.mala_bwd(x["q"], x["k"], x["v"], g["o"], g["lse"], x["do"], tau,
+                   softmax_scale=x["scale"], want_mask=True, fwd_kept=g["kept"])
+    e = m.mala_bwd(x["q"], x["k"], x["v"], g["o"], g["lse"], x["do"], tau,
+                   softmax_scale=x["scale"], want_mask=True, gate_pass=True)
+    torch.cuda.synchronize()
+    assert any(all(torch.equal(c[n], r_[n]) for n in ("dq", "dk", "dv", "mask", "kept"))
+               for r_ in (a, e))
 
 
 def expand_fwd(fmask, shape):
