@@ -14,7 +14,8 @@ import torch
 
 import workloads as W
 from oracle import mala_oracle as O
-from parity_util import add_output_rounding, grad_rounding_bounds, tiling
+from parity_util import (add_output_rounding, grad_rounding_bounds, o_rounding_dk_term,
+                         o_rounding_dq_term, tiling)
 
 
 def _bf(a):
@@ -71,3 +72,40 @@ def test_bound_holds_and_is_tight_for_an_emulated_bf16_backward(tau, split_dq):
         # tight where the rounding terms dominate: some element comes within
         # a factor of two of its bound
         assert ratio.max() >= 0.5, (n, float(ratio.max()))
+
+
+@pytest.mark.parametrize("case", ["structured", "sinks", "one_row"])
+def test_o_rounding_terms_bound_dq_and_dk(case):
+    """The bf16-O rounding terms (o_rounding_dq_term, o_rounding_dk_term)
+    bound how far dQ and dK move when the stored O moves by up to its bf16
+    rounding: the oracle's backward on the same decisions and z, with O moved
+    by one bf16 unit in the direction that moves D = rowsum(O o dO) most, moves
+    dQ and dK within the terms on every element, and reaches a fifth of them
+    somewhere (the terms allow 4u, two units per side)."""
+    (fbq, fbk, _), (bbq, bbk, _), _ = tiling()
+    if case == "one_row":
+        # one query row, non-causal, tau = 100: dQ and dK near zero
+        x = W.make_prefill(W.CONFIGS[2], n=411, hq=2, hkv=2, d=128, planted=4, seed=192)
+        x["q"], x["do"] = x["q"][:, :, -1:], x["do"][:, :, -1:]
+        causal, tau = False, 100.0
+    else:
+        kw = {"sink_logit": 30.0} if case == "sinks" else {}
+        x = W.make_structured(300, hq=2, hkv=1, d=128, **kw)
+        causal, tau = True, 1.0
+    q, k, v, do = (x[n].float().numpy().astype(np.float64) for n in ("q", "k", "v", "do"))
+    sc = x["scale"]
+    fwd = O.mala_fwd(q, k, v, tau, sc, causal, fbq, fbk)
+    ref = O.mala_bwd(q, k, v, fwd["o"], fwd["lse"], do, tau, sc, causal, bbq, bbk,
+                     o_storage="bf16", lse_storage="f32")
+    o_ref = _bf(fwd["o"])
+    o_moved = o_ref + 2.0 ** -8 * np.abs(o_ref) * np.sign(do)
+    got = O.mala_bwd(q, k, v, o_moved, fwd["lse"], do, tau, sc, causal, bbq, bbk,
+                     lse_storage="f32", replay=ref["mask"], band=np.inf)
+    assert np.array_equal(got["mask"], ref["mask"])
+    terms = {"dq": o_rounding_dq_term(q, k, v, do, sc, causal, fwd, ref),
+             "dk": o_rounding_dk_term(q, k, v, do, sc, causal, fwd, ref)}
+    for n, t in terms.items():
+        err = np.abs(got[n] - ref[n])
+        assert (err <= t * (1 + 1e-9) + 1e-300).all(), n
+        assert float((err / np.maximum(t, 1e-300)).max()) >= 0.2, n
+
