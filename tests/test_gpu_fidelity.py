@@ -210,6 +210,8 @@ def test_peak_operator_memory_equals_dense():
             bwd=peak(lambda: m.mala_bwd(q, k, v, f["o"], f["lse"], do, tau, softmax_scale=scale)),
             gate_pass=peak(lambda: m.mala_bwd(q, k, v, f["o"], f["lse"], do, tau,
                                               softmax_scale=scale, gate_pass=True)),
+            auto=peak(lambda: m.mala_bwd(q, k, v, f["o"], f["lse"], do, tau,
+                                         softmax_scale=scale, fwd_kept=f["kept"])),
             decode=peak(lambda: m.mala_decode(qd, kc, vc, seq, tau, max_n_k=3001,
                                               softmax_scale=y["scale"])))
         del f
