@@ -102,11 +102,27 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(int rows, int d, const bf
 // form one byte of the decision bit rows (the workgroup's 8 consecutive
 // 16-key columns); it is gathered in LDS and written with one plain store by
 // the workgroup that owns it.
-template <int D>
+//
+// Row layout at D = 128. The default walk (kSwz) keeps unpadded 256-byte
+// rows with 16-byte chunk c of row r at chunk c xor f(r mod 16),
+// f(r) = r xor (2r mod 16): the 16-byte row reads and the transposing reads
+// of the 16x16x32 operand layouts both run at the conflict-free rate, and on
+// inputs where most tiles skip the walk runs about 4% faster than with padded
+// rows (gradients bit-identical). The gated walks keep padded rows of 176
+// (also conflict-free): the swizzle's per-lane chunk offsets cost them 11
+// registers and 1-2%.
+template <int D, bool kGated = false>
 struct alignas(16) DkdvSmem {
-  // row stride (bf16): 16-byte row reads and transposing reads of the
-  // 16x16x32 operand layouts both run without bank conflicts at 176 (D=128)
-  static constexpr int kStride = D == 128 ? 176 : 80;
+  static constexpr bool kSwz = D == 128 && !kGated;
+  static constexpr int kStride = kSwz ? 128 : (D == 128 ? 176 : 80);
+  // physical 16-byte chunk of chunk c in row r
+  static __device__ __forceinline__ int ch(int r, int c) {
+    if constexpr (kSwz) {
+      r &= 15;
+      return c ^ (r ^ ((2 * r) & 15));
+    }
+    return c;
+  }
   bf16 q[2][64][kStride];
   bf16 dout[2][64][kStride];
   alignas(16) float z2[2][64];  // z_q * log2 e
@@ -270,8 +286,9 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     int8_t* __restrict__ mask, float* __restrict__ part, const int32_t* __restrict__ plan,
     const int32_t* __restrict__ take) {
   if (walk_not_taken(take, kGated ? 1 : 0)) return;
-  __shared__ DkdvSmem<D> sm;
-  constexpr int ST = DkdvSmem<D>::kStride;
+  using Smem = DkdvSmem<D, kGated>;
+  __shared__ Smem sm;
+  constexpr int ST = Smem::kStride;
   constexpr int KS = D / 32;      // 32-wide k-steps over d (16x16x32 MFMA)
   constexpr int DB = D / 16;      // 16-row blocks of dK^T / dV^T
   constexpr int CPR = D / 8;      // 16-byte chunks per row
@@ -357,8 +374,8 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   auto store_step = [&](int buf, int i) {
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
-      store16(&sm.q[buf][p * RPP + srow][8 * sc], qreg[p]);
-      store16(&sm.dout[buf][p * RPP + srow][8 * sc], oreg[p]);
+      store16(&sm.q[buf][p * RPP + srow][8 * Smem::ch(p * RPP + srow, sc)], qreg[p]);
+      store16(&sm.dout[buf][p * RPP + srow][8 * Smem::ch(p * RPP + srow, sc)], oreg[p]);
     }
     if (tid < 64) {
       const int q = i * 64 + tid;
@@ -382,6 +399,12 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
   // the post-score path of one kept 32 x 16 tile (rows 32 half .. + 31 of
   // the step in LDS buffer bf; s0, s1: its scores, illegal entries -inf):
   // P, dP, dS and the dV, dK products
+  // transposing read of this lane's 8 bytes of a 32-row half (tile: its
+  // first row): row r0 + l16 / 4, columns 16 db + 4 (l16 mod 4) .. + 3
+  auto trd = [&](const bf16* tile, int r0, int db) {
+    const int r = r0 + (l16 >> 2), c = 2 * db + ((l16 & 3) >> 1);
+    return lds_read_tr_at(tile + r * ST + 8 * Smem::ch(r, c) + 4 * (l16 & 1));
+  };
   auto kept_tile = [&](int bf, int half, f32x4 s0, f32x4 s1) {
     const int lr = 32 * half;                        // first row of the half in the LDS tile
     f32x4 sh[2] = {s0, s1};
@@ -390,19 +413,17 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
     for (int t = 0; t < KS; ++t)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) orow[t][qb] = load16(&sm.dout[bf][lr + 16 * qb + l16][32 * t + 8 * g]);
+      for (int qb = 0; qb < 2; ++qb) orow[t][qb] = load16(&sm.dout[bf][lr + 16 * qb + l16][8 * Smem::ch(l16, 4 * t + g)]);
     // dO^T and Q^T, the A operands of dV^T = dO^T P and dK^T = Q^T dS,
     // through transposing reads: element e < 4 is query row 4g + e,
     // e >= 4 is row 16 + 4g + (e - 4), for column 16 db + l16.
     bf16x8 ocol[DB], qcol[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      ocol[db] = cat8(lds_read_tr(&sm.dout[bf][lr][0], ST, 4 * g, 16 * db, l16),
-                      lds_read_tr(&sm.dout[bf][lr][0], ST, 16 + 4 * g, 16 * db, l16));
+      ocol[db] = cat8(trd(&sm.dout[bf][lr][0], 4 * g, db), trd(&sm.dout[bf][lr][0], 16 + 4 * g, db));
 #pragma unroll
     for (int db = 0; db < DB; ++db)
-      qcol[db] = cat8(lds_read_tr(&sm.q[bf][lr][0], ST, 4 * g, 16 * db, l16),
-                      lds_read_tr(&sm.q[bf][lr][0], ST, 16 + 4 * g, 16 * db, l16));
+      qcol[db] = cat8(trd(&sm.q[bf][lr][0], 4 * g, db), trd(&sm.q[bf][lr][0], 16 + 4 * g, db));
     // ---- P = exp(S - z) (B operand over the 32 query rows, in the row
     // order of the transposing reads); it does not wait for dP
     bf16x8 pb, dsb;
@@ -510,7 +531,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
         for (int t = 0; t < KS; ++t)
 #pragma unroll
-          for (int qb = 0; qb < 4; ++qb) qrow[t][qb] = load16(&sm.q[buf][16 * qb + l16][32 * t + 8 * g]);
+          for (int qb = 0; qb < 4; ++qb) qrow[t][qb] = load16(&sm.q[buf][16 * qb + l16][8 * Smem::ch(l16, 4 * t + g)]);
 #pragma unroll
         for (int t = 0; t < KS; ++t)
 #pragma unroll
@@ -649,8 +670,8 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
     auto gstore = [&](const StepRegs& R, int bf) {
 #pragma unroll
       for (int p = 0; p < NPASS; ++p) {
-        store16(&sm.q[bf][p * RPP + srow][8 * sc], R.q[p]);
-        store16(&sm.dout[bf][p * RPP + srow][8 * sc], R.o[p]);
+        store16(&sm.q[bf][p * RPP + srow][8 * Smem::ch(p * RPP + srow, sc)], R.q[p]);
+        store16(&sm.dout[bf][p * RPP + srow][8 * Smem::ch(p * RPP + srow, sc)], R.o[p]);
       }
       if (tid < 64) {
         sm.z2[bf][tid] = R.z * 1.4426950408889634f;
@@ -679,7 +700,7 @@ __global__ __launch_bounds__(512, 1) __attribute__((amdgpu_waves_per_eu(2, 2))) 
 #pragma unroll
         for (int k = 0; k < KS; ++k)
 #pragma unroll
-          for (int qb = 0; qb < 4; ++qb) qrow[k][qb] = load16(&sm.q[bf][16 * qb + l16][32 * k + 8 * g]);
+          for (int qb = 0; qb < 4; ++qb) qrow[k][qb] = load16(&sm.q[bf][16 * qb + l16][8 * Smem::ch(l16, 4 * k + g)]);
 #pragma unroll
         for (int k = 0; k < KS; ++k)
 #pragma unroll
