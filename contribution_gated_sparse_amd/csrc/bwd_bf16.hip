@@ -881,7 +881,7 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_kernel(Shape s, const bf16* _
   const int bh_count = s.batch * s.hq;
   // longest blocks first
   const int I = n_qb - 1 - (kSample ? rowstride : 1) * (int)(blockIdx.x / bh_count);
-  const int bh = (int)(blockIdx.x % bh_count);
+  const int bh = xcd_head((int)(blockIdx.x % bh_count), s.batch * s.hkv, s.group);
   const int b = bh / s.hq, h = bh % s.hq, hk = h / s.group;
   const size_t qrow0 = (size_t)bh * (size_t)s.nq;
   const size_t krow0 = ((size_t)b * s.hkv + hk) * (size_t)s.nk;
@@ -1130,7 +1130,7 @@ __global__ __launch_bounds__(512, 1) void bwd_gate_d128_kernel(Shape s, const bf
   const int l32 = lane & 31, hf = lane >> 5;
   const int bh_count = s.batch * s.hq;
   const int I = n_qb - 1 - (int)(blockIdx.x / bh_count);     // longest blocks first
-  const int bh = (int)(blockIdx.x % bh_count);
+  const int bh = xcd_head((int)(blockIdx.x % bh_count), s.batch * s.hkv, s.group);
   const int b = bh / s.hq, h = bh % s.hq, hk = h / s.group;
   const size_t qrow0 = (size_t)bh * (size_t)s.nq;
   const size_t krow0 = ((size_t)b * s.hkv + hk) * (size_t)s.nk;
@@ -1303,7 +1303,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_kernel(
   const int gg = lane >> 4, i16 = lane & 15;
   const int bh_count = s.batch * s.hq;
   const int I = n_qb - 1 - (int)(blockIdx.x / bh_count);
-  const int bh = (int)(blockIdx.x % bh_count);
+  const int bh = xcd_head((int)(blockIdx.x % bh_count), s.batch * s.hkv, s.group);
   const int b = bh / s.hq, h = bh % s.hq, hk = h / s.group;
   const size_t qrow0 = (size_t)bh * (size_t)s.nq;
   const size_t krow0 = ((size_t)b * s.hkv + hk) * (size_t)s.nk;
@@ -1557,7 +1557,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dq_d128_kernel(
   const int gg = lane >> 4, i16 = lane & 15;
   const int bh_count = s.batch * s.hq;
   const int I = n_qb - 1 - (int)(blockIdx.x / bh_count);
-  const int bh = (int)(blockIdx.x % bh_count);
+  const int bh = xcd_head((int)(blockIdx.x % bh_count), s.batch * s.hkv, s.group);
   const int b = bh / s.hq, h = bh % s.hq, hk = h / s.group;
   const size_t qrow0 = (size_t)bh * (size_t)s.nq;
   const size_t krow0 = ((size_t)b * s.hkv + hk) * (size_t)s.nk;

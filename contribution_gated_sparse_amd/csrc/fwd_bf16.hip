@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_kernel(
 
   const int bh_count = s.batch * s.hq;
   const int I = n_qb - 1 - (int)(blockIdx.x / bh_count);     // longest blocks first
-  const int bh = (int)(blockIdx.x % bh_count);
+  const int bh = xcd_head((int)(blockIdx.x % bh_count), s.batch * s.hkv, s.group);
   const int b = bh / s.hq, h = bh % s.hq;
   const int hk = h / s.group;
   const size_t qrow0 = ((size_t)b * s.hq + h) * (size_t)s.nq;
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_bf16_d128_kernel(
 
   const int bh_count = s.batch * s.hq;
   const int I = n_qb - 1 - (int)(blockIdx.x / bh_count);
-  const int bh = (int)(blockIdx.x % bh_count);
+  const int bh = xcd_head((int)(blockIdx.x % bh_count), s.batch * s.hkv, s.group);
   const int b = bh / s.hq, h = bh % s.hq;
   const int hk = h / s.group;
   const size_t qrow0 = ((size_t)b * s.hq + h) * (size_t)s.nq;

@@ -92,6 +92,17 @@ namespace mala {
 
 // Buffer resource over [base, base + bytes): loads past the end return zeros,
 // which pads ragged tiles without branches.
+// Query-major grids: the (batch, query head) index bh that the workgroup at
+// position p (0 <= p < B * H_q) of a row block runs. Workgroups are dealt to
+// the 8 XCDs in turn and B * H_q is then a multiple of 8, so p mod 8 names the
+// XCD. When the B * H_kv KV heads divide by 8, the query heads of one KV head
+// all take positions of one XCD and share its L2 for their K/V stream;
+// otherwise p is bh. A bijection on [0, B * H_q).
+__device__ __forceinline__ int xcd_head(int p, int n_bkv, int group) {
+  if ((n_bkv & 7) != 0) return p;
+  const int x = p & 7, q = p >> 3;
+  return ((q / group) * 8 + x) * group + q % group;
+}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
