@@ -94,10 +94,10 @@ namespace mala {
 // which pads ragged tiles without branches.
 // Query-major grids: the (batch, query head) index bh that the workgroup at
 // position p (0 <= p < B * H_q) of a row block runs. Workgroups are dealt to
-// the 8 XCDs in turn and B * H_q is then a multiple of 8, so p mod 8 names the
-// XCD. When the B * H_kv KV heads divide by 8, the query heads of one KV head
-// all take positions of one XCD and share its L2 for their K/V stream;
-// otherwise p is bh. A bijection on [0, B * H_q).
+// the 8 XCDs in turn. When B * H_kv is a multiple of 8, so is B * H_q, and
+// p mod 8 names the workgroup's XCD: the query heads of one KV head then all
+// take positions of one XCD and share its L2 for their K/V stream. Otherwise
+// p is bh. A bijection on [0, B * H_q).
 __device__ __forceinline__ int xcd_head(int p, int n_bkv, int group) {
   if ((n_bkv & 7) != 0) return p;
   const int x = p & 7, q = p >> 3;
